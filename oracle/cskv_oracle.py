@@ -1,0 +1,317 @@
+"""CPU oracle for the DeepSeek-V4 hybrid compressed attention layer (CSA / HCA).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the package's smoke check and the
+benchmark's CPU-baseline leg may import this module. The GPU library never
+calls it and shares no code with it.
+
+Plain NumPy, float64 arithmetic on the given input values, written for a
+reader to check against the pages by eye; no blocking, fusion or reordering.
+Sources, cited by page title and section:
+
+* "Paper Breakdown: DeepSeek-V4", section 4 "Hybrid Attention: CSA + HCA
+  (§2.3)": the CSA compressor (§2.3.1, two streams, overlapped blocks of 2m
+  entries, softmax with positional biases), the lightning indexer and top-k
+  over compressed keys, MQA core attention plus the uncompressed sliding
+  window; HCA (§2.3.2, one stream, ratio 1/m', no overlap, dense attention);
+  "Additional Techniques (§2.3.3)": query/KV RMSNorm, partial RoPE on the
+  last 64 dims, sliding window, per-head attention sink logits.
+* "How DeepSeek-V4 architecture and training work together", section "Two
+  compressed views of one history": 4-to-1 pooling, 1024 selected entries
+  per query, 128-token local window.
+* "Inside DeepSeek V4", "Two compression regimes" and "Local window":
+  4x overlapping vs 128x non-overlapping blocks; every CSA and HCA layer
+  adds 128 recent uncompressed entries.
+
+Where the pages leave a step open, the plainest reading is taken; each such
+reading is named at the function that uses it.
+
+Conventions: t is an absolute token position; compressed entry i (absolute)
+covers block [m*i, m*i + m - 1]; query t sees entry i iff its block is
+complete, i.e. i < V_t = floor((t + 1) / m) (capped by the entries present).
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+
+F64 = np.float64
+
+
+# ---------------------------------------------------------------------------
+# Storage rounding (the cache stores bf16 in bf16 mode)
+# ---------------------------------------------------------------------------
+
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value (ties to even), kept as float64.
+
+    bfloat16 carries 8 significant bits and float32's exponent range; below
+    2**-126 its quantum is fixed at 2**-133.
+    """
+    x = np.asarray(x, dtype=F64)
+    _, e = np.frexp(x)
+    q = np.maximum(e - 8, -133)
+    r = np.ldexp(np.rint(np.ldexp(x, -q)), q)
+    big = np.ldexp(2.0 - 2.0 ** -8, 127)  # halfway between bf16 max and 2**128
+    r = np.where(np.abs(x) >= big, np.copysign(np.inf, x), r)
+    return np.where(np.isnan(x), np.nan, r)
+
+
+# ---------------------------------------------------------------------------
+# Query / KV RMSNorm and partial RoPE ("Additional Techniques (§2.3.3)")
+# ---------------------------------------------------------------------------
+
+def rmsnorm(x: np.ndarray, gamma: Optional[np.ndarray] = None, eps: float = 1e-6) -> np.ndarray:
+    """y = x / sqrt(mean(x^2) + eps) * gamma over the last axis.
+
+    Reading: eps = 1e-6 and gamma = 1 unless given (the pages name the norm only).
+    """
+    x = np.asarray(x, dtype=F64)
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    y = x / r
+    if gamma is not None:
+        y = y * np.asarray(gamma, dtype=F64)
+    return y
+
+
+def rope(x: np.ndarray, pos, rope_dims: int, base: float = 10000.0) -> np.ndarray:
+    """Rotate the last `rope_dims` dims of x by position `pos` (RoFormer rotary form).
+
+    Reading of "Partial RoPE (last 64 dims)": pairs (2j, 2j+1), counted from
+    the first rotated dim, turn by angle pos * base**(-2j/rope_dims). `pos`
+    broadcasts against x's leading axes.
+    """
+    x = np.array(x, dtype=F64, copy=True)
+    if rope_dims == 0:
+        return x
+    d = x.shape[-1]
+    j = np.arange(rope_dims // 2, dtype=F64)
+    theta = base ** (-2.0 * j / rope_dims)
+    ang = np.asarray(pos, dtype=F64)[..., None] * theta
+    c, s = np.cos(ang), np.sin(ang)
+    x0 = x[..., d - rope_dims + 0::2].copy()
+    x1 = x[..., d - rope_dims + 1::2].copy()
+    x[..., d - rope_dims + 0::2] = x0 * c - x1 * s
+    x[..., d - rope_dims + 1::2] = x0 * s + x1 * c
+    return x
+
+
+def _epilogue(chat, positions, apply_norm, norm_w, eps, rope_dims, rope_base):
+    e = rmsnorm(chat, norm_w, eps) if apply_norm else chat
+    return rope(e, positions, rope_dims, rope_base)
+
+
+# ---------------------------------------------------------------------------
+# KV compression ("Paper Breakdown: DeepSeek-V4", CSA §2.3.1 and HCA §2.3.2)
+# ---------------------------------------------------------------------------
+
+def csa_compress(Ca, Cb, Za, Zb, B, m: int, pos0: int = 0, prev_Cb=None, prev_Zb=None,
+                 apply_norm: bool = False, norm_w=None, eps: float = 1e-6,
+                 rope_dims: int = 0, rope_base: float = 10000.0) -> np.ndarray:
+    """Overlapped 1/m compression with two softmax-weighted streams (one sequence).
+
+    Ca, Cb, Za, Zb: [T, c]; B: [2m, c] holding B^b (rows 0..m-1) above B^a
+    (rows m..2m-1); prev_Cb / prev_Zb: [m, c], the b-stream rows of the block
+    just before row 0 (positions pos0-m .. pos0-1), or None.
+
+    Readings (the sums' ranges are lost in the pages' formula): entry i pools
+    2m entries, the m a-stream rows of its own block and the m b-stream rows
+    of the block before it, under ONE softmax per channel over the 2m logits
+    Z + B; when no preceding block exists the b-half is left out of the
+    softmax. Output entry i has absolute index pos0/m + i; its RoPE position
+    is the first token of its own block, pos0 + m*i.
+    """
+    Ca, Cb, Za, Zb, B = (np.asarray(a, dtype=F64) for a in (Ca, Cb, Za, Zb, B))
+    T, c = Ca.shape
+    assert B.shape == (2 * m, c) and pos0 % m == 0
+    n = T // m
+    out = np.zeros((n, c), dtype=F64)
+    for i in range(n):
+        a_rows = slice(m * i, m * i + m)
+        logits = [Za[a_rows] + B[m:]]
+        values = [Ca[a_rows]]
+        if i > 0:
+            b_rows = slice(m * (i - 1), m * i)
+            logits.insert(0, Zb[b_rows] + B[:m])
+            values.insert(0, Cb[b_rows])
+        elif prev_Cb is not None:
+            logits.insert(0, np.asarray(prev_Zb, dtype=F64) + B[:m])
+            values.insert(0, np.asarray(prev_Cb, dtype=F64))
+        L = np.concatenate(logits, axis=0)  # [2m or m, c]
+        Vv = np.concatenate(values, axis=0)
+        S = np.exp(L - L.max(axis=0, keepdims=True))
+        S = S / S.sum(axis=0, keepdims=True)
+        out[i] = (S * Vv).sum(axis=0)
+    pos = pos0 + m * np.arange(n)
+    return _epilogue(out, pos, apply_norm, norm_w, eps, rope_dims, rope_base)
+
+
+def csa_weights(Za, Zb, B, m: int, i: int) -> np.ndarray:
+    """The 2m (or m) softmax weights per channel used for entry i (for pins)."""
+    Za, Zb, B = (np.asarray(a, dtype=F64) for a in (Za, Zb, B))
+    L = Za[m * i:m * i + m] + B[m:]
+    if i > 0:
+        L = np.concatenate([Zb[m * (i - 1):m * i] + B[:m], L], axis=0)
+    S = np.exp(L - L.max(axis=0, keepdims=True))
+    return S / S.sum(axis=0, keepdims=True)
+
+
+def hca_compress(C, Z=None, B=None, m: int = 128, pos0: int = 0, apply_norm: bool = False,
+                 norm_w=None, eps: float = 1e-6, rope_dims: int = 0,
+                 rope_base: float = 10000.0) -> np.ndarray:
+    """Non-overlapped 1/m' compression of one stream (one sequence).
+
+    C, Z: [T, c] (Z None: uniform weights); B: [m', c] positional bias (None: 0).
+    Entry i = sum over the m' rows of block i of softmax_p(Z + B) * C, per
+    channel; RoPE position pos0 + m'*i. With m' = 1 this prepares raw
+    sliding-window rows (norm + RoPE at their own position).
+    """
+    C = np.asarray(C, dtype=F64)
+    T, c = C.shape
+    Z = np.zeros_like(C) if Z is None else np.asarray(Z, dtype=F64)
+    B = np.zeros((m, c)) if B is None else np.asarray(B, dtype=F64)
+    n = T // m
+    out = np.zeros((n, c), dtype=F64)
+    for i in range(n):
+        L = Z[m * i:m * i + m] + B
+        S = np.exp(L - L.max(axis=0, keepdims=True))
+        S = S / S.sum(axis=0, keepdims=True)
+        out[i] = (S * C[m * i:m * i + m]).sum(axis=0)
+    pos = pos0 + m * np.arange(n)
+    return _epilogue(out, pos, apply_norm, norm_w, eps, rope_dims, rope_base)
+
+
+# ---------------------------------------------------------------------------
+# Lightning indexer and top-k ("Paper Breakdown: DeepSeek-V4", CSA §2.3.1,
+# "DSA on Compressed KV (lightning indexer + top-k)")
+# ---------------------------------------------------------------------------
+
+def visible(t: int, m: int, N: int) -> int:
+    """Number of compressed entries query t may see: complete blocks only, capped at N."""
+    return min(N, (t + 1) // m)
+
+
+def indexer_scores(qI, wI, KI, pos0: int, m: int) -> np.ndarray:
+    """I[j, s] = sum_h w[j,h] * max(0, qI[j,h,:] . KI[s,:]) for s < V_t, -inf elsewhere.
+
+    qI: [Tq, HI, dI]; wI: [Tq, HI]; KI: [N, dI]; query j sits at t = pos0 + j.
+    Reading: the scoring form is a head-weighted sum of ReLU'd dot products
+    (the V3.2 lightning indexer the page names); no scale, norm or RoPE on
+    this path, since a positive scale does not change a top-k.
+    """
+    qI, wI, KI = (np.asarray(a, dtype=F64) for a in (qI, wI, KI))
+    Tq = qI.shape[0]
+    N = KI.shape[0]
+    out = np.full((Tq, N), -np.inf)
+    for j in range(Tq):
+        V = visible(pos0 + j, m, N)
+        dots = KI[:V] @ qI[j].T  # [V, HI]
+        out[j, :V] = (np.maximum(dots, 0.0) * wI[j][None, :]).sum(axis=1)
+    return out
+
+
+def topk_row(scores: np.ndarray, V: int, k: int) -> np.ndarray:
+    """The k largest of scores[:V]; ties go to the smaller index; ascending; -1 padded.
+
+    Readings: when V <= k every visible entry is selected; among equal scores
+    the smaller compressed index wins; the output lists indices in
+    ascending order.
+    """
+    out = np.full(k, -1, dtype=np.int64)
+    if V <= k:
+        out[:V] = np.arange(V)
+        return out
+    s = np.asarray(scores[:V], dtype=F64)
+    order = np.lexsort((np.arange(V), -s))  # primary key -s, then index
+    out[:] = np.sort(order[:k])
+    return out
+
+
+def indexer_topk(qI, wI, KI, pos0: int, m: int, k: int) -> np.ndarray:
+    I = indexer_scores(qI, wI, KI, pos0, m)
+    N = KI.shape[0]
+    return np.stack([topk_row(I[j], visible(pos0 + j, m, N), k) for j in range(I.shape[0])])
+
+
+# ---------------------------------------------------------------------------
+# Core MQA attention over compressed entries + sliding window + sink
+# ("Paper Breakdown: DeepSeek-V4", CSA §2.3.1, HCA §2.3.2, §2.3.3)
+# ---------------------------------------------------------------------------
+
+def prepare_query(q, t: int, apply_norm: bool, norm_w, eps, rope_dims, rope_base):
+    """RMSNorm per head, then RoPE at the query's absolute position t."""
+    x = rmsnorm(q, norm_w, eps) if apply_norm else np.asarray(q, dtype=F64)
+    return rope(x, np.full(x.shape[:-1], t), rope_dims, rope_base)
+
+
+def attend_one(qt: np.ndarray, keys: np.ndarray, sink: Optional[np.ndarray], scale: float):
+    """Softmax attention of prepared queries qt [H, d] over keys [n, d] (K = V = entry).
+
+    The sink z_h joins the denominator with a zero value vector. Returns o [H, d]
+    and lse [H] = log(exp(z_h) + sum_j exp(l_j)).
+    """
+    H = qt.shape[0]
+    z = np.full(H, -np.inf) if sink is None else np.asarray(sink, dtype=F64)
+    l = (qt @ keys.T) * scale  # [H, n]
+    M = np.maximum(z, l.max(axis=1) if l.shape[1] else -np.inf)
+    p = np.exp(l - M[:, None])
+    D = np.exp(z - M) + p.sum(axis=1)
+    o = (p @ keys) / D[:, None]
+    return o, M + np.log(D)
+
+
+def attention(q, kv, win, win_pos0: int, pos0: int, m: int, w: int, idx=None, sink=None,
+              scale: float = 0.0, apply_q_norm: bool = True, q_norm_w=None, eps: float = 1e-6,
+              rope_dims: int = 0, rope_base: float = 10000.0, rope_on_output: bool = True,
+              rows=None) -> Tuple[np.ndarray, np.ndarray]:
+    """CSA (idx given) or HCA (idx None) attention for one sequence.
+
+    q: [Tq, H, d] raw queries (query j at t = pos0 + j); kv: [N, d] compressed
+    entries as stored; win: [W, d] prepared window rows, row r at position
+    win_pos0 + r; idx: [Tq, k] selected entries (-1 = none) for CSA.
+    Key set of query t: the selected (CSA) or all V_t visible (HCA) entries,
+    plus the window rows at positions max(0, t-w+1) .. t.
+
+    Readings: scale 0 means 1/sqrt(d); no de-duplication between window rows
+    and compressed entries; "relative position on core outputs" is read as
+    rotating the output's last rope_dims dims back by -t, so that each value's
+    rotary phase becomes its position relative to the query (a flag).
+    `rows` restricts the computation to a subset of query rows (returned in
+    that order).
+    """
+    q = np.asarray(q, dtype=F64)
+    kv = np.asarray(kv, dtype=F64)
+    win = np.asarray(win, dtype=F64)
+    Tq, H, d = q.shape
+    N = kv.shape[0]
+    sc = scale if scale > 0 else 1.0 / math.sqrt(d)
+    rows = range(Tq) if rows is None else rows
+    outs, lses = [], []
+    for j in rows:
+        t = pos0 + j
+        if idx is None:
+            comp = kv[:visible(t, m, N)]
+        else:
+            sel = [int(s) for s in idx[j] if 0 <= s < N]
+            comp = kv[sel]
+        lo = max(0, t - w + 1)
+        wrows = win[lo - win_pos0:t - win_pos0 + 1]
+        keys = np.concatenate([comp, wrows], axis=0)
+        qt = prepare_query(q[j], t, apply_q_norm, q_norm_w, eps, rope_dims, rope_base)
+        o, lse = attend_one(qt, keys, sink, sc)
+        if rope_on_output:
+            o = rope(o, np.full(H, -t), rope_dims, rope_base)
+        outs.append(o)
+        lses.append(lse)
+    return np.stack(outs), np.stack(lses)
+
+
+# ---------------------------------------------------------------------------
+# Whole-layer drivers (compress -> [indexer -> top-k] -> attention)
+# ---------------------------------------------------------------------------
+
+def prepare_window(raw, win_pos0: int, apply_norm=True, norm_w=None, eps=1e-6,
+                   rope_dims=0, rope_base=10000.0) -> np.ndarray:
+    """Raw per-token KV rows -> window rows: RMSNorm + RoPE at each row's own position."""
+    return hca_compress(raw, None, None, 1, win_pos0, apply_norm, norm_w, eps, rope_dims, rope_base)

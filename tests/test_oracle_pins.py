@@ -1,0 +1,337 @@
+"""Pins for the CPU oracle: closed forms, invariants, brute force and library cross-checks.
+
+The pages print no worked numeric example, so every pin below is a value the
+definitions fix exactly (hand-derived closed forms), a property that must
+hold for any input, a brute-force recount on tiny inputs, or a cross-check
+against an independent library routine. Each is chosen so that a plausible
+slip in the oracle (swapped bias halves, a b-block off by one, a sink with a
+value vector, a wrong RoPE pairing, a transposed operand) fails at least one.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import cskv_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+# ---------------------------------------------------------------- compression
+
+def test_csa_hand_closed_form():
+    # m = 2, one channel. Entry 0 pools only its own a-block (no block before it);
+    # entry 1 pools a-rows 2,3 and b-rows 0,1 under one softmax.
+    Ca = np.array([[1.0], [2.0], [3.0], [4.0]])
+    Cb = np.array([[10.0], [20.0], [30.0], [40.0]])
+    Z = np.zeros((4, 1))
+    B = np.zeros((4, 1))
+    out = O.csa_compress(Ca, Cb, Z, Z, B, m=2)
+    assert np.allclose(out[:, 0], [1.5, (3 + 4 + 10 + 20) / 4], rtol=0, atol=1e-15)
+    # A bias of ln 2 on the first b-row (row 0 of the stacked [B^b; B^a]) doubles its weight.
+    B[0, 0] = math.log(2.0)
+    out = O.csa_compress(Ca, Cb, Z, Z, B, m=2)
+    assert np.allclose(out[:, 0], [1.5, (2 * 10 + 20 + 3 + 4) / 5], rtol=0, atol=1e-14)
+    # The same bias on the first a-row (row m) acts on entry 0 as well.
+    B[:] = 0
+    B[2, 0] = math.log(3.0)
+    out = O.csa_compress(Ca, Cb, Z, Z, B, m=2)
+    assert np.allclose(out[:, 0], [(3 * 1 + 2) / 4, (3 * 3 + 4 + 10 + 20) / 6], rtol=0, atol=1e-14)
+
+
+def test_csa_weights_sum_to_one_shift_and_onehot():
+    m, c, T = 4, 5, 32
+    Za, Zb = rng.normal(size=(T, c)) * 3, rng.normal(size=(T, c)) * 3
+    B = rng.normal(size=(2 * m, c))
+    for i in range(T // m):
+        S = O.csa_weights(Za, Zb, B, m, i)
+        assert S.shape[0] == (m if i == 0 else 2 * m)
+        assert np.allclose(S.sum(axis=0), 1.0, atol=1e-12)
+    # Constant input -> constant output (weights sum to one), for any logits.
+    ones = np.ones((T, c)) * 2.5
+    out = O.csa_compress(ones, ones, Za, Zb, B, m)
+    assert np.allclose(out, 2.5, atol=1e-12)
+    # Shift invariance: adding the same constant to all 2m logits of a block changes nothing.
+    Ca, Cb = rng.normal(size=(T, c)), rng.normal(size=(T, c))
+    base = O.csa_compress(Ca, Cb, Za, Zb, B, m)
+    assert np.allclose(O.csa_compress(Ca, Cb, Za + 7.0, Zb + 7.0, B, m), base, atol=1e-12)
+    # One-hot: a huge logit on b-row 1 of block 2 (feeding entry 3) selects that row.
+    Zb2 = Zb.copy()
+    Zb2[2 * m + 1, :] = 1e4
+    out = O.csa_compress(Ca, Cb, Za, Zb2, B, m)
+    assert np.allclose(out[3], Cb[2 * m + 1], atol=1e-12)
+    assert np.allclose(out[:3], base[:3]) and np.allclose(out[4:], base[4:])
+
+
+def test_csa_m1_identity_and_uniform_pair():
+    T, c = 9, 3
+    Ca, Cb = rng.normal(size=(T, c)), rng.normal(size=(T, c))
+    Za = rng.normal(size=(T, c))
+    B = np.zeros((2, c))
+    # b-stream masked out -> identity on C^a.
+    out = O.csa_compress(Ca, Cb, Za, np.full((T, c), -np.inf), B, m=1)
+    assert np.allclose(out, Ca, atol=1e-15)
+    # Uniform weights: (C^a_i + C^b_{i-1}) / 2, and C^a_0 for the first entry.
+    Z = np.zeros((T, c))
+    out = O.csa_compress(Ca, Cb, Z, Z, B, m=1)
+    assert np.allclose(out[0], Ca[0])
+    assert np.allclose(out[1:], (Ca[1:] + Cb[:-1]) / 2, atol=1e-15)
+
+
+def test_csa_chunk_with_tail_equals_full():
+    m, c, T = 4, 6, 40
+    Ca, Cb, Za, Zb = (rng.normal(size=(T, c)) for _ in range(4))
+    B = rng.normal(size=(2 * m, c))
+    full = O.csa_compress(Ca, Cb, Za, Zb, B, m, apply_norm=True, rope_dims=4)
+    cut = 16
+    part = O.csa_compress(Ca[cut:], Cb[cut:], Za[cut:], Zb[cut:], B, m, pos0=cut,
+                          prev_Cb=Cb[cut - m:cut], prev_Zb=Zb[cut - m:cut], apply_norm=True, rope_dims=4)
+    assert np.allclose(part, full[cut // m:], atol=1e-13)
+
+
+def test_hca_hand_closed_form_and_m1_identity():
+    C = np.array([[1.0, -2.0], [3.0, 4.0]])
+    Z = np.array([[0.0, 0.0], [math.log(3.0), 0.0]])
+    out = O.hca_compress(C, Z, None, m=2)
+    assert np.allclose(out[0], [(1 + 9) / 4, 1.0], atol=1e-15)
+    # m' = 1: the softmax runs over a single row, so any weights give the identity.
+    X = rng.normal(size=(7, 5))
+    out = O.hca_compress(X, rng.normal(size=(7, 5)) * 10, rng.normal(size=(1, 5)), m=1)
+    assert np.allclose(out, X, atol=1e-15)
+    # Trailing partial block is not emitted.
+    assert O.hca_compress(rng.normal(size=(300, 2)), None, None, m=128).shape == (2, 2)
+
+
+def test_hca_uniform_is_block_mean():
+    X = rng.normal(size=(256, 4))
+    out = O.hca_compress(X, None, None, m=128)
+    assert np.allclose(out, X.reshape(2, 128, 4).mean(axis=1), atol=1e-13)
+
+
+# ---------------------------------------------------------- RMSNorm and RoPE
+
+def test_rmsnorm_closed_form_and_unit_rms():
+    assert np.allclose(O.rmsnorm(np.array([3.0, 4.0]), eps=0.0), [3 / math.sqrt(12.5), 4 / math.sqrt(12.5)])
+    X = rng.normal(size=(10, 64)) * 5
+    Y = O.rmsnorm(X, eps=0.0)
+    assert np.allclose(np.sqrt((Y * Y).mean(axis=-1)), 1.0, atol=1e-13)
+    g = rng.uniform(size=64)
+    assert np.allclose(O.rmsnorm(X, g, eps=0.0), Y * g)
+
+
+def test_rope_matches_complex_rotation():
+    d, dr, base = 12, 8, 10000.0
+    x = rng.normal(size=(5, d))
+    pos = np.array([0, 1, 7, 100, 65536])
+    y = O.rope(x, pos, dr, base)
+    assert np.array_equal(y[:, :d - dr], x[:, :d - dr])
+    z = x[:, d - dr::2] + 1j * x[:, d - dr + 1::2]
+    j = np.arange(dr // 2)
+    z = z * np.exp(1j * pos[:, None] * base ** (-2.0 * j / dr))
+    assert np.allclose(y[:, d - dr::2], z.real, atol=1e-12)
+    assert np.allclose(y[:, d - dr + 1::2], z.imag, atol=1e-12)
+    # Hand value: pair 0 turns by pos radians.
+    v = O.rope(np.array([1.0, 0.0, 0.0, 1.0]), np.array(2), 4)
+    assert np.allclose(v, [math.cos(2), math.sin(2), -math.sin(0.02), math.cos(0.02)])
+
+
+def test_rope_norm_and_relative_position():
+    d, dr = 16, 8
+    q, k = rng.normal(size=d), rng.normal(size=d)
+    for t, s, delta in [(10, 3, 5), (1000, 999, 77), (5, 40, 123456)]:
+        a = O.rope(q, np.array(t), dr) @ O.rope(k, np.array(s), dr)
+        b = O.rope(q, np.array(t + delta), dr) @ O.rope(k, np.array(s + delta), dr)
+        assert abs(a - b) < 1e-10
+        assert abs(np.linalg.norm(O.rope(q, np.array(t), dr)) - np.linalg.norm(q)) < 1e-12
+    # Rotating by -t undoes rotating by t.
+    assert np.allclose(O.rope(O.rope(q, np.array(33), dr), np.array(-33), dr), q, atol=1e-13)
+
+
+# ------------------------------------------------------------ indexer, top-k
+
+def test_indexer_hand_closed_form():
+    qI = np.array([[[1.0, 0.0], [0.0, 1.0]]])
+    wI = np.array([[2.0, 3.0]])
+    KI = np.array([[1.0, 1.0], [-1.0, 2.0], [3.0, -1.0], [9.0, 9.0]])
+    # query at t = 2 with m = 1 sees entries 0..2, not entry 3
+    I = O.indexer_scores(qI, wI, KI, pos0=2, m=1)
+    assert np.array_equal(I[0], [5.0, 6.0, 6.0, -np.inf])
+    assert list(O.indexer_topk(qI, wI, KI, 2, 1, 2)[0]) == [1, 2]
+    assert list(O.indexer_topk(qI, wI, KI, 2, 1, 1)[0]) == [1]
+    assert list(O.indexer_topk(qI, wI, KI, 2, 1, 5)[0]) == [0, 1, 2, -1, -1]
+
+
+def test_indexer_visibility_by_complete_blocks():
+    KI = rng.normal(size=(10, 4))
+    qI = rng.normal(size=(12, 2, 4))
+    wI = rng.uniform(size=(12, 2))
+    I = O.indexer_scores(qI, wI, KI, pos0=0, m=4)
+    for t in range(12):
+        V = (t + 1) // 4
+        assert np.all(np.isfinite(I[t, :V])) and np.all(np.isneginf(I[t, V:]))
+
+
+def test_indexer_brute_force_loops():
+    Tq, HI, dI, N = 3, 3, 5, 7
+    qI = rng.integers(-3, 4, size=(Tq, HI, dI)).astype(float)
+    KI = rng.integers(-3, 4, size=(N, dI)).astype(float)
+    wI = rng.uniform(size=(Tq, HI))
+    I = O.indexer_scores(qI, wI, KI, pos0=100, m=4)
+    for t in range(Tq):
+        for s in range(N):
+            ref = 0.0
+            for h in range(HI):
+                dot = sum(qI[t, h, c] * KI[s, c] for c in range(dI))
+                ref += wI[t, h] * (dot if dot > 0 else 0.0)
+            assert abs(I[t, s] - ref) < 1e-12
+
+
+def test_topk_brute_force_with_ties():
+    for trial in range(300):
+        V = int(rng.integers(1, 14))
+        k = int(rng.integers(1, 10))
+        scores = rng.integers(0, 4, size=V).astype(float)  # many exact ties
+        got = O.topk_row(np.concatenate([scores, [-np.inf] * 3]), V, k)
+        if V <= k:
+            ref = list(range(V)) + [-1] * (k - V)
+        else:
+            ranked = sorted(range(V), key=lambda s: (-scores[s], s))
+            ref = sorted(ranked[:k])
+        assert list(got) == ref
+    # exhaustive check of the tie rule on one small case
+    scores = np.array([0.5, 2, 2, 1, 2, 0])
+    assert list(O.topk_row(scores, 6, 2)) == [1, 2]
+    assert list(O.topk_row(scores, 6, 4)) == [1, 2, 3, 4]
+    assert list(O.topk_row(scores, 2, 3)) == [0, 1, -1]
+
+
+# ------------------------------------------------------------------ attention
+
+def _mk_layer(T=24, d=16, dr=4, H=3, m=4, w=5, N=None, seed=0):
+    r = np.random.default_rng(seed)
+    N = T // m if N is None else N
+    return dict(q=r.normal(size=(T, H, d)), kv=r.normal(size=(N, d)), win=r.normal(size=(T, d)),
+                sink=r.normal(size=H), T=T, d=d, dr=dr, H=H, m=m, w=w)
+
+
+def test_attention_hand_two_keys():
+    # kv entries e0 = [1,0], e1 = [0,1]; query at t = 3, m = 2 -> both visible;
+    # window w = 1 holds one zero row; scale 1, no norm/rope; sink 0.
+    q = np.array([[[1.0, 0.0]]])
+    kv = np.array([[1.0, 0.0], [0.0, 1.0]])
+    win = np.zeros((4, 2))
+    o, lse = O.attention(q, kv, win, 0, pos0=3, m=2, w=1, sink=np.array([0.0]), scale=1.0,
+                         apply_q_norm=False, rope_dims=0, rope_on_output=False)
+    e = math.e
+    assert np.allclose(o[0, 0], [e / (e + 3), 1 / (e + 3)], atol=1e-15)
+    assert abs(lse[0, 0] - math.log(e + 3)) < 1e-15
+
+
+def test_attention_one_key_plus_sink_closed_form():
+    # t = 0, m = 4: no compressed entry visible; the window holds only row 0.
+    d = 8
+    e0 = rng.normal(size=(1, d))
+    q = rng.normal(size=(1, 2, d))
+    z = np.array([0.3, -1.2])
+    o, lse = O.attention(q, np.zeros((0, d)), e0, 0, pos0=0, m=4, w=4, sink=z, scale=0.5,
+                         apply_q_norm=False, rope_dims=0, rope_on_output=False)
+    l = (q[0] @ e0[0]) * 0.5
+    sig = 1.0 / (1.0 + np.exp(z - l))
+    assert np.allclose(o[0], sig[:, None] * e0[0][None, :], atol=1e-14)
+    assert np.allclose(lse[0], np.logaddexp(z, l), atol=1e-14)
+
+
+def test_attention_sink_scales_plain_softmax():
+    L = _mk_layer()
+    args = dict(pos0=0, m=L["m"], w=L["w"], rope_dims=L["dr"])
+    o0, lse0 = O.attention(L["q"], L["kv"], L["win"], 0, sink=None, **args)
+    o1, lse1 = O.attention(L["q"], L["kv"], L["win"], 0, sink=L["sink"], **args)
+    frac = 1.0 / (1.0 + np.exp(L["sink"][None, :] - lse0))  # share of mass left to real keys
+    assert np.allclose(o1, o0 * frac[..., None], atol=1e-13)
+    assert np.allclose(lse1, np.logaddexp(lse0, L["sink"][None, :]), atol=1e-13)
+
+
+def test_attention_no_sink_matches_torch_sdpa_fp64():
+    L = _mk_layer(T=24, d=16, dr=0, H=3, m=4, w=5)
+    T, H, d, m, w = L["T"], L["H"], L["d"], L["m"], L["w"]
+    N = L["kv"].shape[0]
+    o, _ = O.attention(L["q"], L["kv"], L["win"], 0, pos0=0, m=m, w=w, sink=None,
+                       apply_q_norm=False, rope_dims=0, rope_on_output=False)
+    keys = torch.from_numpy(np.concatenate([L["kv"], L["win"]]))  # [N + T, d]
+    mask = torch.zeros(T, N + T, dtype=torch.bool)
+    for t in range(T):
+        mask[t, :(t + 1) // m] = True
+        mask[t, N + max(0, t - w + 1):N + t + 1] = True
+    qt = torch.from_numpy(L["q"]).permute(1, 0, 2)  # [H, T, d]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qt, keys.expand(H, -1, -1), keys.expand(H, -1, -1), attn_mask=mask.expand(H, -1, -1))
+    assert np.allclose(o, ref.permute(1, 0, 2).numpy(), atol=1e-12)
+
+
+def test_csa_with_k_at_least_visible_equals_dense():
+    L = _mk_layer(T=32, N=8)
+    kw = dict(pos0=0, m=L["m"], w=L["w"], sink=L["sink"], rope_dims=L["dr"])
+    idx = np.stack([O.topk_row(np.zeros(8), O.visible(t, L["m"], 8), 8) for t in range(32)])
+    o_csa, l_csa = O.attention(L["q"], L["kv"], L["win"], 0, idx=idx, **kw)
+    o_hca, l_hca = O.attention(L["q"], L["kv"], L["win"], 0, idx=None, **kw)
+    assert np.allclose(o_csa, o_hca, atol=1e-14) and np.allclose(l_csa, l_hca, atol=1e-14)
+
+
+def test_attention_rows_with_nothing_visible_are_window_only():
+    L = _mk_layer(T=8, m=4)
+    kw = dict(pos0=0, m=4, w=L["w"], sink=L["sink"], rope_dims=L["dr"])
+    o_full, _ = O.attention(L["q"], L["kv"], L["win"], 0, **kw)
+    o_win, _ = O.attention(L["q"], np.zeros((0, L["d"])), L["win"], 0, **kw)
+    assert np.allclose(o_full[:3], o_win[:3])  # t = 0..2: V_t = 0
+    assert not np.allclose(o_full[3], o_win[3])  # t = 3 sees entry 0
+
+
+def test_attention_output_derotation_is_relative():
+    # Shifting every position (query, entries, window) by the same amount leaves
+    # logits and the de-rotated output unchanged: build the same layer twice.
+    r = np.random.default_rng(5)
+    d, dr, H, m, w = 16, 8, 2, 4, 4
+    raw_kv, raw_win, q = r.normal(size=(3, d)), r.normal(size=(8, d)), r.normal(size=(1, H, d))
+    outs = []
+    for shift in (0, 4096):
+        t = 11 + shift
+        kv = O.rope(O.rmsnorm(raw_kv), np.array([0, 4, 8]) + shift, dr)
+        win = O.rope(O.rmsnorm(raw_win), np.arange(t - 7, t + 1), dr)
+        qt = O.prepare_query(q[0], t, True, None, 1e-6, dr, 10000.0)
+        o, lse = O.attend_one(qt, np.concatenate([kv, win]), None, 0.25)
+        outs.append((O.rope(o, np.full(H, -t), dr), lse))
+    assert np.allclose(outs[0][0], outs[1][0], atol=1e-9)
+    assert np.allclose(outs[0][1], outs[1][1], atol=1e-9)
+
+
+def test_decode_row_equals_prefill_row():
+    L = _mk_layer(T=20)
+    kw = dict(m=L["m"], w=L["w"], sink=L["sink"], rope_dims=L["dr"])
+    o_all, l_all = O.attention(L["q"], L["kv"], L["win"], 0, pos0=0, **kw)
+    for t in (0, 7, 19):
+        o1, l1 = O.attention(L["q"][t:t + 1], L["kv"], L["win"], 0, pos0=t, **kw)
+        assert np.allclose(o1[0], o_all[t]) and np.allclose(l1[0], l_all[t])
+
+
+# -------------------------------------------------------------- storage type
+
+def test_round_bf16_against_torch():
+    x = np.concatenate([rng.normal(size=5000) * 10.0 ** rng.integers(-40, 38, size=5000),
+                        [0.0, -0.0, 1.0, 3.0e38, -3.3e38, 1e-41]])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    # torch rounds via float32; compare only where fp64 -> fp32 is exact enough not to double-round
+    x32 = x.astype(np.float32).astype(np.float64)
+    got = O.round_bf16(x32)
+    assert np.array_equal(got, ref)
+
+
+def test_page_constants_fixture():
+    with open(os.path.join(GOLDEN, "page_constants.json")) as f:
+        g = json.load(f)
+    assert g["csa_ratio_m"]["value"] == 4 and g["hca_ratio_m_prime"]["value"] == 128
+    assert g["topk"]["value"] == 1024 and g["window"]["value"] == 128 and g["rope_dims"]["value"] == 64
