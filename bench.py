@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Throughput of the DeepSeek-V4 hybrid compressed attention layer on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input:
+  * chunked prefill: a 4096-token chunk appended to a 524288-token context,
+    batch 2, through an interleaved CSA/HCA/CSA/HCA stack (compression of the
+    chunk, window rows, indexer scores, top-k 1024, sparse / dense MQA
+    attention with a 128-token window and sinks, 64 heads x 512);
+  * decode at 1M context: one new token per sequence, batch 8, through one
+    CSA layer (262144 cached entries, top-k 1024) and one HCA layer (8192).
+value = query tokens per second = (2 * 4096 + 8) / step time; a query token
+is counted once per layer stack. Inputs are seeded synthetic tensors already
+resident in HBM when timing starts.
+
+Prints one JSON line. `roofline` covers the dominant kernel, the bf16 MFMA
+indexer scoring of the prefill CSA layers, timed with HIP events on its
+stream over the timed region; `roofline_decode` does the same for the
+HBM-bound decode scoring. `cpu_baseline` times the CPU oracle on a bounded
+sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "query-tokens/s for CSA/HCA layer at 1M ctx (prefill+decode); % HBM/MFMA peak"
+PEAK_BF16_FLOPS = 2.5e15
+PEAK_HBM_BYTES = 8.0e12
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def visible_pairs(L) -> int:
+    """Sum over the call's queries of the visible compressed entries (indexer (t, s) pairs)."""
+    tot = 0
+    for j in range(L.T):
+        tot += min(L.N, (L.pos0 + j + 1) // L.m)
+    return tot * L.batch
+
+
+def indexer_flops(L) -> float:
+    return 2.0 * L.HI * L.dI * visible_pairs(L)
+
+
+def decode_score_bytes(L) -> float:
+    # indexer keys read once, queries + weights, fp32 score rows written
+    return L.batch * (L.N * L.dI * 2 + L.HI * L.dI * 2 + L.HI * 4 + L.N * 4)
+
+
+def cpu_baseline(prefill, decode, tp, td, budget_s: float):
+    """Time the CPU oracle on a bounded sample: whole-chunk compression plus a few query rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import cskv_oracle as O
+
+    def np64(t):
+        return t.detach().float().cpu().numpy().astype(np.float64)
+
+    def layer_rows(L, t, rows, compress: bool):
+        b = 0
+        kv = np64(t["cache.kv"][b])
+        ik = np64(t["cache.ik"][b]) if L.kind == "csa" else None
+        win = np64(t["win"][b])
+        h = {k: np64(v[b]) for k, v in t.items() if k.split(".")[-1] in ("Ca", "Cb", "Za", "Zb", "C", "Z",
+                                                                          "prevCb", "prevZb") and v.dim() == 3}
+        hb = {k: np64(v) for k, v in t.items() if k.endswith(".B")}
+        q = {r: np64(t["q"][b, r:r + 1]) for r in rows}
+        qI = {r: (np64(t["qI"][b, r:r + 1]), np64(t["wI"][b, r:r + 1])) for r in rows} if L.kind == "csa" else {}
+        raw = np64(t["win_raw"][b])
+        sink = np64(t["sink"])
+        t0 = time.perf_counter()
+        if compress and L.n_new:
+            if L.kind == "csa":
+                kv[L.n_cached:] = O.csa_compress(h["kv.Ca"], h["kv.Cb"], h["kv.Za"], h["kv.Zb"], hb["kv.B"], L.m,
+                                                 L.pos0, h.get("kv.prevCb"), h.get("kv.prevZb"), True,
+                                                 rope_dims=L.rope_dims)
+                ik[L.n_cached:] = O.csa_compress(h["ik.Ca"], h["ik.Cb"], h["ik.Za"], h["ik.Zb"], hb["ik.B"], L.m,
+                                                 L.pos0, h.get("ik.prevCb"), h.get("ik.prevZb"))
+            else:
+                kv[L.n_cached:] = O.hca_compress(h["kv.C"], h["kv.Z"], hb["kv.B"], L.m, L.pos0, True,
+                                                 rope_dims=L.rope_dims)
+            win[L.win_cached:] = O.prepare_window(raw, L.pos0, rope_dims=L.rope_dims)
+        t_comp = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for r in rows:
+            idx = None
+            if L.kind == "csa":
+                I = O.indexer_scores(qI[r][0], qI[r][1], ik, L.pos0 + r, L.m)[0]
+                idx = O.topk_row(I, O.visible(L.pos0 + r, L.m, L.N), L.k)[None]
+            O.attention(q[r], kv, win, L.win_pos0, L.pos0 + r, L.m, L.w, idx=idx, sink=sink,
+                        rope_dims=L.rope_dims)
+        return t_comp, time.perf_counter() - t0
+
+    # prefill: per-sequence chunk compression amortised over the chunk's tokens, plus n rows
+    n_pre = 4 if budget_s >= 10 else 2
+    rows = [0, 1365, 2730, 4095][:n_pre]
+    per_tok_pre = 0.0
+    for L, t in zip(prefill, tp):
+        tc, tr = layer_rows(L, t, rows, compress=True)
+        per_tok_pre += tc / L.T + tr / len(rows)
+    per_tok_dec = 0.0
+    for L, t in zip(decode, td):
+        tc, tr = layer_rows(L, t, [0], compress=True)  # decode: prepares the new token's window row
+        per_tok_dec += tc + tr
+    n_pre_tok = prefill[0].batch * prefill[0].T
+    n_dec_tok = decode[0].batch
+    value = (n_pre_tok + n_dec_tok) / (n_pre_tok * per_tok_pre + n_dec_tok * per_tok_dec)
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": value, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"sequence 0: whole-chunk compression of all 4 prefill layers amortised over the "
+                       f"chunk, plus {len(rows)} query rows through the 4-layer stack and 1 decode token "
+                       f"through the CSA+HCA decode layers; per-token times weighted by the step's "
+                       f"{n_pre_tok} prefill + {n_dec_tok} decode tokens"),
+            "seconds_per_prefill_token": per_tok_pre, "seconds_per_decode_token": per_tok_dec}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one MI355X; runs on more than one GPU are not supported "
+              "(the layer has no sharded path here).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from compressed_sparse_kv_02_amd import layer as LY
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    prefill = LY.chunked_prefill_512k()
+    decode = LY.decode_1m()
+    tp = [LY.make_inputs(L) for L in prefill]
+    td = [LY.make_inputs(L) for L in decode]
+    torch.cuda.synchronize()
+
+    ev_pool = []
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        ev_pool.append(e)
+        return e
+
+    def step(rec=None):
+        marks = {}
+        for L, t in zip(prefill, tp):
+            LY.compress_step(L, t)
+            if L.kind == "csa" and rec is not None:
+                a, b = ev(), ev()
+                a.record()
+                LY.score_step(L, t)
+                b.record()
+                rec["pre_score"].append((a, b))
+            else:
+                LY.score_step(L, t)
+            LY.topk_step(L, t)
+            LY.attend_step(L, t)
+        if rec is not None:
+            m = ev()
+            m.record()
+            rec["mid"].append(m)
+        for L, t in zip(decode, td):
+            LY.compress_step(L, t)
+            if L.kind == "csa" and rec is not None:
+                a, b = ev(), ev()
+                a.record()
+                LY.score_step(L, t)
+                b.record()
+                rec["dec_score"].append((a, b))
+            else:
+                LY.score_step(L, t)
+            LY.topk_step(L, t)
+            LY.attend_step(L, t)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    rec = {"pre_score": [], "dec_score": [], "mid": []}
+    starts = []
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        s = ev()
+        s.record()
+        starts.append(s)
+        step(rec)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    pre_ms = sum(starts[i].elapsed_time(rec["mid"][i]) for i in range(args.steps)) / args.steps
+    dec_ms = ms - pre_ms
+    n_pre = prefill[0].batch * prefill[0].T
+    n_dec = decode[0].batch
+    value = (n_pre + n_dec) / (ms / 1e3)
+
+    score_ms = sum(a.elapsed_time(b) for a, b in rec["pre_score"]) / len(rec["pre_score"])
+    fl = indexer_flops(prefill[0])
+    achieved = fl / (score_ms / 1e3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        traffic = tr.get("indexer_score_mfma_prefill", {}).get("hbm_bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                "frac": achieved * 1e12 / PEAK_BF16_FLOPS, "traffic": traffic,
+                "kernel": "indexer_score_mfma<2,8,8> (prefill CSA layers)", "avg_launch_ms": score_ms,
+                "algorithmic_flops_per_launch": fl}
+    dscore_ms = sum(a.elapsed_time(b) for a, b in rec["dec_score"]) / len(rec["dec_score"])
+    db = decode_score_bytes(decode[0])
+    dach = db / (dscore_ms / 1e3) / 1e9
+    dtraffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        dtraffic = tr.get("indexer_score_mfma_decode", {}).get("hbm_bytes_per_launch")
+    roofline_dec = {"bound": "hbm", "achieved": dach, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                    "frac": dach * 1e9 / PEAK_HBM_BYTES, "traffic": dtraffic,
+                    "kernel": "indexer_score_mfma<2,8,1> (decode CSA layer)", "avg_launch_ms": dscore_ms,
+                    "algorithmic_bytes_per_launch": db}
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "chunked_prefill_512k_b2_4layer+decode_1m_b8",
+                   "prefill": "batch 2 x 4096-token chunk at pos 524288, layers CSA/HCA/CSA/HCA, "
+                              "64 heads x 512 (RoPE 64), CSA m=4 k=1024, HCA m'=128, window 128, "
+                              "indexer 64 x 128",
+                   "decode": "batch 8 x 1 token at pos 1048576, CSA (262144 entries, k=1024) + HCA (8192)",
+                   "query_tokens_per_step": n_pre + n_dec},
+        "parts": {"prefill_ms": pre_ms, "prefill_query_tokens_per_s": n_pre / (pre_ms / 1e3),
+                  "decode_ms": dec_ms, "decode_query_tokens_per_s": n_dec / (dec_ms / 1e3)},
+        "roofline": roofline,
+        "roofline_decode": roofline_dec,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(prefill, decode, tp, td, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,17 @@
+"""MI355X (gfx950) implementation of DeepSeek-V4's hybrid compressed attention layer.
+
+The compute path is libcskv.so (hand-written HIP kernels behind a C ABI,
+include/cskv.h); `binding` marshals torch tensors into it. Importing the
+package does not load the library; the first binding call does, and fails
+loudly if it has not been built.
+"""
+from . import binding  # noqa: F401
+from .binding import (  # noqa: F401
+    csa_compress,
+    hca_compress,
+    indexer_topk,
+    indexer_scores,
+    topk_select,
+    compressed_attn_prefill,
+    compressed_attn_decode,
+)

@@ -1,0 +1,233 @@
+"""ctypes binding of libcskv.so (include/cskv.h).
+
+Argument marshalling only: every step of the layer runs in the library's
+HIP kernels. Tensors must already be on the GPU and contiguous; outputs and
+workspaces are allocated with torch (device memory and streams are the only
+things torch provides). There is no CPU fallback: a missing library or a CPU
+tensor raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcskv.so")
+
+BF16, F32 = 0, 1
+CSA, HCA = 0, 1
+EXPORTS = ("cskv_version", "cskv_status_string", "csa_compress", "hca_compress",
+           "cskv_indexer_workspace_size", "indexer_topk", "indexer_scores", "topk_select",
+           "compressed_attn_prefill",
+           "cskv_decode_workspace_size", "compressed_attn_decode")
+
+_lib = None
+
+_P, _I, _L, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+_SIGS = {
+    "cskv_version": (_I, []),
+    "cskv_status_string": (ctypes.c_char_p, [_I]),
+    "csa_compress": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _L, _I, _I, _L, _I, _P, _F, _I, _F, _P, _L, _I, _P]),
+    "hca_compress": (_I, [_P, _P, _P, _I, _L, _I, _I, _L, _I, _P, _F, _I, _F, _P, _L, _I, _P]),
+    "cskv_indexer_workspace_size": (_Z, [_I, _L, _L, _I, _I, _I]),
+    "indexer_topk": (_I, [_P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _I, _P, _P, _Z, _I, _P]),
+    "indexer_scores": (_I, [_P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _P, _L, _I, _P]),
+    "topk_select": (_I, [_P, _L, _I, _L, _L, _L, _I, _I, _P, _P]),
+    "compressed_attn_prefill": (_I, [_I, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
+                                     _I, _P, _F, _I, _F, _F, _I, _P, _P, _I, _P]),
+    "cskv_decode_workspace_size": (_Z, [_I, _L, _I, _I, _I]),
+    "compressed_attn_decode": (_I, [_I, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
+                                    _I, _P, _F, _I, _F, _F, _I, _I, _P, _Z, _P, _P, _I, _P]),
+}
+
+
+class CskvError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcskv.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise CskvError(f"{LIB_PATH} is missing: build it with __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().cskv_status_string(code).decode()
+
+
+def _check(name: str, code: int) -> None:
+    if code != 0:
+        raise CskvError(f"{name} failed: {status_string(code)} ({code})")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise CskvError("tensor is not on the GPU (the layer has no CPU path)")
+    if not t.is_contiguous():
+        raise CskvError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise CskvError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def csa_compress(Ca, Cb, Za, Zb, B, m: int, pos0: int = 0, prev_Cb=None, prev_Zb=None,
+                 apply_norm: bool = False, norm_w=None, eps: float = 1e-6, rope_dims: int = 0,
+                 rope_base: float = 10000.0, out=None, out_row0: int = 0) -> torch.Tensor:
+    """Overlapped 1/m compression of [batch, T, c] streams -> [batch, T // m, c].
+
+    With `out` given as a [batch, cap, c] cache, the entries land in rows
+    out_row0 .. out_row0 + T // m - 1 of each sequence (an in-place append).
+    """
+    batch, T, c = Ca.shape
+    if out is None:
+        out = torch.empty(batch, T // m, c, dtype=Ca.dtype, device=Ca.device)
+    _ptr(out)
+    ptr = out.data_ptr() + out_row0 * c * out.element_size()
+    _check("csa_compress", lib().csa_compress(
+        _ptr(Ca), _ptr(Cb), _ptr(Za), _ptr(Zb), _ptr(B), _ptr(prev_Cb), _ptr(prev_Zb), batch, T, c, m,
+        pos0, int(apply_norm), _ptr(norm_w), eps, rope_dims, rope_base, ptr, out.shape[1], _dtype(Ca),
+        _stream(Ca)))
+    return out
+
+
+def hca_compress(C, Z=None, B=None, m: int = 128, pos0: int = 0, apply_norm: bool = False,
+                 norm_w=None, eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 10000.0,
+                 out=None, out_row0: int = 0) -> torch.Tensor:
+    """Non-overlapped 1/m' compression of [batch, T, c] -> [batch, T // m', c] (m' = 1: window rows).
+
+    `out` / `out_row0` append in place into a [batch, cap, c] buffer, as in csa_compress.
+    """
+    batch, T, c = C.shape
+    if out is None:
+        out = torch.empty(batch, T // m, c, dtype=C.dtype, device=C.device)
+    _ptr(out)
+    ptr = out.data_ptr() + out_row0 * c * out.element_size()
+    _check("hca_compress", lib().hca_compress(
+        _ptr(C), _ptr(Z), _ptr(B), batch, T, c, m, pos0, int(apply_norm), _ptr(norm_w), eps,
+        rope_dims, rope_base, ptr, out.shape[1], _dtype(C), _stream(C)))
+    return out
+
+
+def indexer_workspace_bytes(batch: int, Tq: int, N: int, HI: int, k: int, dtype: int) -> int:
+    return int(lib().cskv_indexer_workspace_size(batch, Tq, N, HI, k, dtype))
+
+
+def indexer_topk(qI, wI, KI, pos0: int, m: int, k: int, out=None, workspace=None) -> torch.Tensor:
+    """Top-k compressed entries per query: [batch, Tq, k] int32, ascending, -1 padded."""
+    batch, Tq, HI, dI = qI.shape
+    N = KI.shape[1]
+    dt = _dtype(qI)
+    if out is None:
+        out = torch.empty(batch, Tq, k, dtype=torch.int32, device=qI.device)
+    need = indexer_workspace_bytes(batch, Tq, N, HI, k, dt)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=qI.device)
+    _check("indexer_topk", lib().indexer_topk(
+        _ptr(qI), _ptr(wI), _ptr(KI), batch, Tq, N, HI, dI, pos0, m, k, _ptr(out), _ptr(workspace),
+        workspace.numel(), dt, _stream(qI)))
+    return out
+
+
+def score_ld(N: int) -> int:
+    """Row stride used for score matrices: N rounded up to 64 entries."""
+    return max(64, (N + 63) // 64 * 64)
+
+
+def indexer_scores(qI, wI, KI, pos0: int, m: int, scores=None) -> torch.Tensor:
+    """Lightning-indexer scores [batch, Tq, ld] fp32 (valid for s < V_t)."""
+    batch, Tq, HI, dI = qI.shape
+    N = KI.shape[1]
+    if scores is None:
+        scores = torch.empty(batch, Tq, score_ld(N), dtype=torch.float32, device=qI.device)
+    _check("indexer_scores", lib().indexer_scores(
+        _ptr(qI), _ptr(wI), _ptr(KI), batch, Tq, N, HI, dI, pos0, m, _ptr(scores), scores.shape[-1],
+        _dtype(qI), _stream(qI)))
+    return scores
+
+
+def topk_select(scores, N: int, pos0: int, m: int, k: int, out=None) -> torch.Tensor:
+    """Top-k selection from a score matrix written by indexer_scores."""
+    batch, Tq, ld = scores.shape
+    if out is None:
+        out = torch.empty(batch, Tq, k, dtype=torch.int32, device=scores.device)
+    _check("topk_select", lib().topk_select(_ptr(scores), ld, batch, Tq, N, pos0, m, k, _ptr(out),
+                                            _stream(scores)))
+    return out
+
+
+def _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_norm, q_norm_w, eps,
+                 rope_dims, rope_base, scale, rope_on_output, out, lse, return_lse):
+    batch, Tq, H, d = q.shape
+    N = kv.shape[1]
+    W = win.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty(batch, Tq, H, dtype=torch.float32, device=q.device)
+    if mode == CSA:
+        k = idx.shape[2]
+    args = (mode, _ptr(q), _ptr(kv), _ptr(idx), _ptr(win), win_pos0, W, _ptr(sink), batch, Tq, N, pos0,
+            m, k, w, H, d, int(apply_q_norm), _ptr(q_norm_w), eps, rope_dims, rope_base, scale,
+            int(rope_on_output))
+    return args, out, lse
+
+
+def compressed_attn_prefill(mode: int, q, kv, idx, win, win_pos0: int, sink, pos0: int, m: int,
+                            w: int, k: int = 0, apply_q_norm: bool = True, q_norm_w=None,
+                            eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 10000.0,
+                            scale: float = 0.0, rope_on_output: bool = True, out=None, lse=None,
+                            return_lse: bool = False):
+    """CSA / HCA attention for a chunk of queries: out [batch, Tq, H, d] (and lse [batch, Tq, H])."""
+    args, out, lse = _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_norm,
+                                  q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output, out, lse,
+                                  return_lse)
+    _check("compressed_attn_prefill", lib().compressed_attn_prefill(
+        *args, _ptr(out), _ptr(lse), _dtype(q), _stream(q)))
+    return (out, lse) if return_lse else out
+
+
+def decode_workspace_bytes(batch: int, Tq: int, H: int, d: int, n_splits: int) -> int:
+    return int(lib().cskv_decode_workspace_size(batch, Tq, H, d, n_splits))
+
+
+def compressed_attn_decode(mode: int, q, kv, idx, win, win_pos0: int, sink, pos0: int, m: int,
+                           w: int, k: int = 0, apply_q_norm: bool = True, q_norm_w=None,
+                           eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 10000.0,
+                           scale: float = 0.0, rope_on_output: bool = True, n_splits: int = 0,
+                           workspace=None, out=None, lse=None, return_lse: bool = False):
+    """Split-K attention of a few new tokens against a long cache (same result as prefill)."""
+    args, out, lse = _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_norm,
+                                  q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output, out, lse,
+                                  return_lse)
+    batch, Tq, H, d = q.shape
+    need = decode_workspace_bytes(batch, Tq, H, d, n_splits)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("compressed_attn_decode", lib().compressed_attn_decode(
+        *args, n_splits, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _dtype(q), _stream(q)))
+    return (out, lse) if return_lse else out

@@ -1,0 +1,469 @@
+// Lightning indexer and per-query top-k for gfx950.
+//
+// "Paper Breakdown: DeepSeek-V4", §2.3.1 "DSA on Compressed KV (lightning
+// indexer + top-k)": every query scores every visible compressed indexer key,
+//   I[t, s] = sum_h w[t, h] * ReLU(qI[t, h, :] . KI[s, :]),
+// and keeps the k best entries ("How DeepSeek-V4 architecture and training
+// work together", "Two compressed views of one history": k = 1024).
+//
+// Scoring (bf16): a dense Q.K^T contraction on the matrix cores
+// (v_mfma_f32_32x32x16_bf16; M = 32 heads of one query, N = 32 keys,
+// K = dI), fused with the ReLU and the weighted head-sum in registers. A
+// workgroup of 8 waves holds QB queries (their q rows stay in registers as
+// MFMA A operands) and streams a span of keys through double-buffered LDS
+// tiles, so each key row fetched from HBM feeds QB queries. With QB = 1
+// (decode) the 8 waves take different key blocks and many workgroups split
+// the key range. Scores go to a caller workspace as fp32 rows.
+//
+// Selection: one 1024-thread workgroup per query row finds the exact k-th
+// largest score by a 3-pass radix select (11 + 11 + 10 bits) on an
+// order-preserving uint32 key, histogramming in LDS (the row itself is kept
+// in LDS when it fits), then compacts the winners in index order with block
+// prefix sums, so ties resolve to the smaller index and the output is
+// ascending without a sort.
+#include "device_common.h"
+#include "abi_common.h"
+
+namespace cskv {
+
+__device__ __forceinline__ int64_t visible_entries(int64_t t, int m, int64_t N) {
+  const int64_t v = (t + 1) / m;
+  return v < N ? v : N;
+}
+
+struct IdxArgs {
+  const void* qI;
+  const float* wI;
+  const void* KI;
+  float* scores;  // [batch][rows_ws][ldS]
+  int32_t* out;
+  int64_t Tq, N, pos0, ldS, span;
+  int64_t row0, nrows, rows_ws;  // query rows handled by this chunk
+  int HI, dI, m, k;
+};
+
+// ----------------------------------------------------------------------------
+// bf16 scoring on the matrix cores
+// ----------------------------------------------------------------------------
+template <int HT, int KS, int QB>
+__global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
+  constexpr int WAVES = 8;
+  constexpr int KW = WAVES / QB;       // key blocks per tile
+  constexpr int DI = 16 * KS;
+  constexpr int TILE = KW * 32;        // keys per LDS tile
+  constexpr int ROW = DI + 8;          // padded LDS row (bf16), +16 bytes vs bank conflicts
+  constexpr int CPR = DI / 8;          // 16-byte chunks per key row
+  constexpr int CHUNKS = TILE * CPR;
+  constexpr int CPT = (CHUNKS + 511) / 512;
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][TILE * ROW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int qs = wave % QB, kl = wave / QB;
+  const int b = blockIdx.z;
+  const int64_t qblk = (int64_t)gridDim.y - 1 - blockIdx.y;  // longest rows first
+  const int64_t jr = qblk * QB + qs;                        // row within chunk
+  const bool qvalid = jr < a.nrows;
+  const int64_t j = a.row0 + (qvalid ? jr : 0);
+  int64_t jl = qblk * QB + QB - 1;
+  if (jl > a.nrows - 1) jl = a.nrows - 1;
+  const int64_t vmax = visible_entries(a.pos0 + a.row0 + jl, a.m, a.N);
+  const int64_t kbeg = (int64_t)blockIdx.x * a.span;
+  int64_t kend = kbeg + a.span;
+  if (kend > vmax) kend = vmax;
+  if (kbeg >= kend) return;  // uniform for the workgroup
+  const int64_t vj = qvalid ? visible_entries(a.pos0 + j, a.m, a.N) : 0;
+
+  // A operands: lane holds head (lane % 32) of each 32-head tile, 8 dims per k-step.
+  bf16x8 qa[HT][KS];
+  float wv[HT][16];
+  {
+    const uint16_t* qp = (const uint16_t*)a.qI + ((int64_t)b * a.Tq + j) * a.HI * DI;
+    const float* wp = a.wI + ((int64_t)b * a.Tq + j) * a.HI;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = ht * 32 + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (qvalid && h < a.HI) v = *reinterpret_cast<const u32x4*>(qp + (int64_t)h * DI + ks * 16 + 8 * (lane >> 5));
+        qa[ht][ks] = __builtin_bit_cast(bf16x8, v);
+      }
+      // accumulator rows held by this lane: 8*(i/4) + 4*(lane/32) + i%4
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int hh = ht * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        wv[ht][i] = (qvalid && hh < a.HI) ? wp[hh] : 0.f;
+      }
+    }
+  }
+
+  const uint16_t* kbase = (const uint16_t*)a.KI + (int64_t)b * a.N * DI;
+  float* srow = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
+  const int64_t ntiles = (kend - kbeg + TILE - 1) / TILE;
+
+  u32x4 pre[CPT];
+  auto gload = [&](int64_t t0) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * 512;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ch < CHUNKS) {
+        const int64_t s = t0 + ch / CPR;
+        if (s < kend) v = *reinterpret_cast<const u32x4*>(kbase + s * DI + (ch % CPR) * 8);
+      }
+      pre[c] = v;
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * 512;
+      if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&kt[buf][(ch / CPR) * ROW + (ch % CPR) * 8]) = pre[c];
+    }
+  };
+
+  gload(kbeg);
+  lstore(0);
+  __syncthreads();
+  for (int64_t it = 0; it < ntiles; ++it) {
+    const int64_t t0 = kbeg + it * TILE;
+    if (it + 1 < ntiles) gload(t0 + TILE);
+    f32x16 acc[HT];
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[ht][i] = 0.f;
+    const uint16_t* kp = &kt[it & 1][(kl * 32 + (lane & 31)) * ROW + 8 * (lane >> 5)];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(kp + ks * 16);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][ks], bv, acc[ht], 0, 0, 0);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part += wv[ht][i] * fmaxf(acc[ht][i], 0.f);
+    part += __shfl_xor(part, 32, 64);
+    const int64_t s = t0 + kl * 32 + (lane & 31);
+    if (qvalid && lane < 32 && s < kend) srow[s] = s < vj ? part : -INFINITY;
+    if (it + 1 < ntiles) lstore((it + 1) & 1);
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------------------------------------
+// fp32 scoring on the vector ALUs (fp32 mode: small shapes, correctness)
+// ----------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void indexer_score_f32(IdxArgs a) {
+  extern __shared__ float qsh[];  // [HI * dI + HI]
+  const int b = blockIdx.z;
+  const int64_t jr = blockIdx.y;
+  const int64_t j = a.row0 + jr;
+  const float* qp = (const float*)a.qI + ((int64_t)b * a.Tq + j) * a.HI * a.dI;
+  const float* wp = a.wI + ((int64_t)b * a.Tq + j) * a.HI;
+  for (int i = threadIdx.x; i < a.HI * a.dI; i += blockDim.x) qsh[i] = qp[i];
+  for (int i = threadIdx.x; i < a.HI; i += blockDim.x) qsh[a.HI * a.dI + i] = wp[i];
+  __syncthreads();
+  const int64_t vj = visible_entries(a.pos0 + j, a.m, a.N);
+  const int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= vj) return;
+  const float* kp = (const float*)a.KI + ((int64_t)b * a.N + s) * a.dI;
+  float tot = 0.f;
+  for (int h = 0; h < a.HI; ++h) {
+    float dot = 0.f;
+    for (int c = 0; c < a.dI; ++c) dot = fmaf(qsh[h * a.dI + c], kp[c], dot);
+    tot += qsh[a.HI * a.dI + h] * fmaxf(dot, 0.f);
+  }
+  a.scores[((int64_t)b * a.rows_ws + jr) * a.ldS + s] = tot;
+}
+
+// ----------------------------------------------------------------------------
+// Exact top-k per row
+// ----------------------------------------------------------------------------
+constexpr int TOPK_THREADS = 1024;
+constexpr int TOPK_CACHE = 30720;  // keys kept in LDS (120 KiB)
+
+// Exclusive prefix sum over the workgroup; also returns the total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < TOPK_THREADS / 64; ++w) {
+    const int x = wsum[w];
+    if (w < wave) pre += x;
+    tot += x;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + incl - v;
+}
+
+__global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
+  __shared__ uint32_t cache[TOPK_CACHE];
+  __shared__ int hist[2048];
+  __shared__ int wsum[TOPK_THREADS / 64];
+  __shared__ int sel_bin, sel_above;
+
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y;
+  const int64_t jr = blockIdx.x;
+  const int64_t j = a.row0 + jr;
+  const int k = a.k;
+  int32_t* out = a.out + ((int64_t)b * a.Tq + j) * k;
+  const int64_t V = visible_entries(a.pos0 + j, a.m, a.N);
+  if (V <= k) {
+    for (int i = tid; i < k; i += TOPK_THREADS) out[i] = i < V ? i : -1;
+    return;
+  }
+  const float* row = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
+  const bool cached = V <= TOPK_CACHE;
+  if (cached)
+    for (int64_t s = tid; s < V; s += TOPK_THREADS) cache[s] = score_key(row[s]);
+  auto key_at = [&](int64_t s) -> uint32_t { return cached ? cache[s] : score_key(row[s]); };
+
+  uint32_t prefix = 0, pmask = 0;
+  int need = k;
+  const int shifts[3] = {21, 10, 0};
+  const int nbits[3] = {11, 11, 10};
+  for (int p = 0; p < 3; ++p) {
+    const int nb = 1 << nbits[p];
+    const uint32_t bmask = (uint32_t)nb - 1u;
+    for (int i = tid; i < 2048; i += TOPK_THREADS) hist[i] = 0;
+    __syncthreads();
+    for (int64_t s = tid; s < V; s += TOPK_THREADS) {
+      const uint32_t key = key_at(s);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shifts[p]) & bmask], 1);
+    }
+    __syncthreads();
+    // Bins in descending order; thread owns bpt consecutive ones.
+    const int bpt = nb / TOPK_THREADS;  // 2 or 1
+    int cnt[2] = {0, 0}, loc = 0;
+    for (int q = 0; q < bpt; ++q) {
+      cnt[q] = hist[nb - 1 - (tid * bpt + q)];
+      loc += cnt[q];
+    }
+    int total;
+    int above = block_exclusive_scan(loc, wsum, total);
+    for (int q = 0; q < bpt; ++q) {
+      if (above < need && need <= above + cnt[q]) {
+        sel_bin = nb - 1 - (tid * bpt + q);
+        sel_above = above;
+      }
+      above += cnt[q];
+    }
+    __syncthreads();
+    const int bin = sel_bin;
+    need -= sel_above;
+    prefix |= (uint32_t)bin << shifts[p];
+    pmask |= bmask << shifts[p];
+    __syncthreads();
+  }
+  // prefix is the k-th largest key; `need` equal keys are taken (smallest indices first).
+  const uint32_t tau = prefix;
+  int eq_taken = 0, written = 0;
+  for (int64_t base = 0; base < V; base += TOPK_THREADS) {
+    const int64_t s = base + tid;
+    uint32_t key = 0;
+    if (s < V) key = key_at(s);
+    const int gt = (s < V && key > tau) ? 1 : 0;
+    const int eq = (s < V && key == tau) ? 1 : 0;
+    int eq_tot;
+    const int eq_rank = block_exclusive_scan(eq, wsum, eq_tot);
+    const int sel = gt | (eq && (eq_taken + eq_rank) < need ? 1 : 0);
+    int sel_tot;
+    const int pos = block_exclusive_scan(sel, wsum, sel_tot);
+    if (sel) out[written + pos] = (int32_t)s;
+    eq_taken += eq_tot;
+    written += sel_tot;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Host side
+// ----------------------------------------------------------------------------
+static constexpr int64_t SCORE_CHUNK_BYTES = (int64_t)128 << 20;
+
+struct IdxPlan {
+  int64_t ldS, rows_ws, qb;
+};
+
+static IdxPlan plan_indexer(int batch, int64_t Tq, int64_t N, int dtype) {
+  IdxPlan p;
+  p.ldS = round_up(N > 0 ? N : 1, 64);
+  p.qb = (dtype == CSKV_BF16 && Tq >= 64) ? 8 : 1;
+  int64_t rows = SCORE_CHUNK_BYTES / (p.ldS * 4 * (batch > 0 ? batch : 1));
+  // enough rows per chunk to fill the GPU with selection workgroups
+  if (rows < 2048 / (batch > 0 ? batch : 1)) rows = 2048 / (batch > 0 ? batch : 1);
+  if (rows < p.qb) rows = p.qb;
+  rows = (rows / p.qb) * p.qb;
+  if (rows > 32768) rows = 32768;
+  if (rows > Tq) rows = Tq;
+  p.rows_ws = rows > 0 ? rows : 1;
+  return p;
+}
+
+template <int HT, int KS, int QB>
+static void launch_mfma(const IdxArgs& a, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((indexer_score_mfma<HT, KS, QB>), grid, dim3(512), 0, st, a);
+}
+
+template <int HT, int QB>
+static bool dispatch_ks(int ks, const IdxArgs& a, dim3 grid, hipStream_t st) {
+  switch (ks) {
+    case 2: launch_mfma<HT, 2, QB>(a, grid, st); return true;
+    case 4: launch_mfma<HT, 4, QB>(a, grid, st); return true;
+    case 8: launch_mfma<HT, 8, QB>(a, grid, st); return true;
+    default: return false;
+  }
+}
+
+template <int QB>
+static bool dispatch_mfma(int ht, int ks, const IdxArgs& a, dim3 grid, hipStream_t st) {
+  switch (ht) {
+    case 1: return dispatch_ks<1, QB>(ks, a, grid, st);
+    case 2: return dispatch_ks<2, QB>(ks, a, grid, st);
+    case 4: return dispatch_ks<4, QB>(ks, a, grid, st);
+    default: return false;
+  }
+}
+
+static bool mfma_shape_ok(int HI, int dI) {
+  const int ht = HI <= 32 ? 1 : (HI <= 64 ? 2 : 4);
+  const int ks = dI / 16;
+  if (dI % 16 != 0) return false;
+  (void)ht;
+  return ks == 2 || ks == 4 || ks == 8;
+}
+
+
+// Launch the scoring kernel for rows [a.row0, a.row0 + a.nrows) into a.scores.
+static int launch_scores(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st) {
+  const int64_t last = a.pos0 + a.row0 + a.nrows - 1;
+  int64_t vmax = (last + 1) / a.m;
+  if (vmax > a.N) vmax = a.N;
+  if (vmax <= 0) return CSKV_OK;
+  if (dtype == CSKV_BF16) {
+    const int64_t qblocks = ceil_div(a.nrows, qb);
+    const int64_t tile = (8 / qb) * 32;
+    int64_t splits = ceil_div(1024, qblocks * batch);
+    if (splits < 1) splits = 1;
+    a.span = round_up(ceil_div(vmax, splits), tile);
+    splits = ceil_div(vmax, a.span);
+    dim3 grid((unsigned)splits, (unsigned)qblocks, (unsigned)batch);
+    const int ht = a.HI <= 32 ? 1 : (a.HI <= 64 ? 2 : 4);
+    bool ok = qb == 8 ? dispatch_mfma<8>(ht, a.dI / 16, a, grid, st) : dispatch_mfma<1>(ht, a.dI / 16, a, grid, st);
+    if (!ok) return CSKV_ERR_UNSUPPORTED;
+  } else {
+    dim3 grid((unsigned)ceil_div(vmax, 256), (unsigned)a.nrows, (unsigned)batch);
+    const size_t shm = ((size_t)a.HI * a.dI + a.HI) * 4;
+    hipLaunchKernelGGL(indexer_score_f32, grid, dim3(256), shm, st, a);
+  }
+  return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+}
+
+static int launch_select(IdxArgs& a, int batch, hipStream_t st) {
+  hipLaunchKernelGGL(topk_select, dim3((unsigned)a.nrows, (unsigned)batch), dim3(TOPK_THREADS), 0, st, a);
+  return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+}
+
+static int check_indexer_shape(int batch, int64_t Tq, int64_t N, int HI, int dI, int64_t pos0, int m, int dtype) {
+  if (dtype != CSKV_BF16 && dtype != CSKV_F32) return CSKV_ERR_BAD_DTYPE;
+  if (batch < 0 || Tq < 0 || N < 0 || pos0 < 0 || m < 1) return CSKV_ERR_BAD_SHAPE;
+  if (HI < 1 || HI > CSKV_MAX_HEADS || dI < 16 || dI % 16 != 0) return CSKV_ERR_BAD_SHAPE;
+  if (N > ((int64_t)1 << 31) - 64) return CSKV_ERR_BAD_SHAPE;
+  if (dtype == CSKV_BF16 && !mfma_shape_ok(HI, dI)) return CSKV_ERR_UNSUPPORTED;
+  if (dtype == CSKV_F32 && ((int64_t)HI * dI + HI) * 4 > 48 * 1024) return CSKV_ERR_UNSUPPORTED;
+  return CSKV_OK;
+}
+
+}  // namespace cskv
+
+using namespace cskv;
+
+extern "C" size_t cskv_indexer_workspace_size(int batch, int64_t Tq, int64_t N, int HI, int k,
+                                              int dtype) {
+  (void)HI;
+  (void)k;
+  if (batch <= 0 || Tq <= 0) return 0;
+  IdxPlan p = plan_indexer(batch, Tq, N, dtype);
+  return (size_t)(batch * p.rows_ws * p.ldS * 4);
+}
+
+extern "C" int indexer_topk(const void* qI, const float* wI, const void* KI, int batch, int64_t Tq,
+                            int64_t N, int HI, int dI, int64_t pos0, int m, int k,
+                            int32_t* out_idx, void* workspace, size_t ws_bytes, int dtype,
+                            void* stream) {
+  int st = check_indexer_shape(batch, Tq, N, HI, dI, pos0, m, dtype);
+  if (st) return st;
+  if (k < 1) return CSKV_ERR_BAD_SHAPE;
+  if (k > CSKV_MAX_TOPK) return CSKV_ERR_UNSUPPORTED;
+  if (batch == 0 || Tq == 0) return CSKV_OK;
+  if (!qI || !wI || !out_idx || (N > 0 && !KI)) return CSKV_ERR_INVALID_ARG;
+  if (!aligned16(qI, wI, KI, out_idx, workspace)) return CSKV_ERR_MISALIGNED;
+  IdxPlan p = plan_indexer(batch, Tq, N, dtype);
+  const size_t need_ws = (size_t)(batch * p.rows_ws * p.ldS * 4);
+  if (!workspace || ws_bytes < need_ws) return CSKV_ERR_WORKSPACE;
+
+  hipStream_t hs = (hipStream_t)stream;
+  IdxArgs a{};
+  a.qI = qI; a.wI = wI; a.KI = KI; a.scores = (float*)workspace; a.out = out_idx;
+  a.Tq = Tq; a.N = N; a.pos0 = pos0; a.ldS = p.ldS; a.rows_ws = p.rows_ws;
+  a.HI = HI; a.dI = dI; a.m = m; a.k = k;
+  for (int64_t r0 = 0; r0 < Tq; r0 += p.rows_ws) {
+    a.row0 = r0;
+    a.nrows = (Tq - r0) < p.rows_ws ? (Tq - r0) : p.rows_ws;
+    const int64_t last = pos0 + r0 + a.nrows - 1;
+    int64_t vmax = (last + 1) / m;
+    if (vmax > N) vmax = N;
+    if (vmax > k) {  // rows with V_t <= k need no scores
+      st = launch_scores(a, batch, (int)p.qb, dtype, hs);
+      if (st) return st;
+    }
+    st = launch_select(a, batch, hs);
+    if (st) return st;
+  }
+  return CSKV_OK;
+}
+
+extern "C" int indexer_scores(const void* qI, const float* wI, const void* KI, int batch, int64_t Tq,
+                              int64_t N, int HI, int dI, int64_t pos0, int m, float* scores,
+                              int64_t ld, int dtype, void* stream) {
+  int st = check_indexer_shape(batch, Tq, N, HI, dI, pos0, m, dtype);
+  if (st) return st;
+  if (ld < N || ld % 4 != 0) return CSKV_ERR_BAD_SHAPE;
+  if (batch == 0 || Tq == 0) return CSKV_OK;
+  if (!qI || !wI || !scores || (N > 0 && !KI)) return CSKV_ERR_INVALID_ARG;
+  if (!aligned16(qI, wI, KI, scores)) return CSKV_ERR_MISALIGNED;
+  IdxArgs a{};
+  a.qI = qI; a.wI = wI; a.KI = KI; a.scores = scores;
+  a.Tq = Tq; a.N = N; a.pos0 = pos0; a.ldS = ld; a.rows_ws = Tq; a.row0 = 0; a.nrows = Tq;
+  a.HI = HI; a.dI = dI; a.m = m;
+  const int qb = (dtype == CSKV_BF16 && Tq >= 64) ? 8 : 1;
+  return launch_scores(a, batch, qb, dtype, (hipStream_t)stream);
+}
+
+extern "C" int topk_select(const float* scores, int64_t ld, int batch, int64_t Tq, int64_t N,
+                           int64_t pos0, int m, int k, int32_t* out_idx, void* stream) {
+  if (batch < 0 || Tq < 0 || N < 0 || pos0 < 0 || m < 1 || ld < N) return CSKV_ERR_BAD_SHAPE;
+  if (k < 1) return CSKV_ERR_BAD_SHAPE;
+  if (k > CSKV_MAX_TOPK) return CSKV_ERR_UNSUPPORTED;
+  if (batch == 0 || Tq == 0) return CSKV_OK;
+  if (!out_idx || (N > 0 && !scores)) return CSKV_ERR_INVALID_ARG;
+  if (!aligned16(scores, out_idx)) return CSKV_ERR_MISALIGNED;
+  IdxArgs a{};
+  a.scores = (float*)scores; a.out = out_idx;
+  a.Tq = Tq; a.N = N; a.pos0 = pos0; a.ldS = ld; a.rows_ws = Tq; a.row0 = 0; a.nrows = Tq;
+  a.m = m; a.k = k;
+  return launch_select(a, batch, (hipStream_t)stream);
+}

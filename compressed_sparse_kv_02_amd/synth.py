@@ -25,13 +25,14 @@ def _rng(seed: int, name: str) -> np.random.Generator:
 
 
 def to_bf16_values(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to the nearest bfloat16 (ties to even); return float32."""
-    a = np.ascontiguousarray(x, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    nan = np.isnan(a)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
-    out = u.astype(np.uint32).view(np.float32).copy()
-    out[nan] = np.nan
+    """Round finite float32 values to the nearest bfloat16 (ties to even); return float32."""
+    out = np.array(x, dtype=np.float32, copy=True)
+    u = out.view(np.uint32)
+    lsb = u >> 16
+    lsb &= 1
+    lsb += 0x7FFF
+    u += lsb
+    u &= np.uint32(0xFFFF0000)
     return out
 
 
@@ -131,6 +132,30 @@ def cache_inputs(s: LayerShape, n_entries: int, prefix: str = "") -> Dict[str, n
     if s.kind == "csa":
         out["ik"] = normal(s.seed, prefix + "cache.ik", (s.batch, n_entries, s.dI), dtype=s.dtype)
     return out
+
+
+def normal_device(seed: int, name: str, shape, std: float = 1.0, dtype: str = "bf16", device="cuda"):
+    """Large seeded N(0, std^2) tensors drawn on the GPU with torch's Philox generator.
+
+    Used for the full-size workloads, whose inputs are too large to draw on the
+    host; tests copy the rows they check back to the host for the oracle.
+    """
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1000003 + zlib.crc32(name.encode())) & 0x7FFFFFFFFFFFFFFF)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        x.mul_(std)
+    return x.to(torch.bfloat16) if dtype == "bf16" else x
+
+
+def uniform_device(seed: int, name: str, shape, device="cuda"):
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed((seed * 1000003 + zlib.crc32(name.encode())) & 0x7FFFFFFFFFFFFFFF)
+    return torch.rand(shape, generator=g, device=device, dtype=torch.float32)
 
 
 def sample_rows(seed: int, T: int, n: int, must: Optional[list] = None) -> np.ndarray:

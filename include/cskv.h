@@ -1,0 +1,228 @@
+/*
+ * cskv.h -- C ABI of libcskv.so, the gfx950 (MI355X) implementation of the
+ * DeepSeek-V4 hybrid compressed attention layer: CSA (compressed sparse
+ * attention) and HCA (heavily compressed attention).
+ *
+ * Sources, by page title and section:
+ *   [PB]  "Paper Breakdown: DeepSeek-V4", section 4 "Hybrid Attention: CSA +
+ *         HCA (§2.3)": CSA (§2.3.1), HCA (§2.3.2), Additional Techniques
+ *         (§2.3.3: query/KV RMSNorm, partial RoPE on the last 64 dims,
+ *         sliding window, per-head sink logits).
+ *   [HW]  "How DeepSeek-V4 architecture and training work together",
+ *         section "Two compressed views of one history" (4-to-1 pooling,
+ *         1024 selected entries per query, 128-token window).
+ *   [IV]  "Inside DeepSeek V4", "Two compression regimes" (4x overlapping vs
+ *         128x non-overlapping) and "Local window" (128 uncompressed entries
+ *         in every CSA and HCA layer).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensors are row-major and contiguous, last dimension fastest.
+ *  - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *    where stated. The library never allocates, frees or synchronises, and
+ *    keeps no state between calls: scratch memory comes only from the
+ *    caller's `workspace`, sized by the matching *_workspace_size call.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream). Outputs are valid once that stream reaches this point.
+ *  - `dtype` selects the storage type of q, kv, window rows, streams and
+ *    outputs: CSKV_BF16 (fp32 accumulation, bf16 matrix cores) or CSKV_F32.
+ *    Head weights `wI`, sink logits, norm gains and `lse` are always fp32;
+ *    indices are int32; positions and lengths are int64.
+ *  - Device pointers must be 16-byte aligned.
+ *  - Positions are absolute token positions. Compressed entry i covers the
+ *    block of tokens [m*i, m*i + m - 1] and sits at rotary position m*i; a
+ *    query at position t may see entry i only once that block is complete:
+ *    i < V_t = min(N, floor((t + 1) / m)).
+ *  - Return value: CSKV_OK (0) or a negative CSKV_ERR_* code. Arguments are
+ *    validated before any HIP call; a failed validation enqueues nothing.
+ *    A launch failure returns CSKV_ERR_HIP. No exception crosses the ABI.
+ *  - Results are deterministic: no floating-point atomics, fixed reduction
+ *    order, so repeated calls give bit-identical outputs.
+ */
+#ifndef CSKV_H_
+#define CSKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  CSKV_OK = 0,
+  CSKV_ERR_INVALID_ARG = -1,  /* null pointer where one is required, bad enum */
+  CSKV_ERR_BAD_SHAPE = -2,    /* sizes inconsistent or out of the supported range */
+  CSKV_ERR_BAD_DTYPE = -3,    /* dtype not CSKV_BF16 / CSKV_F32 */
+  CSKV_ERR_MISALIGNED = -4,   /* a pointer is not 16-byte aligned */
+  CSKV_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required */
+  CSKV_ERR_UNSUPPORTED = -6,  /* valid request outside this build's limits (e.g. k > CSKV_MAX_TOPK) */
+  CSKV_ERR_HIP = -7           /* a kernel launch failed */
+};
+
+enum { CSKV_BF16 = 0, CSKV_F32 = 1 };
+enum { CSKV_MODE_CSA = 0, CSKV_MODE_HCA = 1 };
+
+#define CSKV_MAX_TOPK 2048
+#define CSKV_MAX_DIM 1024     /* d (KV/head dim) and dI upper bound */
+#define CSKV_MAX_HEADS 128
+
+/* Library version as 10000*major + 100*minor + patch. */
+int cskv_version(void);
+/* Static text for a status code (never NULL). */
+const char* cskv_status_string(int status);
+
+/*
+ * csa_compress -- overlapped 1/m KV compression with two softmax-weighted
+ * streams [PB §2.3.1 "KV Compression"; IV "Two compression regimes"].
+ *
+ * For each complete block i of m new tokens and each channel, one softmax
+ * runs over 2m logits: the m b-stream rows of the previous block (Zb + B^b)
+ * and the m a-stream rows of block i (Za + B^a). The entry is the
+ * softmax-weighted sum of the matching Cb and Ca rows. Optionally followed by
+ * RMSNorm over the c channels and RoPE on the last rope_dims channels at
+ * position pos0 + m*i ([PB §2.3.3]). Used for the KV entries (d = 512, norm
+ * and RoPE on) and for the indexer keys (dI = 128, both off) [PB §2.3.1,
+ * "Indexer keys compressed same way"].
+ *
+ *   Ca, Cb, Za, Zb : [batch, T, c]   token streams, positions pos0 .. pos0+T-1
+ *   B              : [2m, c]         rows 0..m-1 = B^b, rows m..2m-1 = B^a
+ *   prev_Cb,prev_Zb: [batch, m, c]   b-stream rows at positions pos0-m .. pos0-1
+ *                                    (the tail of the previous chunk), or both
+ *                                    NULL: then entry 0's b-half is left out of
+ *                                    its softmax (first block of a sequence)
+ *   T >= 0, 1 <= m <= 128, pos0 % m == 0, c % 8 == 0, 8 <= c <= CSKV_MAX_DIM
+ *   apply_norm     : 0/1; norm_w [c] fp32 or NULL (gain 1); eps > 0
+ *   rope_dims      : 0 (off) or even, <= c; rope_base > 0
+ *   out            : [batch, out_ld, c]; entry i of sequence b goes to row
+ *                    b*out_ld + i, so new entries can be appended in place
+ *                    to a cache (pass the pointer to the first new row);
+ *                    out_ld = 0 means floor(T/m), else out_ld >= floor(T/m).
+ *                    A trailing partial block is not emitted (the caller
+ *                    carries it to the next chunk).
+ */
+int csa_compress(const void* Ca, const void* Cb, const void* Za, const void* Zb, const void* B,
+                 const void* prev_Cb, const void* prev_Zb, int batch, int64_t T, int c, int m,
+                 int64_t pos0, int apply_norm, const float* norm_w, float eps, int rope_dims,
+                 float rope_base, void* out, int64_t out_ld, int dtype, void* stream);
+
+/*
+ * hca_compress -- non-overlapped 1/m' compression of one stream [PB §2.3.2;
+ * IV "Two compression regimes"]: entry i is the per-channel softmax over
+ * the m' rows of block i (Z + B) weighting C, then optional RMSNorm + RoPE
+ * at position pos0 + m'*i. With m' = 1 the softmax is over a single row, so
+ * the call prepares raw sliding-window rows (RMSNorm + RoPE at each row's own
+ * position) [PB §2.3.1 "Sliding window KV (uncompressed)"; IV "Local window"].
+ *
+ *   C   : [batch, T, c]; Z : [batch, T, c] or NULL (uniform weights)
+ *   B   : [m', c] or NULL (zero bias)
+ *   1 <= m' <= 4096, pos0 % m' == 0; other arguments as in csa_compress
+ *   out : [batch, out_ld, c] as in csa_compress (out_ld = 0: floor(T/m'))
+ */
+int hca_compress(const void* C, const void* Z, const void* B, int batch, int64_t T, int c, int m,
+                 int64_t pos0, int apply_norm, const float* norm_w, float eps, int rope_dims,
+                 float rope_base, void* out, int64_t out_ld, int dtype, void* stream);
+
+/*
+ * indexer_topk -- lightning-indexer scores over compressed keys, then per
+ * query top-k [PB §2.3.1 "DSA on Compressed KV (lightning indexer + top-k)";
+ * HW "Two compressed views of one history" (k = 1024)].
+ *
+ *   I[t, s] = sum_h wI[t, h] * max(0, qI[t, h, :] . KI[s, :])  for s < V_t
+ *
+ * out_idx[t] lists the k entries of largest I in ascending index order;
+ * among equal scores the smaller index wins; when V_t <= k all visible
+ * entries are listed and the rest is -1.
+ *
+ *   qI  : [batch, Tq, HI, dI]  indexer queries, query j at position pos0 + j
+ *   wI  : [batch, Tq, HI]      fp32 head weights
+ *   KI  : [batch, N, dI]       compressed indexer keys (entries 0 .. N-1)
+ *   1 <= HI <= CSKV_MAX_HEADS; bf16: dI in {32, 64, 128}; f32: dI % 16 == 0 and
+ *   (HI * dI + HI) * 4 <= 48 KiB
+ *   1 <= k <= CSKV_MAX_TOPK, m >= 1
+ *   out_idx   : [batch, Tq, k] int32
+ *   workspace : cskv_indexer_workspace_size(...) bytes (fp32 score rows and
+ *               selection counters), device memory
+ */
+size_t cskv_indexer_workspace_size(int batch, int64_t Tq, int64_t N, int HI, int k, int dtype);
+int indexer_topk(const void* qI, const float* wI, const void* KI, int batch, int64_t Tq, int64_t N,
+                 int HI, int dI, int64_t pos0, int m, int k, int32_t* out_idx, void* workspace,
+                 size_t ws_bytes, int dtype, void* stream);
+
+/*
+ * indexer_scores / topk_select -- the two halves of indexer_topk, for callers
+ * that keep the score matrix themselves (e.g. to time or reuse it).
+ *
+ * indexer_scores writes scores[(b*Tq + j)*ld + s] = I[t, s] (fp32) for every
+ * visible entry s < V_t of query j; entries past V_t up to the end of the
+ * swept key range may hold -inf and later ones are left untouched.
+ *   scores : [batch, Tq, ld] fp32, ld >= N and ld % 4 == 0
+ *   other arguments and limits as in indexer_topk
+ * topk_select reads such a matrix and writes out_idx exactly as indexer_topk
+ * does (k largest of the first V_t scores, smaller index first among equal
+ * scores, ascending, -1 padded).
+ */
+int indexer_scores(const void* qI, const float* wI, const void* KI, int batch, int64_t Tq, int64_t N,
+                   int HI, int dI, int64_t pos0, int m, float* scores, int64_t ld, int dtype,
+                   void* stream);
+int topk_select(const float* scores, int64_t ld, int batch, int64_t Tq, int64_t N, int64_t pos0, int m,
+                int k, int32_t* out_idx, void* stream);
+
+/*
+ * compressed_attn_prefill -- MQA core attention over compressed entries,
+ * sliding window and sink [PB §2.3.1 "MQA core attention", §2.3.2 "dense on
+ * compressed KV", §2.3.3; IV "Local window"].
+ *
+ * For query j (position t = pos0 + j) and head h:
+ *   q~ = RoPE_t(RMSNorm(q[j, h]))                   (norm if apply_q_norm)
+ *   keys = { kv[s] : s in idx[j], s >= 0 }           (mode CSKV_MODE_CSA)
+ *        | { kv[s] : s < V_t }                       (mode CSKV_MODE_HCA)
+ *        + { win rows at positions max(0, t-w+1) .. t }
+ *   l_e  = scale * q~ . e    (scale 0 -> 1/sqrt(d)); K = V = e (MQA)
+ *   o    = sum_e exp(l_e - M) e / (exp(z_h - M) + sum_e exp(l_e - M)),
+ *          z_h = sink[h] (sink NULL -> no sink), M the running maximum
+ *   lse  = log(exp(z_h) + sum_e exp(l_e))
+ *   if rope_on_output, o's last rope_dims dims are rotated back by -t.
+ *
+ *   q     : [batch, Tq, H, d]
+ *   kv    : [batch, N, d]     compressed entries as stored (normed + roped)
+ *   idx   : [batch, Tq, k] int32 (CSA; entries outside [0, N) are skipped),
+ *           NULL for HCA
+ *   win   : [batch, W, d]     prepared window rows; row r is position
+ *           win_pos0 + r. Requires win_pos0 <= max(0, pos0 - w + 1) and
+ *           win_pos0 + W >= pos0 + Tq.
+ *   sink  : [H] fp32 or NULL;  q_norm_w : [d] fp32 or NULL (gain 1)
+ *   1 <= H <= CSKV_MAX_HEADS, d % 32 == 0, 32 <= d <= 512 (bf16) or
+ *   CSKV_MAX_DIM (f32), w >= 1, rope_dims even <= d
+ *   out   : [batch, Tq, H, d];  lse : [batch, Tq, H] fp32 or NULL
+ */
+int compressed_attn_prefill(int mode, const void* q, const void* kv, const int32_t* idx,
+                            const void* win, int64_t win_pos0, int64_t W, const float* sink,
+                            int batch, int64_t Tq, int64_t N, int64_t pos0, int m, int k, int w,
+                            int H, int d, int apply_q_norm, const float* q_norm_w, float eps,
+                            int rope_dims, float rope_base, float scale, int rope_on_output,
+                            void* out, float* lse, int dtype, void* stream);
+
+/*
+ * compressed_attn_decode -- the same computation for a few new query tokens
+ * against a long cache, split over the key list ("split-K"): each split
+ * writes a partial (max, sum, weighted sum) to the workspace and a merge
+ * kernel combines the splits in a fixed order. Arguments as in
+ * compressed_attn_prefill, plus:
+ *   n_splits  : 0 = choose from the shape; else 1 .. 256 splits per query
+ *   workspace : cskv_decode_workspace_size(...) bytes of device memory
+ * Any n_splits gives the same result up to fp32 rounding of the merge.
+ */
+size_t cskv_decode_workspace_size(int batch, int64_t Tq, int H, int d, int n_splits);
+int compressed_attn_decode(int mode, const void* q, const void* kv, const int32_t* idx,
+                           const void* win, int64_t win_pos0, int64_t W, const float* sink,
+                           int batch, int64_t Tq, int64_t N, int64_t pos0, int m, int k, int w,
+                           int H, int d, int apply_q_norm, const float* q_norm_w, float eps,
+                           int rope_dims, float rope_base, float scale, int rope_on_output,
+                           int n_splits, void* workspace, size_t ws_bytes, void* out, float* lse,
+                           int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSKV_H_ */

@@ -1,0 +1,133 @@
+"""Host-side helpers for the GPU parity tests: comparisons and the oracle
+pipeline of one layer call. Everything here runs on the CPU; the oracle
+only ever sees the seeded inputs (copied from where the generator drew them),
+never an output of the GPU path."""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+
+from oracle import cskv_oracle as O
+
+
+def np64(t) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |x| (2**-133 below the normal range)."""
+    _, e = np.frexp(np.abs(x))
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def assert_storage_close(gpu: np.ndarray, exact: np.ndarray, dtype: str, what: str, rtol_f32=1e-5):
+    """bf16: within one bf16 ulp of the exact (fp64) value; f32: 1e-5 relative (+1e-6 abs)."""
+    if dtype == "bf16":
+        err = np.abs(gpu - exact)
+        bad = err > bf16_ulp(exact) * (1 + 1e-9)
+        assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} elements beyond 1 bf16 ulp, max err {err.max():.3g}"
+    else:
+        err = np.abs(gpu - exact)
+        bad = err > rtol_f32 * np.abs(exact) + 1e-6
+        assert not bad.any(), f"{what}: {bad.sum()} elements beyond 1e-5 rel, max err {err.max():.3g}"
+
+
+def check_topk_row(gpu_row: np.ndarray, scores: np.ndarray, V: int, k: int, band: float = None,
+                   what: str = "") -> int:
+    """Checks one row of selected indices against oracle scores.
+
+    Bit-exact outside the tie band: every entry scoring above I_k + band must
+    be selected and none scoring below I_k - band; the row is ascending,
+    distinct, visible, and -1 padded. Returns how many selected entries fall
+    inside the band but differ from the oracle's own pick.
+    """
+    gpu_row = np.asarray(gpu_row, dtype=np.int64)
+    if V <= k:
+        exp = np.concatenate([np.arange(V), -np.ones(k - V, dtype=np.int64)])
+        assert np.array_equal(gpu_row, exp), f"{what}: V={V} <= k={k} must list all visible entries"
+        return 0
+    assert (gpu_row >= 0).all() and (gpu_row < V).all(), f"{what}: out-of-range index"
+    assert (np.diff(gpu_row) > 0).all(), f"{what}: not strictly ascending"
+    ref = O.topk_row(scores, V, k)
+    s = scores[:V]
+    Ik = np.sort(s)[::-1][k - 1]
+    if band is None:
+        band = 1e-6 * abs(Ik)
+    sel = np.zeros(V, dtype=bool)
+    sel[gpu_row] = True
+    must_in = s > Ik + band
+    must_out = s < Ik - band
+    assert sel[must_in].all(), f"{what}: {int((~sel[must_in]).sum())} entries above the band missing"
+    assert not sel[must_out].any(), f"{what}: {int(sel[must_out].sum())} entries below the band selected"
+    return len(set(gpu_row.tolist()) ^ set(ref.tolist())) // 2
+
+
+def oracle_layer(L, t, b: int, rows: Iterable[int]):
+    """Oracle pipeline of one layer call for sequence b at the given query rows.
+
+    t holds the seeded device inputs of the call (make_inputs) with the caches
+    and window buffer as they were BEFORE the call; slices are copied to the
+    host as float64. Returns (o [len(rows), H, d], lse [len(rows), H],
+    idx [Tq, k] filled at the rows, extras). Compressed entries and window
+    rows are rounded to the storage type, as the cache stores them.
+    """
+    rnd = O.round_bf16 if L.dtype == "bf16" else (lambda x: x)
+    h = lambda name: np64(t[name][b])
+    opt = lambda name: np64(t[name][b]) if name in t else None
+    rows = list(rows)
+    kv = h("cache.kv")
+    ik = h("cache.ik") if L.kind == "csa" else None
+    extras = {}
+    if L.n_new:
+        if L.kind == "csa":
+            new = O.csa_compress(h("kv.Ca"), h("kv.Cb"), h("kv.Za"), h("kv.Zb"), np64(t["kv.B"]), L.m, L.pos0,
+                                 opt("kv.prevCb"), opt("kv.prevZb"), apply_norm=True, rope_dims=L.rope_dims)
+            kv[L.n_cached:] = rnd(new)
+            newk = O.csa_compress(h("ik.Ca"), h("ik.Cb"), h("ik.Za"), h("ik.Zb"), np64(t["ik.B"]), L.m, L.pos0,
+                                  opt("ik.prevCb"), opt("ik.prevZb"))
+            extras["ik_new_exact"] = newk
+            ik[L.n_cached:] = rnd(newk)
+        else:
+            new = O.hca_compress(h("kv.C"), h("kv.Z"), np64(t["kv.B"]), L.m, L.pos0, apply_norm=True,
+                                 rope_dims=L.rope_dims)
+            kv[L.n_cached:] = rnd(new)
+    win = h("win")
+    win[L.win_cached:] = rnd(O.prepare_window(h("win_raw"), L.pos0, rope_dims=L.rope_dims))
+    sink = np64(t["sink"])
+    idx = np.full((L.T, L.k), -1, dtype=np.int64) if L.kind == "csa" else None
+    extras["scores"] = {}
+    outs, lses = [], []
+    for r in rows:
+        rid = None
+        if L.kind == "csa":
+            qI = np64(t["qI"][b, r:r + 1])
+            wI = np64(t["wI"][b, r:r + 1])
+            I = O.indexer_scores(qI, wI, ik, L.pos0 + r, L.m)[0]
+            extras["scores"][r] = I
+            idx[r] = O.topk_row(I, O.visible(L.pos0 + r, L.m, L.N), L.k)
+            rid = idx[r:r + 1]
+        # one query row at absolute position pos0 + r (a one-row call of the same definition)
+        o, l = O.attention(np64(t["q"][b, r:r + 1]), kv, win, L.win_pos0, L.pos0 + r, L.m, L.w, idx=rid,
+                           sink=sink, rope_dims=L.rope_dims)
+        outs.append(o[0])
+        lses.append(l[0])
+    return np.stack(outs), np.stack(lses), idx, extras
+
+
+def key_rounding_band(qI_row: np.ndarray, wI_row: np.ndarray, ik_new_exact: Optional[np.ndarray],
+                      dtype: str = "bf16") -> float:
+    """Largest change of one indexer score when every recomputed key element moves by one storage ulp.
+
+    |dI_s| <= sum_h |w_h| * sum_c |q_hc| * ulp(K_sc) (ReLU is 1-Lipschitz). Stored
+    cache entries are identical on both sides and add nothing. In fp32 the
+    compressor's own rounding (a few fp32 ulps) stands in for the storage ulp.
+    """
+    if ik_new_exact is None or ik_new_exact.size == 0:
+        return 0.0
+    if dtype == "bf16":
+        u = bf16_ulp(np.abs(ik_new_exact)).max(axis=0)  # per channel, worst entry
+    else:
+        u = np.abs(ik_new_exact).max(axis=0) * 2.0 ** -21
+    return float(np.sum(np.abs(wI_row)[:, None] * np.abs(qI_row) * u[None, :]))

@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments with the documented status before
+any HIP call (so these calls never touch a device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cskv.h")
+LIB = os.path.join(ROOT, "compressed_sparse_kv_02_amd", "libcskv.so")
+
+OK, INVALID, SHAPE, DTYPE, MISALIGNED, WS, UNSUPPORTED = 0, -1, -2, -3, -4, -5, -6
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libcskv.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from compressed_sparse_kv_02_amd import binding
+    return binding.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(L, n), n
+    from compressed_sparse_kv_02_amd import binding
+    assert sorted(binding.EXPORTS) == names
+
+
+def test_version_and_status_strings(L):
+    assert L.cskv_version() == 100
+    for code in range(-7, 1):
+        assert len(L.cskv_status_string(code)) >= 2
+    assert L.cskv_status_string(-99) == b"unknown status"
+
+
+P = 0x1000  # an aligned fake device address: never dereferenced, validation fails first
+
+
+def test_csa_compress_validation(L):
+    f = L.csa_compress
+    base = dict(Ca=P, Cb=P, Za=P, Zb=P, B=P, pCb=None, pZb=None, batch=1, T=16, c=64, m=4, pos0=0,
+                norm=1, nw=None, eps=1e-6, rd=16, rb=10000.0, out=P, ld=0, dt=0, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*a.values())
+    assert call(dt=7) == DTYPE
+    assert call(c=60) == SHAPE            # c % 8
+    assert call(m=0) == SHAPE
+    assert call(pos0=6) == SHAPE          # pos0 % m
+    assert call(rd=15) == SHAPE           # odd rope dims
+    assert call(rd=128) == SHAPE          # rope dims > c
+    assert call(m=256) == UNSUPPORTED
+    assert call(Ca=None) == INVALID
+    assert call(pCb=P) == INVALID         # prev_Cb without prev_Zb
+    assert call(Ca=P + 4) == MISALIGNED
+    assert call(ld=3) == SHAPE            # out_ld < T/m
+    assert call(eps=0.0) == INVALID
+    assert call(T=3) == OK                # no complete block: nothing to do, no launch
+    assert call(batch=0) == OK
+
+
+def test_hca_compress_validation(L):
+    f = L.hca_compress
+    base = dict(C=P, Z=None, B=None, batch=2, T=256, c=512, m=128, pos0=0, norm=1, nw=None, eps=1e-6,
+                rd=64, rb=10000.0, out=P, ld=0, dt=0, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*a.values())
+    assert call(m=5000) == UNSUPPORTED
+    assert call(C=None) == INVALID
+    assert call(out=None) == INVALID
+    assert call(pos0=64) == SHAPE
+    assert call(c=2048) == SHAPE
+    assert call(T=100) == OK
+
+
+def test_indexer_topk_validation(L):
+    f = L.indexer_topk
+    base = dict(qI=P, wI=P, KI=P, batch=1, Tq=64, N=1000, HI=64, dI=128, pos0=0, m=4, k=1024, out=P,
+                ws=P, wsb=1 << 40, dt=0, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*a.values())
+    assert call(k=4096) == UNSUPPORTED
+    assert call(k=0) == SHAPE
+    assert call(dI=100) == SHAPE
+    assert call(dI=256) == UNSUPPORTED    # bf16 indexer supports dI 32/64/128
+    assert call(HI=0) == SHAPE
+    assert call(qI=None) == INVALID
+    assert call(ws=None) == WS
+    assert call(wsb=16) == WS
+    assert call(out=P + 8) == MISALIGNED
+    assert call(Tq=0) == OK
+    need = L.cskv_indexer_workspace_size(1, 64, 1000, 64, 1024, 0)
+    assert need >= 64 * 1000 * 4
+
+
+def test_attention_validation(L):
+    for fname in ("compressed_attn_prefill", "compressed_attn_decode"):
+        f = getattr(L, fname)
+        base = dict(mode=0, q=P, kv=P, idx=P, win=P, wp0=0, W=64, sink=None, batch=1, Tq=64, N=16,
+                    pos0=0, m=4, k=16, w=16, H=64, d=512, qn=1, qnw=None, eps=1e-6, rd=64, rb=1e4,
+                    scale=0.0, roo=1)
+        extra = dict(ns=0, ws=P, wsb=1 << 40) if fname.endswith("decode") else {}
+        tail = dict(out=P, lse=None, dt=0, st=None)
+
+        def call(**kw):
+            a = dict(base, **extra, **tail)
+            a.update(kw)
+            return f(*a.values())
+        assert call(mode=3) == INVALID
+        assert call(dt=2) == DTYPE
+        assert call(d=96) == UNSUPPORTED    # bf16 head dims 64/128/256/512
+        assert call(H=0) == SHAPE
+        assert call(w=0) == SHAPE
+        assert call(k=0) == SHAPE
+        assert call(k=4096) == UNSUPPORTED
+        assert call(W=63) == SHAPE           # window rows do not reach the last query
+        assert call(wp0=1) == SHAPE          # window rows start after the first query's window
+        assert call(idx=None) == INVALID     # CSA needs indices
+        assert call(q=P + 2) == MISALIGNED
+        assert call(Tq=0) == OK
+        if fname.endswith("decode"):
+            assert call(ns=300) == SHAPE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from compressed_sparse_kv_02_amd import binding
+    x = torch.zeros(1, 8, 64)
+    with pytest.raises(binding.CskvError):
+        binding.hca_compress(x, m=1)

@@ -1,0 +1,348 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs. Stage tests feed both sides generator-made inputs for
+every stage; end-to-end tests run the whole layer on both sides."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import cskv_oracle as O
+from compressed_sparse_kv_02_amd import binding as B
+from compressed_sparse_kv_02_amd import layer as LY
+from compressed_sparse_kv_02_amd.synth import normal_device, uniform_device
+from tests.parity_utils import (assert_storage_close, check_topk_row, key_rounding_band, np64,
+                                oracle_layer)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TD = {"bf16": torch.bfloat16, "f32": torch.float32}
+ATOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gen(seed, name, shape, dtype="bf16", std=1.0):
+    return normal_device(seed, name, shape, std, dtype, DEV)
+
+
+# ----------------------------------------------------------------------------- compressors
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("c,m,T,pos0,norm,rope", [
+    (64, 4, 203, 0, True, 16), (512, 4, 1000, 0, True, 64), (128, 4, 77, 96, False, 0),
+    (512, 4, 64, 4096, True, 64), (32 * 8, 2, 9, 0, True, 8), (64, 1, 33, 0, False, 0)])
+def test_csa_compress(dtype, c, m, T, pos0, norm, rope):
+    say("csa_compress", dtype, c, m, T, pos0, norm, rope)
+    bt = 2
+    g = lambda nm, sh: gen(11, f"cc.{nm}", sh, dtype)
+    Ca, Cb, Za, Zb = (g(nm, (bt, T, c)) for nm in ("Ca", "Cb", "Za", "Zb"))
+    Bb = g("B", (2 * m, c))
+    prev = (g("pCb", (bt, m, c)), g("pZb", (bt, m, c))) if pos0 else (None, None)
+    out = B.csa_compress(Ca, Cb, Za, Zb, Bb, m, pos0, *prev, apply_norm=norm, rope_dims=rope)
+    torch.cuda.synchronize()
+    assert out.shape == (bt, T // m, c)
+    for b in range(bt):
+        ref = O.csa_compress(np64(Ca[b]), np64(Cb[b]), np64(Za[b]), np64(Zb[b]), np64(Bb), m, pos0,
+                             np64(prev[0][b]) if pos0 else None, np64(prev[1][b]) if pos0 else None,
+                             apply_norm=norm, rope_dims=rope)
+        assert_storage_close(np64(out[b]), ref, dtype, f"csa b={b}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("c,m,T,pos0,withZ,norm,rope", [
+    (512, 128, 300, 0, True, True, 64), (512, 128, 1024, 128 * 7, True, True, 64), (64, 16, 50, 0, False, True, 16),
+    (512, 1, 37, 1000, False, True, 64), (128, 1, 5, 0, True, False, 0), (512, 4096, 4096, 0, True, True, 64)])
+def test_hca_compress(dtype, c, m, T, pos0, withZ, norm, rope):
+    say("hca_compress", dtype, c, m, T, pos0, withZ, norm, rope)
+    bt = 2
+    C = gen(12, "hc.C", (bt, T, c), dtype)
+    Z = gen(12, "hc.Z", (bt, T, c), dtype) if withZ else None
+    Bb = gen(12, "hc.B", (m, c), dtype, 0.1) if withZ else None
+    out = B.hca_compress(C, Z, Bb, m, pos0, apply_norm=norm, rope_dims=rope)
+    torch.cuda.synchronize()
+    for b in range(bt):
+        ref = O.hca_compress(np64(C[b]), np64(Z[b]) if withZ else None, np64(Bb) if withZ else None, m, pos0,
+                             apply_norm=norm, rope_dims=rope)
+        assert_storage_close(np64(out[b]), ref, dtype, f"hca b={b}")
+
+
+def test_compress_append_in_place():
+    say("compress append in place")
+    c, m, T = 128, 4, 64
+    Ca, Cb, Za, Zb = (gen(13, f"ap.{n}", (2, T, c)) for n in ("Ca", "Cb", "Za", "Zb"))
+    Bb = gen(13, "ap.B", (2 * m, c))
+    cache = torch.full((2, 40, c), 7.0, dtype=torch.bfloat16, device=DEV)
+    B.csa_compress(Ca, Cb, Za, Zb, Bb, m, out=cache, out_row0=20)
+    ref = B.csa_compress(Ca, Cb, Za, Zb, Bb, m)
+    torch.cuda.synchronize()
+    assert torch.equal(cache[:, 20:36], ref)
+    assert (cache[:, :20] == 7).all() and (cache[:, 36:] == 7).all()
+
+
+# ----------------------------------------------------------------------------- indexer + top-k
+
+def _indexer_case(dtype, bt, Tq, N, HI, dI, pos0, m, k, seed, integer=False):
+    if integer:  # small integers: exact scores, many exact ties
+        g = torch.Generator(device=DEV).manual_seed(seed)
+        qI = torch.randint(-2, 3, (bt, Tq, HI, dI), generator=g, device=DEV).to(TD[dtype])
+        KI = torch.randint(-2, 3, (bt, N, dI), generator=g, device=DEV).to(TD[dtype])
+        wI = torch.randint(0, 3, (bt, Tq, HI), generator=g, device=DEV).float()
+    else:
+        qI = gen(seed, "ix.q", (bt, Tq, HI, dI), dtype)
+        KI = gen(seed, "ix.k", (bt, N, dI), dtype)
+        wI = uniform_device(seed, "ix.w", (bt, Tq, HI), DEV)
+    idx = B.indexer_topk(qI, wI, KI, pos0, m, k)
+    torch.cuda.synchronize()
+    return qI, wI, KI, idx
+
+
+@pytest.mark.parametrize("dtype,bt,Tq,N,HI,dI,pos0,m,k", [
+    ("f32", 1, 512, 128, 2, 32, 0, 4, 16),          # tiny CSA indexer shape
+    ("bf16", 2, 300, 400, 64, 128, 0, 4, 64),       # ragged rows, V_t both below and above k
+    ("bf16", 1, 77, 5000, 20, 64, 16000, 4, 100),   # chunk on a cache, HI not a multiple of 32
+    ("bf16", 3, 5, 70000, 64, 128, 4 * 70000, 4, 1024),  # few queries, long rows (key splits)
+    ("bf16", 1, 130, 3000, 32, 32, 3000 * 4 - 64, 4, 2048),  # max k
+])
+def test_indexer_topk(dtype, bt, Tq, N, HI, dI, pos0, m, k):
+    say("indexer_topk", dtype, bt, Tq, N, HI, dI, pos0, m, k)
+    qI, wI, KI, idx = _indexer_case(dtype, bt, Tq, N, HI, dI, pos0, m, k, seed=21)
+    idx = idx.cpu().numpy()
+    rows = range(Tq) if Tq <= 80 else sorted(set(np.linspace(0, Tq - 1, 60).astype(int)) | {0, Tq - 1})
+    n_band = 0
+    for b in range(bt):
+        K = np64(KI[b])
+        for r in rows:
+            I = O.indexer_scores(np64(qI[b, r:r + 1]), np64(wI[b, r:r + 1]), K, pos0 + r, m)[0]
+            n_band += check_topk_row(idx[b, r], I, O.visible(pos0 + r, m, N), k, what=f"b{b} r{r}")
+    say("  tie-band differences:", n_band)
+
+
+def test_indexer_topk_exact_ties():
+    say("indexer_topk integer ties")
+    bt, Tq, N, HI, dI, k = 2, 64, 600, 32, 32, 50
+    qI, wI, KI, idx = _indexer_case("bf16", bt, Tq, N, HI, dI, 4 * 500, 4, k, seed=5, integer=True)
+    idx = idx.cpu().numpy()
+    for b in range(bt):
+        K = np64(KI[b])
+        for r in range(Tq):
+            I = O.indexer_scores(np64(qI[b, r:r + 1]), np64(wI[b, r:r + 1]), K, 2000 + r, 4)[0]
+            V = O.visible(2000 + r, 4, N)
+            # integer scores are exact in fp32: the selection must equal the oracle's, ties included
+            assert np.array_equal(idx[b, r], O.topk_row(I, V, k)), (b, r)
+
+
+def test_indexer_decode_1m_full():
+    say("indexer_topk decode 1M: batch 8, 262144 keys")
+    qI, wI, KI, idx = _indexer_case("bf16", 8, 1, 262144, 64, 128, 1 << 20, 4, 1024, seed=4)
+    idx = idx.cpu().numpy()
+    for b in range(8):
+        I = O.indexer_scores(np64(qI[b]), np64(wI[b]), np64(KI[b]), 1 << 20, 4)[0]
+        check_topk_row(idx[b, 0], I, 262144, 1024, what=f"b{b}")
+
+
+# ----------------------------------------------------------------------------- attention
+
+def _random_idx(bt, Tq, pos0, m, N, k, seed):
+    rng = np.random.default_rng(seed)
+    idx = -np.ones((bt, Tq, k), dtype=np.int32)
+    for b in range(bt):
+        for j in range(Tq):
+            V = O.visible(pos0 + j, m, N)
+            if V <= k:
+                idx[b, j, :V] = np.arange(V)
+            else:
+                idx[b, j] = np.sort(rng.choice(V, size=k, replace=False))
+    return idx
+
+
+@pytest.mark.parametrize("dtype,mode,bt,Tq,N,pos0,m,k,w,H,d,rope,roo,sink", [
+    ("f32", "csa", 1, 96, 32, 0, 4, 16, 16, 4, 64, 16, True, True),
+    ("bf16", "csa", 2, 70, 64, 0, 4, 24, 16, 16, 64, 16, True, True),
+    ("bf16", "hca", 2, 50, 40, 128 * 10, 128, 0, 128, 20, 128, 32, False, True),
+    ("bf16", "csa", 1, 33, 3000, 4 * 2900, 4, 1024, 128, 64, 512, 64, True, True),
+    ("bf16", "hca", 1, 40, 200, 128 * 180, 128, 0, 128, 32, 512, 64, True, False),
+    ("bf16", "csa", 1, 20, 500, 1990, 4, 100, 7, 8, 256, 0, False, True),
+    ("f32", "hca", 2, 30, 10, 0, 4, 0, 5, 3, 96, 32, True, True),
+])
+def test_attention_prefill(dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink):
+    say("attention", dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink)
+    q = gen(31, "at.q", (bt, Tq, H, d), dtype)
+    kv = gen(31, "at.kv", (bt, N, d), dtype)
+    wp0 = max(0, pos0 - w + 1)
+    win = gen(31, "at.win", (bt, pos0 + Tq - wp0, d), dtype)
+    sk = normal_device(31, "at.sink", (H,), 1.0, "f32", DEV) if sink else None
+    idx = torch.from_numpy(_random_idx(bt, Tq, pos0, m, N, k, 3)).to(DEV) if mode == "csa" else None
+    o, lse = B.compressed_attn_prefill(B.CSA if mode == "csa" else B.HCA, q, kv, idx, win, wp0, sk, pos0, m, w,
+                                       k=k, rope_dims=rope, rope_on_output=roo, return_lse=True)
+    torch.cuda.synchronize()
+    for b in range(bt):
+        ro, rl = O.attention(np64(q[b]), np64(kv[b]), np64(win[b]), wp0, pos0, m, w,
+                             idx=idx[b].cpu().numpy() if idx is not None else None,
+                             sink=np64(sk) if sink else None, rope_dims=rope, rope_on_output=roo)
+        err = np.abs(np64(o[b]) - ro).max()
+        lerr = np.abs(np64(lse[b]) - rl).max()
+        say(f"  b{b}: max|o err| {err:.3g}  max|lse err| {lerr:.3g}")
+        assert err <= ATOL[dtype] and lerr <= ATOL[dtype] * 5
+
+
+@pytest.mark.parametrize("mode", ["csa", "hca"])
+def test_decode_splits_and_prefill_agree(mode):
+    say("decode splits", mode)
+    bt, H, d, m, w = 3, 64, 512, (4 if mode == "csa" else 128), 128
+    N = 6000
+    pos0 = N * m
+    k = 1024 if mode == "csa" else 0
+    q = gen(41, "dc.q", (bt, 1, H, d))
+    kv = gen(41, "dc.kv", (bt, N, d))
+    win = gen(41, "dc.win", (bt, w, d))
+    sk = normal_device(41, "dc.sink", (H,), 1.0, "f32", DEV)
+    idx = torch.from_numpy(_random_idx(bt, 1, pos0, m, N, k, 9)).to(DEV) if mode == "csa" else None
+    md = B.CSA if mode == "csa" else B.HCA
+    kw = dict(k=k, rope_dims=64, return_lse=True)
+    outs = [B.compressed_attn_prefill(md, q, kv, idx, win, pos0 - w + 1, sk, pos0, m, w, **kw)]
+    for ns in (1, 3, 7, 0, 64):
+        outs.append(B.compressed_attn_decode(md, q, kv, idx, win, pos0 - w + 1, sk, pos0, m, w, n_splits=ns, **kw))
+    torch.cuda.synchronize()
+    for b in range(bt):
+        ro, rl = O.attention(np64(q[b]), np64(kv[b]), np64(win[b]), pos0 - w + 1, pos0, m, w,
+                             idx=idx[b].cpu().numpy() if idx is not None else None, sink=np64(sk), rope_dims=64)
+        for i, (o, l) in enumerate(outs):
+            err = np.abs(np64(o[b]) - ro).max()
+            assert err <= 2e-2, (b, i, err)
+            assert np.abs(np64(l[b]) - rl).max() <= 1e-1
+    for o, l in outs[1:]:  # every split count agrees with the single pass to fp32-merge rounding
+        assert (o.float() - outs[0][0].float()).abs().max().item() <= 1.6e-2
+
+
+# ----------------------------------------------------------------------------- whole layers
+
+def _check_layer(L, t, rows_per_seq, atol, max_band_rows=0.25):
+    out, lse = t["out"], t["lse"]
+    gidx = t["idx"].cpu().numpy() if L.kind == "csa" else None
+    compared = skipped = 0
+    for b in range(L.batch):
+        rows = rows_per_seq(L)
+        o, l, idx, ex = oracle_layer(L, t, b, rows)
+        for n, r in enumerate(rows):
+            if L.kind == "csa":
+                I = ex["scores"][r]
+                V = O.visible(L.pos0 + r, L.m, L.N)
+                band = 1e-6 * abs(np.sort(I[:V])[::-1][min(L.k, V) - 1]) if V > 0 else 0.0
+                band += key_rounding_band(np64(t["qI"][b, r]), np64(t["wI"][b, r]), ex.get("ik_new_exact"), L.dtype)
+                check_topk_row(gidx[b, r], I, V, L.k, band=band, what=f"b{b} r{r}")
+                if not np.array_equal(gidx[b, r], idx[r]):
+                    skipped += 1
+                    continue
+            err = np.abs(np64(out[b, r]) - o[n]).max()
+            assert err <= atol, f"{L.name} b{b} row {r}: max err {err:.3g}"
+            assert np.abs(np64(lse[b, r]) - l[n]).max() <= 5 * atol
+            compared += 1
+    say(f"  {L.name}: compared {compared} rows, {skipped} rows with a near-tie selection difference")
+    assert skipped <= max_band_rows * (compared + skipped)
+
+
+def _run(L):
+    """Run the layer; return its inputs with the caches and window as they were before the call."""
+    t = LY.make_inputs(L)
+    pre = {k: t[k].clone() for k in ("cache.kv", "cache.ik", "win") if k in t}
+    LY.run_layer(L, t)
+    torch.cuda.synchronize()
+    res = dict(t)
+    res.update(pre)
+    return res
+
+
+def test_tiny_csa_f32_end_to_end():
+    L = LY.tiny_csa("f32")
+    say("tiny CSA f32 end to end", L)
+    t = _run(L)
+    _check_layer(L, t, lambda L: list(range(L.T)), 1e-4, max_band_rows=0.02)
+
+
+def test_tiny_csa_bf16_end_to_end():
+    L = LY.tiny_csa("bf16")
+    say("tiny CSA bf16 end to end")
+    t = _run(L)
+    _check_layer(L, t, lambda L: list(range(L.T)), 2e-2, max_band_rows=0.05)
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_chunked_layer_small(kind):
+    m = 4 if kind == "csa" else 128
+    L = LY.LayerCall(kind, 2, 700, 128 * 40, 128 * 40 // m, d=512, H=20, m=m, w=128, k=256, HI=64, dI=128,
+                     seed=8, name=f"small.{kind}")
+    say("chunked small", L)
+    t = _run(L)
+    _check_layer(L, t, lambda L: sorted({0, 1, 2, 3, 127, 128, 129, 255, 256, 400, 511, 512, 698, 699}), 2e-2)
+
+
+def test_prefill_from_scratch_edges():
+    # rows before the first complete block see the window only; T not a multiple of m
+    L = LY.LayerCall("csa", 1, 301, 0, 0, d=128, rope_dims=32, H=16, m=4, w=9, k=8, HI=32, dI=64, seed=9,
+                     name="edge")
+    say("edge prefill", L)
+    t = _run(L)
+    _check_layer(L, t, lambda L: list(range(L.T)), 2e-2, max_band_rows=0.05)
+
+
+def test_layer_is_deterministic():
+    L = LY.LayerCall("csa", 1, 2048, 0, 0, d=512, H=64, m=4, w=128, k=256, HI=64, dI=128, seed=10, name="det")
+    t = LY.make_inputs(L)
+    a = LY.run_layer(L, t).clone()
+    ia = t["idx"].clone()
+    b = LY.run_layer(L, t)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(ia, t["idx"])
+
+
+# ----------------------------------------------------------------------------- full-size workloads
+
+def test_hca_prefill_16k_sampled():
+    L = LY.hca_prefill_16k()
+    say("HCA prefill 16k", L)
+    t = _run(L)
+    _check_layer(L, t, lambda L: sorted({0, 126, 127, 128, 255, 256, 8191, 8192, 16383} |
+                                         set(np.random.default_rng(0).choice(L.T, 24, replace=False).tolist())), 2e-2)
+
+
+def test_csa_prefill_64k_sampled():
+    L = LY.csa_prefill_64k()
+    say("CSA prefill 64k", L)
+    t = _run(L)
+    _check_layer(L, t, lambda L: sorted({0, 3, 4095, 4096, 4099, 32768, 65535} |
+                                         set(np.random.default_rng(1).choice(L.T, 16, replace=False).tolist())), 2e-2)
+
+
+def test_decode_1m_full():
+    for L in LY.decode_1m():
+        say("decode 1M", L)
+        t = _run(L)
+        _check_layer(L, t, lambda L: [0], 2e-2, max_band_rows=0.25)
+
+
+def test_chunked_prefill_512k_sampled():
+    for L in LY.chunked_prefill_512k():
+        say("chunked prefill 512k", L.name, L.kind)
+        t = _run(L)
+        _check_layer(L, t, lambda L: sorted({0, 1, 127, 128, 2048, 4095} |
+                                             set(np.random.default_rng(2).choice(L.T, 4, replace=False).tolist())), 2e-2)
+
+
+def test_indexer_topk_matches_its_two_halves():
+    # indexer_topk chunks its rows through a bounded workspace; the result must equal
+    # indexer_scores + topk_select over the whole matrix, bit for bit
+    say("indexer_topk == indexer_scores + topk_select")
+    bt, Tq, N, HI, dI, k = 2, 3000, 20000, 64, 128, 512
+    pos0 = N * 4 - Tq
+    qI = gen(51, "h2.q", (bt, Tq, HI, dI))
+    KI = gen(51, "h2.k", (bt, N, dI))
+    wI = uniform_device(51, "h2.w", (bt, Tq, HI), DEV)
+    a = B.indexer_topk(qI, wI, KI, pos0, 4, k)
+    sc = B.indexer_scores(qI, wI, KI, pos0, 4)
+    b = B.topk_select(sc, N, pos0, 4, k)
+    torch.cuda.synchronize()
+    assert B.indexer_workspace_bytes(bt, Tq, N, HI, k, B.BF16) < bt * Tq * B.score_ld(N) * 4  # it did chunk
+    assert torch.equal(a, b)
