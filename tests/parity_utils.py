@@ -23,15 +23,21 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
 
 
 def assert_storage_close(gpu: np.ndarray, exact: np.ndarray, dtype: str, what: str, rtol_f32=1e-5):
-    """bf16: within one bf16 ulp of the exact (fp64) value; f32: 1e-5 relative (+1e-6 abs)."""
+    """bf16: within one bf16 ulp of the exact (fp64) value.
+
+    f32: within 1e-5 of (|x| + RMS of its row). A compressed entry is a
+    weighted sum of up to m' rows; its fp32 rounding error scales with the
+    magnitude of the summed terms, i.e. the row's scale, not with the
+    (possibly cancelled) element itself.
+    """
+    err = np.abs(gpu - exact)
     if dtype == "bf16":
-        err = np.abs(gpu - exact)
         bad = err > bf16_ulp(exact) * (1 + 1e-9)
         assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} elements beyond 1 bf16 ulp, max err {err.max():.3g}"
     else:
-        err = np.abs(gpu - exact)
-        bad = err > rtol_f32 * np.abs(exact) + 1e-6
-        assert not bad.any(), f"{what}: {bad.sum()} elements beyond 1e-5 rel, max err {err.max():.3g}"
+        rms = np.sqrt(np.mean(exact * exact, axis=-1, keepdims=True))
+        bad = err > rtol_f32 * (np.abs(exact) + rms)
+        assert not bad.any(), f"{what}: {bad.sum()} elements beyond 1e-5 (|x| + row rms), max err {err.max():.3g}"
 
 
 def check_topk_row(gpu_row: np.ndarray, scores: np.ndarray, V: int, k: int, band: float = None,
