@@ -7,22 +7,27 @@
 // learnable per-head sink logits). "Inside DeepSeek V4", "Local window":
 // 128 recent uncompressed entries in every CSA and HCA layer.
 //
-// bf16 kernel (one workgroup = one query, all heads; wave w = heads
-// 16w..16w+15):
-//  * The query rows are RMSNormed and rotated at the query's position in
-//    registers, rounded to bf16 and kept as MFMA B operands (Q^T).
-//  * The query's key list -- selected or visible compressed entries, then
+// bf16 kernel: a workgroup takes QG consecutive queries (QG = 2 for HCA
+// prefill, whose neighbouring queries see the same compressed entries) and
+// HW waves of 16 heads per query.
+//  * Each wave RMSNorms and rotates its 16 query rows in registers and keeps
+//    them as bf16 B operands (Q^T); RoPE cos/sin are computed once per
+//    workgroup into LDS (angles formed in fp64).
+//  * The key list -- selected (CSA) or visible (HCA) compressed entries, then
 //    window rows -- is gathered 32 rows at a time into a double-buffered LDS
-//    tile (K = V: one tile serves both products).
-//  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 puts keys on rows, so after the
-//    online-softmax update each lane already holds its P values in the
-//    layout of the A operand of O = P V (lane = head, 8 keys); no shuffle.
-//  * For O = P V each lane reads 8 keys x 8 contiguous dims from LDS with
-//    16-byte loads and transposes them in registers into 8 B operands, so
-//    every O accumulator lane owns 8 contiguous output dims (16-byte stores,
-//    RoPE pairs in-lane).
-//  * Split-K (decode): a split writes (max, sum, unnormalised O) and a merge
-//    kernel combines splits in a fixed order, adds the sink and de-rotates.
+//    tile; one register-staged prefetch overlaps the next tile's loads with
+//    this tile's math. K = V: one tile serves both products.
+//  * S^T = K Q^T (v_mfma_f32_16x16x32_bf16) leaves each lane the logits of
+//    one head for 8 keys, exactly the B operand P^T of O^T = V^T P^T.
+//  * V^T comes straight from the row-major tile through gfx950's transpose
+//    LDS read (ds_read_b64_tr_b16), so no register transposes are needed and
+//    each accumulator lane owns 4 contiguous output dims of a single head:
+//    per-head rescale, sink, normalisation and RoPE de-rotation are in-lane.
+//  * The softmax reference only moves when a logit exceeds it by 2^8, so the
+//    O rescale is almost never executed; the final normalisation uses the
+//    same reference, so the result is unchanged.
+//  * Split-K (decode): a split writes (reference, sum, unnormalised O) and a
+//    merge kernel combines splits in a fixed order, adds the sink, de-rotates.
 // fp32 kernel: plain vector-ALU online softmax, one workgroup per
 // (query, head); it serves the fp32 mode.
 #include "device_common.h"
@@ -88,41 +93,74 @@ __device__ __forceinline__ int64_t key_row(const AttnArgs& a, const KeyList& L, 
   return -2 - (((int64_t)b * a.W + L.win_row0 + (u - L.n_comp)) * a.D);  // window: encoded < -1
 }
 
-// Key slot mapping shared by the P (A) and V (B) operands of O = P V:
-// slot jj of lane group g holds key (jj < 4 ? 4g + jj : 16 + 4g + jj - 4),
-// which is where S^T = K Q^T leaves the logits.
-__device__ __forceinline__ int pv_key(int g, int jj) { return jj < 4 ? 4 * g + jj : 12 + 4 * g + jj; }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_mfma(AttnArgs a) {
+// gfx950 LDS transpose read: within each group of 16 lanes, lane i receives the
+// (i % 4)-th 16-bit element of the 8-byte reads of lanes 4e + i/4, e = 0..3.
+__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+}
+
+// Logits of a query only grow the softmax reference when they exceed it by this
+// much (log2 units): the O/l rescale is then almost never needed, and P <= 2^8.
+constexpr float REF_SLACK = 8.0f;
+
+template <int D, int HW, int QG>
+__global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
+  constexpr int NW = HW * QG;
   constexpr int NT = NW * 64;
   constexpr int ROWE = D + 8;        // padded LDS row, bf16 elements
   constexpr int KS = D / 32;         // k-steps of S^T = K Q^T
-  constexpr int DG = D < 128 ? D : 128;
-  constexpr int E = DG / 16;         // contiguous output dims per lane per group (8 or 4)
-  constexpr int NG = D / DG;
-  constexpr int CPR = D / 8;         // 16-byte chunks per row
-  constexpr int CHUNKS = 32 * CPR;
-  constexpr int CPT = (CHUNKS + NT - 1) / NT;
+  constexpr int NTILE = D / 16;      // 16-dim output tiles of O^T = V^T P^T
+  constexpr int CPR = D / 8;         // 16-byte chunks per key row
+  constexpr int TPK = NT / 32;       // loader threads per key row
+  static_assert(CPR % TPK == 0, "loader mapping");
+  constexpr int CPT = CPR / TPK;     // chunks per loader thread per tile
+  constexpr int MAXPAIRS = D / 2;
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][32 * ROWE];
-  __shared__ uint32_t kvalid[2];
+  __shared__ __attribute__((aligned(16))) int kdesc[2][32];
+  __shared__ float rope_cs[QG][MAXPAIRS][2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
+  const int qi = wave / HW, hw = wave % HW;
+  const int64_t nqb = (a.Tq + QG - 1) / QG;
   const int64_t flat = (int64_t)gridDim.x - 1 - blockIdx.x;  // later (longer) rows first
-  const int b = (int)(flat / a.Tq);
-  const int64_t j = flat % a.Tq;
-  const int split = blockIdx.y;
+  const int b = (int)(flat / nqb);
+  const int64_t jb = (flat % nqb) * QG;
+  const int64_t jl = (jb + QG < a.Tq ? jb + QG : a.Tq) - 1;  // last query of the tile
+  const int64_t j = jb + qi < a.Tq ? jb + qi : jl;
+  const bool qvalid = jb + qi < a.Tq;
   const int64_t t = a.pos0 + j;
-  const int h = wave * 16 + n;
-  const bool hvalid = h < a.H;
-  const KeyList L = make_keys(a, b, j);
-  const int64_t nblk = (L.n_tot + 31) / 32;
+  const int h = hw * 16 + n;
+  const bool hvalid = qvalid && h < a.H;
+  const int split = blockIdx.y;
+  const bool csa = a.mode == CSKV_MODE_CSA;
+
+  // Key list shared by the tile's queries: [0, n_comp) compressed, then window positions lo .. t_last.
+  const int64_t t_first = a.pos0 + jb, t_last = a.pos0 + jl;
+  const int32_t* idxrow = csa ? a.idx + ((int64_t)b * a.Tq + jb) * a.k : nullptr;
+  const int64_t n_comp = csa ? a.k : visible_n(t_last, a.m, a.N);
+  int64_t lo = t_first - a.w + 1;
+  if (lo < 0) lo = 0;
+  const int64_t n_tot = n_comp + (t_last - lo + 1);
+  const int64_t v_q = csa ? 0 : visible_n(t, a.m, a.N);  // this query's visible entries (HCA)
+  const int64_t w_lo = t - a.w + 1;
+  const int64_t nblk = (n_tot + 31) / 32;
   const int64_t bps = (nblk + a.n_splits - 1) / a.n_splits;
   const int64_t blk0 = (int64_t)split * bps;
   const int64_t blk1 = blk0 + bps < nblk ? blk0 + bps : nblk;
 
-  // ---- query prologue: RMSNorm, RoPE at t, bf16 B operands (lane: head n, dims 32ks + 8g + 0..7)
+  // Rotary cos/sin of every pair at each query's position, once per workgroup.
+  const int npairs = a.rope_dims / 2;
+  for (int i = tid; i < QG * npairs; i += NT) {
+    const int q = i / npairs, pj = i % npairs;
+    const int64_t jq = jb + q < a.Tq ? jb + q : jl;
+    rope_cos_sin(a.pos0 + jq, pj, a.rope_dims, a.rope_base, &rope_cs[q][pj][0], &rope_cs[q][pj][1]);
+  }
+  __syncthreads();
+
+  // ---- query prologue: RMSNorm, RoPE at t -> bf16 B operands of S^T (lane: head n, dims 32ks+8g..+7)
   bf16x8 qb[KS];
   {
     const uint16_t* qp = (const uint16_t*)a.q + (((int64_t)b * a.Tq + j) * a.H + (hvalid ? h : 0)) * D;
@@ -144,17 +182,13 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dim = ks * 32 + 8 * g + e;
-        x[ks][e] *= inv * (a.q_norm_w ? a.q_norm_w[dim] : 1.f);
-      }
+      for (int e = 0; e < 8; ++e) x[ks][e] *= inv * (a.q_norm_w ? a.q_norm_w[ks * 32 + 8 * g + e] : 1.f);
       if (a.rope_dims > 0 && ks * 32 + 8 * g + 8 > rstart) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const int dim = ks * 32 + 8 * g + e;
           if (dim >= rstart) {
-            float cs, sn;
-            rope_cos_sin(t, (dim - rstart) >> 1, a.rope_dims, a.rope_base, &cs, &sn);
+            const float cs = rope_cs[qi][(dim - rstart) >> 1][0], sn = rope_cs[qi][(dim - rstart) >> 1][1];
             const float x0 = x[ks][e], x1 = x[ks][e + 1];
             x[ks][e] = x0 * cs - x1 * sn;
             x[ks][e + 1] = x0 * sn + x1 * cs;
@@ -170,44 +204,51 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(AttnArgs a) {
     }
   }
 
-  float m_run = -INFINITY, l_run = 0.f;  // per head n (same in all four lane groups)
-  f32x4 o[NG][E];
+  float m_ref = -INFINITY, l_run = 0.f;  // per head n, identical in the four lane groups
+  f32x4 o[NTILE];                        // O^T tile tt: lane holds dims 16tt+4g+i of head n
 #pragma unroll
-  for (int gr = 0; gr < NG; ++gr)
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[gr][e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < NTILE; ++tt) o[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- gather loader: 32 key rows per tile
-  const uint16_t* kvb = (const uint16_t*)a.kv;
-  const uint16_t* wnb = (const uint16_t*)a.win;
+  // ---- gather loader: thread -> (key row kr, chunks c0 + TPK*i)
+  const int kr = tid / TPK, c0 = tid % TPK;
+  const uint16_t* kvb = (const uint16_t*)a.kv + (int64_t)b * a.N * D;
+  const int64_t wrow0 = (int64_t)b * a.W - a.win_pos0;  // window row of position p: wrow0 + p
   u32x4 pre[CPT];
-  bool pre_ok = false;  // thread tid < 32: validity of key tid of the prefetched tile
+  int pre_desc = -1;
+  // desc: s >= 0 compressed entry; -1 absent; -2 - pos window row at position pos
   auto gload = [&](int64_t blk) {
-#pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NT;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ch < CHUNKS) {
-        const int64_t off = key_row(a, L, b, blk * 32 + ch / CPR);
-        if (off >= 0)
-          v = *reinterpret_cast<const u32x4*>(kvb + off + (ch % CPR) * 8);
-        else if (off < -1)
-          v = *reinterpret_cast<const u32x4*>(wnb + (-2 - off) + (ch % CPR) * 8);
+    const int64_t u = blk * 32 + kr;
+    const uint16_t* src = nullptr;
+    int desc = -1;
+    if (u < n_comp) {
+      const int64_t s_ = idxrow ? (int64_t)idxrow[u] : u;
+      if (s_ >= 0 && s_ < a.N) {
+        desc = (int)s_;
+        src = kvb + s_ * D;
       }
-      pre[c] = v;
+    } else if (u < n_tot) {
+      const int64_t pos = lo + (u - n_comp);
+      desc = -2 - (int)(pos - a.pos0 + a.w);  // window positions relative to pos0 - w, >= 0
+      src = (const uint16_t*)a.win + (wrow0 + pos) * D;
     }
-    if (tid < 32) pre_ok = key_row(a, L, b, blk * 32 + tid) != -1;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (src) v = *reinterpret_cast<const u32x4*>(src + (c0 + TPK * i) * 8);
+      pre[i] = v;
+    }
+    pre_desc = desc;
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * NT;
-      if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&kt[buf][(ch / CPR) * ROWE + (ch % CPR) * 8]) = pre[c];
-    }
-    if (wave == 0) {
-      const uint64_t bal = __ballot(tid < 32 && pre_ok);
-      if (tid == 0) kvalid[buf] = (uint32_t)bal;
-    }
+    for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4*>(&kt[buf][kr * ROWE + (c0 + TPK * i) * 8]) = pre[i];
+    if (c0 == 0) kdesc[buf][kr] = pre_desc;
+  };
+  auto key_ok = [&](int d) -> bool {
+    if (d >= 0) return csa || d < v_q;
+    if (d == -1) return false;
+    const int64_t pos = (int64_t)(-2 - d) + a.pos0 - a.w;
+    return pos >= w_lo && pos <= t;
   };
 
   if (blk0 < blk1) {
@@ -229,149 +270,99 @@ __global__ __launch_bounds__(NW * 64) void attn_mfma(AttnArgs a) {
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[ks], s1, 0, 0, 0);
     }
-    const uint32_t vm = kvalid[buf];
+    const int4 d0 = *reinterpret_cast<const int4*>(&kdesc[buf][4 * g]);
+    const int4 d1 = *reinterpret_cast<const int4*>(&kdesc[buf][16 + 4 * g]);
     float sv[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = ((vm >> (4 * g + i)) & 1u) ? s0[i] * a.scale_log2 : -INFINITY;
-      sv[4 + i] = ((vm >> (16 + 4 * g + i)) & 1u) ? s1[i] * a.scale_log2 : -INFINITY;
-    }
-    float mb = sv[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mb = fmaxf(mb, sv[i]);
+    sv[0] = key_ok(d0.x) ? s0[0] * a.scale_log2 : -INFINITY;
+    sv[1] = key_ok(d0.y) ? s0[1] * a.scale_log2 : -INFINITY;
+    sv[2] = key_ok(d0.z) ? s0[2] * a.scale_log2 : -INFINITY;
+    sv[3] = key_ok(d0.w) ? s0[3] * a.scale_log2 : -INFINITY;
+    sv[4] = key_ok(d1.x) ? s1[0] * a.scale_log2 : -INFINITY;
+    sv[5] = key_ok(d1.y) ? s1[1] * a.scale_log2 : -INFINITY;
+    sv[6] = key_ok(d1.z) ? s1[2] * a.scale_log2 : -INFINITY;
+    sv[7] = key_ok(d1.w) ? s1[3] * a.scale_log2 : -INFINITY;
+    float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    const float m_new = fmaxf(m_run, mb);
-    float alpha = 1.f, p[8];
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = 0.f;
-    } else {
-      alpha = exp2f(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) p[i] = exp2f(sv[i] - m_new);
+    // lazy reference: move it only when a logit exceeds it by REF_SLACK
+    const bool upd = mb > m_ref + REF_SLACK;
+    float alpha = 1.f;
+    if (upd) {
+      alpha = exp2f(m_ref - mb);  // 0 when the reference was -inf
+      m_ref = mb;
     }
-    float ps = 0.f;
+    float p[8], ps = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ps += p[i];
+    for (int i = 0; i < 8; ++i) {
+      p[i] = m_ref == -INFINITY ? 0.f : exp2f(sv[i] - m_ref);
+      ps += p[i];
+    }
     ps += __shfl_xor(ps, 16, 64);
     ps += __shfl_xor(ps, 32, 64);
     l_run = l_run * alpha + ps;
-    m_run = m_new;
-
-    // rescale O rows (heads 4g+i) by their alpha
-    float al[4];
+    if (__ballot(upd) != 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
-#pragma unroll
-    for (int gr = 0; gr < NG; ++gr)
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) o[gr][e][i] *= al[i];
-
+      for (int tt = 0; tt < NTILE; ++tt) o[tt] *= alpha;
+    }
     u32x4 pp;
     pp[0] = pack_bf16x2(p[0], p[1]);
     pp[1] = pack_bf16x2(p[2], p[3]);
     pp[2] = pack_bf16x2(p[4], p[5]);
     pp[3] = pack_bf16x2(p[6], p[7]);
-    const bf16x8 pa = __builtin_bit_cast(bf16x8, pp);
+    const bf16x8 pb = __builtin_bit_cast(bf16x8, pp);
 
-    // O += P V, 8 keys x E dims per lane, transposed in registers into E B operands
+    // O^T += V^T P^T: A = V^T via transpose reads (lane n of group g: keys 4g+e / 16+4g+e for
+    // e = n/4, dims 16tt + 4(n%4) .. +3), B = P^T already in this lane (head n, 8 keys).
+    const uint16_t* vp0 = &kt[buf][(4 * g + (n >> 2)) * ROWE + 4 * (n & 3)];
+    const uint16_t* vp1 = vp0 + 16 * ROWE;
 #pragma unroll
-    for (int gr = 0; gr < NG; ++gr) {
-      uint32_t vr[8][E / 2];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const uint16_t* vp = &kt[buf][pv_key(g, jj) * ROWE + gr * DG + E * n];
-        if constexpr (E == 8) {
-          const u32x4 r = *reinterpret_cast<const u32x4*>(vp);
-          vr[jj][0] = r[0]; vr[jj][1] = r[1]; vr[jj][2] = r[2]; vr[jj][3] = r[3];
-        } else {
-          const uint2 r = *reinterpret_cast<const uint2*>(vp);
-          vr[jj][0] = r.x; vr[jj][1] = r.y;
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        u32x4 bv;
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const uint32_t lo = vr[2 * q2][e >> 1], hi = vr[2 * q2 + 1][e >> 1];
-          bv[q2] = (e & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
-        }
-        o[gr][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, bv), o[gr][e], 0, 0, 0);
-      }
+    for (int tt = 0; tt < NTILE; ++tt) {
+      const v4i16 lo4 = lds_read_tr16(vp0 + 16 * tt);
+      const v4i16 hi4 = lds_read_tr16(vp1 + 16 * tt);
+      const v4i16 av[2] = {lo4, hi4};
+      o[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, o[tt], 0, 0, 0);
     }
     if (blk + 1 < blk1) lstore(buf ^ 1);
     __syncthreads();
   }
 
-  // ---- epilogue. Lane holds O[head 4g+i][gr*DG + E*n + e].
+  // ---- epilogue: lane holds O[head n][16tt + 4g + i]
+  if (!hvalid) return;
   const int64_t row = (int64_t)b * a.Tq + j;
   if (a.n_splits > 1) {
-    float* po = a.part_o + ((row * a.n_splits + split) * a.H) * (int64_t)D;
+    float* po = a.part_o + ((row * a.n_splits + split) * a.H + h) * (int64_t)D + 4 * g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = wave * 16 + 4 * g + i;
-      if (hh >= a.H) continue;
-#pragma unroll
-      for (int gr = 0; gr < NG; ++gr) {
-        float v[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[e] = o[gr][e][i];
-        store_vec<float, 4>(po + (int64_t)hh * D + gr * DG + E * n, v);
-        if constexpr (E == 8) store_vec<float, 4>(po + (int64_t)hh * D + gr * DG + E * n + 4, v + 4);
-      }
-    }
-    if (g == 0 && hvalid) {
+    for (int tt = 0; tt < NTILE; ++tt) *reinterpret_cast<f32x4*>(po + 16 * tt) = o[tt];
+    if (g == 0) {
       float* pm = a.part_ml + ((row * a.n_splits + split) * a.H + h) * 2;
-      pm[0] = m_run;
+      pm[0] = m_ref;
       pm[1] = l_run;
     }
     return;
   }
-
-  // single split: fold the sink, normalise, de-rotate, store
-  const float z = (a.sink && hvalid) ? a.sink[h] * 1.4426950408889634f : -INFINITY;
-  const float M = fmaxf(m_run, z);
-  const float em = m_run == -INFINITY ? 0.f : exp2f(m_run - M);
+  const float z = a.sink ? a.sink[h] * 1.4426950408889634f : -INFINITY;
+  const float M = fmaxf(m_ref, z);
+  const float em = m_ref == -INFINITY ? 0.f : exp2f(m_ref - M);
   const float lt = l_run * em + (z == -INFINITY ? 0.f : exp2f(z - M));
   const float fac = lt > 0.f ? em / lt : 0.f;
-  if (a.lse && g == 0 && hvalid) a.lse[row * a.H + h] = (M + log2f(lt)) * 0.6931471805599453f;
-  float fi[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) fi[i] = __shfl(fac, 4 * g + i, 64);
+  if (a.lse && g == 0) a.lse[row * a.H + h] = (M + log2f(lt)) * 0.6931471805599453f;
   const int rstart = D - a.rope_dims;
+  uint16_t* op = (uint16_t*)a.out + (row * a.H + h) * (int64_t)D + 4 * g;
 #pragma unroll
-  for (int gr = 0; gr < NG; ++gr) {
-    const int d0 = gr * DG + E * n;
-    float cs[E / 2], sn[E / 2];
-    const bool rot = a.rope_on_output && a.rope_dims > 0 && d0 + E > rstart;
-    if (rot) {
+  for (int tt = 0; tt < NTILE; ++tt) {
+    float v[4] = {o[tt][0] * fac, o[tt][1] * fac, o[tt][2] * fac, o[tt][3] * fac};
+    const int d0 = 16 * tt + 4 * g;
+    if (a.rope_on_output && a.rope_dims > 0 && d0 >= rstart) {
 #pragma unroll
-      for (int e = 0; e < E; e += 2) {
-        cs[e / 2] = 1.f;
-        sn[e / 2] = 0.f;
-        if (d0 + e >= rstart) rope_cos_sin(-t, (d0 + e - rstart) >> 1, a.rope_dims, a.rope_base, &cs[e / 2], &sn[e / 2]);
+      for (int e = 0; e < 4; e += 2) {
+        const float cs = rope_cs[qi][(d0 + e - rstart) >> 1][0];
+        const float sn = -rope_cs[qi][(d0 + e - rstart) >> 1][1];  // rotate back by -t
+        const float x0 = v[e], x1 = v[e + 1];
+        v[e] = x0 * cs - x1 * sn;
+        v[e + 1] = x0 * sn + x1 * cs;
       }
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = wave * 16 + 4 * g + i;
-      float v[E];
-#pragma unroll
-      for (int e = 0; e < E; ++e) v[e] = o[gr][e][i] * fi[i];
-      if (rot) {
-#pragma unroll
-        for (int e = 0; e < E; e += 2) {
-          const float x0 = v[e], x1 = v[e + 1];
-          v[e] = x0 * cs[e / 2] - x1 * sn[e / 2];
-          v[e + 1] = x0 * sn[e / 2] + x1 * cs[e / 2];
-        }
-      }
-      if (hh < a.H) store_vec<bf16, E>((bf16*)a.out + (row * a.H + hh) * D + d0, v);
-    }
+    store_vec<bf16, 4>(reinterpret_cast<bf16*>(op + 16 * tt), v);
   }
 }
 
@@ -543,29 +534,57 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------- host
-template <int D, int NW>
+template <int D, int HW, int QG>
 static void launch_attn(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_mfma<D, NW>), grid, dim3(NW * 64), 0, st, a);
+  hipLaunchKernelGGL((attn_mfma<D, HW, QG>), grid, dim3(HW * QG * 64), 0, st, a);
 }
 
-template <int D>
-static bool dispatch_nw(int nw, const AttnArgs& a, dim3 grid, hipStream_t st) {
-  switch (nw) {
-    case 1: launch_attn<D, 1>(a, grid, st); return true;
-    case 2: launch_attn<D, 2>(a, grid, st); return true;
-    case 4: launch_attn<D, 4>(a, grid, st); return true;
-    case 8: launch_attn<D, 8>(a, grid, st); return true;
+// Workgroup shape: HW waves of 16 heads per query; QG queries share one key stream
+// (HCA, where neighbouring queries see the same compressed entries and overlapping windows).
+template <int D, int HW>
+static bool dispatch_qg(int qg, const AttnArgs& a, int batch, hipStream_t st) {
+  const unsigned splits = (unsigned)a.n_splits;
+  switch (qg) {
+    case 1:
+      if constexpr ((D / 8) % (HW * 2) == 0) {
+        launch_attn<D, HW, 1>(a, dim3((unsigned)(batch * a.Tq), splits), st);
+        return true;
+      }
+      return false;
+    case 2:
+      if constexpr (HW * 2 <= 8 && (D / 8) % (HW * 2 * 2) == 0) {
+        launch_attn<D, HW, 2>(a, dim3((unsigned)(batch * ((a.Tq + 1) / 2)), splits), st);
+        return true;
+      }
+      return false;
     default: return false;
   }
 }
 
-static bool dispatch_attn(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  const int nw = a.H <= 16 ? 1 : a.H <= 32 ? 2 : a.H <= 64 ? 4 : 8;
+template <int D>
+static bool dispatch_hw(int hw, int qg, const AttnArgs& a, int batch, hipStream_t st) {
+  switch (hw) {
+    case 1: return dispatch_qg<D, 1>(qg, a, batch, st);
+    case 2: return dispatch_qg<D, 2>(qg, a, batch, st);
+    case 4: return dispatch_qg<D, 4>(qg, a, batch, st);
+    case 8: return dispatch_qg<D, 8>(qg, a, batch, st);
+    default: return false;
+  }
+}
+
+#ifndef CSKV_HCA_QG
+#define CSKV_HCA_QG 2
+#endif
+
+static bool dispatch_attn(const AttnArgs& a, int batch, hipStream_t st) {
+  const int hw = a.H <= 16 ? 1 : a.H <= 32 ? 2 : a.H <= 64 ? 4 : 8;
+  // HCA prefill: CSKV_HCA_QG queries per workgroup share the gathered key tiles
+  const int qg = (a.mode == CSKV_MODE_HCA && a.n_splits == 1 && a.Tq >= 2 && hw <= 4 && a.D >= 128) ? CSKV_HCA_QG : 1;
   switch (a.D) {
-    case 64: return dispatch_nw<64>(nw, a, grid, st);
-    case 128: return dispatch_nw<128>(nw, a, grid, st);
-    case 256: return dispatch_nw<256>(nw, a, grid, st);
-    case 512: return dispatch_nw<512>(nw, a, grid, st);
+    case 64: return dispatch_hw<64>(hw, qg, a, batch, st);
+    case 128: return dispatch_hw<128>(hw, qg, a, batch, st);
+    case 256: return dispatch_hw<256>(hw, qg, a, batch, st);
+    case 512: return dispatch_hw<512>(hw, qg, a, batch, st);
     default: return false;
   }
 }
@@ -644,7 +663,7 @@ extern "C" int compressed_attn_prefill(int mode, const void* q, const void* kv, 
                          out, lse);
   hipStream_t s = (hipStream_t)stream;
   if (dtype == CSKV_F32) return launch_f32(a, batch, s);
-  if (!dispatch_attn(a, dim3((unsigned)(batch * Tq), 1), s)) return CSKV_ERR_UNSUPPORTED;
+  if (!dispatch_attn(a, batch, s)) return CSKV_ERR_UNSUPPORTED;
   return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
 }
 
@@ -686,7 +705,7 @@ extern "C" int compressed_attn_decode(int mode, const void* q, const void* kv, c
   if (dtype == CSKV_F32) return launch_f32(a, batch, s);
   const int S = decode_splits(batch, Tq, max_keys(mode, Tq, N, pos0, m, k, w), n_splits);
   if (S == 1) {
-    if (!dispatch_attn(a, dim3((unsigned)(batch * Tq), 1), s)) return CSKV_ERR_UNSUPPORTED;
+    if (!dispatch_attn(a, batch, s)) return CSKV_ERR_UNSUPPORTED;
     return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
   }
   const size_t need = (size_t)batch * Tq * S * H * ((size_t)d + 2) * 4;
@@ -695,7 +714,7 @@ extern "C" int compressed_attn_decode(int mode, const void* q, const void* kv, c
   a.n_splits = S;
   a.part_o = (float*)workspace;
   a.part_ml = a.part_o + (size_t)batch * Tq * S * H * d;
-  if (!dispatch_attn(a, dim3((unsigned)(batch * Tq), (unsigned)S), s)) return CSKV_ERR_UNSUPPORTED;
+  if (!dispatch_attn(a, batch, s)) return CSKV_ERR_UNSUPPORTED;
   if (hipGetLastError() != hipSuccess) return CSKV_ERR_HIP;
   hipLaunchKernelGGL((attn_merge<bf16>), dim3((unsigned)(batch * Tq), (unsigned)H), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;

@@ -27,8 +27,13 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const bf16x2 r = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 template <typename T>
@@ -128,14 +133,11 @@ __device__ __forceinline__ float wave_max(float v) {
 // to 2^20 and beyond keep full fp32 accuracy in cos/sin.
 __device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, int rope_dims, float base, float* c,
                                              float* s) {
-  double theta = exp2(-(2.0 * j / (double)rope_dims) * log2((double)base));
+  const double theta = pow((double)base, -2.0 * j / (double)rope_dims);
   double a = (double)pos * theta;
   const double two_pi = 6.283185307179586476925286766559;
-  a = a - two_pi * rint(a / two_pi);
-  double sd, cd;
-  sincos(a, &sd, &cd);
-  *c = (float)cd;
-  *s = (float)sd;
+  a = a - two_pi * rint(a / two_pi);  // |a| <= pi, exact to ~1e-16 relative of pos * theta
+  sincosf((float)a, s, c);
 }
 
 // Order-preserving map of an fp32 score to uint32 (larger float -> larger key).

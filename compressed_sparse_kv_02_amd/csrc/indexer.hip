@@ -15,12 +15,14 @@
 // (decode) the 8 waves take different key blocks and many workgroups split
 // the key range. Scores go to a caller workspace as fp32 rows.
 //
-// Selection: one 1024-thread workgroup per query row finds the exact k-th
-// largest score by a 3-pass radix select (11 + 11 + 10 bits) on an
-// order-preserving uint32 key, histogramming in LDS (the row itself is kept
-// in LDS when it fits), then compacts the winners in index order with block
-// prefix sums, so ties resolve to the smaller index and the output is
-// ascending without a sort.
+// Selection: one 1024-thread workgroup per query row. A strided sample of the
+// row gives a threshold that about 3k entries exceed; one vectorised pass
+// keeps those entries (in index order) in LDS, an exact 3-pass radix select
+// (11 + 11 + 10 bits, order-preserving uint32 keys) finds the k-th largest
+// among them, and an in-order pick with block prefix sums writes the result:
+// ties resolve to the smaller index and the output is ascending without a
+// sort. Should the sample miss, the row falls back to the exact radix select
+// over global memory.
 #include "device_common.h"
 #include "abi_common.h"
 
@@ -184,7 +186,8 @@ __global__ __launch_bounds__(256) void indexer_score_f32(IdxArgs a) {
 // Exact top-k per row
 // ----------------------------------------------------------------------------
 constexpr int TOPK_THREADS = 1024;
-constexpr int TOPK_CACHE = 30720;  // keys kept in LDS (120 KiB)
+constexpr int TOPK_CAP = 8192;      // candidate (key, index) pairs held in LDS
+constexpr int TOPK_SAMPLES = 4096;  // strided sample of a long row, for the candidate threshold
 
 // Exclusive prefix sum over the workgroup; also returns the total.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total) {
@@ -209,11 +212,92 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total
   return pre + incl - v;
 }
 
+struct TopkShared {
+  int hist[2048];
+  int wsum[TOPK_THREADS / 64];
+  int sel_bin, sel_above, count;
+};
+
+// Radix select (11 + 11 + 10 bits): the kk-th largest of n keys read through key_at.
+// Returns it in tau; `need` = how many keys equal to tau belong to the top kk.
+template <typename KeyAt>
+__device__ void radix_select(KeyAt key_at, int64_t n, int kk, TopkShared& sh, uint32_t& tau, int& need) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  need = kk;
+  const int shifts[3] = {21, 10, 0};
+  const int nbits[3] = {11, 11, 10};
+  for (int p = 0; p < 3; ++p) {
+    const int nb = 1 << nbits[p];
+    const uint32_t bmask = (uint32_t)nb - 1u;
+    for (int i = tid; i < 2048; i += TOPK_THREADS) sh.hist[i] = 0;
+    __syncthreads();
+    for (int64_t s = tid; s < n; s += TOPK_THREADS) {
+      const uint32_t key = key_at(s);
+      if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shifts[p]) & bmask], 1);
+    }
+    __syncthreads();
+    const int bpt = nb / TOPK_THREADS;  // bins per thread, descending
+    int cnt[2] = {0, 0}, loc = 0;
+    for (int q = 0; q < bpt; ++q) {
+      cnt[q] = sh.hist[nb - 1 - (tid * bpt + q)];
+      loc += cnt[q];
+    }
+    int total;
+    int above = block_exclusive_scan(loc, sh.wsum, total);
+    for (int q = 0; q < bpt; ++q) {
+      if (above < need && need <= above + cnt[q]) {
+        sh.sel_bin = nb - 1 - (tid * bpt + q);
+        sh.sel_above = above;
+      }
+      above += cnt[q];
+    }
+    __syncthreads();
+    need -= sh.sel_above;
+    prefix |= (uint32_t)sh.sel_bin << shifts[p];
+    pmask |= bmask << shifts[p];
+    __syncthreads();
+  }
+  tau = prefix;
+}
+
+// Writes, in index order, the entries with key > tau plus the first `need` with key == tau.
+template <typename KeyAt, typename IdxAt>
+__device__ void ordered_pick(KeyAt key_at, IdxAt idx_at, int64_t n, uint32_t tau, int need, int32_t* out,
+                             TopkShared& sh) {
+  const int tid = threadIdx.x;
+  int eq_taken = 0, written = 0;
+  for (int64_t base = 0; base < n; base += TOPK_THREADS) {
+    const int64_t s = base + tid;
+    uint32_t key = 0;
+    if (s < n) key = key_at(s);
+    const int gt = (s < n && key > tau) ? 1 : 0;
+    const int eq = (s < n && key == tau) ? 1 : 0;
+    int eq_tot;
+    const int eq_rank = block_exclusive_scan(eq, sh.wsum, eq_tot);
+    const int sel = gt | (eq && (eq_taken + eq_rank) < need ? 1 : 0);
+    int sel_tot;
+    const int pos = block_exclusive_scan(sel, sh.wsum, sel_tot);
+    if (sel) out[written + pos] = idx_at(s);
+    eq_taken += eq_tot;
+    written += sel_tot;
+  }
+}
+
+// One 1024-thread workgroup per query row.
+//  * V <= CAP: the whole row becomes the candidate set.
+//  * otherwise: the (3k * S / V)-th largest of S strided samples gives a
+//    threshold tau0; one vectorised pass over the row keeps every entry with
+//    key >= tau0, in index order, as candidates (about 3k of them).
+//  * exact radix select among the candidates, then an in-order pick.
+// If the candidates do not hold at least k entries (or overflow LDS), the
+// row falls back to the exact 3-pass radix select over global memory. Both
+// routes return the same, exact set.
 __global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
-  __shared__ uint32_t cache[TOPK_CACHE];
-  __shared__ int hist[2048];
-  __shared__ int wsum[TOPK_THREADS / 64];
-  __shared__ int sel_bin, sel_above;
+  __shared__ uint32_t ckey[TOPK_CAP];
+  __shared__ int32_t cidx[TOPK_CAP];
+  __shared__ uint32_t samp[TOPK_SAMPLES];
+  __shared__ TopkShared sh;
 
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
@@ -227,65 +311,66 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
     return;
   }
   const float* row = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
-  const bool cached = V <= TOPK_CACHE;
-  if (cached)
-    for (int64_t s = tid; s < V; s += TOPK_THREADS) cache[s] = score_key(row[s]);
-  auto key_at = [&](int64_t s) -> uint32_t { return cached ? cache[s] : score_key(row[s]); };
-
-  uint32_t prefix = 0, pmask = 0;
-  int need = k;
-  const int shifts[3] = {21, 10, 0};
-  const int nbits[3] = {11, 11, 10};
-  for (int p = 0; p < 3; ++p) {
-    const int nb = 1 << nbits[p];
-    const uint32_t bmask = (uint32_t)nb - 1u;
-    for (int i = tid; i < 2048; i += TOPK_THREADS) hist[i] = 0;
-    __syncthreads();
+  int n_cand = 0;
+  if (V <= TOPK_CAP) {
     for (int64_t s = tid; s < V; s += TOPK_THREADS) {
-      const uint32_t key = key_at(s);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shifts[p]) & bmask], 1);
+      ckey[s] = score_key(row[s]);
+      cidx[s] = (int32_t)s;
     }
+    n_cand = (int)V;
     __syncthreads();
-    // Bins in descending order; thread owns bpt consecutive ones.
-    const int bpt = nb / TOPK_THREADS;  // 2 or 1
-    int cnt[2] = {0, 0}, loc = 0;
-    for (int q = 0; q < bpt; ++q) {
-      cnt[q] = hist[nb - 1 - (tid * bpt + q)];
-      loc += cnt[q];
-    }
-    int total;
-    int above = block_exclusive_scan(loc, wsum, total);
-    for (int q = 0; q < bpt; ++q) {
-      if (above < need && need <= above + cnt[q]) {
-        sel_bin = nb - 1 - (tid * bpt + q);
-        sel_above = above;
+  } else {
+    // threshold from a strided sample
+    for (int i = tid; i < TOPK_SAMPLES; i += TOPK_THREADS) samp[i] = score_key(row[(int64_t)i * V / TOPK_SAMPLES]);
+    __syncthreads();
+    int r = (int)(((int64_t)3 * k * TOPK_SAMPLES + V - 1) / V);
+    if (r > TOPK_SAMPLES) r = TOPK_SAMPLES;
+    uint32_t tau0;
+    int need0;
+    radix_select([&](int64_t s) { return samp[s]; }, TOPK_SAMPLES, r, sh, tau0, need0);
+    // one pass: keep key >= tau0 in index order (4 entries per thread per chunk)
+    int cnt = 0;
+    for (int64_t base = 0; base < V; base += 4 * TOPK_THREADS) {
+      const int64_t s0 = base + 4 * tid;
+      float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+      if (s0 < V) v = *reinterpret_cast<const float4*>(row + s0);  // rows are padded to 64 entries
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+      uint32_t kk4[4];
+      int f = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kk4[e] = score_key(vv[e]);
+        if (s0 + e < V && kk4[e] >= tau0) ++f;
       }
-      above += cnt[q];
+      int tot;
+      int pos = cnt + block_exclusive_scan(f, sh.wsum, tot);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (s0 + e < V && kk4[e] >= tau0) {
+          if (pos < TOPK_CAP) {
+            ckey[pos] = kk4[e];
+            cidx[pos] = (int32_t)(s0 + e);
+          }
+          ++pos;
+        }
+      }
+      cnt += tot;
     }
     __syncthreads();
-    const int bin = sel_bin;
-    need -= sel_above;
-    prefix |= (uint32_t)bin << shifts[p];
-    pmask |= bmask << shifts[p];
-    __syncthreads();
+    n_cand = cnt;
   }
-  // prefix is the k-th largest key; `need` equal keys are taken (smallest indices first).
-  const uint32_t tau = prefix;
-  int eq_taken = 0, written = 0;
-  for (int64_t base = 0; base < V; base += TOPK_THREADS) {
-    const int64_t s = base + tid;
-    uint32_t key = 0;
-    if (s < V) key = key_at(s);
-    const int gt = (s < V && key > tau) ? 1 : 0;
-    const int eq = (s < V && key == tau) ? 1 : 0;
-    int eq_tot;
-    const int eq_rank = block_exclusive_scan(eq, wsum, eq_tot);
-    const int sel = gt | (eq && (eq_taken + eq_rank) < need ? 1 : 0);
-    int sel_tot;
-    const int pos = block_exclusive_scan(sel, wsum, sel_tot);
-    if (sel) out[written + pos] = (int32_t)s;
-    eq_taken += eq_tot;
-    written += sel_tot;
+  if (n_cand >= k && n_cand <= TOPK_CAP) {
+    uint32_t tau;
+    int need;
+    radix_select([&](int64_t s) { return ckey[s]; }, n_cand, k, sh, tau, need);
+    ordered_pick([&](int64_t s) { return ckey[s]; }, [&](int64_t s) { return cidx[s]; }, n_cand, tau, need,
+                 out, sh);
+  } else {
+    uint32_t tau;
+    int need;
+    auto key_at = [&](int64_t s) { return score_key(row[s]); };
+    radix_select(key_at, V, k, sh, tau, need);
+    ordered_pick(key_at, [&](int64_t s) { return (int32_t)s; }, V, tau, need, out, sh);
   }
 }
 
