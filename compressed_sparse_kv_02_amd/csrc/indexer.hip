@@ -47,12 +47,17 @@ struct IdxArgs {
 // ----------------------------------------------------------------------------
 // bf16 scoring on the matrix cores
 // ----------------------------------------------------------------------------
+// ReLU on the bit pattern: for non-NaN x, max(bits(x), 0) as int32 is bits(max(x, 0))
+// (negative floats, -0.0 included, are negative as int32). One VALU op, no NaN canonicalisation.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 template <int HT, int KS, int QB>
 __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
   constexpr int WAVES = 8;
-  constexpr int KW = WAVES / QB;       // key blocks per tile
+  constexpr int KW = WAVES / QB;       // key lanes: waves that take different key blocks
+  constexpr int SUB = QB == 8 ? 4 : 1; // 32-key sub-blocks per wave per tile
   constexpr int DI = 16 * KS;
-  constexpr int TILE = KW * 32;        // keys per LDS tile
+  constexpr int TILE = KW * SUB * 32;  // keys per LDS tile (128 or 256)
   constexpr int ROW = DI + 8;          // padded LDS row (bf16), +16 bytes vs bank conflicts
   constexpr int CPR = DI / 8;          // 16-byte chunks per key row
   constexpr int CHUNKS = TILE * CPR;
@@ -74,6 +79,8 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
   if (kend > vmax) kend = vmax;
   if (kbeg >= kend) return;  // uniform for the workgroup
   const int64_t vj = qvalid ? visible_entries(a.pos0 + j, a.m, a.N) : 0;
+  const int nkeys = (int)(kend - kbeg);         // keys of this workgroup (< 2^31)
+  const int vrel = (int)((vj > kbeg ? vj : kbeg) - kbeg);  // visible keys of this query, relative
 
   // A operands: lane holds head (lane % 32) of each 32-head tile, 8 dims per k-step.
   bf16x8 qa[HT][KS];
@@ -99,19 +106,19 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
     }
   }
 
-  const uint16_t* kbase = (const uint16_t*)a.KI + (int64_t)b * a.N * DI;
-  float* srow = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
-  const int64_t ntiles = (kend - kbeg + TILE - 1) / TILE;
+  const uint16_t* kbase = (const uint16_t*)a.KI + ((int64_t)b * a.N + kbeg) * DI;
+  float* srow = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS + kbeg;
+  const int ntiles = (nkeys + TILE - 1) / TILE;
 
   u32x4 pre[CPT];
-  auto gload = [&](int64_t t0) {
+  auto gload = [&](int t0) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ch = tid + c * 512;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (ch < CHUNKS) {
-        const int64_t s = t0 + ch / CPR;
-        if (s < kend) v = *reinterpret_cast<const u32x4*>(kbase + s * DI + (ch % CPR) * 8);
+        const int s = t0 + ch / CPR;
+        if (s < nkeys) v = *reinterpret_cast<const u32x4*>(kbase + (int64_t)s * DI + (ch % CPR) * 8);
       }
       pre[c] = v;
     }
@@ -123,34 +130,41 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
       if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&kt[buf][(ch / CPR) * ROW + (ch % CPR) * 8]) = pre[c];
     }
   };
-
-  gload(kbeg);
-  lstore(0);
-  __syncthreads();
-  for (int64_t it = 0; it < ntiles; ++it) {
-    const int64_t t0 = kbeg + it * TILE;
-    if (it + 1 < ntiles) gload(t0 + TILE);
-    f32x16 acc[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[ht][i] = 0.f;
-    const uint16_t* kp = &kt[it & 1][(kl * 32 + (lane & 31)) * ROW + 8 * (lane >> 5)];
+  auto mma = [&](const uint16_t* kp, f32x16 (&acc)[HT]) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 bv = *reinterpret_cast<const bf16x8*>(kp + ks * 16);
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
-        acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][ks], bv, acc[ht], 0, 0, 0);
+        acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][ks], bv, ks == 0 ? f32x16{} : acc[ht], 0, 0, 0);
     }
+  };
+  // ReLU, head weights, sum over the 32 heads of each tile, then over tiles; lanes 0-31 store key lane%32.
+  auto epilogue = [&](const f32x16 (&acc)[HT], int s0) {
     float part = 0.f;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) part += wv[ht][i] * fmaxf(acc[ht][i], 0.f);
+      for (int i = 0; i < 16; ++i) part = __builtin_fmaf(relu_bits(acc[ht][i]), wv[ht][i], part);
     part += __shfl_xor(part, 32, 64);
-    const int64_t s = t0 + kl * 32 + (lane & 31);
-    if (qvalid && lane < 32 && s < kend) srow[s] = s < vj ? part : -INFINITY;
+    const int s = s0 + (lane & 31);
+    if (qvalid && lane < 32 && s < nkeys) srow[s] = s < vrel ? part : -INFINITY;
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int t0 = it * TILE;
+    if (it + 1 < ntiles) gload(t0 + TILE);
+    const uint16_t* kp = &kt[it & 1][(kl * SUB * 32 + (lane & 31)) * ROW + 8 * (lane >> 5)];
+    f32x16 acc[2][HT];
+    mma(kp, acc[0]);
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      if (sb + 1 < SUB) mma(kp + (sb + 1) * 32 * ROW, acc[(sb + 1) & 1]);  // next sub-block's MFMAs first
+      epilogue(acc[sb & 1], t0 + (kl * SUB + sb) * 32);
+    }
     if (it + 1 < ntiles) lstore((it + 1) & 1);
     __syncthreads();
   }
@@ -440,7 +454,7 @@ static int launch_scores(IdxArgs& a, int batch, int qb, int dtype, hipStream_t s
   if (vmax <= 0) return CSKV_OK;
   if (dtype == CSKV_BF16) {
     const int64_t qblocks = ceil_div(a.nrows, qb);
-    const int64_t tile = (8 / qb) * 32;
+    const int64_t tile = qb == 8 ? 128 : 256;
     int64_t splits = ceil_div(1024, qblocks * batch);
     if (splits < 1) splits = 1;
     a.span = round_up(ceil_div(vmax, splits), tile);
