@@ -16,7 +16,10 @@
 //  * The key list -- selected (CSA) or visible (HCA) compressed entries, then
 //    window rows -- is gathered 32 rows at a time into a double-buffered LDS
 //    tile; one register-staged prefetch overlaps the next tile's loads with
-//    this tile's math. K = V: one tile serves both products.
+//    this tile's math (the CSA index list is staged in LDS first, so row
+//    addresses never wait on a global load). K = V: one tile serves both
+//    products. Keys sit in LDS rows by a fixed permutation that keeps both
+//    the K-operand reads and the transpose reads free of bank conflicts.
 //  * S^T = K Q^T (v_mfma_f32_16x16x32_bf16) leaves each lane the logits of
 //    one head for 8 keys, exactly the B operand P^T of O^T = V^T P^T.
 //  * V^T comes straight from the row-major tile through gfx950's transpose
@@ -101,6 +104,20 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
 }
 
+// LDS row of the tile that holds logical key L (0..31). S^T = K Q^T gives lane
+// group g the logical keys 4g+i (tile 0) and 16+4g+i (tile 1); the transpose
+// read of group g then touches rows P(4g+e), e = 0..3. With 1040-byte rows
+// (row r starts at bank 4r mod 64), this placement makes the 16 rows of a
+// K-operand read and the 8 rows of a 32-lane transpose read fall on distinct
+// banks.
+__device__ __forceinline__ int key_row_of(int L) {
+  return (L & 16) | (2 * (L & 3) + 8 * ((L >> 2) & 1) + ((L >> 3) & 1));
+}
+// Inverse of key_row_of.
+__device__ __forceinline__ int key_of_row(int r) {
+  return (r & 16) | (8 * (r & 1) + 4 * ((r >> 3) & 1) + ((r >> 1) & 3));
+}
+
 // Logits of a query only grow the softmax reference when they exceed it by this
 // much (log2 units): the O/l rescale is then almost never needed, and P <= 2^8.
 constexpr float REF_SLACK = 8.0f;
@@ -118,8 +135,9 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
   constexpr int CPT = CPR / TPK;     // chunks per loader thread per tile
   constexpr int MAXPAIRS = D / 2;
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][32 * ROWE];
-  __shared__ __attribute__((aligned(16))) int kdesc[2][32];
+  __shared__ __attribute__((aligned(16))) int kvq[2][32];  // logical key -> bit q: valid for query q
   __shared__ float rope_cs[QG][MAXPAIRS][2];
+  __shared__ int idx_s[CSKV_MAX_TOPK];  // CSA: the query's selected entries, staged once
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -144,13 +162,14 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
   int64_t lo = t_first - a.w + 1;
   if (lo < 0) lo = 0;
   const int64_t n_tot = n_comp + (t_last - lo + 1);
-  const int64_t v_q = csa ? 0 : visible_n(t, a.m, a.N);  // this query's visible entries (HCA)
-  const int64_t w_lo = t - a.w + 1;
   const int64_t nblk = (n_tot + 31) / 32;
   const int64_t bps = (nblk + a.n_splits - 1) / a.n_splits;
   const int64_t blk0 = (int64_t)split * bps;
   const int64_t blk1 = blk0 + bps < nblk ? blk0 + bps : nblk;
 
+  // Stage the selected-entry list in LDS so that row addresses never wait on a global load.
+  if (csa)
+    for (int i = tid; i < a.k; i += NT) idx_s[i] = idxrow[i];
   // Rotary cos/sin of every pair at each query's position, once per workgroup.
   const int npairs = a.rope_dims / 2;
   for (int i = tid; i < QG * npairs; i += NT) {
@@ -213,23 +232,33 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
   const int kr = tid / TPK, c0 = tid % TPK;
   const uint16_t* kvb = (const uint16_t*)a.kv + (int64_t)b * a.N * D;
   const int64_t wrow0 = (int64_t)b * a.W - a.win_pos0;  // window row of position p: wrow0 + p
+  // per-query bounds of the tile's queries, for the loader's validity bits
+  int64_t vis_q[QG], t_q[QG];
+#pragma unroll
+  for (int q = 0; q < QG; ++q) {
+    t_q[q] = a.pos0 + (jb + q < a.Tq ? jb + q : jl);
+    vis_q[q] = csa ? 0 : visible_n(t_q[q], a.m, a.N);
+  }
   u32x4 pre[CPT];
-  int pre_desc = -1;
-  // desc: s >= 0 compressed entry; -1 absent; -2 - pos window row at position pos
+  int pre_ok = 0;
+  // Loader thread: key u = blk*32 + kr of the key list goes to LDS row kr; its validity
+  // bits (bit q: query q of the tile may attend to it) go to the logical slot of row kr.
   auto gload = [&](int64_t blk) {
     const int64_t u = blk * 32 + kr;
     const uint16_t* src = nullptr;
-    int desc = -1;
+    int ok = 0;
     if (u < n_comp) {
-      const int64_t s_ = idxrow ? (int64_t)idxrow[u] : u;
+      const int64_t s_ = csa ? (int64_t)idx_s[u] : u;
       if (s_ >= 0 && s_ < a.N) {
-        desc = (int)s_;
         src = kvb + s_ * D;
+#pragma unroll
+        for (int q = 0; q < QG; ++q) ok |= (csa || s_ < vis_q[q]) ? (1 << q) : 0;
       }
     } else if (u < n_tot) {
       const int64_t pos = lo + (u - n_comp);
-      desc = -2 - (int)(pos - a.pos0 + a.w);  // window positions relative to pos0 - w, >= 0
       src = (const uint16_t*)a.win + (wrow0 + pos) * D;
+#pragma unroll
+      for (int q = 0; q < QG; ++q) ok |= (pos >= t_q[q] - a.w + 1 && pos <= t_q[q]) ? (1 << q) : 0;
     }
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
@@ -237,18 +266,12 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
       if (src) v = *reinterpret_cast<const u32x4*>(src + (c0 + TPK * i) * 8);
       pre[i] = v;
     }
-    pre_desc = desc;
+    pre_ok = ok;
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4*>(&kt[buf][kr * ROWE + (c0 + TPK * i) * 8]) = pre[i];
-    if (c0 == 0) kdesc[buf][kr] = pre_desc;
-  };
-  auto key_ok = [&](int d) -> bool {
-    if (d >= 0) return csa || d < v_q;
-    if (d == -1) return false;
-    const int64_t pos = (int64_t)(-2 - d) + a.pos0 - a.w;
-    return pos >= w_lo && pos <= t;
+    if (c0 == 0) kvq[buf][key_of_row(kr)] = pre_ok;
   };
 
   if (blk0 < blk1) {
@@ -262,7 +285,7 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
 
     // S^T = K Q^T: s0 -> keys 4g+i, s1 -> keys 16+4g+i; column = head n
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* kp = &kt[buf][n * ROWE + 8 * g];
+    const uint16_t* kp = &kt[buf][key_row_of(n) * ROWE + 8 * g];  // logical key n; 16+n is 16 rows on
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kp + ks * 32);
@@ -270,17 +293,17 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[ks], s1, 0, 0, 0);
     }
-    const int4 d0 = *reinterpret_cast<const int4*>(&kdesc[buf][4 * g]);
-    const int4 d1 = *reinterpret_cast<const int4*>(&kdesc[buf][16 + 4 * g]);
+    const int4 d0 = *reinterpret_cast<const int4*>(&kvq[buf][4 * g]);
+    const int4 d1 = *reinterpret_cast<const int4*>(&kvq[buf][16 + 4 * g]);
     float sv[8];
-    sv[0] = key_ok(d0.x) ? s0[0] * a.scale_log2 : -INFINITY;
-    sv[1] = key_ok(d0.y) ? s0[1] * a.scale_log2 : -INFINITY;
-    sv[2] = key_ok(d0.z) ? s0[2] * a.scale_log2 : -INFINITY;
-    sv[3] = key_ok(d0.w) ? s0[3] * a.scale_log2 : -INFINITY;
-    sv[4] = key_ok(d1.x) ? s1[0] * a.scale_log2 : -INFINITY;
-    sv[5] = key_ok(d1.y) ? s1[1] * a.scale_log2 : -INFINITY;
-    sv[6] = key_ok(d1.z) ? s1[2] * a.scale_log2 : -INFINITY;
-    sv[7] = key_ok(d1.w) ? s1[3] * a.scale_log2 : -INFINITY;
+    sv[0] = ((d0.x >> qi) & 1) ? s0[0] * a.scale_log2 : -INFINITY;
+    sv[1] = ((d0.y >> qi) & 1) ? s0[1] * a.scale_log2 : -INFINITY;
+    sv[2] = ((d0.z >> qi) & 1) ? s0[2] * a.scale_log2 : -INFINITY;
+    sv[3] = ((d0.w >> qi) & 1) ? s0[3] * a.scale_log2 : -INFINITY;
+    sv[4] = ((d1.x >> qi) & 1) ? s1[0] * a.scale_log2 : -INFINITY;
+    sv[5] = ((d1.y >> qi) & 1) ? s1[1] * a.scale_log2 : -INFINITY;
+    sv[6] = ((d1.z >> qi) & 1) ? s1[2] * a.scale_log2 : -INFINITY;
+    sv[7] = ((d1.w >> qi) & 1) ? s1[3] * a.scale_log2 : -INFINITY;
     float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
@@ -313,7 +336,7 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
 
     // O^T += V^T P^T: A = V^T via transpose reads (lane n of group g: keys 4g+e / 16+4g+e for
     // e = n/4, dims 16tt + 4(n%4) .. +3), B = P^T already in this lane (head n, 8 keys).
-    const uint16_t* vp0 = &kt[buf][(4 * g + (n >> 2)) * ROWE + 4 * (n & 3)];
+    const uint16_t* vp0 = &kt[buf][key_row_of(4 * g + (n >> 2)) * ROWE + 4 * (n & 3)];
     const uint16_t* vp1 = vp0 + 16 * ROWE;
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt) {

@@ -139,16 +139,14 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
         acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][ks], bv, ks == 0 ? f32x16{} : acc[ht], 0, 0, 0);
     }
   };
-  // ReLU, head weights, sum over the 32 heads of each tile, then over tiles; lanes 0-31 store key lane%32.
-  auto epilogue = [&](const f32x16 (&acc)[HT], int s0) {
+  // ReLU, head weights, sum over the 32 heads of each tile, then over tiles (lane = key lane%32).
+  auto epilogue = [&](const f32x16 (&acc)[HT]) -> float {
     float part = 0.f;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
       for (int i = 0; i < 16; ++i) part = __builtin_fmaf(relu_bits(acc[ht][i]), wv[ht][i], part);
-    part += __shfl_xor(part, 32, 64);
-    const int s = s0 + (lane & 31);
-    if (qvalid && lane < 32 && s < nkeys) srow[s] = s < vrel ? part : -INFINITY;
+    return part + __shfl_xor(part, 32, 64);
   };
 
   gload(0);
@@ -159,11 +157,28 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
     if (it + 1 < ntiles) gload(t0 + TILE);
     const uint16_t* kp = &kt[it & 1][(kl * SUB * 32 + (lane & 31)) * ROW + 8 * (lane >> 5)];
     f32x16 acc[2][HT];
+    float res[SUB];
     mma(kp, acc[0]);
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb) {
-      if (sb + 1 < SUB) mma(kp + (sb + 1) * 32 * ROW, acc[(sb + 1) & 1]);  // next sub-block's MFMAs first
-      epilogue(acc[sb & 1], t0 + (kl * SUB + sb) * 32);
+      if (sb + 1 < SUB) {
+        // next sub-block's MFMAs interleaved with this sub-block's ReLU/weight epilogue
+        mma(kp + (sb + 1) * 32 * ROW, acc[(sb + 1) & 1]);
+        res[sb] = epilogue(acc[sb & 1]);
+        __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // B-operand LDS reads first
+#pragma unroll
+        for (int i = 0; i < KS * HT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
+        }
+      } else {
+        res[sb] = epilogue(acc[sb & 1]);
+      }
+    }
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      const int s = t0 + (kl * SUB + sb) * 32 + (lane & 31);
+      if (qvalid && lane < 32 && s < nkeys) srow[s] = s < vrel ? res[sb] : -INFINITY;
     }
     if (it + 1 < ntiles) lstore((it + 1) & 1);
     __syncthreads();
