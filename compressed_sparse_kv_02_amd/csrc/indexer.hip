@@ -139,14 +139,16 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
         acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][ks], bv, ks == 0 ? f32x16{} : acc[ht], 0, 0, 0);
     }
   };
-  // ReLU, head weights, sum over the 32 heads of each tile, then over tiles (lane = key lane%32).
-  auto epilogue = [&](const f32x16 (&acc)[HT]) -> float {
+  // ReLU, head weights, sum over the 32 heads of each tile, then over tiles; lanes 0-31 store key lane%32.
+  auto epilogue = [&](const f32x16 (&acc)[HT], int s0) {
     float part = 0.f;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
       for (int i = 0; i < 16; ++i) part = __builtin_fmaf(relu_bits(acc[ht][i]), wv[ht][i], part);
-    return part + __shfl_xor(part, 32, 64);
+    part += __shfl_xor(part, 32, 64);
+    const int s = s0 + (lane & 31);
+    if (qvalid && lane < 32 && s < nkeys) srow[s] = s < vrel ? part : -INFINITY;
   };
 
   gload(0);
@@ -157,28 +159,11 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
     if (it + 1 < ntiles) gload(t0 + TILE);
     const uint16_t* kp = &kt[it & 1][(kl * SUB * 32 + (lane & 31)) * ROW + 8 * (lane >> 5)];
     f32x16 acc[2][HT];
-    float res[SUB];
     mma(kp, acc[0]);
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb) {
-      if (sb + 1 < SUB) {
-        // next sub-block's MFMAs interleaved with this sub-block's ReLU/weight epilogue
-        mma(kp + (sb + 1) * 32 * ROW, acc[(sb + 1) & 1]);
-        res[sb] = epilogue(acc[sb & 1]);
-        __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);  // B-operand LDS reads first
-#pragma unroll
-        for (int i = 0; i < KS * HT; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four VALU
-        }
-      } else {
-        res[sb] = epilogue(acc[sb & 1]);
-      }
-    }
-#pragma unroll
-    for (int sb = 0; sb < SUB; ++sb) {
-      const int s = t0 + (kl * SUB + sb) * 32 + (lane & 31);
-      if (qvalid && lane < 32 && s < nkeys) srow[s] = s < vrel ? res[sb] : -INFINITY;
+      if (sb + 1 < SUB) mma(kp + (sb + 1) * 32 * ROW, acc[(sb + 1) & 1]);  // next sub-block's MFMAs first
+      epilogue(acc[sb & 1], t0 + (kl * SUB + sb) * 32);
     }
     if (it + 1 < ntiles) lstore((it + 1) & 1);
     __syncthreads();
@@ -325,8 +310,9 @@ __device__ void ordered_pick(KeyAt key_at, IdxAt idx_at, int64_t n, uint32_t tau
 __global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
   __shared__ uint32_t ckey[TOPK_CAP];
   __shared__ int32_t cidx[TOPK_CAP];
-  __shared__ uint32_t samp[TOPK_SAMPLES];
   __shared__ TopkShared sh;
+  uint32_t* samp = reinterpret_cast<uint32_t*>(cidx);  // the sample is done before candidates exist
+  static_assert(TOPK_SAMPLES <= TOPK_CAP, "sample buffer aliases the candidate indices");
 
   const int tid = threadIdx.x;
   const int b = blockIdx.y;
@@ -357,33 +343,45 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
     uint32_t tau0;
     int need0;
     radix_select([&](int64_t s) { return samp[s]; }, TOPK_SAMPLES, r, sh, tau0, need0);
-    // one pass: keep key >= tau0 in index order (4 entries per thread per chunk)
+    __syncthreads();  // the sample (aliasing cidx) is consumed
+    // one pass: keep key >= tau0 in index order. Each thread owns 4 consecutive entries per
+    // 4096-entry chunk; UNR chunks are loaded before any is scanned, to keep loads in flight.
+    constexpr int UNR = 4;
+    constexpr int CHUNK = 4 * TOPK_THREADS;
     int cnt = 0;
-    for (int64_t base = 0; base < V; base += 4 * TOPK_THREADS) {
-      const int64_t s0 = base + 4 * tid;
-      float4 v = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      if (s0 < V) v = *reinterpret_cast<const float4*>(row + s0);  // rows are padded to 64 entries
-      const float vv[4] = {v.x, v.y, v.z, v.w};
-      uint32_t kk4[4];
-      int f = 0;
+    for (int64_t base = 0; base < V; base += UNR * CHUNK) {
+      float4 v[UNR];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kk4[e] = score_key(vv[e]);
-        if (s0 + e < V && kk4[e] >= tau0) ++f;
+      for (int u = 0; u < UNR; ++u) {
+        const int64_t s0 = base + u * CHUNK + 4 * tid;
+        v[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (s0 < V) v[u] = *reinterpret_cast<const float4*>(row + s0);  // rows are padded to 64 entries
       }
-      int tot;
-      int pos = cnt + block_exclusive_scan(f, sh.wsum, tot);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (s0 + e < V && kk4[e] >= tau0) {
-          if (pos < TOPK_CAP) {
-            ckey[pos] = kk4[e];
-            cidx[pos] = (int32_t)(s0 + e);
-          }
-          ++pos;
+      for (int u = 0; u < UNR; ++u) {
+        const int64_t s0 = base + u * CHUNK + 4 * tid;
+        const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        uint32_t kk4[4];
+        int f = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kk4[e] = score_key(vv[e]);
+          if (s0 + e < V && kk4[e] >= tau0) ++f;
         }
+        int tot;
+        int pos = cnt + block_exclusive_scan(f, sh.wsum, tot);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (s0 + e < V && kk4[e] >= tau0) {
+            if (pos < TOPK_CAP) {
+              ckey[pos] = kk4[e];
+              cidx[pos] = (int32_t)(s0 + e);
+            }
+            ++pos;
+          }
+        }
+        cnt += tot;
       }
-      cnt += tot;
     }
     __syncthreads();
     n_cand = cnt;
