@@ -33,6 +33,76 @@ METRIC = "query-tokens/s for CSA/HCA layer at 1M ctx (prefill+decode); % HBM/MFM
 PEAK_BF16_FLOPS = 2.5e15
 PEAK_HBM_BYTES = 8.0e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# Sources whose kernels the stored counter figures describe; a change to any of
+# them makes those figures stale (reported as null).
+TRAFFIC_SOURCES = ("compressed_sparse_kv_02_amd/csrc/indexer.hip", "compressed_sparse_kv_02_amd/csrc/device_common.h")
+COPY_PROBE_BYTES = 1 << 30   # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE
+
+
+def sources_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    """Stored HBM bytes per launch of the scoring kernels, or None when absent or stale."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        tr = json.load(f)
+    if tr.get("sources_sha256") != sources_digest():
+        return None
+    return tr
+
+
+def write_traffic(fetch_csv: str, write_csv: str) -> None:
+    """Turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE, KiB per
+    dispatch) of `bench.py --copy-probe` into HBM bytes per launch of the scoring kernels.
+
+    Each counter is scaled by bytes / counter of the calibration copy (a fp32 negation of
+    COPY_PROBE_BYTES in, COPY_PROBE_BYTES out), so the figures are in the units the copy
+    defines: bytes that crossed from HBM (or the memory-side cache) into L2 and back.
+    """
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return vals
+
+    out = {"sources_sha256": sources_digest(), "copy_probe_bytes": COPY_PROBE_BYTES}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        vals = per_kernel(path, counter)
+        copy = [v for (name, grid), vs in vals.items() if "neg_kernel" in name for v in vs]
+        assert copy, f"no calibration copy dispatch in {path}"
+        kib = statistics.median(copy)
+        factor = COPY_PROBE_BYTES / (kib * 1024.0)
+        out[f"{counter}_copy_kib"] = kib
+        out[f"{counter}_factor"] = factor
+        for tag, tmpl in (("prefill", "indexer_score_mfma<2, 8, 8>"), ("decode", "indexer_score_mfma<2, 8, 1>")):
+            vs = [v for (name, grid), xs in vals.items() if tmpl in name for v in xs]
+            assert vs, f"no {tmpl} dispatch in {path}"
+            ent = out.setdefault(f"indexer_score_mfma_{tag}", {})
+            ent[f"{counter}_kib_mean"] = statistics.mean(vs)
+            ent[f"{counter}_dispatches"] = len(vs)
+            ent[f"{counter}_bytes"] = statistics.mean(vs) * 1024.0 * factor
+    for tag in ("prefill", "decode"):
+        ent = out[f"indexer_score_mfma_{tag}"]
+        ent["hbm_bytes_per_launch"] = ent["FETCH_SIZE_bytes"] + ent["WRITE_SIZE_bytes"]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out, indent=1))
 
 
 def visible_pairs(L) -> int:
@@ -126,7 +196,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB copy (counter calibration for --write-traffic)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one MI355X; runs on more than one GPU are not supported "
               "(the layer has no sharded path here).", file=sys.stderr)
@@ -198,6 +275,13 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     pre_ms = sum(starts[i].elapsed_time(rec["mid"][i]) for i in range(args.steps)) / args.steps
     dec_ms = ms - pre_ms
     n_pre = prefill[0].batch * prefill[0].T
@@ -207,11 +291,8 @@ def main():
     score_ms = sum(a.elapsed_time(b) for a, b in rec["pre_score"]) / len(rec["pre_score"])
     fl = indexer_flops(prefill[0])
     achieved = fl / (score_ms / 1e3) / 1e12
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        traffic = tr.get("indexer_score_mfma_prefill", {}).get("hbm_bytes_per_launch")
+    tr = load_traffic() or {}
+    traffic = tr.get("indexer_score_mfma_prefill", {}).get("hbm_bytes_per_launch")
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                 "frac": achieved * 1e12 / PEAK_BF16_FLOPS, "traffic": traffic,
                 "kernel": "indexer_score_mfma<2,8,8> (prefill CSA layers)", "avg_launch_ms": score_ms,
@@ -219,9 +300,7 @@ def main():
     dscore_ms = sum(a.elapsed_time(b) for a, b in rec["dec_score"]) / len(rec["dec_score"])
     db = decode_score_bytes(decode[0])
     dach = db / (dscore_ms / 1e3) / 1e9
-    dtraffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        dtraffic = tr.get("indexer_score_mfma_decode", {}).get("hbm_bytes_per_launch")
+    dtraffic = tr.get("indexer_score_mfma_decode", {}).get("hbm_bytes_per_launch")
     roofline_dec = {"bound": "hbm", "achieved": dach, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                     "frac": dach * 1e9 / PEAK_HBM_BYTES, "traffic": dtraffic,
                     "kernel": "indexer_score_mfma<2,8,1> (decode CSA layer)", "avg_launch_ms": dscore_ms,
