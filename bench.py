@@ -35,7 +35,8 @@ PEAK_HBM_BYTES = 8.0e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Sources whose kernels the stored counter figures describe; a change to any of
 # them makes those figures stale (reported as null).
-TRAFFIC_SOURCES = ("compressed_sparse_kv_02_amd/csrc/indexer.hip", "compressed_sparse_kv_02_amd/csrc/device_common.h")
+TRAFFIC_SOURCES = ("compressed_sparse_kv_02_amd/csrc/indexer.hip", "compressed_sparse_kv_02_amd/csrc/indexer.h",
+                   "compressed_sparse_kv_02_amd/csrc/device_common.h")
 COPY_PROBE_BYTES = 1 << 30   # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE
 
 

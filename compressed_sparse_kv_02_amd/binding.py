@@ -21,7 +21,7 @@ BF16, F32 = 0, 1
 CSA, HCA = 0, 1
 EXPORTS = ("cskv_version", "cskv_status_string", "csa_compress", "hca_compress",
            "cskv_indexer_workspace_size", "indexer_topk", "indexer_scores", "topk_select",
-           "compressed_attn_prefill",
+           "cskv_topk_workspace_size", "compressed_attn_prefill",
            "cskv_decode_workspace_size", "compressed_attn_decode")
 
 _lib = None
@@ -36,7 +36,8 @@ _SIGS = {
     "cskv_indexer_workspace_size": (_Z, [_I, _L, _L, _I, _I, _I]),
     "indexer_topk": (_I, [_P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _I, _P, _P, _Z, _I, _P]),
     "indexer_scores": (_I, [_P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _P, _L, _I, _P]),
-    "topk_select": (_I, [_P, _L, _I, _L, _L, _L, _I, _I, _P, _P]),
+    "topk_select": (_I, [_P, _L, _I, _L, _L, _L, _I, _I, _P, _P, _Z, _P]),
+    "cskv_topk_workspace_size": (_Z, [_I, _L, _L, _I]),
     "compressed_attn_prefill": (_I, [_I, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
                                      _I, _P, _F, _I, _F, _F, _I, _P, _P, _I, _P]),
     "cskv_decode_workspace_size": (_Z, [_I, _L, _I, _I, _I]),
@@ -170,12 +171,21 @@ def indexer_scores(qI, wI, KI, pos0: int, m: int, scores=None) -> torch.Tensor:
     return scores
 
 
-def topk_select(scores, N: int, pos0: int, m: int, k: int, out=None) -> torch.Tensor:
-    """Top-k selection from a score matrix written by indexer_scores."""
+def topk_workspace_bytes(batch: int, Tq: int, N: int, k: int) -> int:
+    return int(lib().cskv_topk_workspace_size(batch, Tq, N, k))
+
+
+def topk_select(scores, N: int, pos0: int, m: int, k: int, out=None, workspace=None) -> torch.Tensor:
+    """Top-k selection from a score matrix written by indexer_scores.
+
+    `workspace` (optional, cskv_topk_workspace_size bytes) lets few long rows be
+    selected with several workgroups per row; the result is the same without it.
+    """
     batch, Tq, ld = scores.shape
     if out is None:
         out = torch.empty(batch, Tq, k, dtype=torch.int32, device=scores.device)
-    _check("topk_select", lib().topk_select(_ptr(scores), ld, batch, Tq, N, pos0, m, k, _ptr(out),
+    ws, nbytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
+    _check("topk_select", lib().topk_select(_ptr(scores), ld, batch, Tq, N, pos0, m, k, _ptr(out), ws, nbytes,
                                             _stream(scores)))
     return out
 

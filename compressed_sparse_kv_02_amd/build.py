@@ -1,7 +1,8 @@
 """Build libcskv.so (gfx950) in-tree with hipcc.
 
 Every HIP source is compiled for gfx950 only, with packed-fp32 instruction
-selection disabled, then linked into one shared library next to this file.
+selection disabled, then linked into one shared library next to this file
+that exports the C ABI of include/cskv.h only (csrc/exports.map).
 """
 from __future__ import annotations
 
@@ -13,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcskv.so")
-SOURCES = ["compress.hip", "indexer.hip", "attention.hip", "abi.cpp"]
+SOURCES = ["compress.hip", "indexer.hip", "topk.hip", "attention.hip", "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
@@ -42,7 +43,8 @@ def build(verbose: bool = False) -> str:
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-o", tmp, *objs]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-o", tmp, *objs,
+           "-Wl,--version-script=" + os.path.join(CSRC, "exports.map")]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB

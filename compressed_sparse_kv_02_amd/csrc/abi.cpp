@@ -1,7 +1,7 @@
 // Version and status text of the C ABI declared in include/cskv.h.
 #include "abi_common.h"
 
-extern "C" int cskv_version(void) { return 10000 * 0 + 100 * 1 + 0; }
+extern "C" int cskv_version(void) { return 10000 * 0 + 100 * 2 + 0; }
 
 extern "C" const char* cskv_status_string(int status) {
   switch (status) {

@@ -690,10 +690,13 @@ extern "C" int compressed_attn_prefill(int mode, const void* q, const void* kv, 
   return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
 }
 
+// Splits per query: about one workgroup per compute unit (256) over the whole call, at
+// least 4 key tiles each. Every split costs a query prologue and an fp32 partial of
+// H x d written and merged, so more splits than CUs only add traffic.
 static int decode_splits(int batch, int64_t Tq, int64_t max_k, int n_splits) {
   if (n_splits > 0) return n_splits;
   const int64_t nblk = (max_k + 31) / 32;
-  int64_t s = (1024 + batch * Tq - 1) / (batch * Tq);
+  int64_t s = (256 + batch * Tq - 1) / (batch * Tq);
   const int64_t cap = (nblk + 3) / 4;
   if (s > cap) s = cap;
   if (s > 256) s = 256;

@@ -1,0 +1,43 @@
+// Internal interface between the lightning-indexer scoring (indexer.hip) and
+// the per-query top-k selection (topk.hip): their shared argument block and
+// the host-side launchers each file provides to the other's entry points.
+#pragma once
+
+#include "device_common.h"
+#include "abi_common.h"
+
+namespace cskv {
+
+__device__ __forceinline__ int64_t visible_entries(int64_t t, int m, int64_t N) {
+  const int64_t v = (t + 1) / m;
+  return v < N ? v : N;
+}
+
+struct IdxArgs {
+  const void* qI;
+  const float* wI;
+  const void* KI;
+  float* scores;  // [batch][rows_ws][ldS]
+  int32_t* out;
+  int64_t Tq, N, pos0, ldS, span;
+  int64_t row0, nrows, rows_ws;  // query rows handled by this chunk
+  int HI, dI, m, k;
+  // two-kernel selection of few long rows (topk_part + topk_merge)
+  uint8_t* sel_ws;     // per row: keys [CAP] u32, indices [CAP] i32, part records [MAX_PARTS] int4
+  int64_t part_len;    // entries per part
+  int kp;              // candidates kept per part
+};
+
+// Scores of rows [a.row0, a.row0 + a.nrows) into a.scores; bf16 takes qb
+// queries per workgroup (8 for prefill, 1 for decode).
+int launch_scores(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st);
+
+// Top-k of rows [a.row0, a.row0 + a.nrows) from a.scores into a.out; sel_ws
+// (optional, sel_bytes long) enables the several-workgroups-per-row route.
+int launch_select(IdxArgs& a, int batch, void* sel_ws, size_t sel_bytes, hipStream_t st);
+
+// Workspace bytes for the several-workgroups-per-row selection of `rows`
+// rows of up to vmax entries; 0 when that route is not taken.
+size_t split_ws_bytes(int64_t rows, int64_t vmax, int k);
+
+}  // namespace cskv

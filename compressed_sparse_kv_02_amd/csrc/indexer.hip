@@ -1,10 +1,12 @@
-// Lightning indexer and per-query top-k for gfx950.
+// Lightning-indexer scoring for gfx950.
 //
 // "Paper Breakdown: DeepSeek-V4", §2.3.1 "DSA on Compressed KV (lightning
 // indexer + top-k)": every query scores every visible compressed indexer key,
 //   I[t, s] = sum_h w[t, h] * ReLU(qI[t, h, :] . KI[s, :]),
 // and keeps the k best entries ("How DeepSeek-V4 architecture and training
-// work together", "Two compressed views of one history": k = 1024).
+// work together", "Two compressed views of one history": k = 1024). The
+// selection is in topk.hip; this file scores and holds the indexer_topk and
+// indexer_scores entry points.
 //
 // Scoring (bf16): a dense Q.K^T contraction on the matrix cores
 // (v_mfma_f32_32x32x16_bf16; M = 32 heads of one query, N = 32 keys,
@@ -14,35 +16,9 @@
 // tiles, so each key row fetched from HBM feeds QB queries. With QB = 1
 // (decode) the 8 waves take different key blocks and many workgroups split
 // the key range. Scores go to a caller workspace as fp32 rows.
-//
-// Selection: one 1024-thread workgroup per query row. A strided sample of the
-// row gives a threshold that about 3k entries exceed; one vectorised pass
-// keeps those entries (in index order) in LDS, an exact 3-pass radix select
-// (11 + 11 + 10 bits, order-preserving uint32 keys) finds the k-th largest
-// among them, and an in-order pick with block prefix sums writes the result:
-// ties resolve to the smaller index and the output is ascending without a
-// sort. Should the sample miss, the row falls back to the exact radix select
-// over global memory.
-#include "device_common.h"
-#include "abi_common.h"
+#include "indexer.h"
 
 namespace cskv {
-
-__device__ __forceinline__ int64_t visible_entries(int64_t t, int m, int64_t N) {
-  const int64_t v = (t + 1) / m;
-  return v < N ? v : N;
-}
-
-struct IdxArgs {
-  const void* qI;
-  const float* wI;
-  const void* KI;
-  float* scores;  // [batch][rows_ws][ldS]
-  int32_t* out;
-  int64_t Tq, N, pos0, ldS, span;
-  int64_t row0, nrows, rows_ws;  // query rows handled by this chunk
-  int HI, dI, m, k;
-};
 
 // ----------------------------------------------------------------------------
 // bf16 scoring on the matrix cores
@@ -197,211 +173,6 @@ __global__ __launch_bounds__(256) void indexer_score_f32(IdxArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Exact top-k per row
-// ----------------------------------------------------------------------------
-constexpr int TOPK_THREADS = 1024;
-constexpr int TOPK_CAP = 8192;      // candidate (key, index) pairs held in LDS
-constexpr int TOPK_SAMPLES = 4096;  // strided sample of a long row, for the candidate threshold
-
-// Exclusive prefix sum over the workgroup; also returns the total.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) wsum[wave] = incl;
-  __syncthreads();
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < TOPK_THREADS / 64; ++w) {
-    const int x = wsum[w];
-    if (w < wave) pre += x;
-    tot += x;
-  }
-  __syncthreads();
-  total = tot;
-  return pre + incl - v;
-}
-
-struct TopkShared {
-  int hist[2048];
-  int wsum[TOPK_THREADS / 64];
-  int sel_bin, sel_above, count;
-};
-
-// Radix select (11 + 11 + 10 bits): the kk-th largest of n keys read through key_at.
-// Returns it in tau; `need` = how many keys equal to tau belong to the top kk.
-template <typename KeyAt>
-__device__ void radix_select(KeyAt key_at, int64_t n, int kk, TopkShared& sh, uint32_t& tau, int& need) {
-  const int tid = threadIdx.x;
-  uint32_t prefix = 0, pmask = 0;
-  need = kk;
-  const int shifts[3] = {21, 10, 0};
-  const int nbits[3] = {11, 11, 10};
-  for (int p = 0; p < 3; ++p) {
-    const int nb = 1 << nbits[p];
-    const uint32_t bmask = (uint32_t)nb - 1u;
-    for (int i = tid; i < 2048; i += TOPK_THREADS) sh.hist[i] = 0;
-    __syncthreads();
-    for (int64_t s = tid; s < n; s += TOPK_THREADS) {
-      const uint32_t key = key_at(s);
-      if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shifts[p]) & bmask], 1);
-    }
-    __syncthreads();
-    const int bpt = nb / TOPK_THREADS;  // bins per thread, descending
-    int cnt[2] = {0, 0}, loc = 0;
-    for (int q = 0; q < bpt; ++q) {
-      cnt[q] = sh.hist[nb - 1 - (tid * bpt + q)];
-      loc += cnt[q];
-    }
-    int total;
-    int above = block_exclusive_scan(loc, sh.wsum, total);
-    for (int q = 0; q < bpt; ++q) {
-      if (above < need && need <= above + cnt[q]) {
-        sh.sel_bin = nb - 1 - (tid * bpt + q);
-        sh.sel_above = above;
-      }
-      above += cnt[q];
-    }
-    __syncthreads();
-    need -= sh.sel_above;
-    prefix |= (uint32_t)sh.sel_bin << shifts[p];
-    pmask |= bmask << shifts[p];
-    __syncthreads();
-  }
-  tau = prefix;
-}
-
-// Writes, in index order, the entries with key > tau plus the first `need` with key == tau.
-template <typename KeyAt, typename IdxAt>
-__device__ void ordered_pick(KeyAt key_at, IdxAt idx_at, int64_t n, uint32_t tau, int need, int32_t* out,
-                             TopkShared& sh) {
-  const int tid = threadIdx.x;
-  int eq_taken = 0, written = 0;
-  for (int64_t base = 0; base < n; base += TOPK_THREADS) {
-    const int64_t s = base + tid;
-    uint32_t key = 0;
-    if (s < n) key = key_at(s);
-    const int gt = (s < n && key > tau) ? 1 : 0;
-    const int eq = (s < n && key == tau) ? 1 : 0;
-    int eq_tot;
-    const int eq_rank = block_exclusive_scan(eq, sh.wsum, eq_tot);
-    const int sel = gt | (eq && (eq_taken + eq_rank) < need ? 1 : 0);
-    int sel_tot;
-    const int pos = block_exclusive_scan(sel, sh.wsum, sel_tot);
-    if (sel) out[written + pos] = idx_at(s);
-    eq_taken += eq_tot;
-    written += sel_tot;
-  }
-}
-
-// One 1024-thread workgroup per query row.
-//  * V <= CAP: the whole row becomes the candidate set.
-//  * otherwise: the (3k * S / V)-th largest of S strided samples gives a
-//    threshold tau0; one vectorised pass over the row keeps every entry with
-//    key >= tau0, in index order, as candidates (about 3k of them).
-//  * exact radix select among the candidates, then an in-order pick.
-// If the candidates do not hold at least k entries (or overflow LDS), the
-// row falls back to the exact 3-pass radix select over global memory. Both
-// routes return the same, exact set.
-__global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
-  __shared__ uint32_t ckey[TOPK_CAP];
-  __shared__ int32_t cidx[TOPK_CAP];
-  __shared__ TopkShared sh;
-  uint32_t* samp = reinterpret_cast<uint32_t*>(cidx);  // the sample is done before candidates exist
-  static_assert(TOPK_SAMPLES <= TOPK_CAP, "sample buffer aliases the candidate indices");
-
-  const int tid = threadIdx.x;
-  const int b = blockIdx.y;
-  const int64_t jr = blockIdx.x;
-  const int64_t j = a.row0 + jr;
-  const int k = a.k;
-  int32_t* out = a.out + ((int64_t)b * a.Tq + j) * k;
-  const int64_t V = visible_entries(a.pos0 + j, a.m, a.N);
-  if (V <= k) {
-    for (int i = tid; i < k; i += TOPK_THREADS) out[i] = i < V ? i : -1;
-    return;
-  }
-  const float* row = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
-  int n_cand = 0;
-  if (V <= TOPK_CAP) {
-    for (int64_t s = tid; s < V; s += TOPK_THREADS) {
-      ckey[s] = score_key(row[s]);
-      cidx[s] = (int32_t)s;
-    }
-    n_cand = (int)V;
-    __syncthreads();
-  } else {
-    // threshold from a strided sample
-    for (int i = tid; i < TOPK_SAMPLES; i += TOPK_THREADS) samp[i] = score_key(row[(int64_t)i * V / TOPK_SAMPLES]);
-    __syncthreads();
-    int r = (int)(((int64_t)3 * k * TOPK_SAMPLES + V - 1) / V);
-    if (r > TOPK_SAMPLES) r = TOPK_SAMPLES;
-    uint32_t tau0;
-    int need0;
-    radix_select([&](int64_t s) { return samp[s]; }, TOPK_SAMPLES, r, sh, tau0, need0);
-    __syncthreads();  // the sample (aliasing cidx) is consumed
-    // one pass: keep key >= tau0 in index order. Each thread owns 4 consecutive entries per
-    // 4096-entry chunk; UNR chunks are loaded before any is scanned, to keep loads in flight.
-    constexpr int UNR = 4;
-    constexpr int CHUNK = 4 * TOPK_THREADS;
-    int cnt = 0;
-    for (int64_t base = 0; base < V; base += UNR * CHUNK) {
-      float4 v[UNR];
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int64_t s0 = base + u * CHUNK + 4 * tid;
-        v[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        if (s0 < V) v[u] = *reinterpret_cast<const float4*>(row + s0);  // rows are padded to 64 entries
-      }
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int64_t s0 = base + u * CHUNK + 4 * tid;
-        const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-        uint32_t kk4[4];
-        int f = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kk4[e] = score_key(vv[e]);
-          if (s0 + e < V && kk4[e] >= tau0) ++f;
-        }
-        int tot;
-        int pos = cnt + block_exclusive_scan(f, sh.wsum, tot);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (s0 + e < V && kk4[e] >= tau0) {
-            if (pos < TOPK_CAP) {
-              ckey[pos] = kk4[e];
-              cidx[pos] = (int32_t)(s0 + e);
-            }
-            ++pos;
-          }
-        }
-        cnt += tot;
-      }
-    }
-    __syncthreads();
-    n_cand = cnt;
-  }
-  if (n_cand >= k && n_cand <= TOPK_CAP) {
-    uint32_t tau;
-    int need;
-    radix_select([&](int64_t s) { return ckey[s]; }, n_cand, k, sh, tau, need);
-    ordered_pick([&](int64_t s) { return ckey[s]; }, [&](int64_t s) { return cidx[s]; }, n_cand, tau, need,
-                 out, sh);
-  } else {
-    uint32_t tau;
-    int need;
-    auto key_at = [&](int64_t s) { return score_key(row[s]); };
-    radix_select(key_at, V, k, sh, tau, need);
-    ordered_pick(key_at, [&](int64_t s) { return (int32_t)s; }, V, tau, need, out, sh);
-  }
-}
-
-// ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
 static constexpr int64_t SCORE_CHUNK_BYTES = (int64_t)128 << 20;
@@ -460,7 +231,7 @@ static bool mfma_shape_ok(int HI, int dI) {
 
 
 // Launch the scoring kernel for rows [a.row0, a.row0 + a.nrows) into a.scores.
-static int launch_scores(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st) {
+int launch_scores(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st) {
   const int64_t last = a.pos0 + a.row0 + a.nrows - 1;
   int64_t vmax = (last + 1) / a.m;
   if (vmax > a.N) vmax = a.N;
@@ -484,11 +255,6 @@ static int launch_scores(IdxArgs& a, int batch, int qb, int dtype, hipStream_t s
   return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
 }
 
-static int launch_select(IdxArgs& a, int batch, hipStream_t st) {
-  hipLaunchKernelGGL(topk_select, dim3((unsigned)a.nrows, (unsigned)batch), dim3(TOPK_THREADS), 0, st, a);
-  return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
-}
-
 static int check_indexer_shape(int batch, int64_t Tq, int64_t N, int HI, int dI, int64_t pos0, int m, int dtype) {
   if (dtype != CSKV_BF16 && dtype != CSKV_F32) return CSKV_ERR_BAD_DTYPE;
   if (batch < 0 || Tq < 0 || N < 0 || pos0 < 0 || m < 1) return CSKV_ERR_BAD_SHAPE;
@@ -509,7 +275,7 @@ extern "C" size_t cskv_indexer_workspace_size(int batch, int64_t Tq, int64_t N, 
   (void)k;
   if (batch <= 0 || Tq <= 0) return 0;
   IdxPlan p = plan_indexer(batch, Tq, N, dtype);
-  return (size_t)(batch * p.rows_ws * p.ldS * 4);
+  return (size_t)(batch * p.rows_ws * p.ldS * 4) + split_ws_bytes((int64_t)batch * p.rows_ws, N, k);
 }
 
 extern "C" int indexer_topk(const void* qI, const float* wI, const void* KI, int batch, int64_t Tq,
@@ -524,8 +290,12 @@ extern "C" int indexer_topk(const void* qI, const float* wI, const void* KI, int
   if (!qI || !wI || !out_idx || (N > 0 && !KI)) return CSKV_ERR_INVALID_ARG;
   if (!aligned16(qI, wI, KI, out_idx, workspace)) return CSKV_ERR_MISALIGNED;
   IdxPlan p = plan_indexer(batch, Tq, N, dtype);
-  const size_t need_ws = (size_t)(batch * p.rows_ws * p.ldS * 4);
+  const size_t score_bytes = (size_t)(batch * p.rows_ws * p.ldS * 4);
+  const size_t need_ws = score_bytes + split_ws_bytes((int64_t)batch * p.rows_ws, N, k);
   if (!workspace || ws_bytes < need_ws) return CSKV_ERR_WORKSPACE;
+  // the selection area follows the score rows (score_bytes is a multiple of 256: ldS % 64 == 0)
+  uint8_t* sel_ws = need_ws > score_bytes ? (uint8_t*)workspace + score_bytes : nullptr;
+  const size_t sel_bytes = sel_ws ? ws_bytes - score_bytes : 0;
 
   hipStream_t hs = (hipStream_t)stream;
   IdxArgs a{};
@@ -542,7 +312,7 @@ extern "C" int indexer_topk(const void* qI, const float* wI, const void* KI, int
       st = launch_scores(a, batch, (int)p.qb, dtype, hs);
       if (st) return st;
     }
-    st = launch_select(a, batch, hs);
+    st = launch_select(a, batch, sel_ws, sel_bytes, hs);
     if (st) return st;
   }
   return CSKV_OK;
@@ -563,19 +333,4 @@ extern "C" int indexer_scores(const void* qI, const float* wI, const void* KI, i
   a.HI = HI; a.dI = dI; a.m = m;
   const int qb = (dtype == CSKV_BF16 && Tq >= 64) ? 8 : 1;
   return launch_scores(a, batch, qb, dtype, (hipStream_t)stream);
-}
-
-extern "C" int topk_select(const float* scores, int64_t ld, int batch, int64_t Tq, int64_t N,
-                           int64_t pos0, int m, int k, int32_t* out_idx, void* stream) {
-  if (batch < 0 || Tq < 0 || N < 0 || pos0 < 0 || m < 1 || ld < N) return CSKV_ERR_BAD_SHAPE;
-  if (k < 1) return CSKV_ERR_BAD_SHAPE;
-  if (k > CSKV_MAX_TOPK) return CSKV_ERR_UNSUPPORTED;
-  if (batch == 0 || Tq == 0) return CSKV_OK;
-  if (!out_idx || (N > 0 && !scores)) return CSKV_ERR_INVALID_ARG;
-  if (!aligned16(scores, out_idx)) return CSKV_ERR_MISALIGNED;
-  IdxArgs a{};
-  a.scores = (float*)scores; a.out = out_idx;
-  a.Tq = Tq; a.N = N; a.pos0 = pos0; a.ldS = ld; a.rows_ws = Tq; a.row0 = 0; a.nrows = Tq;
-  a.m = m; a.k = k;
-  return launch_select(a, batch, (hipStream_t)stream);
 }

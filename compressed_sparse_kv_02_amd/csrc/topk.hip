@@ -1,0 +1,422 @@
+// Per-query exact top-k selection for gfx950.
+//
+// "Paper Breakdown: DeepSeek-V4", §2.3.1 "DSA on Compressed KV (lightning
+// indexer + top-k)": each query keeps the k compressed entries of largest
+// indexer score ("How DeepSeek-V4 architecture and training work together",
+// "Two compressed views of one history": k = 1024). The pages leave ties and
+// order open; here the smaller index wins among equal scores and the list is
+// ascending, -1 padded when fewer than k entries are visible.
+//
+// Scores are compared through an order-preserving uint32 key, so the
+// selection is integer work and deterministic.
+//
+// Many rows (prefill): one 1024-thread workgroup per row. A strided sample
+// of the row gives a threshold that about 3k entries exceed; one vectorised
+// pass keeps those entries (in index order) in LDS, an exact 3-pass radix
+// select (11 + 11 + 10 bits) finds the k-th largest among them, and an
+// in-order pick with block prefix sums writes the result without a sort.
+// Should the sample miss, the row falls back to the exact radix select over
+// global memory.
+//
+// Few long rows (decode): the row is cut into parts selected by separate
+// workgroups, then merged (topk_part / topk_merge below).
+#include "indexer.h"
+
+namespace cskv {
+
+// ----------------------------------------------------------------------------
+// Exact top-k per row
+// ----------------------------------------------------------------------------
+constexpr int TOPK_THREADS = 1024;
+constexpr int TOPK_CAP = 8192;      // candidate (key, index) pairs held in LDS
+constexpr int TOPK_SAMPLES = 4096;  // strided sample of a long row, for the candidate threshold
+
+// Exclusive prefix sum over the workgroup; also returns the total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < TOPK_THREADS / 64; ++w) {
+    const int x = wsum[w];
+    if (w < wave) pre += x;
+    tot += x;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + incl - v;
+}
+
+struct TopkShared {
+  int hist[2048];
+  int wsum[TOPK_THREADS / 64];
+  int sel_bin, sel_above, count;
+};
+
+// Radix select (11 + 11 + 10 bits): the kk-th largest of n keys read through key_at.
+// Returns it in tau; `need` = how many keys equal to tau belong to the top kk.
+template <typename KeyAt>
+__device__ void radix_select(KeyAt key_at, int64_t n, int kk, TopkShared& sh, uint32_t& tau, int& need) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  need = kk;
+  const int shifts[3] = {21, 10, 0};
+  const int nbits[3] = {11, 11, 10};
+  for (int p = 0; p < 3; ++p) {
+    const int nb = 1 << nbits[p];
+    const uint32_t bmask = (uint32_t)nb - 1u;
+    for (int i = tid; i < 2048; i += TOPK_THREADS) sh.hist[i] = 0;
+    __syncthreads();
+    for (int64_t s = tid; s < n; s += TOPK_THREADS) {
+      const uint32_t key = key_at(s);
+      if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shifts[p]) & bmask], 1);
+    }
+    __syncthreads();
+    const int bpt = nb / TOPK_THREADS;  // bins per thread, descending
+    int cnt[2] = {0, 0}, loc = 0;
+    for (int q = 0; q < bpt; ++q) {
+      cnt[q] = sh.hist[nb - 1 - (tid * bpt + q)];
+      loc += cnt[q];
+    }
+    int total;
+    int above = block_exclusive_scan(loc, sh.wsum, total);
+    for (int q = 0; q < bpt; ++q) {
+      if (above < need && need <= above + cnt[q]) {
+        sh.sel_bin = nb - 1 - (tid * bpt + q);
+        sh.sel_above = above;
+      }
+      above += cnt[q];
+    }
+    __syncthreads();
+    need -= sh.sel_above;
+    prefix |= (uint32_t)sh.sel_bin << shifts[p];
+    pmask |= bmask << shifts[p];
+    __syncthreads();
+  }
+  tau = prefix;
+}
+
+// Emits, in index order, the entries with key > tau plus the first `need` with key == tau:
+// emit(position among the emitted, s).
+template <typename KeyAt, typename Emit>
+__device__ void ordered_pick(KeyAt key_at, Emit emit, int64_t n, uint32_t tau, int need, TopkShared& sh) {
+  const int tid = threadIdx.x;
+  int eq_taken = 0, written = 0;
+  for (int64_t base = 0; base < n; base += TOPK_THREADS) {
+    const int64_t s = base + tid;
+    uint32_t key = 0;
+    if (s < n) key = key_at(s);
+    const int gt = (s < n && key > tau) ? 1 : 0;
+    const int eq = (s < n && key == tau) ? 1 : 0;
+    int eq_tot;
+    const int eq_rank = block_exclusive_scan(eq, sh.wsum, eq_tot);
+    const int sel = gt | (eq && (eq_taken + eq_rank) < need ? 1 : 0);
+    int sel_tot;
+    const int pos = block_exclusive_scan(sel, sh.wsum, sel_tot);
+    if (sel) emit(written + pos, s);
+    eq_taken += eq_tot;
+    written += sel_tot;
+  }
+}
+
+// Exact top-k of one row straight from global memory (3 radix passes + in-order pick).
+__device__ void select_row_global(const float* row, int64_t V, int k, int32_t* out, TopkShared& sh) {
+  uint32_t tau;
+  int need;
+  auto key_at = [&](int64_t s) { return score_key(row[s]); };
+  radix_select(key_at, V, k, sh, tau, need);
+  ordered_pick(key_at, [&](int pos, int64_t s) { out[pos] = (int32_t)s; }, V, tau, need, sh);
+}
+
+// One 1024-thread workgroup per query row.
+//  * V <= CAP: the whole row becomes the candidate set.
+//  * otherwise: the (3k * S / V)-th largest of S strided samples gives a
+//    threshold tau0; one vectorised pass over the row keeps every entry with
+//    key >= tau0, in index order, as candidates (about 3k of them).
+//  * exact radix select among the candidates, then an in-order pick.
+// If the candidates do not hold at least k entries (or overflow LDS), the
+// row falls back to the exact 3-pass radix select over global memory. Both
+// routes return the same, exact set.
+__global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
+  __shared__ uint32_t ckey[TOPK_CAP];
+  __shared__ int32_t cidx[TOPK_CAP];
+  __shared__ TopkShared sh;
+  uint32_t* samp = reinterpret_cast<uint32_t*>(cidx);  // the sample is done before candidates exist
+  static_assert(TOPK_SAMPLES <= TOPK_CAP, "sample buffer aliases the candidate indices");
+
+  const int tid = threadIdx.x;
+  const int b = blockIdx.y;
+  const int64_t jr = blockIdx.x;
+  const int64_t j = a.row0 + jr;
+  const int k = a.k;
+  int32_t* out = a.out + ((int64_t)b * a.Tq + j) * k;
+  const int64_t V = visible_entries(a.pos0 + j, a.m, a.N);
+  if (V <= k) {
+    for (int i = tid; i < k; i += TOPK_THREADS) out[i] = i < V ? i : -1;
+    return;
+  }
+  const float* row = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
+  int n_cand = 0;
+  if (V <= TOPK_CAP) {
+    for (int64_t s = tid; s < V; s += TOPK_THREADS) {
+      ckey[s] = score_key(row[s]);
+      cidx[s] = (int32_t)s;
+    }
+    n_cand = (int)V;
+    __syncthreads();
+  } else {
+    // threshold from a strided sample
+    for (int i = tid; i < TOPK_SAMPLES; i += TOPK_THREADS) samp[i] = score_key(row[(int64_t)i * V / TOPK_SAMPLES]);
+    __syncthreads();
+    int r = (int)(((int64_t)3 * k * TOPK_SAMPLES + V - 1) / V);
+    if (r > TOPK_SAMPLES) r = TOPK_SAMPLES;
+    uint32_t tau0;
+    int need0;
+    radix_select([&](int64_t s) { return samp[s]; }, TOPK_SAMPLES, r, sh, tau0, need0);
+    __syncthreads();  // the sample (aliasing cidx) is consumed
+    // one pass: keep key >= tau0 in index order. Each thread owns 4 consecutive entries per
+    // 4096-entry chunk; UNR chunks are loaded before any is scanned, to keep loads in flight.
+    constexpr int UNR = 4;
+    constexpr int CHUNK = 4 * TOPK_THREADS;
+    int cnt = 0;
+    for (int64_t base = 0; base < V; base += UNR * CHUNK) {
+      float4 v[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int64_t s0 = base + u * CHUNK + 4 * tid;
+        v[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+        if (s0 < V) v[u] = *reinterpret_cast<const float4*>(row + s0);  // rows are padded to 64 entries
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int64_t s0 = base + u * CHUNK + 4 * tid;
+        const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+        uint32_t kk4[4];
+        int f = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kk4[e] = score_key(vv[e]);
+          if (s0 + e < V && kk4[e] >= tau0) ++f;
+        }
+        int tot;
+        int pos = cnt + block_exclusive_scan(f, sh.wsum, tot);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (s0 + e < V && kk4[e] >= tau0) {
+            if (pos < TOPK_CAP) {
+              ckey[pos] = kk4[e];
+              cidx[pos] = (int32_t)(s0 + e);
+            }
+            ++pos;
+          }
+        }
+        cnt += tot;
+      }
+    }
+    __syncthreads();
+    n_cand = cnt;
+  }
+  if (n_cand >= k && n_cand <= TOPK_CAP) {
+    uint32_t tau;
+    int need;
+    radix_select([&](int64_t s) { return ckey[s]; }, n_cand, k, sh, tau, need);
+    ordered_pick([&](int64_t s) { return ckey[s]; }, [&](int pos, int64_t s) { out[pos] = cidx[s]; }, n_cand,
+                 tau, need, sh);
+  } else {
+    select_row_global(row, V, k, out, sh);
+  }
+}
+
+// Few long rows (decode): one workgroup per row would leave most of the GPU idle,
+// so each row is cut into parts of part_len entries.
+//  * topk_part (one workgroup per part): the part's kp best entries (exact, by
+//    key then smaller index), in index order, go to the row's candidate list at
+//    slot p * kp, with a record {count, kp-th key, truncated}.
+//  * topk_merge (one workgroup per row): the exact top-k of the concatenated
+//    candidates (index order is kept, parts being consecutive ranges). An entry
+//    a truncated part dropped has a key <= that part's kp-th key; if every such
+//    key is below the candidates' k-th key, at least k kept entries beat every
+//    dropped one, so the candidates hold the row's exact top-k. Otherwise the
+//    row falls back to the exact select over global memory.
+constexpr int TOPK_MAX_PARTS = 128;
+constexpr int64_t TOPK_SEL_STRIDE = (int64_t)TOPK_CAP * 8 + TOPK_MAX_PARTS * 16;
+
+__global__ __launch_bounds__(TOPK_THREADS) void topk_part(IdxArgs a) {
+  __shared__ uint32_t ckey[TOPK_CAP];
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x;
+  const int p = blockIdx.x;
+  const int64_t jr = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t V = visible_entries(a.pos0 + a.row0 + jr, a.m, a.N);
+  if (V <= a.k) return;
+  uint8_t* ws = a.sel_ws + ((int64_t)b * a.nrows + jr) * TOPK_SEL_STRIDE;
+  uint32_t* wkey = reinterpret_cast<uint32_t*>(ws) + (int64_t)p * a.kp;
+  int32_t* widx = reinterpret_cast<int32_t*>(ws + (int64_t)TOPK_CAP * 4) + (int64_t)p * a.kp;
+  int4* rec = reinterpret_cast<int4*>(ws + (int64_t)TOPK_CAP * 8) + p;
+  const int64_t s0 = (int64_t)p * a.part_len;
+  const int n = (int)(V - s0 < a.part_len ? (V - s0 > 0 ? V - s0 : 0) : a.part_len);
+  if (n == 0) {
+    if (tid == 0) *rec = make_int4(0, 0, 0, 0);
+    return;
+  }
+  const float* row = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS + s0;
+  for (int i = 4 * tid; i < n; i += 4 * TOPK_THREADS) {  // s0 % 4 == 0; rows are padded to 64 entries
+    const float4 v = *reinterpret_cast<const float4*>(row + i);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (i + e < n) ckey[i + e] = score_key(vv[e]);
+  }
+  __syncthreads();
+  if (n <= a.kp) {
+    for (int i = tid; i < n; i += TOPK_THREADS) {
+      wkey[i] = ckey[i];
+      widx[i] = (int32_t)(s0 + i);
+    }
+    if (tid == 0) *rec = make_int4(n, 0, 0, 0);
+    return;
+  }
+  uint32_t tau;
+  int need;
+  radix_select([&](int64_t s) { return ckey[s]; }, n, a.kp, sh, tau, need);
+  ordered_pick([&](int64_t s) { return ckey[s]; },
+               [&](int pos, int64_t s) {
+                 wkey[pos] = ckey[s];
+                 widx[pos] = (int32_t)(s0 + s);
+               },
+               n, tau, need, sh);
+  if (tid == 0) *rec = make_int4(a.kp, (int)tau, 1, 0);
+}
+
+__global__ __launch_bounds__(TOPK_THREADS) void topk_merge(IdxArgs a) {
+  __shared__ uint32_t ckey[TOPK_CAP];
+  __shared__ int32_t cidx[TOPK_CAP];
+  __shared__ int pcnt[TOPK_MAX_PARTS], poff[TOPK_MAX_PARTS];
+  __shared__ TopkShared sh;
+  const int tid = threadIdx.x;
+  const int64_t jr = blockIdx.x;
+  const int b = blockIdx.y;
+  const int k = a.k;
+  int32_t* out = a.out + ((int64_t)b * a.Tq + a.row0 + jr) * k;
+  const int64_t V = visible_entries(a.pos0 + a.row0 + jr, a.m, a.N);
+  if (V <= k) {
+    for (int i = tid; i < k; i += TOPK_THREADS) out[i] = i < V ? i : -1;
+    return;
+  }
+  const uint8_t* ws = a.sel_ws + ((int64_t)b * a.nrows + jr) * TOPK_SEL_STRIDE;
+  const uint32_t* wkey = reinterpret_cast<const uint32_t*>(ws);
+  const int32_t* widx = reinterpret_cast<const int32_t*>(ws + (int64_t)TOPK_CAP * 4);
+  const int4* rec = reinterpret_cast<const int4*>(ws + (int64_t)TOPK_CAP * 8);
+  const int P = (int)((V + a.part_len - 1) / a.part_len);
+  const int4 r = tid < P ? rec[tid] : make_int4(0, 0, 0, 0);
+  int n_cand;
+  const int off = block_exclusive_scan(r.x, sh.wsum, n_cand);
+  if (tid < P) {
+    pcnt[tid] = r.x;
+    poff[tid] = off;
+  }
+  __syncthreads();
+  for (int i = tid; i < P * a.kp; i += TOPK_THREADS) {
+    const int p = i / a.kp, e = i - p * a.kp;
+    if (e < pcnt[p]) {
+      ckey[poff[p] + e] = wkey[i];
+      cidx[poff[p] + e] = widx[i];
+    }
+  }
+  __syncthreads();
+  const float* row = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
+  if (n_cand < k) {
+    select_row_global(row, V, k, out, sh);
+    return;
+  }
+  uint32_t tau;
+  int need;
+  radix_select([&](int64_t s) { return ckey[s]; }, n_cand, k, sh, tau, need);
+  const bool unsafe = tid < P && r.z != 0 && (uint32_t)r.y >= tau;
+  if (__syncthreads_or(unsafe)) {
+    select_row_global(row, V, k, out, sh);
+    return;
+  }
+  ordered_pick([&](int64_t s) { return ckey[s]; }, [&](int pos, int64_t s) { out[pos] = cidx[s]; }, n_cand,
+               tau, need, sh);
+}
+
+// ----------------------------------------------------------------------------
+// Host side
+// ----------------------------------------------------------------------------
+// Parts for the two-kernel selection: rows of at least 4 parts of TOPK_CAP entries, and
+// at most 64 rows in the call (more rows fill the GPU one workgroup per row).
+struct SplitPlan {
+  int parts, kp;
+};
+
+static bool plan_split(int64_t rows, int64_t vmax, int k, SplitPlan& sp) {
+  if (rows > 64) return false;
+  const int64_t P = ceil_div(vmax, (int64_t)TOPK_CAP);
+  if (P < 4 || P > TOPK_MAX_PARTS) return false;
+  int64_t kp = round_up(ceil_div(4 * (int64_t)k, P), (int64_t)64);
+  if (P * kp > TOPK_CAP) return false;
+  sp.parts = (int)P;
+  sp.kp = (int)kp;
+  return true;
+}
+
+size_t split_ws_bytes(int64_t rows, int64_t vmax, int k) {
+  SplitPlan sp;
+  return plan_split(rows, vmax, k, sp) ? (size_t)(rows * TOPK_SEL_STRIDE) : 0;
+}
+
+// Selection for rows [a.row0, a.row0 + a.nrows); sel_ws/sel_bytes: optional workspace
+// for the two-kernel route.
+int launch_select(IdxArgs& a, int batch, void* sel_ws, size_t sel_bytes, hipStream_t st) {
+  const int64_t last = a.pos0 + a.row0 + a.nrows - 1;
+  int64_t vmax = (last + 1) / a.m;
+  if (vmax > a.N) vmax = a.N;
+  SplitPlan sp;
+  const int64_t rows = (int64_t)batch * a.nrows;
+  if (sel_ws && plan_split(rows, vmax, a.k, sp) && sel_bytes >= (size_t)(rows * TOPK_SEL_STRIDE)) {
+    a.sel_ws = (uint8_t*)sel_ws;
+    a.part_len = TOPK_CAP;
+    a.kp = sp.kp;
+    hipLaunchKernelGGL(topk_part, dim3((unsigned)sp.parts, (unsigned)a.nrows, (unsigned)batch),
+                       dim3(TOPK_THREADS), 0, st, a);
+    hipLaunchKernelGGL(topk_merge, dim3((unsigned)a.nrows, (unsigned)batch), dim3(TOPK_THREADS), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(topk_select, dim3((unsigned)a.nrows, (unsigned)batch), dim3(TOPK_THREADS), 0, st, a);
+  }
+  return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+}
+
+}  // namespace cskv
+
+using namespace cskv;
+
+extern "C" size_t cskv_topk_workspace_size(int batch, int64_t Tq, int64_t N, int k) {
+  if (batch <= 0 || Tq <= 0 || k < 1) return 0;
+  return split_ws_bytes((int64_t)batch * Tq, N, k);
+}
+
+extern "C" int topk_select(const float* scores, int64_t ld, int batch, int64_t Tq, int64_t N,
+                           int64_t pos0, int m, int k, int32_t* out_idx, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  if (batch < 0 || Tq < 0 || N < 0 || pos0 < 0 || m < 1 || ld < N) return CSKV_ERR_BAD_SHAPE;
+  if (ld % 4 != 0) return CSKV_ERR_BAD_SHAPE;
+  if (k < 1) return CSKV_ERR_BAD_SHAPE;
+  if (k > CSKV_MAX_TOPK) return CSKV_ERR_UNSUPPORTED;
+  if (batch == 0 || Tq == 0) return CSKV_OK;
+  if (!out_idx || (N > 0 && !scores)) return CSKV_ERR_INVALID_ARG;
+  if (!aligned16(scores, out_idx, workspace)) return CSKV_ERR_MISALIGNED;
+  IdxArgs a{};
+  a.scores = (float*)scores; a.out = out_idx;
+  a.Tq = Tq; a.N = N; a.pos0 = pos0; a.ldS = ld; a.rows_ws = Tq; a.row0 = 0; a.nrows = Tq;
+  a.m = m; a.k = k;
+  return launch_select(a, batch, workspace, workspace ? ws_bytes : 0, (hipStream_t)stream);
+}

@@ -116,6 +116,9 @@ def make_inputs(L: LayerCall, device="cuda") -> Dict[str, torch.Tensor]:
         t["wI"] = uniform_device(L.seed, f"{L.name}.wI", (Bt, T, L.HI), device)
         t["idx"] = torch.empty(Bt, T, L.k, dtype=torch.int32, device=device)
         t["ws.scores"] = torch.empty(Bt, T, B.score_ld(L.N), dtype=torch.float32, device=device)
+        nsel = B.topk_workspace_bytes(Bt, T, L.N, L.k)
+        if nsel:
+            t["ws.topk"] = torch.empty(nsel, dtype=torch.uint8, device=device)
     t["out"] = torch.empty(Bt, T, L.H, d, dtype=L.torch_dtype, device=device)
     t["lse"] = torch.empty(Bt, T, L.H, dtype=torch.float32, device=device)
     if L.decode:
@@ -150,7 +153,7 @@ def score_step(L: LayerCall, t: Dict[str, torch.Tensor]) -> None:
 def topk_step(L: LayerCall, t: Dict[str, torch.Tensor]) -> None:
     """Step 4b (CSA only): per-query top-k of the scores (indexer_topk's second half)."""
     if L.kind == "csa":
-        B.topk_select(t["ws.scores"], L.N, L.pos0, L.m, L.k, out=t["idx"])
+        B.topk_select(t["ws.scores"], L.N, L.pos0, L.m, L.k, out=t["idx"], workspace=t.get("ws.topk"))
 
 
 def select_step(L: LayerCall, t: Dict[str, torch.Tensor]) -> None:

@@ -141,8 +141,9 @@ int hca_compress(const void* C, const void* Z, const void* B, int batch, int64_t
  *   (HI * dI + HI) * 4 <= 48 KiB
  *   1 <= k <= CSKV_MAX_TOPK, m >= 1
  *   out_idx   : [batch, Tq, k] int32
- *   workspace : cskv_indexer_workspace_size(...) bytes (fp32 score rows and
- *               selection counters), device memory
+ *   workspace : cskv_indexer_workspace_size(...) bytes of device memory (fp32
+ *               score rows, and per-part candidates when few long rows are
+ *               selected with several workgroups per row)
  */
 size_t cskv_indexer_workspace_size(int batch, int64_t Tq, int64_t N, int HI, int k, int dtype);
 int indexer_topk(const void* qI, const float* wI, const void* KI, int batch, int64_t Tq, int64_t N,
@@ -160,13 +161,23 @@ int indexer_topk(const void* qI, const float* wI, const void* KI, int batch, int
  *   other arguments and limits as in indexer_topk
  * topk_select reads such a matrix and writes out_idx exactly as indexer_topk
  * does (k largest of the first V_t scores, smaller index first among equal
- * scores, ascending, -1 padded).
+ * scores, ascending, -1 padded). Its workspace is optional (see
+ * cskv_topk_workspace_size); ld % 4 == 0 and 16-byte aligned rows.
  */
 int indexer_scores(const void* qI, const float* wI, const void* KI, int batch, int64_t Tq, int64_t N,
                    int HI, int dI, int64_t pos0, int m, float* scores, int64_t ld, int dtype,
                    void* stream);
 int topk_select(const float* scores, int64_t ld, int batch, int64_t Tq, int64_t N, int64_t pos0, int m,
-                int k, int32_t* out_idx, void* stream);
+                int k, int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * cskv_topk_workspace_size -- device bytes topk_select may use to select few
+ * long rows (at most 64 rows of at least 4 x 8192 visible entries, e.g.
+ * decode) with several workgroups per row; 0 when the call has no use for
+ * it. A NULL or smaller workspace is allowed: every row is then selected by
+ * one workgroup, with the same result.
+ */
+size_t cskv_topk_workspace_size(int batch, int64_t Tq, int64_t N, int k);
 
 /*
  * compressed_attn_prefill -- MQA core attention over compressed entries,

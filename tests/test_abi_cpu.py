@@ -4,6 +4,8 @@ any HIP call (so these calls never touch a device)."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 
 import pytest
 
@@ -30,15 +32,24 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(L, n), n
     from compressed_sparse_kv_02_amd import binding
     assert sorted(binding.EXPORTS) == names
 
 
+def test_exports_nothing_else():
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = sorted(ln.split()[-1] for ln in out.splitlines() if ln.split()[1:2] == ["T"])
+    assert exported == declared_functions()
+
+
 def test_version_and_status_strings(L):
-    assert L.cskv_version() == 100
+    assert L.cskv_version() == 200
     for code in range(-7, 1):
         assert len(L.cskv_status_string(code)) >= 2
     assert L.cskv_status_string(-99) == b"unknown status"
@@ -107,6 +118,28 @@ def test_indexer_topk_validation(L):
     assert call(Tq=0) == OK
     need = L.cskv_indexer_workspace_size(1, 64, 1000, 64, 1024, 0)
     assert need >= 64 * 1000 * 4
+
+
+def test_topk_select_validation(L):
+    f = L.topk_select
+    base = dict(scores=P, ld=1024, batch=1, Tq=4, N=1000, pos0=0, m=4, k=64, out=P, ws=None, wsb=0, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*a.values())
+    assert call(k=4096) == UNSUPPORTED
+    assert call(k=0) == SHAPE
+    assert call(ld=999) == SHAPE       # ld < N
+    assert call(ld=1002) == SHAPE      # ld % 4 != 0
+    assert call(out=None) == INVALID
+    assert call(out=P + 8) == MISALIGNED
+    assert call(ws=P + 8, wsb=1 << 20) == MISALIGNED
+    assert call(Tq=0) == OK
+    # the two-kernel route is offered to few rows of at least 4 x 8192 entries only
+    assert L.cskv_topk_workspace_size(8, 1, 262144, 1024) > 0
+    assert L.cskv_topk_workspace_size(8, 1, 20000, 1024) == 0
+    assert L.cskv_topk_workspace_size(2, 4096, 262144, 1024) == 0
+    assert L.cskv_topk_workspace_size(1, 1, 1 << 21, 1024) == 0   # more than 128 parts
 
 
 def test_attention_validation(L):

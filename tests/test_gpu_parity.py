@@ -143,6 +143,42 @@ def test_indexer_decode_1m_full():
         check_topk_row(idx[b, 0], I, 262144, 1024, what=f"b{b}")
 
 
+@pytest.mark.parametrize("kind,bt,Tq,N,k", [
+    ("normal", 2, 3, 200000, 1024),
+    ("normal", 1, 2, 262144, 2048),   # max k: 32 parts x 256 candidates
+    ("ramp", 1, 2, 100000, 1024),     # the top-k sits in the last part: fallback route
+    ("descending", 1, 1, 100000, 1024),  # the top-k sits in the first part: fallback route
+    ("ties", 2, 2, 65536, 2048),      # 16 distinct values: ties across parts
+    ("equal", 1, 1, 40000, 100),      # one value: the first k indices
+])
+def test_topk_split_route(kind, bt, Tq, N, k):
+    """Few long rows go through the two-kernel route (parts + merge); it must equal the
+    one-workgroup-per-row route and the oracle's top-k exactly (same fp32 scores on both sides)."""
+    say("topk split route", kind, bt, Tq, N, k)
+    ld = B.score_ld(N)
+    if kind == "normal":
+        sc = normal_device(61, "tk.normal", (bt, Tq, ld), 1.0, "f32", DEV)
+    elif kind == "ties":
+        sc = torch.floor(uniform_device(61, "tk.ties", (bt, Tq, ld), DEV) * 16.0)
+    elif kind == "equal":
+        sc = torch.full((bt, Tq, ld), 0.5, dtype=torch.float32, device=DEV)
+    else:
+        ramp = torch.arange(ld, dtype=torch.float32, device=DEV)
+        sc = (ramp if kind == "ramp" else -ramp).expand(bt, Tq, ld).contiguous()
+    pos0 = 4 * N - Tq + 1 - 8   # rows of V = N - 2 .. N
+    assert B.topk_workspace_bytes(bt, Tq, N, k) > 0
+    ws = torch.empty(B.topk_workspace_bytes(bt, Tq, N, k), dtype=torch.uint8, device=DEV)
+    a = B.topk_select(sc, N, pos0, 4, k, workspace=ws)
+    b = B.topk_select(sc, N, pos0, 4, k)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    a, scn = a.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
+    for bb in range(bt):
+        for r in range(Tq):
+            V = O.visible(pos0 + r, 4, N)
+            assert np.array_equal(a[bb, r], O.topk_row(scn[bb, r], V, k)), (bb, r)
+
+
 # ----------------------------------------------------------------------------- attention
 
 def _random_idx(bt, Tq, pos0, m, N, k, seed):
