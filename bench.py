@@ -89,7 +89,7 @@ def write_traffic(fetch_csv: str, write_csv: str) -> None:
         factor = COPY_PROBE_BYTES / (kib * 1024.0)
         out[f"{counter}_copy_kib"] = kib
         out[f"{counter}_factor"] = factor
-        for tag, tmpl in (("prefill", "indexer_score_mfma<2, 8, 8>"), ("decode", "indexer_score_mfma<2, 8, 1>")):
+        for tag, tmpl in (("prefill", "indexer_score_mfma<2, 8>"), ("decode", "indexer_score_stream<2, 8>")):
             vs = [v for (name, grid), xs in vals.items() if tmpl in name for v in xs]
             assert vs, f"no {tmpl} dispatch in {path}"
             ent = out.setdefault(f"indexer_score_mfma_{tag}", {})
@@ -296,7 +296,7 @@ def main():
     traffic = tr.get("indexer_score_mfma_prefill", {}).get("hbm_bytes_per_launch")
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                 "frac": achieved * 1e12 / PEAK_BF16_FLOPS, "traffic": traffic,
-                "kernel": "indexer_score_mfma<2,8,8> (prefill CSA layers)", "avg_launch_ms": score_ms,
+                "kernel": "indexer_score_mfma<2,8> (prefill CSA layers)", "avg_launch_ms": score_ms,
                 "algorithmic_flops_per_launch": fl}
     dscore_ms = sum(a.elapsed_time(b) for a, b in rec["dec_score"]) / len(rec["dec_score"])
     db = decode_score_bytes(decode[0])
@@ -304,7 +304,7 @@ def main():
     dtraffic = tr.get("indexer_score_mfma_decode", {}).get("hbm_bytes_per_launch")
     roofline_dec = {"bound": "hbm", "achieved": dach, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                     "frac": dach * 1e9 / PEAK_HBM_BYTES, "traffic": dtraffic,
-                    "kernel": "indexer_score_mfma<2,8,1> (decode CSA layer)", "avg_launch_ms": dscore_ms,
+                    "kernel": "indexer_score_stream<2,8> (decode CSA layer)", "avg_launch_ms": dscore_ms,
                     "algorithmic_bytes_per_launch": db}
 
     out = {

@@ -19,7 +19,8 @@ struct IdxArgs {
   const void* KI;
   float* scores;  // [batch][rows_ws][ldS]
   int32_t* out;
-  int64_t Tq, N, pos0, ldS, span;
+  int64_t Tq, N, pos0, ldS, span;  // span: keys per workgroup (prefill scoring)
+  int64_t row_waves;               // decode scoring: waves sharing one query row
   int64_t row0, nrows, rows_ws;  // query rows handled by this chunk
   int HI, dI, m, k;
   // two-kernel selection of few long rows (topk_part + topk_merge)

@@ -27,13 +27,14 @@ namespace cskv {
 // (negative floats, -0.0 included, are negative as int32). One VALU op, no NaN canonicalisation.
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-template <int HT, int KS, int QB>
+// Prefill rows: 8 queries per workgroup, one per wave, sharing 128-key LDS tiles.
+template <int HT, int KS>
 __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
-  constexpr int WAVES = 8;
-  constexpr int KW = WAVES / QB;       // key lanes: waves that take different key blocks
-  constexpr int SUB = QB == 8 ? 4 : 1; // 32-key sub-blocks per wave per tile
+  constexpr int QB = 8;                // queries per workgroup (one per wave)
+  constexpr int KW = 1;                // waves that take different key blocks
+  constexpr int SUB = 4;               // 32-key sub-blocks per wave per tile
   constexpr int DI = 16 * KS;
-  constexpr int TILE = KW * SUB * 32;  // keys per LDS tile (128 or 256)
+  constexpr int TILE = KW * SUB * 32;  // keys per LDS tile
   constexpr int ROW = DI + 8;          // padded LDS row (bf16), +16 bytes vs bank conflicts
   constexpr int CPR = DI / 8;          // 16-byte chunks per key row
   constexpr int CHUNKS = TILE * CPR;
@@ -146,6 +147,118 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
   }
 }
 
+// Decode-shaped rows (fewer than 64 queries in the call): row_waves waves score
+// one query, wave r taking the 32-key blocks r, r + row_waves, r + 2 row_waves,
+// ..., so the waves of a row read one contiguous, advancing window of keys
+// (every HBM channel busy) rather than each streaming its own distant span. A
+// key serves one query only, so waves share nothing: each loads its block with
+// fully coalesced 16-byte loads (1 KiB per instruction) NB blocks ahead into
+// registers, and turns it into the MFMA B layout through its own padded LDS
+// rows (no workgroup barrier; a wave's LDS operations run in order). The K
+// dimension is permuted the same way in A and B (lane half h, k-step ks: dims
+// h*8*KS + 8*ks .. +8), so each lane reads one contiguous half row from LDS;
+// every dot product is unchanged.
+template <int HT, int KS>
+__global__ __launch_bounds__(256) void indexer_score_stream(IdxArgs a) {
+  constexpr int DI = 16 * KS;
+  constexpr int NB = 2;  // key blocks in registers: the current one + 1 in flight
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, kl = lane & 31;
+  const int b = blockIdx.z;
+  const int64_t jr = blockIdx.y;
+  const int64_t j = a.row0 + jr;
+  const int64_t vj = visible_entries(a.pos0 + j, a.m, a.N);
+  const int64_t wr = (int64_t)blockIdx.x * 4 + wave;  // this wave's rank in the row
+  const int64_t row_blk = (vj + 31) / 32;
+  if (wr >= row_blk) return;  // per wave: the kernel has no workgroup barrier
+  const int nblk = (int)((row_blk - wr + a.row_waves - 1) / a.row_waves);  // blocks of this wave
+
+  bf16x8 qa[HT][KS];
+  float wv[HT][16];
+  {
+    const uint16_t* qp = (const uint16_t*)a.qI + ((int64_t)b * a.Tq + j) * a.HI * DI + half * 8 * KS;
+    const float* wp = a.wI + ((int64_t)b * a.Tq + j) * a.HI;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht) {
+      const int h = ht * 32 + kl;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (h < a.HI) v = *reinterpret_cast<const u32x4*>(qp + (int64_t)h * DI + 8 * ks);
+        qa[ht][ks] = __builtin_bit_cast(bf16x8, v);
+      }
+      // accumulator rows held by this lane: 8*(i/4) + 4*(lane/32) + i%4
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int hh = ht * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+        wv[ht][i] = hh < a.HI ? wp[hh] : 0.f;
+      }
+    }
+  }
+
+  const uint16_t* kbase = (const uint16_t*)a.KI + (int64_t)b * a.N * DI + half * 8 * KS;
+  float* srow = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
+  auto key_of = [&](int blk) { return (wr + (int64_t)blk * a.row_waves) * 32 + kl; };
+  constexpr int RB = 32 * KS;  // bytes per key row
+  constexpr int RS = RB + 16;  // padded LDS row
+  __shared__ __attribute__((aligned(16))) uint8_t kst[4][32 * RS];
+  uint8_t* my = kst[wave];
+  const uint8_t* kb0 = (const uint8_t*)a.KI + (int64_t)b * a.N * RB;
+  u32x4 kb[NB][KS];
+  auto load = [&](int blk, u32x4 (&dst)[KS]) {
+    if (blk >= nblk) return;
+    const int64_t key0 = (wr + (int64_t)blk * a.row_waves) * 32;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int off = i * 1024 + lane * 16;
+      int64_t r = key0 + off / RB;
+      if (r > vj - 1) r = vj - 1;
+      dst[i] = *reinterpret_cast<const u32x4*>(kb0 + r * RB + (off % RB));
+    }
+  };
+  auto step = [&](int blk, const u32x4 (&src)[KS]) {
+    if (blk >= nblk) return;
+    // wave-scope fences: the previous block's LDS reads precede these writes, which
+    // precede the reads below (other lanes' rows)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const int off = i * 1024 + lane * 16;
+      *reinterpret_cast<u32x4*>(my + (off / RB) * RS + (off % RB)) = src[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    u32x4 bop[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bop[ks] = *reinterpret_cast<const u32x4*>(my + kl * RS + (half * KS + ks) * 16);
+    f32x16 acc[HT];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, bop[ks]);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht)
+        acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][ks], bv, ks == 0 ? f32x16{} : acc[ht], 0, 0, 0);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part = __builtin_fmaf(relu_bits(acc[ht][i]), wv[ht][i], part);
+    part += __shfl_xor(part, 32, 64);
+    const int64_t s = key_of(blk);
+    if (lane < 32 && s < vj) srow[s] = part;
+  };
+
+#pragma unroll
+  for (int p = 0; p < NB; ++p) load(p, kb[p]);
+  for (int it = 0; it < nblk; it += NB) {
+#pragma unroll
+    for (int p = 0; p < NB; ++p) {
+      step(it + p, kb[p]);
+      load(it + p + NB, kb[p]);
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------
 // fp32 scoring on the vector ALUs (fp32 mode: small shapes, correctness)
 // ----------------------------------------------------------------------------
@@ -176,6 +289,7 @@ __global__ __launch_bounds__(256) void indexer_score_f32(IdxArgs a) {
 // Host side
 // ----------------------------------------------------------------------------
 static constexpr int64_t SCORE_CHUNK_BYTES = (int64_t)128 << 20;
+static constexpr int64_t STREAM_WAVES = 4096;  // decode scoring: waves over the whole call
 
 struct IdxPlan {
   int64_t ldS, rows_ws, qb;
@@ -196,27 +310,31 @@ static IdxPlan plan_indexer(int batch, int64_t Tq, int64_t N, int dtype) {
   return p;
 }
 
-template <int HT, int KS, int QB>
+// STREAM = false: indexer_score_mfma (512 threads), true: indexer_score_stream (256 threads).
+template <int HT, int KS, bool STREAM>
 static void launch_mfma(const IdxArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((indexer_score_mfma<HT, KS, QB>), grid, dim3(512), 0, st, a);
+  if constexpr (STREAM)
+    hipLaunchKernelGGL((indexer_score_stream<HT, KS>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((indexer_score_mfma<HT, KS>), grid, dim3(512), 0, st, a);
 }
 
-template <int HT, int QB>
+template <int HT, bool STREAM>
 static bool dispatch_ks(int ks, const IdxArgs& a, dim3 grid, hipStream_t st) {
   switch (ks) {
-    case 2: launch_mfma<HT, 2, QB>(a, grid, st); return true;
-    case 4: launch_mfma<HT, 4, QB>(a, grid, st); return true;
-    case 8: launch_mfma<HT, 8, QB>(a, grid, st); return true;
+    case 2: launch_mfma<HT, 2, STREAM>(a, grid, st); return true;
+    case 4: launch_mfma<HT, 4, STREAM>(a, grid, st); return true;
+    case 8: launch_mfma<HT, 8, STREAM>(a, grid, st); return true;
     default: return false;
   }
 }
 
-template <int QB>
+template <bool STREAM>
 static bool dispatch_mfma(int ht, int ks, const IdxArgs& a, dim3 grid, hipStream_t st) {
   switch (ht) {
-    case 1: return dispatch_ks<1, QB>(ks, a, grid, st);
-    case 2: return dispatch_ks<2, QB>(ks, a, grid, st);
-    case 4: return dispatch_ks<4, QB>(ks, a, grid, st);
+    case 1: return dispatch_ks<1, STREAM>(ks, a, grid, st);
+    case 2: return dispatch_ks<2, STREAM>(ks, a, grid, st);
+    case 4: return dispatch_ks<4, STREAM>(ks, a, grid, st);
     default: return false;
   }
 }
@@ -237,15 +355,27 @@ int launch_scores(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st) {
   if (vmax > a.N) vmax = a.N;
   if (vmax <= 0) return CSKV_OK;
   if (dtype == CSKV_BF16) {
-    const int64_t qblocks = ceil_div(a.nrows, qb);
-    const int64_t tile = qb == 8 ? 128 : 256;
-    int64_t splits = ceil_div(1024, qblocks * batch);
-    if (splits < 1) splits = 1;
-    a.span = round_up(ceil_div(vmax, splits), tile);
-    splits = ceil_div(vmax, a.span);
-    dim3 grid((unsigned)splits, (unsigned)qblocks, (unsigned)batch);
     const int ht = a.HI <= 32 ? 1 : (a.HI <= 64 ? 2 : 4);
-    bool ok = qb == 8 ? dispatch_mfma<8>(ht, a.dI / 16, a, grid, st) : dispatch_mfma<1>(ht, a.dI / 16, a, grid, st);
+    bool ok;
+    if (qb == 8) {
+      // key spans (multiples of the 128-key tile) so that about 1024 workgroups run
+      const int64_t qblocks = ceil_div(a.nrows, (int64_t)8);
+      int64_t splits = ceil_div(1024, qblocks * batch);
+      if (splits < 1) splits = 1;
+      a.span = round_up(ceil_div(vmax, splits), (int64_t)128);
+      splits = ceil_div(vmax, a.span);
+      dim3 grid((unsigned)splits, (unsigned)qblocks, (unsigned)batch);
+      ok = dispatch_mfma<false>(ht, a.dI / 16, a, grid, st);
+    } else {
+      // about STREAM_WAVES waves in all, at least 4 blocks of 32 keys per wave
+      const int64_t rows = a.nrows * batch;
+      int64_t per_row = ceil_div(STREAM_WAVES, rows);
+      const int64_t cap = ceil_div(vmax, (int64_t)128);
+      if (per_row > cap) per_row = cap;
+      a.row_waves = round_up(per_row, (int64_t)4);
+      dim3 grid((unsigned)(a.row_waves / 4), (unsigned)a.nrows, (unsigned)batch);
+      ok = dispatch_mfma<true>(ht, a.dI / 16, a, grid, st);
+    }
     if (!ok) return CSKV_ERR_UNSUPPORTED;
   } else {
     dim3 grid((unsigned)ceil_div(vmax, 256), (unsigned)a.nrows, (unsigned)batch);
