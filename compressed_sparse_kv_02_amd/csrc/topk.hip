@@ -10,9 +10,11 @@
 // Scores are compared through an order-preserving uint32 key, so the
 // selection is integer work and deterministic.
 //
-// Many rows (prefill): one 1024-thread workgroup per row. A strided sample
-// of the row gives a threshold that about 3k entries exceed; one vectorised
-// pass keeps those entries (in index order) in LDS, an exact 3-pass radix
+// Many rows (prefill): one 512-thread workgroup per row (two fit a compute
+// unit). A sample of the row (128 runs of 32 consecutive entries) gives a
+// threshold that about 3k entries exceed; one vectorised pass, each wave over
+// its own contiguous share of the row, keeps those entries (in index order)
+// in LDS, an exact 3-pass radix
 // select (11 + 11 + 10 bits) finds the k-th largest among them, and an
 // in-order pick with block prefix sums writes the result without a sort.
 // Should the sample miss, the row falls back to the exact radix select over
@@ -27,9 +29,10 @@ namespace cskv {
 // ----------------------------------------------------------------------------
 // Exact top-k per row
 // ----------------------------------------------------------------------------
-constexpr int TOPK_THREADS = 1024;
+constexpr int TOPK_THREADS = 512;
 constexpr int TOPK_CAP = 8192;      // candidate (key, index) pairs held in LDS
-constexpr int TOPK_SAMPLES = 4096;  // strided sample of a long row, for the candidate threshold
+constexpr int TOPK_SAMPLES = 4096;     // sample of a long row, for the candidate threshold
+constexpr int TOPK_SAMPLE_RUNS = 128;  // ... taken as runs of 32 consecutive entries
 
 // Exclusive prefix sum over the workgroup; also returns the total.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total) {
@@ -57,6 +60,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total
 struct TopkShared {
   int hist[2048];
   int wsum[TOPK_THREADS / 64];
+  int wcnt[TOPK_THREADS / 64];  // candidates found by each wave
   int sel_bin, sel_above, count;
 };
 
@@ -80,7 +84,7 @@ __device__ void radix_select(KeyAt key_at, int64_t n, int kk, TopkShared& sh, ui
     }
     __syncthreads();
     const int bpt = nb / TOPK_THREADS;  // bins per thread, descending
-    int cnt[2] = {0, 0}, loc = 0;
+    int cnt[2048 / TOPK_THREADS] = {}, loc = 0;
     for (int q = 0; q < bpt; ++q) {
       cnt[q] = sh.hist[nb - 1 - (tid * bpt + q)];
       loc += cnt[q];
@@ -135,9 +139,9 @@ __device__ void select_row_global(const float* row, int64_t V, int k, int32_t* o
   ordered_pick(key_at, [&](int pos, int64_t s) { out[pos] = (int32_t)s; }, V, tau, need, sh);
 }
 
-// One 1024-thread workgroup per query row.
+// One workgroup per query row.
 //  * V <= CAP: the whole row becomes the candidate set.
-//  * otherwise: the (3k * S / V)-th largest of S strided samples gives a
+//  * otherwise: the (3k * S / V)-th largest of S sampled entries gives a
 //    threshold tau0; one vectorised pass over the row keeps every entry with
 //    key >= tau0, in index order, as candidates (about 3k of them).
 //  * exact radix select among the candidates, then an in-order pick.
@@ -172,8 +176,19 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
     n_cand = (int)V;
     __syncthreads();
   } else {
-    // threshold from a strided sample
-    for (int i = tid; i < TOPK_SAMPLES; i += TOPK_THREADS) samp[i] = score_key(row[(int64_t)i * V / TOPK_SAMPLES]);
+    // threshold from a sample: TOPK_SAMPLE_RUNS runs of consecutive entries spread evenly
+    // over the row (whole cache lines, 16-byte loads)
+    constexpr int RUN = TOPK_SAMPLES / TOPK_SAMPLE_RUNS;
+    static_assert(RUN % 4 == 0 && TOPK_SAMPLES % (4 * TOPK_THREADS) == 0, "sample runs are read as float4");
+    for (int i = 4 * tid; i < TOPK_SAMPLES; i += 4 * TOPK_THREADS) {
+      const int run = i / RUN;
+      const int64_t start = ((int64_t)run * (V - RUN) / (TOPK_SAMPLE_RUNS - 1)) & ~(int64_t)3;
+      const float4 v = *reinterpret_cast<const float4*>(row + start + (i - run * RUN));
+      samp[i] = score_key(v.x);
+      samp[i + 1] = score_key(v.y);
+      samp[i + 2] = score_key(v.z);
+      samp[i + 3] = score_key(v.w);
+    }
     __syncthreads();
     int r = (int)(((int64_t)3 * k * TOPK_SAMPLES + V - 1) / V);
     if (r > TOPK_SAMPLES) r = TOPK_SAMPLES;
@@ -181,47 +196,99 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
     int need0;
     radix_select([&](int64_t s) { return samp[s]; }, TOPK_SAMPLES, r, sh, tau0, need0);
     __syncthreads();  // the sample (aliasing cidx) is consumed
-    // one pass: keep key >= tau0 in index order. Each thread owns 4 consecutive entries per
-    // 4096-entry chunk; UNR chunks are loaded before any is scanned, to keep loads in flight.
+    // one pass: keep key >= tau0 in index order. Wave w scans its own contiguous
+    // sixteenth of the row (4 consecutive entries per lane per 256-entry chunk, UNR
+    // chunks loaded before any is scanned) and appends to its own LDS segment of SEG
+    // slots with a wave-level prefix sum: no workgroup barrier inside the pass.
+    constexpr int NWAVE = TOPK_THREADS / 64;
+    constexpr int SEG = TOPK_CAP / NWAVE;
     constexpr int UNR = 4;
-    constexpr int CHUNK = 4 * TOPK_THREADS;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int64_t len = ((V + NWAVE - 1) / NWAVE + 3) & ~(int64_t)3;  // a multiple of 4
+    const int64_t lo = wave * len;
+    const int64_t hi = lo + len < V ? lo + len : V;
+    uint32_t* wkey = ckey + wave * SEG;
+    int32_t* widx = cidx + wave * SEG;
     int cnt = 0;
-    for (int64_t base = 0; base < V; base += UNR * CHUNK) {
+    for (int64_t base = lo; base < hi; base += UNR * 256) {
       float4 v[UNR];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int64_t s0 = base + u * CHUNK + 4 * tid;
+        const int64_t s0 = base + u * 256 + 4 * lane;
         v[u] = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-        if (s0 < V) v[u] = *reinterpret_cast<const float4*>(row + s0);  // rows are padded to 64 entries
+        if (s0 < hi) v[u] = *reinterpret_cast<const float4*>(row + s0);  // rows are padded to 64 entries
       }
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int64_t s0 = base + u * CHUNK + 4 * tid;
+        const int64_t s0 = base + u * 256 + 4 * lane;
         const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
         uint32_t kk4[4];
         int f = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           kk4[e] = score_key(vv[e]);
-          if (s0 + e < V && kk4[e] >= tau0) ++f;
+          if (s0 + e < hi && kk4[e] >= tau0) ++f;
         }
-        int tot;
-        int pos = cnt + block_exclusive_scan(f, sh.wsum, tot);
+        int incl = f;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
+        }
+        int pos = cnt + incl - f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (s0 + e < V && kk4[e] >= tau0) {
-            if (pos < TOPK_CAP) {
-              ckey[pos] = kk4[e];
-              cidx[pos] = (int32_t)(s0 + e);
+          if (s0 + e < hi && kk4[e] >= tau0) {
+            if (pos < SEG) {
+              wkey[pos] = kk4[e];
+              widx[pos] = (int32_t)(s0 + e);
             }
             ++pos;
           }
         }
-        cnt += tot;
+        cnt += __shfl(incl, 63, 64);
       }
     }
+    if (lane == 0) sh.wcnt[wave] = cnt;
     __syncthreads();
-    n_cand = cnt;
+    // segments -> one contiguous list in index order (gather to registers, then scatter)
+    int cw[NWAVE], off[NWAVE], total = 0;
+    bool overflow = false;
+#pragma unroll
+    for (int w = 0; w < NWAVE; ++w) {
+      cw[w] = sh.wcnt[w];
+      off[w] = total;
+      total += cw[w];
+      overflow |= cw[w] > SEG;
+    }
+    n_cand = overflow ? TOPK_CAP + 1 : total;  // an overflowing segment sends the row to the fallback
+    if (n_cand >= k && n_cand <= TOPK_CAP) {
+      constexpr int SPT = TOPK_CAP / TOPK_THREADS;
+      uint32_t kr[SPT];
+      int32_t ir[SPT];
+      int dst[SPT];
+#pragma unroll
+      for (int q = 0; q < SPT; ++q) {
+        const int slot = q * TOPK_THREADS + tid;
+        const int w = slot / SEG, e = slot - w * SEG;
+        dst[q] = -1;
+#pragma unroll
+        for (int ww = 0; ww < NWAVE; ++ww)  // static indexing of cw/off
+          if (ww == w && e < cw[ww]) dst[q] = off[ww] + e;
+        if (dst[q] >= 0) {
+          kr[q] = ckey[slot];
+          ir[q] = cidx[slot];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < SPT; ++q)
+        if (dst[q] >= 0) {
+          ckey[dst[q]] = kr[q];
+          cidx[dst[q]] = ir[q];
+        }
+      __syncthreads();
+    }
   }
   if (n_cand >= k && n_cand <= TOPK_CAP) {
     uint32_t tau;
