@@ -235,6 +235,91 @@ def indexer_topk(qI, wI, KI, pos0: int, m: int, k: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Low-precision indexer ("Paper Breakdown: DeepSeek-V4", section 4,
+# "Efficiency (§2.3.4)": indexer compute FP8 in V3.2 and FP4 in V4;
+# infrastructure table: FP4 quantization-aware training of the indexer QK
+# path). The pages name the precision only. Readings: FP8 is the OCP E4M3
+# format (4 exponent bits, bias 7, 3 mantissa bits, no infinities, largest
+# finite value 448); "block scales" are one fp32 scale per row of dI values
+# (one compressed key, or one (query, head) of the indexer queries).
+# ---------------------------------------------------------------------------
+
+FP8_MAX = 448.0
+
+
+def e4m3_values() -> np.ndarray:
+    """Value of each non-negative finite E4M3 code 0..126 (code 127 is NaN).
+
+    Codes 0..7 are subnormal, c * 2**-9; codes 8..126 are normal, with
+    exponent field e = c // 8 and mantissa field f = c % 8:
+    (1 + f/8) * 2**(e - 7) = (8 + f) * 2**(e - 10).
+    """
+    c = np.arange(127)
+    sub = c * 2.0 ** -9
+    nor = (8 + c % 8) * np.exp2(c // 8 - 10.0)
+    return np.where(c < 8, sub, nor).astype(F64)
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """Nearest E4M3 code of each value (ties to the even code), saturating at +-448.
+
+    Negative values (and -0.0) carry the sign bit 0x80. Input is taken as
+    float64; NaN is not expected.
+    """
+    y = np.asarray(y, dtype=F64)
+    a = np.minimum(np.abs(y), FP8_MAX)
+    vals = e4m3_values()
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, 126)  # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - vals[lo]
+    d_hi = vals[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    return np.where(np.signbit(y), code | 0x80, code).astype(np.uint8)
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """float64 value of E4M3 codes (0x7F and 0xFF decode to NaN)."""
+    c = np.asarray(codes, dtype=np.int64)
+    mag = c & 0x7F
+    v = np.where(mag == 127, np.nan, e4m3_values()[np.minimum(mag, 126)])
+    return np.where(c & 0x80, -v, v)
+
+
+def quantize_rows_fp8(x) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-row E4M3 codes and scales: x ~= decode(codes) * scale[..., None].
+
+    Per row: amax = max |x|; code = e4m3(x * (448 / amax)); scale = amax / 448.
+    The quotient, the product and the scale are float32 operations: they
+    decide integer codes, so they are taken in the kernel's precision. A row
+    of zeros gets code 0 and scale 0.
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    safe = np.where(amax > 0, amax, np.float32(1))
+    inv = (np.float32(FP8_MAX) / safe).astype(np.float32)
+    y = (x32 * inv[..., None]).astype(np.float32)
+    codes = e4m3_encode(y)
+    codes = np.where((amax > 0)[..., None], codes, np.uint8(0)).astype(np.uint8)
+    scale = np.where(amax > 0, (amax / np.float32(FP8_MAX)).astype(np.float32), np.float32(0))
+    return codes, scale.astype(np.float32)
+
+
+def indexer_scores_fp8(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int) -> np.ndarray:
+    """Indexer scores on E4M3 rows: the plain indexer on the dequantised values.
+
+    q_codes [Tq, HI, dI] with q_scales [Tq, HI]; k_codes [N, dI] with
+    k_scales [N]. Since ReLU commutes with a positive scale,
+    I[j, s] = ks[s] * sum_h wI[j,h] * qs[j,h] * max(0, dq[j,h,:] . dk[s,:]),
+    dq, dk the decoded codes; computed here as indexer_scores of
+    dq * qs and dk * ks, in float64.
+    """
+    q = e4m3_decode(q_codes) * np.asarray(q_scales, dtype=F64)[..., None]
+    kk = e4m3_decode(k_codes) * np.asarray(k_scales, dtype=F64)[..., None]
+    return indexer_scores(q, wI, kk, pos0, m)
+
+
+# ---------------------------------------------------------------------------
 # Core MQA attention over compressed entries + sliding window + sink
 # ("Paper Breakdown: DeepSeek-V4", CSA §2.3.1, HCA §2.3.2, §2.3.3)
 # ---------------------------------------------------------------------------

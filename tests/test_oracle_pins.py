@@ -330,6 +330,79 @@ def test_round_bf16_against_torch():
     assert np.array_equal(got, ref)
 
 
+# ---------------------------------------------------------------- FP8 (E4M3) indexer
+
+def _torch_e4m3(y):
+    """torch's own float32 -> float8_e4m3fn conversion (an independent implementation)."""
+    return torch.tensor(np.asarray(y, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_table_and_anchors():
+    # every finite code decodes as torch's float8_e4m3fn does; spec anchors by hand
+    t = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    d = O.e4m3_decode(np.arange(256))
+    finite = ~np.isnan(t)
+    assert np.array_equal(np.isnan(d), np.isnan(t))
+    assert np.array_equal(d[finite], t[finite])
+    for code, val in ((0x38, 1.0), (0x7E, 448.0), (0x08, 2.0 ** -6), (0x01, 2.0 ** -9), (0x40, 2.0),
+                      (0x3C, 1.5), (0xB8, -1.0), (0x77, 240.0)):
+        assert O.e4m3_decode(code) == val, hex(code)
+        assert O.e4m3_encode(val) == code, hex(code)
+
+
+def test_e4m3_encode_matches_torch_incl_ties():
+    vals = O.e4m3_values()
+    mids = (vals[:-1] + vals[1:]) / 2                          # exact ties: must go to the even code
+    near = np.concatenate([np.nextafter(mids, 0), np.nextafter(mids, 1e9)])
+    rnd = rng.uniform(-448, 448, 20000) * np.exp2(rng.integers(-14, 1, 20000))
+    for y in (mids, -mids, near, -near, rnd, vals, -vals):
+        y32 = np.asarray(y, dtype=np.float32)
+        ok = np.abs(y32.astype(np.float64)) <= 448
+        assert np.array_equal(O.e4m3_encode(y32[ok]), _torch_e4m3(y32[ok]))
+    # ties land on even codes, and each midpoint is exactly between the two neighbours
+    c = O.e4m3_encode(mids)
+    assert (c % 2 == 0).all()
+    assert O.e4m3_encode(500.0) == 0x7E and O.e4m3_encode(-1e6) == 0xFE   # saturation
+    assert O.e4m3_encode(-0.0) == 0x80
+
+
+def test_quantize_rows_fp8():
+    x = rng.standard_normal((64, 128)).astype(np.float32)
+    x[3] = 0.0
+    codes, scale = O.quantize_rows_fp8(x)
+    assert codes.dtype == np.uint8 and scale.dtype == np.float32
+    assert (codes[3] == 0).all() and scale[3] == 0
+    rows = [r for r in range(64) if r != 3]
+    # the row's largest magnitude maps to +-448 exactly
+    am = np.argmax(np.abs(x[rows]), axis=1)
+    assert np.array_equal(codes[rows, am] & 0x7F, np.full(len(rows), 0x7E))
+    # dequantised values: within half an E4M3 step of x (relative 1/16 for normals, plus the subnormal quantum)
+    deq = O.e4m3_decode(codes) * scale[:, None].astype(np.float64)
+    err = np.abs(deq - x)
+    assert (err[rows] <= np.abs(x[rows]) / 16 + scale[rows, None] * 2.0 ** -10 + 1e-30).all()
+    # codes of the float32 product follow torch's conversion
+    inv = (np.float32(448) / np.max(np.abs(x[rows]), axis=1)).astype(np.float32)
+    assert np.array_equal(codes[rows], _torch_e4m3((x[rows] * inv[:, None]).astype(np.float32)))
+
+
+def test_indexer_fp8_reduces_to_plain_indexer():
+    # codes of small integers with unit scales: the same scores as the plain indexer on those integers
+    ints = np.array([0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 16], dtype=np.float64)
+    q = rng.choice(np.concatenate([ints, -ints]), (5, 3, 32))
+    k = rng.choice(np.concatenate([ints, -ints]), (40, 32))
+    w = rng.uniform(0, 1, (5, 3))
+    qc, kc = O.e4m3_encode(q), O.e4m3_encode(k)
+    assert np.array_equal(O.e4m3_decode(qc), q) and np.array_equal(O.e4m3_decode(kc), k)
+    one_q, one_k = np.ones((5, 3)), np.ones(40)
+    I8 = O.indexer_scores_fp8(qc, one_q, w, kc, one_k, pos0=100, m=4)
+    assert np.array_equal(I8, O.indexer_scores(q, w, k, pos0=100, m=4))
+    # per-key scale multiplies that key's score; per-(query, head) scale weights that head
+    ks = rng.uniform(0.5, 2.0, 40)
+    qs = rng.uniform(0.5, 2.0, (5, 3))
+    I8s = O.indexer_scores_fp8(qc, qs, w, kc, ks, pos0=100, m=4)
+    assert np.allclose(I8s, O.indexer_scores(q, w * qs, k, pos0=100, m=4) * ks[None, :], rtol=1e-13, atol=0)
+
+
 def test_page_constants_fixture():
     with open(os.path.join(GOLDEN, "page_constants.json")) as f:
         g = json.load(f)
