@@ -12,6 +12,9 @@ from .binding import (  # noqa: F401
     indexer_topk,
     indexer_scores,
     topk_select,
+    quantize_fp8,
+    indexer_scores_fp8,
+    indexer_topk_fp8,
     compressed_attn_prefill,
     compressed_attn_decode,
 )

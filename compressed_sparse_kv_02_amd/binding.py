@@ -17,11 +17,12 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcskv.so")
 
-BF16, F32 = 0, 1
+BF16, F32, FP8 = 0, 1, 2
 CSA, HCA = 0, 1
 EXPORTS = ("cskv_version", "cskv_status_string", "csa_compress", "hca_compress",
            "cskv_indexer_workspace_size", "indexer_topk", "indexer_scores", "topk_select",
-           "cskv_topk_workspace_size", "compressed_attn_prefill",
+           "cskv_topk_workspace_size", "cskv_quantize_fp8", "indexer_scores_fp8", "indexer_topk_fp8",
+           "compressed_attn_prefill",
            "cskv_decode_workspace_size", "compressed_attn_decode")
 
 _lib = None
@@ -38,6 +39,9 @@ _SIGS = {
     "indexer_scores": (_I, [_P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _P, _L, _I, _P]),
     "topk_select": (_I, [_P, _L, _I, _L, _L, _L, _I, _I, _P, _P, _Z, _P]),
     "cskv_topk_workspace_size": (_Z, [_I, _L, _L, _I]),
+    "cskv_quantize_fp8": (_I, [_P, _L, _I, _I, _P, _P, _P]),
+    "indexer_scores_fp8": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _P, _L, _P]),
+    "indexer_topk_fp8": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _I, _P, _P, _Z, _P]),
     "compressed_attn_prefill": (_I, [_I, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
                                      _I, _P, _F, _I, _F, _F, _I, _P, _P, _I, _P]),
     "cskv_decode_workspace_size": (_Z, [_I, _L, _I, _I, _I]),
@@ -187,6 +191,45 @@ def topk_select(scores, N: int, pos0: int, m: int, k: int, out=None, workspace=N
     ws, nbytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
     _check("topk_select", lib().topk_select(_ptr(scores), ld, batch, Tq, N, pos0, m, k, _ptr(out), ws, nbytes,
                                             _stream(scores)))
+    return out
+
+
+def quantize_fp8(x) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-row E4M3 codes (uint8, x's shape) and fp32 scales (x.shape[:-1]) of x (bf16 or fp32)."""
+    dim = x.shape[-1]
+    rows = x.numel() // dim if dim else 0
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check("cskv_quantize_fp8", lib().cskv_quantize_fp8(_ptr(x), rows, dim, _dtype(x), _ptr(codes), _ptr(scales),
+                                                        _stream(x)))
+    return codes, scales
+
+
+def indexer_scores_fp8(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int, scores=None) -> torch.Tensor:
+    """Indexer scores on E4M3 rows: [batch, Tq, ld] fp32 (valid for s < V_t)."""
+    batch, Tq, HI, dI = q_codes.shape
+    N = k_codes.shape[1]
+    if scores is None:
+        scores = torch.empty(batch, Tq, score_ld(N), dtype=torch.float32, device=q_codes.device)
+    _check("indexer_scores_fp8", lib().indexer_scores_fp8(
+        _ptr(q_codes), _ptr(q_scales), _ptr(wI), _ptr(k_codes), _ptr(k_scales), batch, Tq, N, HI, dI, pos0, m,
+        _ptr(scores), scores.shape[-1], _stream(q_codes)))
+    return scores
+
+
+def indexer_topk_fp8(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int, k: int, out=None,
+                     workspace=None) -> torch.Tensor:
+    """Top-k compressed entries per query from E4M3 rows: [batch, Tq, k] int32, ascending, -1 padded."""
+    batch, Tq, HI, dI = q_codes.shape
+    N = k_codes.shape[1]
+    if out is None:
+        out = torch.empty(batch, Tq, k, dtype=torch.int32, device=q_codes.device)
+    need = indexer_workspace_bytes(batch, Tq, N, HI, k, FP8)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_codes.device)
+    _check("indexer_topk_fp8", lib().indexer_topk_fp8(
+        _ptr(q_codes), _ptr(q_scales), _ptr(wI), _ptr(k_codes), _ptr(k_scales), batch, Tq, N, HI, dI, pos0, m, k,
+        _ptr(out), _ptr(workspace), workspace.numel(), _stream(q_codes)))
     return out
 
 

@@ -17,6 +17,8 @@ struct IdxArgs {
   const void* qI;
   const float* wI;
   const void* KI;
+  const float* q_scale;  // FP8: [batch][Tq][HI] scale of each (query, head) row
+  const float* k_scale;  // FP8: [batch][N] scale of each key row
   float* scores;  // [batch][rows_ws][ldS]
   int32_t* out;
   int64_t Tq, N, pos0, ldS, span;  // span: keys per workgroup (prefill scoring)
@@ -29,6 +31,10 @@ struct IdxArgs {
   int kp;              // candidates kept per part
 };
 
+// ReLU on the bit pattern: for non-NaN x, max(bits(x), 0) as int32 is bits(max(x, 0))
+// (negative floats, -0.0 included, are negative as int32). One VALU op, no NaN canonicalisation.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Scores of rows [a.row0, a.row0 + a.nrows) into a.scores; bf16 takes qb
 // queries per workgroup (8 for prefill, 1 for decode).
 int launch_scores(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st);
@@ -36,6 +42,16 @@ int launch_scores(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st);
 // Top-k of rows [a.row0, a.row0 + a.nrows) from a.scores into a.out; sel_ws
 // (optional, sel_bytes long) enables the several-workgroups-per-row route.
 int launch_select(IdxArgs& a, int batch, void* sel_ws, size_t sel_bytes, hipStream_t st);
+
+// Score chunking shared by the bf16 and FP8 entry points: score row stride,
+// rows per chunk, queries per scoring workgroup.
+struct IdxPlan {
+  int64_t ldS, rows_ws, qb;
+};
+IdxPlan plan_indexer(int batch, int64_t Tq, int64_t N, int dtype);
+
+// FP8 (E4M3) scoring of rows [a.row0, a.row0 + a.nrows) into a.scores (indexer_fp8.hip).
+int launch_scores_fp8(IdxArgs& a, int batch, int qb, hipStream_t st);
 
 // Workspace bytes for the several-workgroups-per-row selection of `rows`
 // rows of up to vmax entries; 0 when that route is not taken.

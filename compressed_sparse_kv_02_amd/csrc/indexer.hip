@@ -23,9 +23,6 @@ namespace cskv {
 // ----------------------------------------------------------------------------
 // bf16 scoring on the matrix cores
 // ----------------------------------------------------------------------------
-// ReLU on the bit pattern: for non-NaN x, max(bits(x), 0) as int32 is bits(max(x, 0))
-// (negative floats, -0.0 included, are negative as int32). One VALU op, no NaN canonicalisation.
-__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Prefill rows: 8 queries per workgroup, one per wave, sharing 128-key LDS tiles.
 template <int HT, int KS>
@@ -291,14 +288,10 @@ __global__ __launch_bounds__(256) void indexer_score_f32(IdxArgs a) {
 static constexpr int64_t SCORE_CHUNK_BYTES = (int64_t)128 << 20;
 static constexpr int64_t STREAM_WAVES = 4096;  // decode scoring: waves over the whole call
 
-struct IdxPlan {
-  int64_t ldS, rows_ws, qb;
-};
-
-static IdxPlan plan_indexer(int batch, int64_t Tq, int64_t N, int dtype) {
+IdxPlan plan_indexer(int batch, int64_t Tq, int64_t N, int dtype) {
   IdxPlan p;
   p.ldS = round_up(N > 0 ? N : 1, 64);
-  p.qb = (dtype == CSKV_BF16 && Tq >= 64) ? 8 : 1;
+  p.qb = (dtype != CSKV_F32 && Tq >= 64) ? 8 : 1;
   int64_t rows = SCORE_CHUNK_BYTES / (p.ldS * 4 * (batch > 0 ? batch : 1));
   // enough rows per chunk to fill the GPU with selection workgroups
   if (rows < 2048 / (batch > 0 ? batch : 1)) rows = 2048 / (batch > 0 ? batch : 1);
@@ -402,7 +395,6 @@ using namespace cskv;
 extern "C" size_t cskv_indexer_workspace_size(int batch, int64_t Tq, int64_t N, int HI, int k,
                                               int dtype) {
   (void)HI;
-  (void)k;
   if (batch <= 0 || Tq <= 0) return 0;
   IdxPlan p = plan_indexer(batch, Tq, N, dtype);
   return (size_t)(batch * p.rows_ws * p.ldS * 4) + split_ws_bytes((int64_t)batch * p.rows_ws, N, k);

@@ -1,0 +1,450 @@
+// Lightning-indexer scoring on FP8 (E4M3) rows for gfx950.
+//
+// "Paper Breakdown: DeepSeek-V4", section 4, "Efficiency (§2.3.4)": the
+// indexer computes in FP8 in V3.2 and in FP4 in V4 (infrastructure table:
+// FP4 quantization-aware training of the indexer QK path). The pages name
+// the precision only; here the format is OCP E4M3 with one fp32 scale per
+// row (one compressed key, or one (query, head) of the indexer queries).
+// Since ReLU commutes with a positive scale,
+//   I[t, s] = ks[s] * sum_h (w[t,h] * qs[t,h]) * ReLU(dq[t,h,:] . dk[s,:]),
+// dq, dk the decoded codes. A product of two E4M3 values is exact in fp32;
+// v_mfma_f32_32x32x64_f8f6f4 (64 products per output per instruction, about
+// 2.3x the bf16 32x32x16 rate) sums them in fp32.
+//
+// cskv_quantize_fp8 writes the codes: per row, amax = max |x|, codes =
+// E4M3(x * (448 / amax)) (nearest, ties to the even code, saturating) and
+// scale = amax / 448, the quotient and product correctly rounded in fp32.
+//
+// The scoring kernels follow the bf16 ones: 8 queries per workgroup sharing
+// 128-key LDS tiles for prefill; for decode, interleaved 32-key blocks per
+// wave with coalesced loads turned into the MFMA layout through per-wave LDS
+// rows. A key row is dI bytes; each lane holds one contiguous half of it
+// (the K dimension permuted identically in A and B: lane half h, k-step ks
+// holds bytes h*dI/2 + 32*ks .. +32).
+#include "indexer.h"
+
+namespace cskv {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// E4M3 code of y: nearest value, ties to the even code, saturating at +-448;
+// the sign bit is set for negative y (and -0.0).
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.f);
+  uint32_t c;
+  if (a < 0.015625f) {
+    c = (uint32_t)rintf(a * 512.f);  // subnormal steps of 2^-9 (8 is the smallest normal)
+  } else {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);  // round the fp32 mantissa to 3 bits, ties to even
+    c = (u >> 20) - (120u << 3);       // exponent bias 127 -> 7
+  }
+  return sign | c;
+}
+
+// One wave per row (4 rows per workgroup); dim % 4 == 0, dim <= 1024.
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const T* x, int64_t rows, int dim, uint8_t* codes,
+                                                          float* scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const T* xr = x + r * dim;
+  const int nc = dim / 4;  // 4-element chunks: lane takes chunks lane, lane + 64, ...
+  float v[16];
+  float amax = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = lane + 64 * q;
+    if (c < nc) {
+      load_vec<T, 4>(xr + 4 * c, &v[4 * q]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(v[4 * q + e]));
+    }
+  }
+  amax = wave_max(amax);
+  const float inv = amax > 0.f ? __fdiv_rn(448.f, amax) : 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = lane + 64 * q;
+    if (c < nc) {
+      uint32_t w = 0;
+      if (amax > 0.f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w |= e4m3_code(v[4 * q + e] * inv) << (8 * e);
+      *reinterpret_cast<uint32_t*>(codes + r * dim + 4 * c) = w;
+    }
+  }
+  if (lane == 0) scales[r] = amax > 0.f ? __fdiv_rn(amax, 448.f) : 0.f;
+}
+
+__device__ __forceinline__ i32x8 load32(const uint8_t* p) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(p);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(p + 16);
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // format 0 (E4M3) for both operands; zero scales select the unscaled instruction
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Query operands (A) and folded head weights (w * qs) of query j; lane holds head lane%32 of each tile.
+template <int HT, int KS8>
+__device__ __forceinline__ void load_query_fp8(const IdxArgs& a, int b, int64_t j, bool qvalid, int lane,
+                                               i32x8 (&qa)[HT][KS8], float (&wv)[HT][16]) {
+  constexpr int DI = 64 * KS8;
+  const uint8_t* qp = (const uint8_t*)a.qI + ((int64_t)b * a.Tq + j) * a.HI * DI + (DI / 2) * (lane >> 5);
+  const float* wp = a.wI + ((int64_t)b * a.Tq + j) * a.HI;
+  const float* sp = a.q_scale + ((int64_t)b * a.Tq + j) * a.HI;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int h = ht * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks)
+      qa[ht][ks] = (qvalid && h < a.HI) ? load32(qp + (int64_t)h * DI + 32 * ks) : i32x8{};
+    // accumulator rows held by this lane: 8*(i/4) + 4*(lane/32) + i%4
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int hh = ht * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      wv[ht][i] = (qvalid && hh < a.HI) ? wp[hh] * sp[hh] : 0.f;
+    }
+  }
+}
+
+// Prefill rows: 8 queries per workgroup (one per wave) sharing 128-key LDS tiles.
+template <int HT, int KS8>
+__global__ __launch_bounds__(512) void indexer_score_fp8_mfma(IdxArgs a) {
+  constexpr int QB = 8;
+  constexpr int SUB = 4;               // 32-key sub-blocks per wave per tile
+  constexpr int TILE = SUB * 32;
+  constexpr int DI = 64 * KS8;         // bytes per key row
+  constexpr int ROW = DI + 16;         // padded LDS row, against bank conflicts
+  constexpr int CPR = DI / 16;
+  constexpr int CHUNKS = TILE * CPR;
+  constexpr int CPT = (CHUNKS + 511) / 512;
+  __shared__ __attribute__((aligned(16))) uint8_t kt[2][TILE * ROW];
+  __shared__ float ksc[2][TILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.z;
+  const int64_t qblk = (int64_t)gridDim.y - 1 - blockIdx.y;  // longest rows first
+  const int64_t jr = qblk * QB + wave;
+  const bool qvalid = jr < a.nrows;
+  const int64_t j = a.row0 + (qvalid ? jr : 0);
+  int64_t jl = qblk * QB + QB - 1;
+  if (jl > a.nrows - 1) jl = a.nrows - 1;
+  const int64_t vmax = visible_entries(a.pos0 + a.row0 + jl, a.m, a.N);
+  const int64_t kbeg = (int64_t)blockIdx.x * a.span;
+  int64_t kend = kbeg + a.span;
+  if (kend > vmax) kend = vmax;
+  if (kbeg >= kend) return;  // uniform for the workgroup
+  const int64_t vj = qvalid ? visible_entries(a.pos0 + j, a.m, a.N) : 0;
+  const int nkeys = (int)(kend - kbeg);
+  const int vrel = (int)((vj > kbeg ? vj : kbeg) - kbeg);
+
+  i32x8 qa[HT][KS8];
+  float wv[HT][16];
+  load_query_fp8<HT, KS8>(a, b, j, qvalid, lane, qa, wv);
+
+  const uint8_t* kbase = (const uint8_t*)a.KI + ((int64_t)b * a.N + kbeg) * DI;
+  const float* kscale = a.k_scale + (int64_t)b * a.N + kbeg;
+  float* srow = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS + kbeg;
+  const int ntiles = (nkeys + TILE - 1) / TILE;
+
+  u32x4 pre[CPT];
+  float pre_s = 0.f;
+  auto gload = [&](int t0) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * 512;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ch < CHUNKS) {
+        const int s = t0 + ch / CPR;
+        if (s < nkeys) v = *reinterpret_cast<const u32x4*>(kbase + (int64_t)s * DI + (ch % CPR) * 16);
+      }
+      pre[c] = v;
+    }
+    if (tid < TILE) pre_s = t0 + tid < nkeys ? kscale[t0 + tid] : 0.f;
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + c * 512;
+      if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&kt[buf][(ch / CPR) * ROW + (ch % CPR) * 16]) = pre[c];
+    }
+    if (tid < TILE) ksc[buf][tid] = pre_s;
+  };
+  auto mma = [&](const uint8_t* kp, f32x16 (&acc)[HT]) {
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks) {
+      const i32x8 bv = load32(kp + 32 * ks);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_fp8(qa[ht][ks], bv, ks == 0 ? f32x16{} : acc[ht]);
+    }
+  };
+  // ReLU, folded head weights, head sum; lanes 0-31 scale by their key's ks and store.
+  auto epilogue = [&](const f32x16 (&acc)[HT], int sub0, int t0, int buf) {
+    float part = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part = __builtin_fmaf(relu_bits(acc[ht][i]), wv[ht][i], part);
+    part += __shfl_xor(part, 32, 64);
+    const int kt_i = sub0 + (lane & 31);  // key within the tile
+    const int s = t0 + kt_i;
+    if (qvalid && lane < 32 && s < nkeys) srow[s] = s < vrel ? part * ksc[buf][kt_i] : -INFINITY;
+  };
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int it = 0; it < ntiles; ++it) {
+    const int t0 = it * TILE;
+    const int buf = it & 1;
+    if (it + 1 < ntiles) gload(t0 + TILE);
+    const uint8_t* kp = &kt[buf][(lane & 31) * ROW + (DI / 2) * (lane >> 5)];
+    f32x16 acc[2][HT];
+    mma(kp, acc[0]);
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      if (sb + 1 < SUB) mma(kp + (sb + 1) * 32 * ROW, acc[(sb + 1) & 1]);  // next sub-block's MFMAs first
+      epilogue(acc[sb & 1], sb * 32, t0, buf);
+    }
+    if (it + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+}
+
+// Decode-shaped rows: row_waves waves per query row, wave r taking the 32-key
+// blocks r, r + row_waves, ...; each block loaded with coalesced 16-byte loads
+// one block ahead and turned into the MFMA layout through the wave's own LDS rows.
+template <int HT, int KS8>
+__global__ __launch_bounds__(256) void indexer_score_fp8_stream(IdxArgs a) {
+  constexpr int DI = 64 * KS8;      // bytes per key row
+  constexpr int RS = DI + 16;       // padded LDS row
+  constexpr int NB = 2;             // key blocks in registers: the current one + 1 in flight
+  constexpr int LPB = 32 * DI / 1024;  // 1 KiB loads per 32-key block
+  __shared__ __attribute__((aligned(16))) uint8_t kst[4][32 * RS];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = lane >> 5, kl = lane & 31;
+  const int b = blockIdx.z;
+  const int64_t jr = blockIdx.y;
+  const int64_t j = a.row0 + jr;
+  const int64_t vj = visible_entries(a.pos0 + j, a.m, a.N);
+  const int64_t wr = (int64_t)blockIdx.x * 4 + wave;  // this wave's rank in the row
+  const int64_t row_blk = (vj + 31) / 32;
+  if (wr >= row_blk) return;  // per wave: the kernel has no workgroup barrier
+  const int nblk = (int)((row_blk - wr + a.row_waves - 1) / a.row_waves);
+
+  i32x8 qa[HT][KS8];
+  float wv[HT][16];
+  load_query_fp8<HT, KS8>(a, b, j, true, lane, qa, wv);
+
+  uint8_t* my = kst[wave];
+  const uint8_t* kb0 = (const uint8_t*)a.KI + (int64_t)b * a.N * DI;
+  const float* ksp = a.k_scale + (int64_t)b * a.N;
+  float* srow = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
+  auto key_of = [&](int blk) { return (wr + (int64_t)blk * a.row_waves) * 32 + kl; };
+  u32x4 kb[NB][LPB];
+  float kss[NB];
+  auto load = [&](int blk, u32x4 (&dst)[LPB], float& sc) {
+    if (blk >= nblk) return;
+    const int64_t key0 = (wr + (int64_t)blk * a.row_waves) * 32;
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      const int off = i * 1024 + lane * 16;
+      int64_t r = key0 + off / DI;
+      if (r > vj - 1) r = vj - 1;  // past the visible keys: a valid row, its score is not stored
+      dst[i] = *reinterpret_cast<const u32x4*>(kb0 + r * DI + (off % DI));
+    }
+    int64_t s = key0 + kl;
+    if (s > vj - 1) s = vj - 1;
+    sc = ksp[s];
+  };
+  auto step = [&](int blk, const u32x4 (&src)[LPB], float sc) {
+    if (blk >= nblk) return;
+    // wave-scope fences: the previous block's LDS reads precede these writes, which
+    // precede the reads below (other lanes' rows)
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int i = 0; i < LPB; ++i) {
+      const int off = i * 1024 + lane * 16;
+      *reinterpret_cast<u32x4*>(my + (off / DI) * RS + (off % DI)) = src[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    f32x16 acc[HT];
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks) {
+      const i32x8 bv = load32(my + kl * RS + (DI / 2) * half + 32 * ks);
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_fp8(qa[ht][ks], bv, ks == 0 ? f32x16{} : acc[ht]);
+    }
+    float part = 0.f;
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) part = __builtin_fmaf(relu_bits(acc[ht][i]), wv[ht][i], part);
+    part += __shfl_xor(part, 32, 64);
+    const int64_t s = key_of(blk);
+    if (lane < 32 && s < vj) srow[s] = part * sc;
+  };
+
+#pragma unroll
+  for (int p = 0; p < NB; ++p) load(p, kb[p], kss[p]);
+  for (int it = 0; it < nblk; it += NB) {
+#pragma unroll
+    for (int p = 0; p < NB; ++p) {
+      step(it + p, kb[p], kss[p]);
+      load(it + p + NB, kb[p], kss[p]);
+    }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Host side
+// ----------------------------------------------------------------------------
+static constexpr int64_t FP8_STREAM_WAVES = 4096;  // decode scoring: waves over the whole call
+
+template <int HT, int KS8, bool STREAM>
+static void launch_fp8(const IdxArgs& a, dim3 grid, hipStream_t st) {
+  if constexpr (STREAM)
+    hipLaunchKernelGGL((indexer_score_fp8_stream<HT, KS8>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((indexer_score_fp8_mfma<HT, KS8>), grid, dim3(512), 0, st, a);
+}
+
+template <bool STREAM>
+static bool dispatch_fp8(int ht, int ks8, const IdxArgs& a, dim3 grid, hipStream_t st) {
+  if (ks8 == 1) {
+    switch (ht) {
+      case 1: launch_fp8<1, 1, STREAM>(a, grid, st); return true;
+      case 2: launch_fp8<2, 1, STREAM>(a, grid, st); return true;
+      case 4: launch_fp8<4, 1, STREAM>(a, grid, st); return true;
+    }
+  } else if (ks8 == 2) {
+    switch (ht) {
+      case 1: launch_fp8<1, 2, STREAM>(a, grid, st); return true;
+      case 2: launch_fp8<2, 2, STREAM>(a, grid, st); return true;
+      case 4: launch_fp8<4, 2, STREAM>(a, grid, st); return true;
+    }
+  }
+  return false;
+}
+
+int launch_scores_fp8(IdxArgs& a, int batch, int qb, hipStream_t st) {
+  const int64_t last = a.pos0 + a.row0 + a.nrows - 1;
+  int64_t vmax = (last + 1) / a.m;
+  if (vmax > a.N) vmax = a.N;
+  if (vmax <= 0) return CSKV_OK;
+  const int ht = a.HI <= 32 ? 1 : (a.HI <= 64 ? 2 : 4);
+  bool ok;
+  if (qb == 8) {
+    const int64_t qblocks = ceil_div(a.nrows, (int64_t)8);
+    int64_t splits = ceil_div(1024, qblocks * batch);
+    if (splits < 1) splits = 1;
+    a.span = round_up(ceil_div(vmax, splits), (int64_t)128);
+    splits = ceil_div(vmax, a.span);
+    dim3 grid((unsigned)splits, (unsigned)qblocks, (unsigned)batch);
+    ok = dispatch_fp8<false>(ht, a.dI / 64, a, grid, st);
+  } else {
+    const int64_t rows = a.nrows * batch;
+    int64_t per_row = ceil_div(FP8_STREAM_WAVES, rows);
+    const int64_t cap = ceil_div(vmax, (int64_t)128);
+    if (per_row > cap) per_row = cap;
+    a.row_waves = round_up(per_row, (int64_t)4);
+    dim3 grid((unsigned)(a.row_waves / 4), (unsigned)a.nrows, (unsigned)batch);
+    ok = dispatch_fp8<true>(ht, a.dI / 64, a, grid, st);
+  }
+  if (!ok) return CSKV_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+}
+
+static int check_fp8_shape(int batch, int64_t Tq, int64_t N, int HI, int dI, int64_t pos0, int m) {
+  if (batch < 0 || Tq < 0 || N < 0 || pos0 < 0 || m < 1) return CSKV_ERR_BAD_SHAPE;
+  if (HI < 1 || HI > CSKV_MAX_HEADS) return CSKV_ERR_BAD_SHAPE;
+  if (N > ((int64_t)1 << 31) - 64) return CSKV_ERR_BAD_SHAPE;
+  if (dI != 64 && dI != 128) return CSKV_ERR_UNSUPPORTED;
+  return CSKV_OK;
+}
+
+}  // namespace cskv
+
+using namespace cskv;
+
+extern "C" int cskv_quantize_fp8(const void* x, int64_t rows, int dim, int dtype, uint8_t* codes, float* scales,
+                                 void* stream) {
+  if (dtype != CSKV_BF16 && dtype != CSKV_F32) return CSKV_ERR_BAD_DTYPE;
+  if (rows < 0 || dim < 4 || dim % 4 != 0 || dim > 1024) return CSKV_ERR_BAD_SHAPE;
+  if (ceil_div(rows, (int64_t)4) > 0x7fffffff) return CSKV_ERR_BAD_SHAPE;
+  if (rows == 0) return CSKV_OK;
+  if (!x || !codes || !scales) return CSKV_ERR_INVALID_ARG;
+  if (!aligned16(x, codes, scales)) return CSKV_ERR_MISALIGNED;
+  dim3 grid((unsigned)ceil_div(rows, (int64_t)4));
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == CSKV_BF16)
+    hipLaunchKernelGGL(quantize_fp8_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)x, rows, dim, codes, scales);
+  else
+    hipLaunchKernelGGL(quantize_fp8_kernel<float>, grid, dim3(256), 0, st, (const float*)x, rows, dim, codes,
+                       scales);
+  return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+}
+
+extern "C" int indexer_scores_fp8(const uint8_t* qI, const float* q_scale, const float* wI, const uint8_t* KI,
+                                  const float* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                                  int64_t pos0, int m, float* scores, int64_t ld, void* stream) {
+  int st = check_fp8_shape(batch, Tq, N, HI, dI, pos0, m);
+  if (st) return st;
+  if (ld < N || ld % 4 != 0) return CSKV_ERR_BAD_SHAPE;
+  if (batch == 0 || Tq == 0) return CSKV_OK;
+  if (!qI || !q_scale || !wI || !scores || (N > 0 && (!KI || !k_scale))) return CSKV_ERR_INVALID_ARG;
+  if (!aligned16(qI, q_scale, wI, KI, k_scale, scores)) return CSKV_ERR_MISALIGNED;
+  IdxArgs a{};
+  a.qI = qI; a.q_scale = q_scale; a.wI = wI; a.KI = KI; a.k_scale = k_scale; a.scores = scores;
+  a.Tq = Tq; a.N = N; a.pos0 = pos0; a.ldS = ld; a.rows_ws = Tq; a.row0 = 0; a.nrows = Tq;
+  a.HI = HI; a.dI = dI; a.m = m;
+  const IdxPlan p = plan_indexer(batch, Tq, N, CSKV_FP8);
+  return launch_scores_fp8(a, batch, (int)p.qb, (hipStream_t)stream);
+}
+
+extern "C" int indexer_topk_fp8(const uint8_t* qI, const float* q_scale, const float* wI, const uint8_t* KI,
+                                const float* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                                int64_t pos0, int m, int k, int32_t* out_idx, void* workspace, size_t ws_bytes,
+                                void* stream) {
+  int st = check_fp8_shape(batch, Tq, N, HI, dI, pos0, m);
+  if (st) return st;
+  if (k < 1) return CSKV_ERR_BAD_SHAPE;
+  if (k > CSKV_MAX_TOPK) return CSKV_ERR_UNSUPPORTED;
+  if (batch == 0 || Tq == 0) return CSKV_OK;
+  if (!qI || !q_scale || !wI || !out_idx || (N > 0 && (!KI || !k_scale))) return CSKV_ERR_INVALID_ARG;
+  if (!aligned16(qI, q_scale, wI, KI, k_scale, out_idx, workspace)) return CSKV_ERR_MISALIGNED;
+  const IdxPlan p = plan_indexer(batch, Tq, N, CSKV_FP8);
+  const size_t score_bytes = (size_t)(batch * p.rows_ws * p.ldS * 4);
+  const size_t need_ws = score_bytes + split_ws_bytes((int64_t)batch * p.rows_ws, N, k);
+  if (!workspace || ws_bytes < need_ws) return CSKV_ERR_WORKSPACE;
+  // the selection area follows the score rows (score_bytes is a multiple of 256: ldS % 64 == 0)
+  uint8_t* sel_ws = need_ws > score_bytes ? (uint8_t*)workspace + score_bytes : nullptr;
+  const size_t sel_bytes = sel_ws ? ws_bytes - score_bytes : 0;
+
+  hipStream_t hs = (hipStream_t)stream;
+  IdxArgs a{};
+  a.qI = qI; a.q_scale = q_scale; a.wI = wI; a.KI = KI; a.k_scale = k_scale;
+  a.scores = (float*)workspace; a.out = out_idx;
+  a.Tq = Tq; a.N = N; a.pos0 = pos0; a.ldS = p.ldS; a.rows_ws = p.rows_ws;
+  a.HI = HI; a.dI = dI; a.m = m; a.k = k;
+  for (int64_t r0 = 0; r0 < Tq; r0 += p.rows_ws) {
+    a.row0 = r0;
+    a.nrows = (Tq - r0) < p.rows_ws ? (Tq - r0) : p.rows_ws;
+    const int64_t last = pos0 + r0 + a.nrows - 1;
+    int64_t vmax = (last + 1) / m;
+    if (vmax > N) vmax = N;
+    if (vmax > k) {  // rows with V_t <= k need no scores
+      st = launch_scores_fp8(a, batch, (int)p.qb, hs);
+      if (st) return st;
+    }
+    st = launch_select(a, batch, sel_ws, sel_bytes, hs);
+    if (st) return st;
+  }
+  return CSKV_OK;
+}

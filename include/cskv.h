@@ -60,7 +60,7 @@ enum {
   CSKV_ERR_HIP = -7           /* a kernel launch failed */
 };
 
-enum { CSKV_BF16 = 0, CSKV_F32 = 1 };
+enum { CSKV_BF16 = 0, CSKV_F32 = 1, CSKV_FP8 = 2 /* E4M3 codes with fp32 row scales */ };
 enum { CSKV_MODE_CSA = 0, CSKV_MODE_HCA = 1 };
 
 #define CSKV_MAX_TOPK 2048
@@ -178,6 +178,46 @@ int topk_select(const float* scores, int64_t ld, int batch, int64_t Tq, int64_t 
  * one workgroup, with the same result.
  */
 size_t cskv_topk_workspace_size(int batch, int64_t Tq, int64_t N, int k);
+
+/*
+ * FP8 lightning indexer [PB §2.3.4 "Efficiency": indexer compute FP8 in
+ * V3.2, FP4 in V4; infrastructure table: FP4 quantization-aware training of
+ * the indexer QK path]. The pages name the precision only; here the format is
+ * OCP FP8 E4M3 (bias 7, no infinities, largest finite 448) with one fp32
+ * scale per row.
+ *
+ * cskv_quantize_fp8 -- per-row E4M3 quantisation of x [rows, dim]:
+ *   amax = max |x[r, :]|; codes[r, :] = E4M3(x[r, :] * (448 / amax)), nearest
+ *   value, ties to the even code, saturating; scales[r] = amax / 448. The
+ *   quotient and product are correctly rounded fp32. A row of zeros gets
+ *   codes 0 and scale 0.
+ *   x : [rows, dim] (dtype CSKV_BF16 or CSKV_F32); 4 <= dim <= 1024, dim % 4 == 0
+ *   codes : [rows, dim] uint8; scales : [rows] fp32
+ *   Use it on indexer keys ([batch*N, dI]) and indexer queries
+ *   ([batch*Tq*HI, dI]).
+ *
+ * indexer_scores_fp8 / indexer_topk_fp8 -- indexer_scores / indexer_topk on
+ * E4M3 rows:
+ *   I[t, s] = k_scale[s] * sum_h wI[t,h] * q_scale[t,h]
+ *                        * max(0, dq[t,h,:] . dk[s,:])
+ *   with dq, dk the decoded codes (exact products, fp32 sums on
+ *   v_mfma_f32_32x32x64_f8f6f4), which equals the bf16 formula on the
+ *   dequantised rows.
+ *   qI : [batch, Tq, HI, dI] uint8, q_scale : [batch, Tq, HI] fp32
+ *   KI : [batch, N, dI] uint8,      k_scale : [batch, N] fp32
+ *   dI in {64, 128}; other arguments, limits and outputs as in indexer_scores /
+ *   indexer_topk; the workspace of indexer_topk_fp8 is
+ *   cskv_indexer_workspace_size(batch, Tq, N, HI, k, CSKV_FP8) bytes.
+ */
+int cskv_quantize_fp8(const void* x, int64_t rows, int dim, int dtype, uint8_t* codes, float* scales,
+                      void* stream);
+int indexer_scores_fp8(const uint8_t* qI, const float* q_scale, const float* wI, const uint8_t* KI,
+                       const float* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                       int64_t pos0, int m, float* scores, int64_t ld, void* stream);
+int indexer_topk_fp8(const uint8_t* qI, const float* q_scale, const float* wI, const uint8_t* KI,
+                     const float* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                     int64_t pos0, int m, int k, int32_t* out_idx, void* workspace, size_t ws_bytes,
+                     void* stream);
 
 /*
  * compressed_attn_prefill -- MQA core attention over compressed entries,

@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(L, n), n
     from compressed_sparse_kv_02_amd import binding
@@ -140,6 +140,40 @@ def test_topk_select_validation(L):
     assert L.cskv_topk_workspace_size(8, 1, 20000, 1024) == 0
     assert L.cskv_topk_workspace_size(2, 4096, 262144, 1024) == 0
     assert L.cskv_topk_workspace_size(1, 1, 1 << 21, 1024) == 0   # more than 128 parts
+
+
+def test_fp8_indexer_validation(L):
+    q = L.cskv_quantize_fp8
+    assert q(P, 10, 128, 2, P, P, None) == DTYPE     # input must be bf16 or fp32
+    assert q(P, 10, 130, 0, P, P, None) == SHAPE     # dim % 4
+    assert q(P, 10, 2048, 0, P, P, None) == SHAPE    # dim > 1024
+    assert q(P, 10, 128, 0, None, P, None) == INVALID
+    assert q(P, 10, 128, 0, P + 4, P, None) == MISALIGNED
+    assert q(P, 0, 128, 0, P, P, None) == OK
+    s = L.indexer_scores_fp8
+    base = dict(q=P, qs=P, w=P, k=P, ks=P, batch=1, Tq=4, N=1000, HI=64, dI=128, pos0=0, m=4, sc=P, ld=1024,
+                st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return s(*a.values())
+    assert call(dI=96) == UNSUPPORTED
+    assert call(HI=0) == SHAPE
+    assert call(ld=999) == SHAPE
+    assert call(qs=None) == INVALID
+    assert call(ks=P + 4) == MISALIGNED
+    assert call(Tq=0) == OK
+    t = L.indexer_topk_fp8
+    tb = dict(q=P, qs=P, w=P, k=P, ks=P, batch=1, Tq=64, N=1000, HI=64, dI=128, pos0=0, m=4, kk=1024, out=P,
+              ws=P, wsb=1 << 40, st=None)
+
+    def tcall(**kw):
+        a = dict(tb, **kw)
+        return t(*a.values())
+    assert tcall(kk=4096) == UNSUPPORTED
+    assert tcall(ws=None) == WS
+    assert tcall(dI=32) == UNSUPPORTED
+    assert L.cskv_indexer_workspace_size(1, 64, 1000, 64, 1024, 2) >= 64 * 1000 * 4
 
 
 def test_attention_validation(L):

@@ -11,8 +11,8 @@ from oracle import cskv_oracle as O
 from compressed_sparse_kv_02_amd import binding as B
 from compressed_sparse_kv_02_amd import layer as LY
 from compressed_sparse_kv_02_amd.synth import normal_device, uniform_device
-from tests.parity_utils import (assert_storage_close, check_topk_row, key_rounding_band, np64,
-                                oracle_layer)
+from tests.parity_utils import (assert_storage_close, check_topk_row, check_topk_row_bounded, fp8_score_bound,
+                                key_rounding_band, np64, oracle_layer)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -177,6 +177,86 @@ def test_topk_split_route(kind, bt, Tq, N, k):
         for r in range(Tq):
             V = O.visible(pos0 + r, 4, N)
             assert np.array_equal(a[bb, r], O.topk_row(scn[bb, r], V, k)), (bb, r)
+
+
+# ----------------------------------------------------------------------------- FP8 (E4M3) indexer
+
+@pytest.mark.parametrize("dtype,rows,dim", [("bf16", 1000, 128), ("f32", 333, 64), ("bf16", 7, 1024),
+                                            ("bf16", 130, 4)])
+def test_quantize_fp8(dtype, rows, dim):
+    say("quantize_fp8", dtype, rows, dim)
+    x = gen(71, "q8.x", (rows, dim), dtype, std=3.0)
+    x[1] = 0.0                                     # a zero row
+    x[2, : dim // 2] = -x[2, dim // 2: 2 * (dim // 2)]  # exact ties in magnitude
+    x[3] *= 1e-30 if dtype == "f32" else 1.0       # tiny values: subnormal codes after scaling
+    codes, scales = B.quantize_fp8(x)
+    torch.cuda.synchronize()
+    oc, osc = O.quantize_rows_fp8(np64(x).astype(np.float32))
+    assert np.array_equal(codes.cpu().numpy(), oc)
+    assert np.array_equal(scales.cpu().numpy(), osc)
+
+
+def _fp8_case(bt, Tq, N, HI, dI, seed):
+    qI = gen(seed, "i8.q", (bt, Tq, HI, dI))
+    KI = gen(seed, "i8.k", (bt, N, dI))
+    wI = uniform_device(seed, "i8.w", (bt, Tq, HI), DEV)
+    qc, qs = B.quantize_fp8(qI)
+    kc, ks = B.quantize_fp8(KI)
+    torch.cuda.synchronize()
+    return qI, KI, wI, qc, qs, kc, ks
+
+
+@pytest.mark.parametrize("bt,Tq,N,HI,dI,pos0,m,k", [
+    (2, 300, 2000, 64, 128, 4 * 2000 - 300, 4, 256),   # prefill route (8 queries per workgroup), ragged tail
+    (1, 77, 5000, 20, 64, 16000, 4, 100),             # dI 64, HI not a multiple of 32
+    (3, 5, 70000, 64, 128, 4 * 70000, 4, 1024),       # decode route (streaming waves), two-kernel top-k
+    (1, 2, 3000, 128, 128, 3000 * 4 - 2, 4, 2048),    # 128 heads, max k
+])
+def test_indexer_fp8(bt, Tq, N, HI, dI, pos0, m, k):
+    """FP8 scores and top-k against the oracle on its own quantisation of the same raw inputs."""
+    say("indexer fp8", bt, Tq, N, HI, dI, pos0, m, k)
+    qI, KI, wI, qc, qs, kc, ks = _fp8_case(bt, Tq, N, HI, dI, seed=31)
+    sc = B.indexer_scores_fp8(qc, qs, wI, kc, ks, pos0, m)
+    idx = B.indexer_topk_fp8(qc, qs, wI, kc, ks, pos0, m, k)
+    torch.cuda.synchronize()
+    sc, idx = sc.cpu().numpy(), idx.cpu().numpy()
+    rows = range(Tq) if Tq <= 80 else sorted(set(np.linspace(0, Tq - 1, 40).astype(int)) | {0, Tq - 1})
+    n_band, worst = 0, 0.0
+    for b in range(bt):
+        okc, oks = O.quantize_rows_fp8(np64(KI[b]).astype(np.float32))
+        assert np.array_equal(okc, kc[b].cpu().numpy())
+        for r in rows:
+            oqc, oqs = O.quantize_rows_fp8(np64(qI[b, r]).astype(np.float32))
+            I = O.indexer_scores_fp8(oqc[None], oqs[None], np64(wI[b, r:r + 1]), okc, oks, pos0 + r, m)[0]
+            V = O.visible(pos0 + r, m, N)
+            if V == 0:
+                continue
+            bound = fp8_score_bound(oqc, oqs, np64(wI[b, r]), okc, oks, V)
+            err = np.abs(sc[b, r, :V] - I[:V])
+            assert (err <= bound).all(), (b, r, float((err / bound).max()))
+            worst = max(worst, float((err / bound).max()))
+            n_band += check_topk_row_bounded(idx[b, r], I, bound, V, k, what=f"b{b} r{r}")
+    say(f"  undecided entries: {n_band}; largest error / bound: {worst:.3g}")
+
+
+def test_indexer_fp8_decode_1m():
+    say("indexer fp8 decode 1M: batch 8, 262144 keys")
+    N, pos0 = 262144, 1 << 20
+    qI, KI, wI, qc, qs, kc, ks = _fp8_case(8, 1, N, 64, 128, seed=4)
+    idx = B.indexer_topk_fp8(qc, qs, wI, kc, ks, pos0, 4, 1024)
+    ref = B.indexer_topk(qI, wI, KI, pos0, 4, 1024)   # the bf16 selection, for the overlap figure only
+    torch.cuda.synchronize()
+    idx, ref = idx.cpu().numpy(), ref.cpu().numpy()
+    overlap = []
+    for b in range(8):
+        okc, oks = O.quantize_rows_fp8(np64(KI[b]).astype(np.float32))
+        oqc, oqs = O.quantize_rows_fp8(np64(qI[b, 0]).astype(np.float32))
+        I = O.indexer_scores_fp8(oqc[None], oqs[None], np64(wI[b]), okc, oks, pos0, 4)[0]
+        bound = fp8_score_bound(oqc, oqs, np64(wI[b, 0]), okc, oks, N)
+        und = check_topk_row_bounded(idx[b, 0], I, bound, N, 1024, what=f"b{b}")
+        overlap.append(len(set(idx[b, 0].tolist()) & set(ref[b, 0].tolist())) / 1024)
+        say(f"  b{b}: undecided entries {und}")
+    say("  fp8 vs bf16 selection overlap per row:", [round(o, 3) for o in overlap])
 
 
 # ----------------------------------------------------------------------------- attention
