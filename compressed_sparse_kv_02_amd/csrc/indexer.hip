@@ -24,12 +24,12 @@ namespace cskv {
 // bf16 scoring on the matrix cores
 // ----------------------------------------------------------------------------
 
-// Prefill rows: 8 queries per workgroup, one per wave, sharing 128-key LDS tiles.
+// Prefill rows: 8 queries per workgroup, one per wave, sharing 256-key LDS tiles.
 template <int HT, int KS>
 __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
   constexpr int QB = 8;                // queries per workgroup (one per wave)
   constexpr int KW = 1;                // waves that take different key blocks
-  constexpr int SUB = 4;               // 32-key sub-blocks per wave per tile
+  constexpr int SUB = 8;               // 32-key sub-blocks per wave per tile
   constexpr int DI = 16 * KS;
   constexpr int TILE = KW * SUB * 32;  // keys per LDS tile
   constexpr int ROW = DI + 8;          // padded LDS row (bf16), +16 bytes vs bank conflicts
@@ -351,7 +351,7 @@ int launch_scores(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st) {
     const int ht = a.HI <= 32 ? 1 : (a.HI <= 64 ? 2 : 4);
     bool ok;
     if (qb == 8) {
-      // key spans (multiples of the 128-key tile) so that about 1024 workgroups run
+      // key spans (multiples of 128 keys) so that about 1024 workgroups run
       const int64_t qblocks = ceil_div(a.nrows, (int64_t)8);
       int64_t splits = ceil_div(1024, qblocks * batch);
       if (splits < 1) splits = 1;

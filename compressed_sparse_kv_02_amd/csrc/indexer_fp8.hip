@@ -16,7 +16,7 @@
 // scale = amax / 448, the quotient and product correctly rounded in fp32.
 //
 // The scoring kernels follow the bf16 ones: 8 queries per workgroup sharing
-// 128-key LDS tiles for prefill; for decode, interleaved 32-key blocks per
+// 256-key LDS tiles for prefill; for decode, interleaved 32-key blocks per
 // wave with coalesced loads turned into the MFMA layout through per-wave LDS
 // rows. A key row is dI bytes; each lane holds one contiguous half of it
 // (the K dimension permuted identically in A and B: lane half h, k-step ks
@@ -113,11 +113,11 @@ __device__ __forceinline__ void load_query_fp8(const IdxArgs& a, int b, int64_t 
   }
 }
 
-// Prefill rows: 8 queries per workgroup (one per wave) sharing 128-key LDS tiles.
+// Prefill rows: 8 queries per workgroup (one per wave) sharing 256-key LDS tiles.
 template <int HT, int KS8>
 __global__ __launch_bounds__(512) void indexer_score_fp8_mfma(IdxArgs a) {
   constexpr int QB = 8;
-  constexpr int SUB = 4;               // 32-key sub-blocks per wave per tile
+  constexpr int SUB = 8;               // 32-key sub-blocks per wave per tile
   constexpr int TILE = SUB * 32;
   constexpr int DI = 64 * KS8;         // bytes per key row
   constexpr int ROW = DI + 16;         // padded LDS row, against bank conflicts
