@@ -59,10 +59,18 @@ __device__ __forceinline__ int64_t visible_n(int64_t t, int m, int64_t N) {
   return v < N ? v : N;
 }
 
+// Row of the window buffer that holds position p: (p - win_pos0) mod W. A buffer
+// filled in position order from win_pos0 and a ring of W rows (position p in row
+// p mod W, win_pos0 = 0) are both read this way.
+__device__ __forceinline__ int64_t win_row_of(const AttnArgs& a, int64_t p) {
+  int64_t r = (p - a.win_pos0) % a.W;
+  return r < 0 ? r + a.W : r;
+}
+
 // Key list of query (b, j): [0, n_comp) compressed (selected or visible), then window rows.
 struct KeyList {
   const int32_t* idxrow;
-  int64_t n_comp, n_tot, win_row0;  // win_row0: row of position max(0, t-w+1) in `win`
+  int64_t n_comp, n_tot, win_row0;  // win_row0: row of position max(0, t-w+1) in `win` (0 .. W-1)
 };
 
 __device__ __forceinline__ KeyList make_keys(const AttnArgs& a, int b, int64_t j) {
@@ -78,7 +86,7 @@ __device__ __forceinline__ KeyList make_keys(const AttnArgs& a, int b, int64_t j
   int64_t lo = t - a.w + 1;
   if (lo < 0) lo = 0;
   L.n_tot = L.n_comp + (t - lo + 1);
-  L.win_row0 = lo - a.win_pos0;
+  L.win_row0 = win_row_of(a, lo);
   return L;
 }
 
@@ -93,7 +101,9 @@ __device__ __forceinline__ int64_t key_row(const AttnArgs& a, const KeyList& L, 
     }
     return ((int64_t)b * a.N + s) * a.D;
   }
-  return -2 - (((int64_t)b * a.W + L.win_row0 + (u - L.n_comp)) * a.D);  // window: encoded < -1
+  int64_t r = L.win_row0 + (u - L.n_comp);  // window rows wrap at W
+  if (r >= a.W) r -= a.W;
+  return -2 - (((int64_t)b * a.W + r) * a.D);  // window: encoded < -1
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -231,7 +241,8 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
   // ---- gather loader: thread -> (key row kr, chunks c0 + TPK*i)
   const int kr = tid / TPK, c0 = tid % TPK;
   const uint16_t* kvb = (const uint16_t*)a.kv + (int64_t)b * a.N * D;
-  const int64_t wrow0 = (int64_t)b * a.W - a.win_pos0;  // window row of position p: wrow0 + p
+  const int64_t wbase = (int64_t)b * a.W;
+  const int64_t wr_lo = win_row_of(a, lo);  // window row of position lo; rows wrap at W
   // per-query bounds of the tile's queries, for the loader's validity bits
   int64_t vis_q[QG], t_q[QG];
 #pragma unroll
@@ -256,7 +267,9 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
       }
     } else if (u < n_tot) {
       const int64_t pos = lo + (u - n_comp);
-      src = (const uint16_t*)a.win + (wrow0 + pos) * D;
+      int64_t wr = wr_lo + (u - n_comp);
+      if (wr >= a.W) wr -= a.W;
+      src = (const uint16_t*)a.win + (wbase + wr) * D;
 #pragma unroll
       for (int q = 0; q < QG; ++q) ok |= (pos >= t_q[q] - a.w + 1 && pos <= t_q[q]) ? (1 << q) : 0;
     }
@@ -631,7 +644,8 @@ static int validate_attn(int mode, const void* q, const void* kv, const int32_t*
   if (batch == 0 || Tq == 0) return CSKV_OK;
   int64_t lo = pos0 - w + 1;
   if (lo < 0) lo = 0;
-  if (win_pos0 < 0 || win_pos0 > lo || win_pos0 + W < pos0 + Tq) return CSKV_ERR_BAD_SHAPE;
+  // positions lo .. pos0 + Tq - 1 must fit in the W rows of `win`
+  if (win_pos0 < 0 || W < pos0 + Tq - lo) return CSKV_ERR_BAD_SHAPE;
   if (!q || !win || !out || (N > 0 && !kv) || (mode == CSKV_MODE_CSA && !idx)) return CSKV_ERR_INVALID_ARG;
   if (!aligned16(q, kv, idx, win, sink, q_norm_w, out, lse)) return CSKV_ERR_MISALIGNED;
   return CSKV_OK;

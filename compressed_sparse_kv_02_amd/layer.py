@@ -181,6 +181,102 @@ def run_layer(L: LayerCall, t: Dict[str, torch.Tensor]) -> torch.Tensor:
     return t["out"]
 
 
+# --------------------------------------------------------------------------- streaming decode
+
+class DecodeStream:
+    """Token-by-token decode of one layer whose caches grow as tokens arrive.
+
+    A compressed entry exists once its block is complete ("Paper Breakdown:
+    DeepSeek-V4", §2.3.1 and §2.3.2): CSA entry i pools the a-rows of block i
+    and the b-rows of block i-1, HCA entry i the m' rows of block i. The raw
+    rows of the producer (C^a, C^b, Z^a, Z^b per stream for CSA; C, Z for HCA)
+    go into rings that the producer writes directly (`slot`):
+
+      * CSA: [2, batch, m, c] -- block i in half i % 2, so the completed block
+        and the b-rows of the block before it are each one contiguous
+        [batch, m, c] argument of csa_compress;
+      * HCA: [batch, m', c] -- the block being filled;
+      * window: a ring of w prepared rows, position p in row p mod w, read by
+        the attention entry points with win_pos0 = 0.
+
+    `step(t, ...)` prepares token t's window row in place, appends a cache
+    entry (KV, and indexer key for CSA) when t completes a block, then runs the
+    indexer, top-k and split-K attention against the caches. The caches are
+    allocated for `capacity` entries and passed whole: the kernels read only
+    entries visible at t, i.e. complete blocks, so rows not yet written are
+    never read. All arithmetic is the library's; this class only keeps state.
+    """
+
+    def __init__(self, L: LayerCall, capacity: int, device="cuda"):
+        self.L = L
+        self.capacity = capacity
+        td = L.torch_dtype
+        Bt, d, m = L.batch, L.d, L.m
+        self.streams = [("kv", d)] + ([("ik", L.dI)] if L.kind == "csa" else [])
+        self.ring: Dict[str, torch.Tensor] = {}
+        self.cache: Dict[str, torch.Tensor] = {}
+        for tag, c in self.streams:
+            names = ("Ca", "Cb", "Za", "Zb") if L.kind == "csa" else ("C", "Z")
+            for nm in names:
+                shape = (2, Bt, m, c) if L.kind == "csa" else (Bt, m, c)
+                self.ring[f"{tag}.{nm}"] = torch.zeros(shape, dtype=td, device=device)
+            self.cache[tag] = torch.zeros(Bt, capacity, c, dtype=td, device=device)
+        self.win = torch.zeros(Bt, L.w, d, dtype=td, device=device)
+        self.out = torch.empty(Bt, 1, L.H, d, dtype=td, device=device)
+        self.lse = torch.empty(Bt, 1, L.H, dtype=torch.float32, device=device)
+        self.ws_dec = torch.empty(max(16, B.decode_workspace_bytes(Bt, 1, L.H, d, L.n_splits)),
+                                  dtype=torch.uint8, device=device)
+        if L.kind == "csa":
+            self.idx = torch.empty(Bt, 1, L.k, dtype=torch.int32, device=device)
+            self.scores = torch.empty(Bt, 1, B.score_ld(capacity), dtype=torch.float32, device=device)
+            nsel = B.topk_workspace_bytes(Bt, 1, capacity, L.k)
+            self.ws_topk = torch.empty(nsel, dtype=torch.uint8, device=device) if nsel else None
+        self.n_entries = 0
+
+    def slot(self, name: str, t: int) -> torch.Tensor:
+        """[batch, c] view where the producer writes raw row `name` (e.g. "kv.Ca") of token t."""
+        m = self.L.m
+        if self.L.kind == "csa":
+            return self.ring[name][(t // m) % 2, :, t % m]
+        return self.ring[name][:, t % m]
+
+    def _compress(self, i: int, biases: Dict[str, torch.Tensor]) -> None:
+        """Cache entry i from the ring (block i complete)."""
+        L, m = self.L, self.L.m
+        if i >= self.capacity:
+            raise ValueError("DecodeStream capacity exceeded")
+        for tag, _ in self.streams:
+            r = lambda nm, h: self.ring[f"{tag}.{nm}"][h]
+            if L.kind == "csa":
+                cur, prev = i % 2, (i - 1) % 2
+                pb = (r("Cb", prev), r("Zb", prev)) if i > 0 else (None, None)
+                kv = tag == "kv"
+                B.csa_compress(r("Ca", cur), r("Cb", cur), r("Za", cur), r("Zb", cur), biases[f"{tag}.B"], m,
+                               m * i, pb[0], pb[1], apply_norm=kv, rope_dims=L.rope_dims if kv else 0,
+                               out=self.cache[tag], out_row0=i)
+            else:
+                B.hca_compress(self.ring["kv.C"], self.ring["kv.Z"], biases["kv.B"], m, m * i, apply_norm=True,
+                               rope_dims=L.rope_dims, out=self.cache["kv"], out_row0=i)
+        self.n_entries = i + 1
+
+    def step(self, t: int, q, win_raw, sink, biases: Dict[str, torch.Tensor], qI=None, wI=None) -> torch.Tensor:
+        """Decode token t (its raw rows already in their slots); returns its attention output [batch, 1, H, d]."""
+        L = self.L
+        B.hca_compress(win_raw, None, None, 1, t, apply_norm=True, rope_dims=L.rope_dims, out=self.win,
+                       out_row0=t % L.w)
+        if (t + 1) % L.m == 0:
+            self._compress((t + 1) // L.m - 1, biases)
+        mode = B.CSA if L.kind == "csa" else B.HCA
+        idx = None
+        if L.kind == "csa":
+            B.indexer_scores(qI, wI, self.cache["ik"], t, L.m, scores=self.scores)
+            B.topk_select(self.scores, self.capacity, t, L.m, L.k, out=self.idx, workspace=self.ws_topk)
+            idx = self.idx
+        return B.compressed_attn_decode(mode, q, self.cache["kv"], idx, self.win, 0, sink, t, L.m, L.w, k=L.k,
+                                        apply_q_norm=True, rope_dims=L.rope_dims, rope_on_output=True,
+                                        n_splits=L.n_splits, workspace=self.ws_dec, out=self.out, lse=self.lse)
+
+
 # --------------------------------------------------------------------------- workloads
 
 def tiny_csa(dtype="f32", seed=0) -> LayerCall:

@@ -239,9 +239,12 @@ int indexer_topk_fp8(const uint8_t* qI, const float* q_scale, const float* wI, c
  *   kv    : [batch, N, d]     compressed entries as stored (normed + roped)
  *   idx   : [batch, Tq, k] int32 (CSA; entries outside [0, N) are skipped),
  *           NULL for HCA
- *   win   : [batch, W, d]     prepared window rows; row r is position
- *           win_pos0 + r. Requires win_pos0 <= max(0, pos0 - w + 1) and
- *           win_pos0 + W >= pos0 + Tq.
+ *   win   : [batch, W, d]     prepared window rows; position p is row
+ *           (p - win_pos0) mod W, so rows filled in position order from
+ *           win_pos0 and a ring of W rows (row p mod W, win_pos0 = 0, as a
+ *           decode loop keeps it) are both accepted. The positions
+ *           max(0, pos0 - w + 1) .. pos0 + Tq - 1 must fit: W >= their count;
+ *           win_pos0 >= 0.
  *   sink  : [H] fp32 or NULL;  q_norm_w : [d] fp32 or NULL (gain 1)
  *   1 <= H <= CSKV_MAX_HEADS, d % 32 == 0, 32 <= d <= 512 (bf16) or
  *   CSKV_MAX_DIM (f32), w >= 1, rope_dims even <= d

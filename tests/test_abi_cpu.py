@@ -197,7 +197,7 @@ def test_attention_validation(L):
         assert call(k=0) == SHAPE
         assert call(k=4096) == UNSUPPORTED
         assert call(W=63) == SHAPE           # window rows do not reach the last query
-        assert call(wp0=1) == SHAPE          # window rows start after the first query's window
+        assert call(wp0=-1) == SHAPE         # window base before position 0
         assert call(idx=None) == INVALID     # CSA needs indices
         assert call(q=P + 2) == MISALIGNED
         assert call(Tq=0) == OK

@@ -1,6 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
 same seeded inputs. Stage tests feed both sides generator-made inputs for
 every stage; end-to-end tests run the whole layer on both sides."""
+import dataclasses
 import math
 
 import numpy as np
@@ -393,6 +394,61 @@ def test_chunked_layer_small(kind):
     say("chunked small", L)
     t = _run(L)
     _check_layer(L, t, lambda L: sorted({0, 1, 2, 3, 127, 128, 129, 255, 256, 400, 511, 512, 698, 699}), 2e-2)
+
+
+@pytest.mark.parametrize("kind", ["csa", "hca"])
+def test_streaming_decode_grows_caches_like_prefill(kind):
+    """Decode a sequence token by token from empty caches: the caches the stream appends
+    must equal a one-shot prefill's, and every step must match the oracle's row."""
+    say("streaming decode", kind)
+    m, T = (4, 96) if kind == "csa" else (8, 96)
+    L = LY.LayerCall(kind, 2, T, 0, 0, d=64, rope_dims=16, H=4, m=m, w=16, k=16, HI=4, dI=32, seed=77,
+                     name=f"stream.{kind}")
+    t = LY.make_inputs(L)
+    LY.run_layer(L, t)  # reference: the whole sequence at once
+    S = LY.DecodeStream(dataclasses.replace(L, T=1), capacity=T // m)
+    biases = {nm: v for nm, v in t.items() if nm.endswith(".B")}
+    outs, lses, idxs = [], [], []
+    row = lambda nm, p: t[nm][:, p:p + 1].contiguous()
+    for p in range(T):
+        for nm in S.ring:
+            S.slot(nm, p).copy_(t[nm][:, p])  # the producer's rows of token p
+        o = S.step(p, row("q", p), row("win_raw", p), t["sink"], biases,
+                   qI=row("qI", p) if kind == "csa" else None, wI=row("wI", p) if kind == "csa" else None)
+        outs.append(o.clone())
+        lses.append(S.lse.clone())
+        if kind == "csa":
+            idxs.append(S.idx.clone())
+    torch.cuda.synchronize()
+    assert S.n_entries == T // m
+    for tag in S.cache:
+        assert torch.equal(S.cache[tag], t[f"cache.{tag}"]), tag
+    td = dict(t)
+    td["out"], td["lse"] = torch.cat(outs, 1), torch.cat(lses, 1)
+    if kind == "csa":
+        td["idx"] = torch.cat(idxs, 1)
+    _check_layer(L, td, lambda L: list(range(T)), ATOL["bf16"])
+
+
+def test_window_ring_equals_linear_window():
+    """A window kept as a ring of w rows (row p mod w, win_pos0 = 0) gives the same result as
+    the same rows laid out in position order."""
+    say("window ring")
+    bt, H, d, w, N, m, k = 2, 8, 128, 16, 300, 4, 32
+    pos0 = 4 * N - 5                      # window positions pos0 - 15 .. pos0, wrapping the ring
+    q = gen(81, "wr.q", (bt, 1, H, d))
+    kv = gen(81, "wr.kv", (bt, N, d))
+    lin = gen(81, "wr.win", (bt, w, d))   # positions pos0 - w + 1 .. pos0 in order
+    ring = torch.empty_like(lin)
+    for i in range(w):
+        ring[:, (pos0 - w + 1 + i) % w] = lin[:, i]
+    sink = normal_device(81, "wr.sink", (H,), 1.0, "f32", DEV)
+    idx = torch.tensor(_random_idx(bt, 1, pos0, m, N, k, 5), dtype=torch.int32, device=DEV)
+    for mode in (B.CSA, B.HCA):
+        a = B.compressed_attn_decode(mode, q, kv, idx, lin, pos0 - w + 1, sink, pos0, m, w, k=k, rope_dims=64)
+        r = B.compressed_attn_decode(mode, q, kv, idx, ring, 0, sink, pos0, m, w, k=k, rope_dims=64)
+        torch.cuda.synchronize()
+        assert torch.equal(a, r), mode
 
 
 def test_prefill_from_scratch_edges():
