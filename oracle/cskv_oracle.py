@@ -319,6 +319,63 @@ def indexer_scores_fp8(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: i
     return indexer_scores(q, wI, kk, pos0, m)
 
 
+FP4_MAX = 6.0
+
+
+def e2m1_values() -> np.ndarray:
+    """Value of each non-negative FP4 E2M1 code 0..7 (OCP: 2 exponent bits, bias 1, 1 mantissa bit).
+
+    Codes 0 and 1 are 0 and the subnormal 0.5; codes 2..7 have exponent field
+    e = c // 2 and mantissa bit f = c % 2: (1 + f/2) * 2**(e - 1).
+    """
+    c = np.arange(8)
+    return np.where(c < 2, c * 0.5, (2 + c % 2) * np.exp2(c // 2 - 2.0)).astype(F64)
+
+
+def e2m1_encode(y) -> np.ndarray:
+    """Nearest E2M1 code of each value (ties to the even code), saturating at +-6; bit 3 = sign."""
+    y = np.asarray(y, dtype=F64)
+    a = np.minimum(np.abs(y), FP4_MAX)
+    vals = e2m1_values()
+    d = np.abs(a[..., None] - vals)                       # distance to every value
+    best = d.min(axis=-1, keepdims=True)
+    tied = d == best
+    even = tied & (np.arange(8) % 2 == 0)
+    code = np.where(even.any(axis=-1), np.argmax(even, axis=-1), np.argmax(tied, axis=-1)).astype(np.uint8)
+    return np.where(np.signbit(y), code | 0x8, code).astype(np.uint8)
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    c = np.asarray(codes, dtype=np.int64)
+    v = e2m1_values()[c & 0x7]
+    return np.where(c & 0x8, -v, v)
+
+
+def pack_nibbles(codes) -> np.ndarray:
+    """Two 4-bit codes per byte along the last axis: element 2i in the low nibble of byte i."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def quantize_rows_fp4(x) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-row E2M1 codes (unpacked, one per element) and scales, as quantize_rows_fp8 with 6 for 448."""
+    x32 = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x32), axis=-1)
+    safe = np.where(amax > 0, amax, np.float32(1))
+    inv = (np.float32(FP4_MAX) / safe).astype(np.float32)
+    y = (x32 * inv[..., None]).astype(np.float32)
+    codes = np.where((amax > 0)[..., None], e2m1_encode(y), np.uint8(0)).astype(np.uint8)
+    scale = np.where(amax > 0, (amax / np.float32(FP4_MAX)).astype(np.float32), np.float32(0))
+    return codes, scale.astype(np.float32)
+
+
+def indexer_scores_fp4(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int) -> np.ndarray:
+    """Indexer scores on E2M1 rows (unpacked codes): the plain indexer on the dequantised values."""
+    q = e2m1_decode(q_codes) * np.asarray(q_scales, dtype=F64)[..., None]
+    kk = e2m1_decode(k_codes) * np.asarray(k_scales, dtype=F64)[..., None]
+    return indexer_scores(q, wI, kk, pos0, m)
+
+
 # ---------------------------------------------------------------------------
 # Core MQA attention over compressed entries + sliding window + sink
 # ("Paper Breakdown: DeepSeek-V4", CSA §2.3.1, HCA §2.3.2, §2.3.3)

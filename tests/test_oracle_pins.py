@@ -403,6 +403,53 @@ def test_indexer_fp8_reduces_to_plain_indexer():
     assert np.allclose(I8s, O.indexer_scores(q, w * qs, k, pos0=100, m=4) * ks[None, :], rtol=1e-13, atol=0)
 
 
+# ---------------------------------------------------------------- FP4 (E2M1) indexer
+
+def test_e2m1_table_ties_and_thresholds():
+    vals = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]  # the OCP E2M1 magnitudes, by hand
+    assert np.array_equal(O.e2m1_values(), vals)
+    assert np.array_equal(O.e2m1_decode(np.arange(16)), vals + [-v for v in vals])
+    # every midpoint rounds to the even code
+    for y, code in ((0.25, 0), (0.75, 2), (1.25, 2), (1.75, 4), (2.5, 4), (3.5, 6), (5.0, 6)):
+        assert O.e2m1_encode(y) == code, y
+        assert O.e2m1_encode(-y) == code | 8, y
+    assert O.e2m1_encode(7.0) == 7 and O.e2m1_encode(-100.0) == 15 and O.e2m1_encode(-0.0) == 8
+    # nearest-value search against a count of the rounding thresholds, on dense values
+    y = np.linspace(-8, 8, 64001)
+    a = np.abs(y)
+    cnt = ((a > 0.25).astype(int) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) + (a > 2.5) + (a >= 3.5) + (a > 5))
+    assert np.array_equal(O.e2m1_encode(y) & 7, cnt)
+
+
+def test_quantize_rows_fp4_and_packing():
+    x = rng.standard_normal((40, 64)).astype(np.float32)
+    x[5] = 0.0
+    codes, scale = O.quantize_rows_fp4(x)
+    assert (codes[5] == 0).all() and scale[5] == 0
+    rows = [r for r in range(40) if r != 5]
+    am = np.argmax(np.abs(x[rows]), axis=1)
+    assert np.array_equal(codes[rows, am] & 7, np.full(len(rows), 7))   # the largest magnitude maps to 6
+    deq = O.e2m1_decode(codes) * scale[:, None].astype(np.float64)
+    assert (np.abs(deq - x)[rows] <= scale[rows, None] * 1.0 + 1e-12).all()  # half of the widest step (4..6)
+    packed = O.pack_nibbles(codes)
+    assert packed.shape == (40, 32)
+    assert np.array_equal(packed & 0xF, codes[:, 0::2]) and np.array_equal(packed >> 4, codes[:, 1::2])
+
+
+def test_indexer_fp4_reduces_to_plain_indexer():
+    v = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
+    q = rng.choice(np.concatenate([v, -v]), (4, 3, 32))
+    k = rng.choice(np.concatenate([v, -v]), (30, 32))
+    w = rng.uniform(0, 1, (4, 3))
+    qc, kc = O.e2m1_encode(q), O.e2m1_encode(k)
+    assert np.array_equal(O.e2m1_decode(qc), q) and np.array_equal(O.e2m1_decode(kc), k)
+    I4 = O.indexer_scores_fp4(qc, np.ones((4, 3)), w, kc, np.ones(30), pos0=80, m=4)
+    assert np.array_equal(I4, O.indexer_scores(q, w, k, pos0=80, m=4))
+    ks = rng.uniform(0.5, 2.0, 30)
+    assert np.allclose(O.indexer_scores_fp4(qc, np.ones((4, 3)), w, kc, ks, pos0=80, m=4),
+                       O.indexer_scores(q, w, k, pos0=80, m=4) * ks[None, :], rtol=1e-13, atol=0)
+
+
 def test_page_constants_fixture():
     with open(os.path.join(GOLDEN, "page_constants.json")) as f:
         g = json.load(f)
