@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "query-tokens/s for CSA/HCA layer at 1M ctx (prefill+decode); % HBM/MFMA peak"
 PEAK_BF16_FLOPS = 2.5e15
 PEAK_FP8_FLOPS = 5.0e15
+PEAK_FP4_FLOPS = 10.1e15
 PEAK_HBM_BYTES = 8.0e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # Sources whose kernels the stored counter figures describe; a change to any of
@@ -191,12 +192,12 @@ def cpu_baseline(prefill, decode, tp, td, budget_s: float):
             "seconds_per_prefill_token": per_tok_pre, "seconds_per_decode_token": per_tok_dec}
 
 
-def fp8_indexer_rows(prefill, tp, decode, td, reps: int = 3):
-    """FP8 (E4M3) indexer scoring on the same inputs as the timed step's CSA layers.
+def lowp_indexer_rows(prefill, tp, decode, td, reps: int = 3):
+    """Low-precision indexer scoring (FP8 E4M3, FP4 E2M1) on the timed step's CSA inputs.
 
     The indexer keys and queries of prefill layer 0 and of the decode CSA layer
-    are quantised once (outside the timing); indexer_scores_fp8 is then timed
-    with HIP events on the launch stream, reps launches each.
+    are quantised once (outside the timing); the scoring entry point is then
+    timed with HIP events on the launch stream, reps launches each.
     """
     import torch
     from compressed_sparse_kv_02_amd import binding as B
@@ -212,29 +213,32 @@ def fp8_indexer_rows(prefill, tp, decode, td, reps: int = 3):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    res = {}
-    for tag, L, t in (("prefill", prefill[0], tp[0]), ("decode", decode[0], td[0])):
-        kc, ks = B.quantize_fp8(t["cache.ik"])
-        qc, qs = B.quantize_fp8(t["qI"])
-        # the keys a step appends (one per sequence at decode) are quantised as they arrive
-        new_keys = (t["cache.ik"][:, L.n_cached:] if L.n_new else t["cache.ik"][:, :1]).contiguous()
-        ms = timed(lambda: B.indexer_scores_fp8(qc, qs, t["wI"], kc, ks, L.pos0, L.m, scores=t["ws.scores"]))
-        q_ms = timed(lambda: B.quantize_fp8(new_keys))
-        if tag == "prefill":
-            fl = indexer_flops(L)
-            ent = {"kernel": "indexer_score_fp8_mfma<2,2>", "bound": "mfma", "avg_launch_ms": ms,
-                   "achieved": fl / (ms / 1e3) / 1e12, "peak": PEAK_FP8_FLOPS / 1e12, "unit": "TFLOP/s",
-                   "algorithmic_flops_per_launch": fl}
-        else:
-            by = L.batch * (L.N * (L.dI + 4) + L.HI * L.dI + 2 * L.HI * 4 + L.N * 4)
-            ent = {"kernel": "indexer_score_fp8_stream<2,2>", "bound": "hbm", "avg_launch_ms": ms,
-                   "achieved": by / (ms / 1e3) / 1e9, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
-                   "algorithmic_bytes_per_launch": by}
-        ent["frac"] = ent["achieved"] / ent["peak"]
-        ent["quantize_new_keys_ms"] = q_ms
-        res[tag] = ent
-        del kc, ks, qc, qs
-    return res
+    out = {}
+    for fmt, quant, score, peak, bits in (("fp8", B.quantize_fp8, B.indexer_scores_fp8, PEAK_FP8_FLOPS, 8),
+                                          ("fp4", B.quantize_fp4, B.indexer_scores_fp4, PEAK_FP4_FLOPS, 4)):
+        res = {}
+        for tag, L, t in (("prefill", prefill[0], tp[0]), ("decode", decode[0], td[0])):
+            kc, ks = quant(t["cache.ik"])
+            qc, qs = quant(t["qI"])
+            # the keys a step appends (one per sequence at decode) are quantised as they arrive
+            new_keys = (t["cache.ik"][:, L.n_cached:] if L.n_new else t["cache.ik"][:, :1]).contiguous()
+            ms = timed(lambda: score(qc, qs, t["wI"], kc, ks, L.pos0, L.m, scores=t["ws.scores"]))
+            q_ms = timed(lambda: quant(new_keys))
+            kern = f"indexer_score_lowp_{'mfma' if tag == 'prefill' else 'stream'}<{fmt}>"
+            if tag == "prefill":
+                fl = indexer_flops(L)
+                ent = {"kernel": kern, "bound": "mfma", "avg_launch_ms": ms, "achieved": fl / (ms / 1e3) / 1e12,
+                       "peak": peak / 1e12, "unit": "TFLOP/s", "algorithmic_flops_per_launch": fl}
+            else:
+                by = L.batch * (L.N * (L.dI * bits // 8 + 4) + L.HI * L.dI * bits // 8 + 2 * L.HI * 4 + L.N * 4)
+                ent = {"kernel": kern, "bound": "hbm", "avg_launch_ms": ms, "achieved": by / (ms / 1e3) / 1e9,
+                       "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s", "algorithmic_bytes_per_launch": by}
+            ent["frac"] = ent["achieved"] / ent["peak"]
+            ent["quantize_new_keys_ms"] = q_ms
+            res[tag] = ent
+            del kc, ks, qc, qs
+        out[f"indexer_{fmt}"] = res
+    return out
 
 
 def main():
@@ -369,7 +373,7 @@ def main():
         "roofline": roofline,
         "roofline_decode": roofline_dec,
         "cpu_baseline": None,
-        "next_rows": {"indexer_fp8": fp8_indexer_rows(prefill, tp, decode, td)},
+        "next_rows": lowp_indexer_rows(prefill, tp, decode, td),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(prefill, decode, tp, td, args.cpu_budget)

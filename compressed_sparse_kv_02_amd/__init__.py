@@ -15,6 +15,9 @@ from .binding import (  # noqa: F401
     quantize_fp8,
     indexer_scores_fp8,
     indexer_topk_fp8,
+    quantize_fp4,
+    indexer_scores_fp4,
+    indexer_topk_fp4,
     compressed_attn_prefill,
     compressed_attn_decode,
 )

@@ -17,11 +17,12 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcskv.so")
 
-BF16, F32, FP8 = 0, 1, 2
+BF16, F32, FP8, FP4 = 0, 1, 2, 3
 CSA, HCA = 0, 1
 EXPORTS = ("cskv_version", "cskv_status_string", "csa_compress", "hca_compress",
            "cskv_indexer_workspace_size", "indexer_topk", "indexer_scores", "topk_select",
            "cskv_topk_workspace_size", "cskv_quantize_fp8", "indexer_scores_fp8", "indexer_topk_fp8",
+           "cskv_quantize_fp4", "indexer_scores_fp4", "indexer_topk_fp4",
            "compressed_attn_prefill",
            "cskv_decode_workspace_size", "compressed_attn_decode")
 
@@ -42,6 +43,9 @@ _SIGS = {
     "cskv_quantize_fp8": (_I, [_P, _L, _I, _I, _P, _P, _P]),
     "indexer_scores_fp8": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _P, _L, _P]),
     "indexer_topk_fp8": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _I, _P, _P, _Z, _P]),
+    "cskv_quantize_fp4": (_I, [_P, _L, _I, _I, _P, _P, _P]),
+    "indexer_scores_fp4": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _P, _L, _P]),
+    "indexer_topk_fp4": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _I, _P, _P, _Z, _P]),
     "compressed_attn_prefill": (_I, [_I, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
                                      _I, _P, _F, _I, _F, _F, _I, _P, _P, _I, _P]),
     "cskv_decode_workspace_size": (_Z, [_I, _L, _I, _I, _I]),
@@ -194,43 +198,79 @@ def topk_select(scores, N: int, pos0: int, m: int, k: int, out=None, workspace=N
     return out
 
 
-def quantize_fp8(x) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Per-row E4M3 codes (uint8, x's shape) and fp32 scales (x.shape[:-1]) of x (bf16 or fp32)."""
+_LOWP = {FP8: ("fp8", 1), FP4: ("fp4", 2)}  # name suffix, values per byte
+
+
+def _quantize(x, fmt):
+    suffix, per_byte = _LOWP[fmt]
     dim = x.shape[-1]
     rows = x.numel() // dim if dim else 0
-    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    codes = torch.empty(*x.shape[:-1], dim // per_byte, dtype=torch.uint8, device=x.device)
     scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _check("cskv_quantize_fp8", lib().cskv_quantize_fp8(_ptr(x), rows, dim, _dtype(x), _ptr(codes), _ptr(scales),
-                                                        _stream(x)))
+    name = f"cskv_quantize_{suffix}"
+    _check(name, getattr(lib(), name)(_ptr(x), rows, dim, _dtype(x), _ptr(codes), _ptr(scales), _stream(x)))
     return codes, scales
+
+
+def quantize_fp8(x) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-row E4M3 codes (uint8, x's shape) and fp32 scales (x.shape[:-1]) of x (bf16 or fp32)."""
+    return _quantize(x, FP8)
+
+
+def quantize_fp4(x) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-row E2M1 codes, two per byte ([..., dim / 2] uint8), and fp32 scales of x (bf16 or fp32)."""
+    return _quantize(x, FP4)
+
+
+def _scores_lowp(fmt, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, scores):
+    suffix, per_byte = _LOWP[fmt]
+    batch, Tq, HI, db = q_codes.shape
+    N = k_codes.shape[1]
+    if scores is None:
+        scores = torch.empty(batch, Tq, score_ld(N), dtype=torch.float32, device=q_codes.device)
+    name = f"indexer_scores_{suffix}"
+    _check(name, getattr(lib(), name)(
+        _ptr(q_codes), _ptr(q_scales), _ptr(wI), _ptr(k_codes), _ptr(k_scales), batch, Tq, N, HI, db * per_byte,
+        pos0, m, _ptr(scores), scores.shape[-1], _stream(q_codes)))
+    return scores
+
+
+def _topk_lowp(fmt, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, k, out, workspace):
+    suffix, per_byte = _LOWP[fmt]
+    batch, Tq, HI, db = q_codes.shape
+    N = k_codes.shape[1]
+    if out is None:
+        out = torch.empty(batch, Tq, k, dtype=torch.int32, device=q_codes.device)
+    need = indexer_workspace_bytes(batch, Tq, N, HI, k, fmt)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_codes.device)
+    name = f"indexer_topk_{suffix}"
+    _check(name, getattr(lib(), name)(
+        _ptr(q_codes), _ptr(q_scales), _ptr(wI), _ptr(k_codes), _ptr(k_scales), batch, Tq, N, HI, db * per_byte,
+        pos0, m, k, _ptr(out), _ptr(workspace), workspace.numel(), _stream(q_codes)))
+    return out
 
 
 def indexer_scores_fp8(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int, scores=None) -> torch.Tensor:
     """Indexer scores on E4M3 rows: [batch, Tq, ld] fp32 (valid for s < V_t)."""
-    batch, Tq, HI, dI = q_codes.shape
-    N = k_codes.shape[1]
-    if scores is None:
-        scores = torch.empty(batch, Tq, score_ld(N), dtype=torch.float32, device=q_codes.device)
-    _check("indexer_scores_fp8", lib().indexer_scores_fp8(
-        _ptr(q_codes), _ptr(q_scales), _ptr(wI), _ptr(k_codes), _ptr(k_scales), batch, Tq, N, HI, dI, pos0, m,
-        _ptr(scores), scores.shape[-1], _stream(q_codes)))
-    return scores
+    return _scores_lowp(FP8, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, scores)
+
+
+def indexer_scores_fp4(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int, scores=None) -> torch.Tensor:
+    """Indexer scores on E2M1 rows (two codes per byte): [batch, Tq, ld] fp32 (valid for s < V_t)."""
+    return _scores_lowp(FP4, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, scores)
 
 
 def indexer_topk_fp8(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int, k: int, out=None,
                      workspace=None) -> torch.Tensor:
     """Top-k compressed entries per query from E4M3 rows: [batch, Tq, k] int32, ascending, -1 padded."""
-    batch, Tq, HI, dI = q_codes.shape
-    N = k_codes.shape[1]
-    if out is None:
-        out = torch.empty(batch, Tq, k, dtype=torch.int32, device=q_codes.device)
-    need = indexer_workspace_bytes(batch, Tq, N, HI, k, FP8)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_codes.device)
-    _check("indexer_topk_fp8", lib().indexer_topk_fp8(
-        _ptr(q_codes), _ptr(q_scales), _ptr(wI), _ptr(k_codes), _ptr(k_scales), batch, Tq, N, HI, dI, pos0, m, k,
-        _ptr(out), _ptr(workspace), workspace.numel(), _stream(q_codes)))
-    return out
+    return _topk_lowp(FP8, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, k, out, workspace)
+
+
+def indexer_topk_fp4(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int, k: int, out=None,
+                     workspace=None) -> torch.Tensor:
+    """Top-k compressed entries per query from E2M1 rows: [batch, Tq, k] int32, ascending, -1 padded."""
+    return _topk_lowp(FP4, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, k, out, workspace)
 
 
 def _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_norm, q_norm_w, eps,

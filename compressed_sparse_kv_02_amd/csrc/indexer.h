@@ -17,8 +17,8 @@ struct IdxArgs {
   const void* qI;
   const float* wI;
   const void* KI;
-  const float* q_scale;  // FP8: [batch][Tq][HI] scale of each (query, head) row
-  const float* k_scale;  // FP8: [batch][N] scale of each key row
+  const float* q_scale;  // FP8/FP4: [batch][Tq][HI] scale of each (query, head) row
+  const float* k_scale;  // FP8/FP4: [batch][N] scale of each key row
   float* scores;  // [batch][rows_ws][ldS]
   int32_t* out;
   int64_t Tq, N, pos0, ldS, span;  // span: keys per workgroup (prefill scoring)
@@ -50,8 +50,9 @@ struct IdxPlan {
 };
 IdxPlan plan_indexer(int batch, int64_t Tq, int64_t N, int dtype);
 
-// FP8 (E4M3) scoring of rows [a.row0, a.row0 + a.nrows) into a.scores (indexer_fp8.hip).
-int launch_scores_fp8(IdxArgs& a, int batch, int qb, hipStream_t st);
+// Low-precision scoring (dtype CSKV_FP8: E4M3 codes, CSKV_FP4: E2M1 codes) of rows
+// [a.row0, a.row0 + a.nrows) into a.scores (indexer_lowp.hip).
+int launch_scores_lowp(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st);
 
 // Workspace bytes for the several-workgroups-per-row selection of `rows`
 // rows of up to vmax entries; 0 when that route is not taken.

@@ -60,7 +60,8 @@ enum {
   CSKV_ERR_HIP = -7           /* a kernel launch failed */
 };
 
-enum { CSKV_BF16 = 0, CSKV_F32 = 1, CSKV_FP8 = 2 /* E4M3 codes with fp32 row scales */ };
+enum { CSKV_BF16 = 0, CSKV_F32 = 1, CSKV_FP8 = 2 /* E4M3 codes, fp32 row scales */,
+       CSKV_FP4 = 3 /* E2M1 codes, two per byte, fp32 row scales */ };
 enum { CSKV_MODE_CSA = 0, CSKV_MODE_HCA = 1 };
 
 #define CSKV_MAX_TOPK 2048
@@ -215,6 +216,32 @@ int indexer_scores_fp8(const uint8_t* qI, const float* q_scale, const float* wI,
                        const float* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
                        int64_t pos0, int m, float* scores, int64_t ld, void* stream);
 int indexer_topk_fp8(const uint8_t* qI, const float* q_scale, const float* wI, const uint8_t* KI,
+                     const float* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                     int64_t pos0, int m, int k, int32_t* out_idx, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * FP4 lightning indexer -- the V4 setting of the same table [PB §2.3.4]:
+ * OCP FP4 E2M1 codes (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their
+ * negatives; bit 3 is the sign), two per byte (element 2i in the low nibble
+ * of byte i), one fp32 scale per row.
+ *
+ * cskv_quantize_fp4 -- as cskv_quantize_fp8 with 6 in place of 448:
+ *   codes = E2M1(x * (6 / amax)) (nearest, ties to the even code,
+ *   saturating); scales = amax / 6.
+ *   codes : [rows, dim / 2] bytes
+ * indexer_scores_fp4 / indexer_topk_fp4 -- as the FP8 calls on E2M1 rows:
+ *   qI : [batch, Tq, HI, dI / 2], KI : [batch, N, dI / 2] bytes. Products of
+ *   two E2M1 values are multiples of 1/4 below 36, so each dot product is
+ *   exact and only the fp32 head sum rounds. The workspace of
+ *   indexer_topk_fp4 is cskv_indexer_workspace_size(..., CSKV_FP4) bytes.
+ */
+int cskv_quantize_fp4(const void* x, int64_t rows, int dim, int dtype, uint8_t* codes, float* scales,
+                      void* stream);
+int indexer_scores_fp4(const uint8_t* qI, const float* q_scale, const float* wI, const uint8_t* KI,
+                       const float* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                       int64_t pos0, int m, float* scores, int64_t ld, void* stream);
+int indexer_topk_fp4(const uint8_t* qI, const float* q_scale, const float* wI, const uint8_t* KI,
                      const float* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
                      int64_t pos0, int m, int k, int32_t* out_idx, void* workspace, size_t ws_bytes,
                      void* stream);

@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(L, n), n
     from compressed_sparse_kv_02_amd import binding
@@ -174,6 +174,16 @@ def test_fp8_indexer_validation(L):
     assert tcall(ws=None) == WS
     assert tcall(dI=32) == UNSUPPORTED
     assert L.cskv_indexer_workspace_size(1, 64, 1000, 64, 1024, 2) >= 64 * 1000 * 4
+    # FP4 entry points share the validation
+    assert L.cskv_quantize_fp4(P, 10, 130, 0, P, P, None) == SHAPE
+    assert L.cskv_quantize_fp4(P, 10, 128, 2, P, P, None) == DTYPE
+    a = dict(base)
+    a.update(dI=96)
+    assert L.indexer_scores_fp4(*a.values()) == UNSUPPORTED
+    a = dict(tb)
+    a.update(ws=None)
+    assert L.indexer_topk_fp4(*a.values()) == WS
+    assert L.cskv_indexer_workspace_size(1, 64, 1000, 64, 1024, 3) >= 64 * 1000 * 4
 
 
 def test_attention_validation(L):

@@ -260,6 +260,84 @@ def test_indexer_fp8_decode_1m():
     say("  fp8 vs bf16 selection overlap per row:", [round(o, 3) for o in overlap])
 
 
+# ----------------------------------------------------------------------------- FP4 (E2M1) indexer
+
+@pytest.mark.parametrize("dtype,rows,dim", [("bf16", 1000, 128), ("f32", 333, 64), ("bf16", 9, 1024)])
+def test_quantize_fp4(dtype, rows, dim):
+    say("quantize_fp4", dtype, rows, dim)
+    x = gen(73, "q4.x", (rows, dim), dtype, std=2.0)
+    x[1] = 0.0
+    codes, scales = B.quantize_fp4(x)
+    torch.cuda.synchronize()
+    oc, osc = O.quantize_rows_fp4(np64(x).astype(np.float32))
+    assert np.array_equal(codes.cpu().numpy(), O.pack_nibbles(oc))
+    assert np.array_equal(scales.cpu().numpy(), osc)
+
+
+def _unpack(packed_row):
+    p = np.asarray(packed_row, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2], out[..., 1::2] = p & 0xF, p >> 4
+    return out
+
+
+@pytest.mark.parametrize("bt,Tq,N,HI,dI,pos0,m,k", [
+    (2, 300, 2000, 64, 128, 4 * 2000 - 300, 4, 256),   # prefill route, ragged tail
+    (1, 77, 5000, 20, 64, 16000, 4, 100),             # dI 64, HI not a multiple of 32
+    (3, 5, 70000, 64, 128, 4 * 70000, 4, 1024),       # decode route, two-kernel top-k
+    (1, 2, 3000, 128, 128, 3000 * 4 - 2, 4, 2048),    # 128 heads, max k
+])
+def test_indexer_fp4(bt, Tq, N, HI, dI, pos0, m, k):
+    """FP4 scores and top-k against the oracle on its own quantisation. E2M1 dot products are exact,
+    so the selection is held to the same 1e-6 tie band as the bf16 path."""
+    say("indexer fp4", bt, Tq, N, HI, dI, pos0, m, k)
+    qI = gen(33, "i4.q", (bt, Tq, HI, dI))
+    KI = gen(33, "i4.k", (bt, N, dI))
+    wI = uniform_device(33, "i4.w", (bt, Tq, HI), DEV)
+    qc, qs = B.quantize_fp4(qI)
+    kc, ks = B.quantize_fp4(KI)
+    sc = B.indexer_scores_fp4(qc, qs, wI, kc, ks, pos0, m)
+    idx = B.indexer_topk_fp4(qc, qs, wI, kc, ks, pos0, m, k)
+    torch.cuda.synchronize()
+    sc, idx = sc.cpu().numpy(), idx.cpu().numpy()
+    rows = range(Tq) if Tq <= 80 else sorted(set(np.linspace(0, Tq - 1, 40).astype(int)) | {0, Tq - 1})
+    n_band = 0
+    for b in range(bt):
+        okc, oks = O.quantize_rows_fp4(np64(KI[b]).astype(np.float32))
+        assert np.array_equal(okc, _unpack(kc[b].cpu().numpy()))
+        for r in rows:
+            oqc, oqs = O.quantize_rows_fp4(np64(qI[b, r]).astype(np.float32))
+            I = O.indexer_scores_fp4(oqc[None], oqs[None], np64(wI[b, r:r + 1]), okc, oks, pos0 + r, m)[0]
+            V = O.visible(pos0 + r, m, N)
+            if V == 0:
+                continue
+            assert np.abs(sc[b, r, :V] - I[:V]).max() <= 1e-5 * np.abs(I[:V]).max(), (b, r)
+            n_band += check_topk_row(idx[b, r], I, V, k, what=f"b{b} r{r}")
+    say("  tie-band differences:", n_band)
+
+
+def test_indexer_fp4_decode_1m():
+    say("indexer fp4 decode 1M: batch 8, 262144 keys")
+    N, pos0 = 262144, 1 << 20
+    qI = gen(4, "i4d.q", (8, 1, 64, 128))
+    KI = gen(4, "i4d.k", (8, N, 128))
+    wI = uniform_device(4, "i4d.w", (8, 1, 64), DEV)
+    qc, qs = B.quantize_fp4(qI)
+    kc, ks = B.quantize_fp4(KI)
+    idx = B.indexer_topk_fp4(qc, qs, wI, kc, ks, pos0, 4, 1024)
+    ref = B.indexer_topk(qI, wI, KI, pos0, 4, 1024)   # the bf16 selection, for the overlap figure only
+    torch.cuda.synchronize()
+    idx, ref = idx.cpu().numpy(), ref.cpu().numpy()
+    overlap = []
+    for b in range(8):
+        okc, oks = O.quantize_rows_fp4(np64(KI[b]).astype(np.float32))
+        oqc, oqs = O.quantize_rows_fp4(np64(qI[b, 0]).astype(np.float32))
+        I = O.indexer_scores_fp4(oqc[None], oqs[None], np64(wI[b]), okc, oks, pos0, 4)[0]
+        check_topk_row(idx[b, 0], I, N, 1024, what=f"b{b}")
+        overlap.append(len(set(idx[b, 0].tolist()) & set(ref[b, 0].tolist())) / 1024)
+    say("  fp4 vs bf16 selection overlap per row:", [round(o, 3) for o in overlap])
+
+
 # ----------------------------------------------------------------------------- attention
 
 def _random_idx(bt, Tq, pos0, m, N, k, seed):
