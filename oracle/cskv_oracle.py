@@ -377,6 +377,44 @@ def indexer_scores_fp4(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: i
 
 
 # ---------------------------------------------------------------------------
+# FP8 KV storage ("Paper Breakdown: DeepSeek-V4", "Efficiency (§2.3.4)": V4
+# stores the KV cache as FP8 for the non-RoPE dims and BF16 for the RoPE dims).
+# Readings: the FP8 part is OCP E4M3 with one scale per entry; the scale is a
+# power of two, the smallest that keeps the entry's non-RoPE values within
+# +-448, so the stored values are exact multiples and dequantisation is exact.
+# ---------------------------------------------------------------------------
+
+def kv_scale_exponent(amax) -> np.ndarray:
+    """Smallest integer e with amax <= 448 * 2**e (0 where amax == 0)."""
+    a = np.asarray(amax, dtype=F64)
+    _, E = np.frexp(np.where(a > 0, a, 1.0))      # a = f * 2**E, f in [0.5, 1): a in [2**(E-1), 2**E)
+    e = E - 9                                      # a * 2**-e in [256, 512)
+    e = np.where(a * np.exp2(-e) > FP8_MAX, e + 1, e)
+    return np.where(a > 0, e, 0).astype(np.int64)
+
+
+def quantize_kv_fp8(x, rope_dims: int):
+    """One compressed entry (or a stack of them) to its FP8 + BF16 storage.
+
+    Returns (codes [..., d - rope_dims] uint8, rope [..., rope_dims] bf16
+    values as float64, scale [...] float64 powers of two).
+    """
+    x = np.asarray(x, dtype=F64)
+    nope = x.shape[-1] - rope_dims
+    xn = x[..., :nope]
+    e = kv_scale_exponent(np.max(np.abs(xn), axis=-1))
+    scale = np.exp2(e.astype(F64))
+    codes = e4m3_encode(xn * np.exp2(-e.astype(F64))[..., None])
+    return codes, round_bf16(x[..., nope:]), scale
+
+
+def dequantize_kv_fp8(codes, rope, scale) -> np.ndarray:
+    """Stored FP8 + BF16 entry back to its values: decode(codes) * scale, then the RoPE dims."""
+    v = e4m3_decode(codes) * np.asarray(scale, dtype=F64)[..., None]
+    return np.concatenate([v, np.asarray(rope, dtype=F64)], axis=-1)
+
+
+# ---------------------------------------------------------------------------
 # Core MQA attention over compressed entries + sliding window + sink
 # ("Paper Breakdown: DeepSeek-V4", CSA §2.3.1, HCA §2.3.2, §2.3.3)
 # ---------------------------------------------------------------------------

@@ -450,6 +450,37 @@ def test_indexer_fp4_reduces_to_plain_indexer():
                        O.indexer_scores(q, w, k, pos0=80, m=4) * ks[None, :], rtol=1e-13, atol=0)
 
 
+# ---------------------------------------------------------------- FP8 + BF16 KV storage
+
+def test_kv_scale_exponent_is_the_smallest_that_fits():
+    a = np.concatenate([rng.uniform(0, 1, 2000) * np.exp2(rng.integers(-40, 40, 2000)),
+                        448 * np.exp2(np.arange(-10, 10)), 448 * np.exp2(np.arange(-10, 10)) * (1 + 2.0 ** -20)])
+    e = O.kv_scale_exponent(a)
+    assert (a <= 448 * np.exp2(e.astype(float))).all()            # fits
+    assert (a > 448 * np.exp2(e.astype(float) - 1)).all()         # and one power lower does not
+    assert O.kv_scale_exponent(0.0) == 0
+
+
+def test_kv_fp8_roundtrip_and_errors():
+    d, r = 512, 64
+    x = O.round_bf16(rng.standard_normal((50, d)) * rng.uniform(0.01, 100, (50, 1)))
+    x[7] = 0.0
+    codes, rope, scale = O.quantize_kv_fp8(x, r)
+    assert codes.shape == (50, d - r) and rope.shape == (50, r)
+    assert np.array_equal(np.log2(scale), np.round(np.log2(scale)))   # powers of two
+    back = O.dequantize_kv_fp8(codes, rope, scale)
+    assert np.array_equal(back[:, d - r:], x[:, d - r:])              # RoPE dims kept exactly (bf16 input)
+    err = np.abs(back[:, : d - r] - x[:, : d - r])
+    # half an E4M3 step: 1/16 relative for normals, 2**-10 * scale in the subnormal range
+    assert (err <= np.abs(x[:, : d - r]) / 16 + scale[:, None] * 2.0 ** -10).all()
+    assert (codes[7] == 0).all() and scale[7] == 1.0
+    # values already on the grid come back exactly
+    grid = O.e4m3_decode(rng.integers(0, 126, (5, d - r))) * np.exp2(rng.integers(-5, 5, (5, 1)))
+    g = np.concatenate([grid, np.zeros((5, r))], axis=1)
+    c2, r2, s2 = O.quantize_kv_fp8(g, r)
+    assert np.array_equal(O.dequantize_kv_fp8(c2, r2, s2), g)
+
+
 def test_page_constants_fixture():
     with open(os.path.join(GOLDEN, "page_constants.json")) as f:
         g = json.load(f)
