@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     quantize_fp4,
     indexer_scores_fp4,
     indexer_topk_fp4,
+    quantize_kv_fp8,
     compressed_attn_prefill,
     compressed_attn_decode,
 )

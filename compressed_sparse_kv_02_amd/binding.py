@@ -23,6 +23,7 @@ EXPORTS = ("cskv_version", "cskv_status_string", "csa_compress", "hca_compress",
            "cskv_indexer_workspace_size", "indexer_topk", "indexer_scores", "topk_select",
            "cskv_topk_workspace_size", "cskv_quantize_fp8", "indexer_scores_fp8", "indexer_topk_fp8",
            "cskv_quantize_fp4", "indexer_scores_fp4", "indexer_topk_fp4",
+           "cskv_quantize_kv_fp8", "compressed_attn_prefill_kv8", "compressed_attn_decode_kv8",
            "compressed_attn_prefill",
            "cskv_decode_workspace_size", "compressed_attn_decode")
 
@@ -46,6 +47,11 @@ _SIGS = {
     "cskv_quantize_fp4": (_I, [_P, _L, _I, _I, _P, _P, _P]),
     "indexer_scores_fp4": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _P, _L, _P]),
     "indexer_topk_fp4": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _I, _P, _P, _Z, _P]),
+    "cskv_quantize_kv_fp8": (_I, [_P, _I, _L, _I, _I, _I, _P, _P, _L, _P]),
+    "compressed_attn_prefill_kv8": (_I, [_I, _P, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
+                                         _I, _P, _F, _I, _F, _F, _I, _P, _P, _P]),
+    "compressed_attn_decode_kv8": (_I, [_I, _P, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
+                                        _I, _P, _F, _I, _F, _F, _I, _I, _P, _Z, _P, _P, _P]),
     "compressed_attn_prefill": (_I, [_I, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
                                      _I, _P, _F, _I, _F, _F, _I, _P, _P, _I, _P]),
     "cskv_decode_workspace_size": (_Z, [_I, _L, _I, _I, _I]),
@@ -273,6 +279,28 @@ def indexer_topk_fp4(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int
     return _topk_lowp(FP4, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, k, out, workspace)
 
 
+def kv_fp8_row_bytes(d: int, rope_dims: int) -> int:
+    return d - rope_dims + 2 * rope_dims
+
+
+def quantize_kv_fp8(x, rope_dims: int, out=None, scales=None, out_row0: int = 0):
+    """FP8 (non-RoPE dims) + BF16 (RoPE dims) storage of entries x [batch, n, d] (bf16 or fp32).
+
+    Returns (rows [batch, cap, row bytes] uint8, scales [batch, cap] fp32); `out` / `scales` /
+    `out_row0` append in place into a cache of capacity cap.
+    """
+    batch, n, d = x.shape
+    rb = kv_fp8_row_bytes(d, rope_dims)
+    if out is None:
+        out = torch.empty(batch, n, rb, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(batch, n, dtype=torch.float32, device=x.device)
+    cap = out.shape[1]
+    _check("cskv_quantize_kv_fp8", lib().cskv_quantize_kv_fp8(
+        _ptr(x), batch, n, d, rope_dims, _dtype(x), out.data_ptr() + out_row0 * rb,
+        scales.data_ptr() + out_row0 * 4, cap, _stream(x)))
+    return out, scales
+
+
 def _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_norm, q_norm_w, eps,
                  rope_dims, rope_base, scale, rope_on_output, out, lse, return_lse):
     batch, Tq, H, d = q.shape
@@ -294,13 +322,20 @@ def compressed_attn_prefill(mode: int, q, kv, idx, win, win_pos0: int, sink, pos
                             w: int, k: int = 0, apply_q_norm: bool = True, q_norm_w=None,
                             eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 10000.0,
                             scale: float = 0.0, rope_on_output: bool = True, out=None, lse=None,
-                            return_lse: bool = False):
-    """CSA / HCA attention for a chunk of queries: out [batch, Tq, H, d] (and lse [batch, Tq, H])."""
+                            return_lse: bool = False, kv_scale=None):
+    """CSA / HCA attention for a chunk of queries: out [batch, Tq, H, d] (and lse [batch, Tq, H]).
+
+    With kv_scale, kv is an FP8 KV cache written by quantize_kv_fp8 ([batch, N, row bytes] uint8).
+    """
     args, out, lse = _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_norm,
                                   q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output, out, lse,
                                   return_lse)
-    _check("compressed_attn_prefill", lib().compressed_attn_prefill(
-        *args, _ptr(out), _ptr(lse), _dtype(q), _stream(q)))
+    if kv_scale is not None:  # FP8 KV storage: kv holds the stored entries (uint8 rows)
+        _check("compressed_attn_prefill_kv8", lib().compressed_attn_prefill_kv8(
+            *args[:3], _ptr(kv_scale), *args[3:], _ptr(out), _ptr(lse), _stream(q)))
+    else:
+        _check("compressed_attn_prefill", lib().compressed_attn_prefill(
+            *args, _ptr(out), _ptr(lse), _dtype(q), _stream(q)))
     return (out, lse) if return_lse else out
 
 
@@ -312,7 +347,7 @@ def compressed_attn_decode(mode: int, q, kv, idx, win, win_pos0: int, sink, pos0
                            w: int, k: int = 0, apply_q_norm: bool = True, q_norm_w=None,
                            eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 10000.0,
                            scale: float = 0.0, rope_on_output: bool = True, n_splits: int = 0,
-                           workspace=None, out=None, lse=None, return_lse: bool = False):
+                           workspace=None, out=None, lse=None, return_lse: bool = False, kv_scale=None):
     """Split-K attention of a few new tokens against a long cache (same result as prefill)."""
     args, out, lse = _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_norm,
                                   q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output, out, lse,
@@ -321,6 +356,11 @@ def compressed_attn_decode(mode: int, q, kv, idx, win, win_pos0: int, sink, pos0
     need = decode_workspace_bytes(batch, Tq, H, d, n_splits)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _check("compressed_attn_decode", lib().compressed_attn_decode(
-        *args, n_splits, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _dtype(q), _stream(q)))
+    if kv_scale is not None:
+        _check("compressed_attn_decode_kv8", lib().compressed_attn_decode_kv8(
+            *args[:3], _ptr(kv_scale), *args[3:], n_splits, _ptr(workspace), workspace.numel(), _ptr(out),
+            _ptr(lse), _stream(q)))
+    else:
+        _check("compressed_attn_decode", lib().compressed_attn_decode(
+            *args, n_splits, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _dtype(q), _stream(q)))
     return (out, lse) if return_lse else out

@@ -45,6 +45,7 @@ struct AttnArgs {
   const void* win;
   const float* sink;
   const float* q_norm_w;
+  const float* kv_scale;  // FP8 KV storage: [batch][N] power-of-two scale of each entry
   void* out;
   float* lse;
   float* part_o;   // [batch*Tq][splits][H][D]
@@ -132,7 +133,11 @@ __device__ __forceinline__ int key_of_row(int r) {
 // much (log2 units): the O/l rescale is then almost never needed, and P <= 2^8.
 constexpr float REF_SLACK = 8.0f;
 
-template <int D, int HW, int QG>
+// KV8: compressed entries stored as FP8 E4M3 codes of the first D - rope_dims dims (one
+// power-of-two scale per entry) followed by the RoPE dims in bf16; the loader widens them
+// to bf16 rows in LDS (exact: E4M3 times a power of two is a bf16 value), so the rest of
+// the kernel is unchanged. Window rows stay bf16.
+template <int D, int HW, int QG, bool KV8>
 __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
   constexpr int NW = HW * QG;
   constexpr int NT = NW * 64;
@@ -241,6 +246,9 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
   // ---- gather loader: thread -> (key row kr, chunks c0 + TPK*i)
   const int kr = tid / TPK, c0 = tid % TPK;
   const uint16_t* kvb = (const uint16_t*)a.kv + (int64_t)b * a.N * D;
+  const int nope8 = (D - a.rope_dims) / 8;            // KV8: 16-byte LDS chunks that hold FP8 codes
+  const int64_t rb8 = (D - a.rope_dims) + 2 * a.rope_dims;  // KV8: bytes per stored entry
+  const uint8_t* kv8b = (const uint8_t*)a.kv + (int64_t)b * a.N * rb8;
   const int64_t wbase = (int64_t)b * a.W;
   const int64_t wr_lo = win_row_of(a, lo);  // window row of position lo; rows wrap at W
   // per-query bounds of the tile's queries, for the loader's validity bits
@@ -252,16 +260,23 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
   }
   u32x4 pre[CPT];
   int pre_ok = 0;
+  float pre_sc = 0.f;   // KV8: scale of the entry in flight (0: not an FP8 entry)
   // Loader thread: key u = blk*32 + kr of the key list goes to LDS row kr; its validity
   // bits (bit q: query q of the tile may attend to it) go to the logical slot of row kr.
   auto gload = [&](int64_t blk) {
     const int64_t u = blk * 32 + kr;
     const uint16_t* src = nullptr;
+    const uint8_t* src8 = nullptr;
     int ok = 0;
     if (u < n_comp) {
       const int64_t s_ = csa ? (int64_t)idx_s[u] : u;
       if (s_ >= 0 && s_ < a.N) {
-        src = kvb + s_ * D;
+        if constexpr (KV8) {
+          src8 = kv8b + s_ * rb8;
+          pre_sc = a.kv_scale[(int64_t)b * a.N + s_];
+        } else {
+          src = kvb + s_ * D;
+        }
 #pragma unroll
         for (int q = 0; q < QG; ++q) ok |= (csa || s_ < vis_q[q]) ? (1 << q) : 0;
       }
@@ -273,17 +288,39 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int q = 0; q < QG; ++q) ok |= (pos >= t_q[q] - a.w + 1 && pos <= t_q[q]) ? (1 << q) : 0;
     }
+    if (KV8 && !src8) pre_sc = 0.f;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
+      const int oc = c0 + TPK * i;  // 16-byte chunk of the bf16 row: dims 8*oc .. +8
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (src) v = *reinterpret_cast<const u32x4*>(src + (c0 + TPK * i) * 8);
+      if (KV8 && src8) {
+        if (oc < nope8) {
+          const uint2 c = *reinterpret_cast<const uint2*>(src8 + 8 * oc);  // 8 E4M3 codes
+          v = u32x4{c.x, c.y, 0u, 0u};
+        } else {
+          v = *reinterpret_cast<const u32x4*>(src8 + (D - a.rope_dims) + 16 * (oc - nope8));
+        }
+      } else if (src) {
+        v = *reinterpret_cast<const u32x4*>(src + oc * 8);
+      }
       pre[i] = v;
     }
     pre_ok = ok;
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) *reinterpret_cast<u32x4*>(&kt[buf][kr * ROWE + (c0 + TPK * i) * 8]) = pre[i];
+    for (int i = 0; i < CPT; ++i) {
+      const int oc = c0 + TPK * i;
+      u32x4 v = pre[i];
+      if (KV8 && pre_sc != 0.f && oc < nope8) {  // widen 8 codes to bf16 (times the power-of-two scale)
+        const uint32_t c01 = v.x, c23 = v.y;
+        v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c01, pre_sc, false));
+        v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c01, pre_sc, true));
+        v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c23, pre_sc, false));
+        v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c23, pre_sc, true));
+      }
+      *reinterpret_cast<u32x4*>(&kt[buf][kr * ROWE + oc * 8]) = v;
+    }
     if (c0 == 0) kvq[buf][key_of_row(kr)] = pre_ok;
   };
 
@@ -572,7 +609,10 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
 // ---------------------------------------------------------------------------- host
 template <int D, int HW, int QG>
 static void launch_attn(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((attn_mfma<D, HW, QG>), grid, dim3(HW * QG * 64), 0, st, a);
+  if (a.kv_scale)
+    hipLaunchKernelGGL((attn_mfma<D, HW, QG, true>), grid, dim3(HW * QG * 64), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_mfma<D, HW, QG, false>), grid, dim3(HW * QG * 64), 0, st, a);
 }
 
 // Workgroup shape: HW waves of 16 heads per query; QG queries share one key stream
@@ -651,6 +691,14 @@ static int validate_attn(int mode, const void* q, const void* kv, const int32_t*
   return CSKV_OK;
 }
 
+// FP8 KV storage: bf16 path only; whole 16-byte chunks of codes and of RoPE dims.
+static int validate_kv8(const float* kv_scale, int64_t N, int d, int rope_dims, int dtype) {
+  if (dtype != CSKV_BF16) return CSKV_ERR_BAD_DTYPE;
+  if ((d - rope_dims) % 16 != 0 || rope_dims % 8 != 0) return CSKV_ERR_BAD_SHAPE;
+  if (N > 0 && !aligned16(kv_scale)) return CSKV_ERR_MISALIGNED;
+  return CSKV_OK;
+}
+
 static AttnArgs make_args(int mode, const void* q, const void* kv, const int32_t* idx, const void* win,
                           int64_t win_pos0, int64_t W, const float* sink, int64_t Tq, int64_t N,
                           int64_t pos0, int m, int k, int w, int H, int d, int apply_q_norm,
@@ -684,6 +732,25 @@ static int64_t max_keys(int mode, int64_t Tq, int64_t N, int64_t pos0, int m, in
 
 using namespace cskv;
 
+static int attn_prefill_impl(int mode, const void* q, const void* kv, const float* kv_scale, const int32_t* idx,
+                             const void* win, int64_t win_pos0, int64_t W, const float* sink, int batch,
+                             int64_t Tq, int64_t N, int64_t pos0, int m, int k, int w, int H, int d,
+                             int apply_q_norm, const float* q_norm_w, float eps, int rope_dims, float rope_base,
+                             float scale, int rope_on_output, void* out, float* lse, int dtype, void* stream) {
+  int st = validate_attn(mode, q, kv, idx, win, win_pos0, W, sink, batch, Tq, N, pos0, m, k, w, H, d,
+                         apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale, out, lse, dtype);
+  if (!st && kv_scale) st = validate_kv8(kv_scale, N, d, rope_dims, dtype);
+  if (st || batch == 0 || Tq == 0) return st;
+  AttnArgs a = make_args(mode, q, kv, idx, win, win_pos0, W, sink, Tq, N, pos0, m, k, w, H, d,
+                         apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output,
+                         out, lse);
+  a.kv_scale = kv_scale;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == CSKV_F32) return launch_f32(a, batch, s);
+  if (!dispatch_attn(a, batch, s)) return CSKV_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+}
+
 extern "C" int compressed_attn_prefill(int mode, const void* q, const void* kv, const int32_t* idx,
                                        const void* win, int64_t win_pos0, int64_t W,
                                        const float* sink, int batch, int64_t Tq, int64_t N,
@@ -692,16 +759,21 @@ extern "C" int compressed_attn_prefill(int mode, const void* q, const void* kv, 
                                        int rope_dims, float rope_base, float scale,
                                        int rope_on_output, void* out, float* lse, int dtype,
                                        void* stream) {
-  int st = validate_attn(mode, q, kv, idx, win, win_pos0, W, sink, batch, Tq, N, pos0, m, k, w, H, d,
-                         apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale, out, lse, dtype);
-  if (st || batch == 0 || Tq == 0) return st;
-  AttnArgs a = make_args(mode, q, kv, idx, win, win_pos0, W, sink, Tq, N, pos0, m, k, w, H, d,
-                         apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output,
-                         out, lse);
-  hipStream_t s = (hipStream_t)stream;
-  if (dtype == CSKV_F32) return launch_f32(a, batch, s);
-  if (!dispatch_attn(a, batch, s)) return CSKV_ERR_UNSUPPORTED;
-  return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+  return attn_prefill_impl(mode, q, kv, nullptr, idx, win, win_pos0, W, sink, batch, Tq, N, pos0, m, k, w, H, d,
+                           apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output, out, lse,
+                           dtype, stream);
+}
+
+extern "C" int compressed_attn_prefill_kv8(int mode, const void* q, const uint8_t* kv, const float* kv_scale,
+                                           const int32_t* idx, const void* win, int64_t win_pos0, int64_t W,
+                                           const float* sink, int batch, int64_t Tq, int64_t N, int64_t pos0,
+                                           int m, int k, int w, int H, int d, int apply_q_norm,
+                                           const float* q_norm_w, float eps, int rope_dims, float rope_base,
+                                           float scale, int rope_on_output, void* out, float* lse, void* stream) {
+  if (N > 0 && !kv_scale) return CSKV_ERR_INVALID_ARG;
+  return attn_prefill_impl(mode, q, kv, N > 0 ? kv_scale : nullptr, idx, win, win_pos0, W, sink, batch, Tq, N,
+                           pos0, m, k, w, H, d, apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale,
+                           rope_on_output, out, lse, CSKV_BF16, stream);
 }
 
 // Splits per query: about one workgroup per compute unit (256) over the whole call, at
@@ -724,23 +796,22 @@ extern "C" size_t cskv_decode_workspace_size(int batch, int64_t Tq, int H, int d
   return (size_t)batch * Tq * s * H * ((size_t)d + 2) * 4 + 256;
 }
 
-extern "C" int compressed_attn_decode(int mode, const void* q, const void* kv, const int32_t* idx,
-                                      const void* win, int64_t win_pos0, int64_t W,
-                                      const float* sink, int batch, int64_t Tq, int64_t N,
-                                      int64_t pos0, int m, int k, int w, int H, int d,
-                                      int apply_q_norm, const float* q_norm_w, float eps,
-                                      int rope_dims, float rope_base, float scale,
-                                      int rope_on_output, int n_splits, void* workspace,
-                                      size_t ws_bytes, void* out, float* lse, int dtype,
-                                      void* stream) {
+static int attn_decode_impl(int mode, const void* q, const void* kv, const float* kv_scale, const int32_t* idx,
+                            const void* win, int64_t win_pos0, int64_t W, const float* sink, int batch,
+                            int64_t Tq, int64_t N, int64_t pos0, int m, int k, int w, int H, int d,
+                            int apply_q_norm, const float* q_norm_w, float eps, int rope_dims, float rope_base,
+                            float scale, int rope_on_output, int n_splits, void* workspace, size_t ws_bytes,
+                            void* out, float* lse, int dtype, void* stream) {
   int st = validate_attn(mode, q, kv, idx, win, win_pos0, W, sink, batch, Tq, N, pos0, m, k, w, H, d,
                          apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale, out, lse, dtype);
+  if (!st && kv_scale) st = validate_kv8(kv_scale, N, d, rope_dims, dtype);
   if (st) return st;
   if (n_splits < 0 || n_splits > 256) return CSKV_ERR_BAD_SHAPE;
   if (batch == 0 || Tq == 0) return CSKV_OK;
   AttnArgs a = make_args(mode, q, kv, idx, win, win_pos0, W, sink, Tq, N, pos0, m, k, w, H, d,
                          apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output,
                          out, lse);
+  a.kv_scale = kv_scale;
   hipStream_t s = (hipStream_t)stream;
   if (dtype == CSKV_F32) return launch_f32(a, batch, s);
   const int S = decode_splits(batch, Tq, max_keys(mode, Tq, N, pos0, m, k, w), n_splits);
@@ -758,4 +829,31 @@ extern "C" int compressed_attn_decode(int mode, const void* q, const void* kv, c
   if (hipGetLastError() != hipSuccess) return CSKV_ERR_HIP;
   hipLaunchKernelGGL((attn_merge<bf16>), dim3((unsigned)(batch * Tq), (unsigned)H), dim3(256), 0, s, a);
   return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+}
+
+extern "C" int compressed_attn_decode(int mode, const void* q, const void* kv, const int32_t* idx,
+                                      const void* win, int64_t win_pos0, int64_t W,
+                                      const float* sink, int batch, int64_t Tq, int64_t N,
+                                      int64_t pos0, int m, int k, int w, int H, int d,
+                                      int apply_q_norm, const float* q_norm_w, float eps,
+                                      int rope_dims, float rope_base, float scale,
+                                      int rope_on_output, int n_splits, void* workspace,
+                                      size_t ws_bytes, void* out, float* lse, int dtype,
+                                      void* stream) {
+  return attn_decode_impl(mode, q, kv, nullptr, idx, win, win_pos0, W, sink, batch, Tq, N, pos0, m, k, w, H, d,
+                          apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output, n_splits,
+                          workspace, ws_bytes, out, lse, dtype, stream);
+}
+
+extern "C" int compressed_attn_decode_kv8(int mode, const void* q, const uint8_t* kv, const float* kv_scale,
+                                          const int32_t* idx, const void* win, int64_t win_pos0, int64_t W,
+                                          const float* sink, int batch, int64_t Tq, int64_t N, int64_t pos0,
+                                          int m, int k, int w, int H, int d, int apply_q_norm,
+                                          const float* q_norm_w, float eps, int rope_dims, float rope_base,
+                                          float scale, int rope_on_output, int n_splits, void* workspace,
+                                          size_t ws_bytes, void* out, float* lse, void* stream) {
+  if (N > 0 && !kv_scale) return CSKV_ERR_INVALID_ARG;
+  return attn_decode_impl(mode, q, kv, N > 0 ? kv_scale : nullptr, idx, win, win_pos0, W, sink, batch, Tq, N,
+                          pos0, m, k, w, H, d, apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale,
+                          rope_on_output, n_splits, workspace, ws_bytes, out, lse, CSKV_BF16, stream);
 }

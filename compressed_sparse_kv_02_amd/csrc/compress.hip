@@ -192,6 +192,65 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   }
 }
 
+// FP8 KV storage of compressed entries ("Paper Breakdown: DeepSeek-V4", §2.3.4
+// "Efficiency": FP8 for the non-RoPE dims, BF16 for the RoPE dims). One wave per
+// entry: the first d - rope dims become E4M3 codes of x * 2^-e, e the smallest
+// integer with max |x| <= 448 * 2^e (exact scaling), the RoPE dims are kept as
+// bf16, and 2^e is the entry's scale.
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_kv_fp8_kernel(const T* x, int64_t n, int d, int rope,
+                                                             uint8_t* out, float* scales, int64_t out_ld) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (r >= n) return;
+  const T* xr = x + ((int64_t)b * n + r) * d;
+  const int nope = d - rope, nch = d / 8;
+  float v[2][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = lane + 64 * q;
+    if (c < nch) {
+      load_vec<T, 8>(xr + 8 * c, v[q]);
+      if (8 * c < nope)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[q][i]));
+    }
+  }
+  amax = wave_max(amax);
+  int e = 0;
+  if (amax > 0.f) {
+    int E;
+    frexpf(amax, &E);  // amax in [2^(E-1), 2^E)
+    e = E - 9;         // amax * 2^-e in [256, 512)
+    if (ldexpf(amax, -e) > 448.f) e += 1;
+  }
+  uint8_t* orow = out + ((int64_t)b * out_ld + r) * (nope + 2 * rope);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = lane + 64 * q;
+    if (c >= nch) continue;
+    if (8 * c < nope) {
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w0 |= e4m3_code(ldexpf(v[q][i], -e)) << (8 * i);
+        w1 |= e4m3_code(ldexpf(v[q][4 + i], -e)) << (8 * i);
+      }
+      *reinterpret_cast<uint2*>(orow + 8 * c) = make_uint2(w0, w1);
+    } else {
+      uint4 o;
+      o.x = pack_bf16x2(v[q][0], v[q][1]);
+      o.y = pack_bf16x2(v[q][2], v[q][3]);
+      o.z = pack_bf16x2(v[q][4], v[q][5]);
+      o.w = pack_bf16x2(v[q][6], v[q][7]);
+      *reinterpret_cast<uint4*>(orow + nope + 2 * (8 * c - nope)) = o;
+    }
+  }
+  if (lane == 0) scales[(int64_t)b * out_ld + r] = ldexpf(1.f, e);
+}
+
 static int launch_compress(CompressArgs& a, int batch, int dtype, hipStream_t st) {
   if (a.n_out == 0 || batch == 0) return CSKV_OK;
   const int VEC = dtype == CSKV_BF16 ? 8 : 4;
@@ -269,4 +328,26 @@ extern "C" int hca_compress(const void* C, const void* Z, const void* B, int bat
   a.T = T; a.pos0 = pos0; a.out_ld = out_ld; a.c = c; a.m = m; a.n_out = (int)n_out; a.csa = 0;
   a.apply_norm = apply_norm; a.rope_dims = rope_dims; a.eps = eps; a.rope_base = rope_base;
   return launch_compress(a, batch, dtype, (hipStream_t)stream);
+}
+
+extern "C" int cskv_quantize_kv_fp8(const void* x, int batch, int64_t n, int d, int rope_dims, int dtype,
+                                    uint8_t* out, float* scales, int64_t out_ld, void* stream) {
+  if (dtype != CSKV_BF16 && dtype != CSKV_F32) return CSKV_ERR_BAD_DTYPE;
+  if (batch < 0 || n < 0 || d < 16 || d > CSKV_MAX_DIM || rope_dims < 0 || rope_dims > d) return CSKV_ERR_BAD_SHAPE;
+  if ((d - rope_dims) % 16 != 0 || rope_dims % 8 != 0) return CSKV_ERR_BAD_SHAPE;
+  if (out_ld == 0) out_ld = n;
+  if (out_ld < n || ceil_div(n, (int64_t)4) > 0x7fffffff) return CSKV_ERR_BAD_SHAPE;
+  if (batch == 0 || n == 0) return CSKV_OK;
+  if (!x || !out || !scales) return CSKV_ERR_INVALID_ARG;
+  if (!aligned16(x, out)) return CSKV_ERR_MISALIGNED;
+  if (((uintptr_t)scales) % 4 != 0) return CSKV_ERR_MISALIGNED;
+  dim3 grid((unsigned)ceil_div(n, (int64_t)4), (unsigned)batch);
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == CSKV_BF16)
+    hipLaunchKernelGGL(quantize_kv_fp8_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)x, n, d, rope_dims, out,
+                       scales, out_ld);
+  else
+    hipLaunchKernelGGL(quantize_kv_fp8_kernel<float>, grid, dim3(256), 0, st, (const float*)x, n, d, rope_dims, out,
+                       scales, out_ld);
+  return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
 }

@@ -140,6 +140,22 @@ __device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, int rope_dims, 
   sincosf((float)a, s, c);
 }
 
+// E4M3 code of y: nearest value, ties to the even code, saturating at +-448;
+// the sign bit is set for negative y (and -0.0).
+__device__ __forceinline__ uint32_t e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.f);
+  uint32_t c;
+  if (a < 0.015625f) {
+    c = (uint32_t)rintf(a * 512.f);  // subnormal steps of 2^-9 (8 is the smallest normal)
+  } else {
+    uint32_t u = __float_as_uint(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);  // round the fp32 mantissa to 3 bits, ties to even
+    c = (u >> 20) - (120u << 3);       // exponent bias 127 -> 7
+  }
+  return sign | c;
+}
+
 // Order-preserving map of an fp32 score to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t score_key(float f) {
   uint32_t u = __float_as_uint(f);

@@ -40,22 +40,6 @@ struct LowP {
   static constexpr int OB = 32 * BITS / 8;  // operand bytes per lane per k-step (32 values)
 };
 
-// E4M3 code of y: nearest value, ties to the even code, saturating at +-448;
-// the sign bit is set for negative y (and -0.0).
-__device__ __forceinline__ uint32_t e4m3_code(float y) {
-  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
-  const float a = fminf(fabsf(y), 448.f);
-  uint32_t c;
-  if (a < 0.015625f) {
-    c = (uint32_t)rintf(a * 512.f);  // subnormal steps of 2^-9 (8 is the smallest normal)
-  } else {
-    uint32_t u = __float_as_uint(a);
-    u += 0x7FFFFu + ((u >> 20) & 1u);  // round the fp32 mantissa to 3 bits, ties to even
-    c = (u >> 20) - (120u << 3);       // exponent bias 127 -> 7
-  }
-  return sign | c;
-}
-
 // One wave per row (4 rows per workgroup); dim % 4 == 0, dim <= 1024.
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_fp8_kernel(const T* x, int64_t rows, int dim, uint8_t* codes,

@@ -303,6 +303,39 @@ int compressed_attn_decode(int mode, const void* q, const void* kv, const int32_
                            int n_splits, void* workspace, size_t ws_bytes, void* out, float* lse,
                            int dtype, void* stream);
 
+/*
+ * FP8 KV storage [PB §2.3.4 "Efficiency": KV storage FP8 for the non-RoPE
+ * dims, BF16 for the RoPE dims]. A stored entry is the E4M3 codes of its
+ * first d - rope_dims values (x * 2^-e, e the smallest integer with
+ * max |x| <= 448 * 2^e, nearest code, ties to even) followed by its last
+ * rope_dims values in bf16: d - rope_dims + 2 * rope_dims bytes, plus one fp32
+ * scale 2^e. (d - rope_dims) % 16 == 0 and rope_dims % 8 == 0.
+ *
+ * cskv_quantize_kv_fp8 -- x [batch, n, d] (bf16 or f32) to out [batch,
+ *   out_ld, row bytes] and scales [batch, out_ld] fp32 (out_ld = 0: n); pass
+ *   pointers offset to row r0 to append to a cache. scales 4-byte aligned.
+ * compressed_attn_prefill_kv8 / compressed_attn_decode_kv8 -- the attention
+ *   entry points with kv such a cache ([batch, N, row bytes]) and kv_scale
+ *   [batch, N]; q, win and out are bf16. The loader widens each entry to
+ *   bf16 exactly (E4M3 times a power of two is a bf16 value), so the result
+ *   is the bf16 attention over the dequantised entries.
+ */
+int cskv_quantize_kv_fp8(const void* x, int batch, int64_t n, int d, int rope_dims, int dtype, uint8_t* out,
+                         float* scales, int64_t out_ld, void* stream);
+int compressed_attn_prefill_kv8(int mode, const void* q, const uint8_t* kv, const float* kv_scale,
+                                const int32_t* idx, const void* win, int64_t win_pos0, int64_t W,
+                                const float* sink, int batch, int64_t Tq, int64_t N, int64_t pos0, int m,
+                                int k, int w, int H, int d, int apply_q_norm, const float* q_norm_w,
+                                float eps, int rope_dims, float rope_base, float scale, int rope_on_output,
+                                void* out, float* lse, void* stream);
+int compressed_attn_decode_kv8(int mode, const void* q, const uint8_t* kv, const float* kv_scale,
+                               const int32_t* idx, const void* win, int64_t win_pos0, int64_t W,
+                               const float* sink, int batch, int64_t Tq, int64_t N, int64_t pos0, int m,
+                               int k, int w, int H, int d, int apply_q_norm, const float* q_norm_w,
+                               float eps, int rope_dims, float rope_base, float scale, int rope_on_output,
+                               int n_splits, void* workspace, size_t ws_bytes, void* out, float* lse,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(L, n), n
     from compressed_sparse_kv_02_amd import binding
@@ -184,6 +184,28 @@ def test_fp8_indexer_validation(L):
     a.update(ws=None)
     assert L.indexer_topk_fp4(*a.values()) == WS
     assert L.cskv_indexer_workspace_size(1, 64, 1000, 64, 1024, 3) >= 64 * 1000 * 4
+
+
+def test_kv8_validation(L):
+    q = L.cskv_quantize_kv_fp8
+    assert q(P, 1, 4, 512, 64, 2, P, P, 0, None) == DTYPE
+    assert q(P, 1, 4, 512, 60, 0, P, P, 0, None) == SHAPE     # rope dims not a multiple of 8
+    assert q(P, 1, 4, 520, 64, 0, P, P, 0, None) == SHAPE     # non-RoPE dims not a multiple of 16
+    assert q(P, 1, 4, 512, 64, 0, P, P, 3, None) == SHAPE     # out_ld < n
+    assert q(P, 1, 4, 512, 64, 0, None, P, 0, None) == INVALID
+    assert q(P, 1, 0, 512, 64, 0, P, P, 0, None) == OK
+    f = L.compressed_attn_prefill_kv8
+    base = dict(mode=0, q=P, kv=P, ks=P, idx=P, win=P, wp0=0, W=64, sink=None, batch=1, Tq=64, N=16,
+                pos0=0, m=4, k=16, w=16, H=64, d=512, qn=1, qnw=None, eps=1e-6, rd=64, rb=1e4,
+                scale=0.0, roo=1, out=P, lse=None, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*a.values())
+    assert call(ks=None) == INVALID
+    assert call(rd=60) == SHAPE
+    assert call(ks=P + 4) == MISALIGNED
+    assert call(Tq=0) == OK
 
 
 def test_attention_validation(L):

@@ -383,6 +383,62 @@ def test_attention_prefill(dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, ro
         assert err <= ATOL[dtype] and lerr <= ATOL[dtype] * 5
 
 
+# ----------------------------------------------------------------------------- FP8 KV storage
+
+@pytest.mark.parametrize("dtype,bt,n,d,rope", [("bf16", 2, 37, 512, 64), ("f32", 1, 20, 128, 32),
+                                               ("bf16", 1, 9, 256, 0)])
+def test_quantize_kv_fp8(dtype, bt, n, d, rope):
+    say("quantize_kv_fp8", dtype, bt, n, d, rope)
+    x = gen(75, "kv8.x", (bt, n, d), dtype) * torch.logspace(-3, 3, n, device=DEV)[None, :, None].to(TD[dtype])
+    x[0, 1] = 0.0
+    rows, sc = B.quantize_kv_fp8(x, rope)
+    torch.cuda.synchronize()
+    rows, sc = rows.cpu(), sc.cpu().numpy()
+    for b in range(bt):
+        codes, rp, osc = O.quantize_kv_fp8(np64(x[b]), rope)
+        assert np.array_equal(rows[b, :, : d - rope].numpy(), codes)
+        gpu_rope = rows[b, :, d - rope:].contiguous().view(torch.bfloat16).float().numpy().astype(np.float64)
+        assert np.array_equal(gpu_rope, rp)
+        assert np.array_equal(sc[b].astype(np.float64), osc)
+
+
+def _kv8_oracle(kv_raw_b, rope):
+    codes, rp, osc = O.quantize_kv_fp8(np64(kv_raw_b), rope)
+    return O.dequantize_kv_fp8(codes, rp, osc)
+
+
+@pytest.mark.parametrize("mode,bt,Tq,N,pos0,m,k,w,H,d,rope", [
+    ("csa", 1, 33, 3000, 4 * 2900, 4, 1024, 128, 64, 512, 64),
+    ("hca", 2, 40, 200, 128 * 180, 128, 0, 128, 32, 512, 64),
+    ("csa", 2, 50, 64, 0, 4, 24, 16, 16, 64, 16),
+])
+def test_attention_kv8_prefill_and_decode(mode, bt, Tq, N, pos0, m, k, w, H, d, rope):
+    """Attention over an FP8 + BF16 KV cache equals the oracle's attention over its own
+    dequantisation of the same entries (prefill, and decode of the last query row)."""
+    say("attention kv8", mode, bt, Tq, N, pos0, m, k, w, H, d, rope)
+    q = gen(37, "a8.q", (bt, Tq, H, d))
+    kv = gen(37, "a8.kv", (bt, N, d))
+    wp0 = max(0, pos0 - w + 1)
+    win = gen(37, "a8.win", (bt, pos0 + Tq - wp0, d))
+    sk = normal_device(37, "a8.sink", (H,), 1.0, "f32", DEV)
+    idx = torch.from_numpy(_random_idx(bt, Tq, pos0, m, N, k, 4)).to(DEV) if mode == "csa" else None
+    md = B.CSA if mode == "csa" else B.HCA
+    rows, sc = B.quantize_kv_fp8(kv, rope)
+    o = B.compressed_attn_prefill(md, q, rows, idx, win, wp0, sk, pos0, m, w, k=k, rope_dims=rope, kv_scale=sc)
+    last = Tq - 1
+    od = B.compressed_attn_decode(md, q[:, last:].contiguous(), rows, idx[:, last:].contiguous() if idx is not None
+                                  else None, win, wp0, sk, pos0 + last, m, w, k=k, rope_dims=rope, kv_scale=sc)
+    torch.cuda.synchronize()
+    for b in range(bt):
+        deq = _kv8_oracle(kv[b], rope)
+        ro, _ = O.attention(np64(q[b]), deq, np64(win[b]), wp0, pos0, m, w,
+                            idx=idx[b].cpu().numpy() if idx is not None else None, sink=np64(sk), rope_dims=rope)
+        err = np.abs(np64(o[b]) - ro).max()
+        derr = np.abs(np64(od[b, 0]) - ro[last]).max()
+        say(f"  b{b}: max|o err| {err:.3g}, decode row {derr:.3g}")
+        assert err <= ATOL["bf16"] and derr <= ATOL["bf16"]
+
+
 @pytest.mark.parametrize("mode", ["csa", "hca"])
 def test_decode_splits_and_prefill_agree(mode):
     say("decode splits", mode)
