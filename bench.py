@@ -241,6 +241,50 @@ def lowp_indexer_rows(prefill, tp, decode, td, reps: int = 3):
     return out
 
 
+def kv_fp8_attention_rows(prefill, tp, decode, td, reps: int = 3):
+    """Attention over FP8 + BF16 stored entries beside the bf16 cache, same inputs.
+
+    Each layer's compressed cache is quantised once (outside the timing); both
+    attention calls are timed with HIP events on the launch stream.
+    """
+    import torch
+    from compressed_sparse_kv_02_amd import binding as B
+    from compressed_sparse_kv_02_amd import layer as LY
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    res = {}
+    for tag, L, t in (("prefill_csa", prefill[0], tp[0]), ("prefill_hca", prefill[1], tp[1]),
+                      ("decode_csa", decode[0], td[0]), ("decode_hca", decode[1], td[1])):
+        rows, sc = B.quantize_kv_fp8(t["cache.kv"], L.rope_dims)
+        mode = B.CSA if L.kind == "csa" else B.HCA
+        kw = dict(k=L.k, apply_q_norm=True, rope_dims=L.rope_dims, rope_on_output=True, out=t["out"], lse=t["lse"])
+        idx = t.get("idx") if L.kind == "csa" else None
+        if L.decode:
+            kw.update(n_splits=L.n_splits, workspace=t["ws.dec"])
+            call = lambda kv, s_: B.compressed_attn_decode(mode, t["q"], kv, idx, t["win"], L.win_pos0, t["sink"],
+                                                           L.pos0, L.m, L.w, kv_scale=s_, **kw)
+        else:
+            call = lambda kv, s_: B.compressed_attn_prefill(mode, t["q"], kv, idx, t["win"], L.win_pos0, t["sink"],
+                                                            L.pos0, L.m, L.w, kv_scale=s_, **kw)
+        ms16 = timed(lambda: call(t["cache.kv"], None))
+        ms8 = timed(lambda: call(rows, sc))
+        res[tag] = {"bf16_cache_ms": ms16, "fp8_cache_ms": ms8,
+                    "entry_bytes": {"bf16": 2 * L.d, "fp8": B.kv_fp8_row_bytes(L.d, L.rope_dims)}}
+        del rows, sc
+    LY.attend_step(prefill[0], tp[0])  # leave the step's own outputs in place
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -373,7 +417,8 @@ def main():
         "roofline": roofline,
         "roofline_decode": roofline_dec,
         "cpu_baseline": None,
-        "next_rows": lowp_indexer_rows(prefill, tp, decode, td),
+        "next_rows": dict(lowp_indexer_rows(prefill, tp, decode, td),
+                          kv_fp8_attention=kv_fp8_attention_rows(prefill, tp, decode, td)),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(prefill, decode, tp, td, args.cpu_budget)

@@ -133,12 +133,13 @@ __device__ __forceinline__ int key_of_row(int r) {
 // much (log2 units): the O/l rescale is then almost never needed, and P <= 2^8.
 constexpr float REF_SLACK = 8.0f;
 
-// KV8: compressed entries stored as FP8 E4M3 codes of the first D - rope_dims dims (one
-// power-of-two scale per entry) followed by the RoPE dims in bf16; the loader widens them
-// to bf16 rows in LDS (exact: E4M3 times a power of two is a bf16 value), so the rest of
-// the kernel is unchanged. Window rows stay bf16.
-template <int D, int HW, int QG, bool KV8>
+// KVR >= 0: compressed entries stored as FP8 E4M3 codes of the first D - KVR dims (one
+// power-of-two scale per entry) followed by the KVR RoPE dims in bf16; the loader widens
+// them to bf16 rows in LDS (exact: E4M3 times a power of two is a bf16 value), so the rest
+// of the kernel is unchanged. Window rows stay bf16. KVR < 0: bf16 entries.
+template <int D, int HW, int QG, int KVR>
 __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
+  constexpr bool KV8 = KVR >= 0;
   constexpr int NW = HW * QG;
   constexpr int NT = NW * 64;
   constexpr int ROWE = D + 8;        // padded LDS row, bf16 elements
@@ -154,7 +155,8 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
   __shared__ float rope_cs[QG][MAXPAIRS][2];
   __shared__ int idx_s[CSKV_MAX_TOPK];  // CSA: the query's selected entries, staged once
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps wave-derived values scalar
   const int n = lane & 15, g = lane >> 4;
   const int qi = wave / HW, hw = wave % HW;
   const int64_t nqb = (a.Tq + QG - 1) / QG;
@@ -246,8 +248,8 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
   // ---- gather loader: thread -> (key row kr, chunks c0 + TPK*i)
   const int kr = tid / TPK, c0 = tid % TPK;
   const uint16_t* kvb = (const uint16_t*)a.kv + (int64_t)b * a.N * D;
-  const int nope8 = (D - a.rope_dims) / 8;            // KV8: 16-byte LDS chunks that hold FP8 codes
-  const int64_t rb8 = (D - a.rope_dims) + 2 * a.rope_dims;  // KV8: bytes per stored entry
+  constexpr int nope8 = (D - (KV8 ? KVR : 0)) / 8;      // KV8: 16-byte LDS chunks that hold FP8 codes
+  constexpr int64_t rb8 = (D - (KV8 ? KVR : 0)) + 2 * (KV8 ? KVR : 0);  // KV8: bytes per stored entry
   const uint8_t* kv8b = (const uint8_t*)a.kv + (int64_t)b * a.N * rb8;
   const int64_t wbase = (int64_t)b * a.W;
   const int64_t wr_lo = win_row_of(a, lo);  // window row of position lo; rows wrap at W
@@ -260,7 +262,8 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
   }
   u32x4 pre[CPT];
   int pre_ok = 0;
-  float pre_sc = 0.f;   // KV8: scale of the entry in flight (0: not an FP8 entry)
+  float pre_sc = 0.f;   // KV8: scale of the entry in flight
+  bool pre8 = false;    // KV8: the entry in flight is an FP8 row (not a window row or padding)
   // Loader thread: key u = blk*32 + kr of the key list goes to LDS row kr; its validity
   // bits (bit q: query q of the tile may attend to it) go to the logical slot of row kr.
   auto gload = [&](int64_t blk) {
@@ -288,7 +291,9 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int q = 0; q < QG; ++q) ok |= (pos >= t_q[q] - a.w + 1 && pos <= t_q[q]) ? (1 << q) : 0;
     }
-    if (KV8 && !src8) pre_sc = 0.f;
+    // pre8 depends on addresses only: selecting on the loaded scale here would wait for that
+    // load before the current tile's compute and expose the full gather latency.
+    pre8 = KV8 && src8 != nullptr;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int oc = c0 + TPK * i;  // 16-byte chunk of the bf16 row: dims 8*oc .. +8
@@ -298,7 +303,7 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
           const uint2 c = *reinterpret_cast<const uint2*>(src8 + 8 * oc);  // 8 E4M3 codes
           v = u32x4{c.x, c.y, 0u, 0u};
         } else {
-          v = *reinterpret_cast<const u32x4*>(src8 + (D - a.rope_dims) + 16 * (oc - nope8));
+          v = *reinterpret_cast<const u32x4*>(src8 + 8 * nope8 + 16 * (oc - nope8));
         }
       } else if (src) {
         v = *reinterpret_cast<const u32x4*>(src + oc * 8);
@@ -312,7 +317,7 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
     for (int i = 0; i < CPT; ++i) {
       const int oc = c0 + TPK * i;
       u32x4 v = pre[i];
-      if (KV8 && pre_sc != 0.f && oc < nope8) {  // widen 8 codes to bf16 (times the power-of-two scale)
+      if (KV8 && pre8 && oc < nope8) {  // widen 8 codes to bf16 (times the power-of-two scale)
         const uint32_t c01 = v.x, c23 = v.y;
         v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c01, pre_sc, false));
         v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c01, pre_sc, true));
@@ -607,12 +612,22 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------- host
+template <int D, int HW, int QG, int KVR>
+static void launch_kvr(const AttnArgs& a, dim3 grid, hipStream_t st) {
+  if constexpr (KVR <= D)
+    hipLaunchKernelGGL((attn_mfma<D, HW, QG, KVR>), grid, dim3(HW * QG * 64), 0, st, a);
+}
+
+// FP8 entries are compiled for RoPE widths 0, 16, 32 and 64 (validated before launch).
 template <int D, int HW, int QG>
 static void launch_attn(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  if (a.kv_scale)
-    hipLaunchKernelGGL((attn_mfma<D, HW, QG, true>), grid, dim3(HW * QG * 64), 0, st, a);
-  else
-    hipLaunchKernelGGL((attn_mfma<D, HW, QG, false>), grid, dim3(HW * QG * 64), 0, st, a);
+  if (!a.kv_scale) return launch_kvr<D, HW, QG, -1>(a, grid, st);
+  switch (a.rope_dims) {
+    case 0: return launch_kvr<D, HW, QG, 0>(a, grid, st);
+    case 16: return launch_kvr<D, HW, QG, 16>(a, grid, st);
+    case 32: return launch_kvr<D, HW, QG, 32>(a, grid, st);
+    default: return launch_kvr<D, HW, QG, 64>(a, grid, st);
+  }
 }
 
 // Workgroup shape: HW waves of 16 heads per query; QG queries share one key stream
@@ -695,6 +710,7 @@ static int validate_attn(int mode, const void* q, const void* kv, const int32_t*
 static int validate_kv8(const float* kv_scale, int64_t N, int d, int rope_dims, int dtype) {
   if (dtype != CSKV_BF16) return CSKV_ERR_BAD_DTYPE;
   if ((d - rope_dims) % 16 != 0 || rope_dims % 8 != 0) return CSKV_ERR_BAD_SHAPE;
+  if (rope_dims != 0 && rope_dims != 16 && rope_dims != 32 && rope_dims != 64) return CSKV_ERR_UNSUPPORTED;
   if (N > 0 && !aligned16(kv_scale)) return CSKV_ERR_MISALIGNED;
   return CSKV_OK;
 }

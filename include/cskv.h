@@ -309,7 +309,8 @@ int compressed_attn_decode(int mode, const void* q, const void* kv, const int32_
  * first d - rope_dims values (x * 2^-e, e the smallest integer with
  * max |x| <= 448 * 2^e, nearest code, ties to even) followed by its last
  * rope_dims values in bf16: d - rope_dims + 2 * rope_dims bytes, plus one fp32
- * scale 2^e. (d - rope_dims) % 16 == 0 and rope_dims % 8 == 0.
+ * scale 2^e. (d - rope_dims) % 16 == 0 and rope_dims % 8 == 0; the attention
+ * entry points take rope_dims in {0, 16, 32, 64}.
  *
  * cskv_quantize_kv_fp8 -- x [batch, n, d] (bf16 or f32) to out [batch,
  *   out_ld, row bytes] and scales [batch, out_ld] fp32 (out_ld = 0: n); pass

@@ -204,6 +204,7 @@ def test_kv8_validation(L):
         return f(*a.values())
     assert call(ks=None) == INVALID
     assert call(rd=60) == SHAPE
+    assert call(rd=48) == UNSUPPORTED
     assert call(ks=P + 4) == MISALIGNED
     assert call(Tq=0) == OK
 

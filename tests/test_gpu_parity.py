@@ -411,6 +411,8 @@ def _kv8_oracle(kv_raw_b, rope):
     ("csa", 1, 33, 3000, 4 * 2900, 4, 1024, 128, 64, 512, 64),
     ("hca", 2, 40, 200, 128 * 180, 128, 0, 128, 32, 512, 64),
     ("csa", 2, 50, 64, 0, 4, 24, 16, 16, 64, 16),
+    ("hca", 1, 20, 50, 128 * 40, 128, 0, 16, 16, 128, 32),
+    ("csa", 1, 17, 40, 4 * 30, 4, 16, 8, 16, 64, 0),
 ])
 def test_attention_kv8_prefill_and_decode(mode, bt, Tq, N, pos0, m, k, w, H, d, rope):
     """Attention over an FP8 + BF16 KV cache equals the oracle's attention over its own
