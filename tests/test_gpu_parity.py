@@ -361,6 +361,9 @@ def _random_idx(bt, Tq, pos0, m, N, k, seed):
     ("bf16", "hca", 1, 40, 200, 128 * 180, 128, 0, 128, 32, 512, 64, True, False),
     ("bf16", "csa", 1, 20, 500, 1990, 4, 100, 7, 8, 256, 0, False, True),
     ("f32", "hca", 2, 30, 10, 0, 4, 0, 5, 3, 96, 32, True, True),
+    ("bf16", "hca", 2, 41, 300, 128 * 250, 128, 0, 128, 64, 512, 64, True, True),
+    ("bf16", "csa", 1, 37, 90, 0, 4, 256, 16, 64, 512, 64, True, False),
+    ("bf16", "csa", 2, 9, 400, 4 * 390, 4, 64, 128, 64, 512, 64, False, True),
 ])
 def test_attention_prefill(dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink):
     say("attention", dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink)
@@ -381,6 +384,43 @@ def test_attention_prefill(dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, ro
         lerr = np.abs(np64(lse[b]) - rl).max()
         say(f"  b{b}: max|o err| {err:.3g}  max|lse err| {lerr:.3g}")
         assert err <= ATOL[dtype] and lerr <= ATOL[dtype] * 5
+
+
+@pytest.mark.parametrize("mode,Tq", [("hca", 6), ("csa", 1)])
+def test_attention_logits_outgrow_reference(mode, Tq):
+    """Logits that rise far above the first tiles': the first 64 entries are 100x smaller,
+    and a sharp softmax scale makes later logits exceed the early maximum by far more than
+    2^64 (base 2), so the kernel's softmax reference must move (and O be rescaled) many
+    times. Queries are used as given (no RMSNorm, no RoPE), so the bf16 operands are exact
+    and logits of this size carry only fp32 summation error."""
+    say("attention outgrow", mode, Tq)
+    bt, H, d, m, w, N = 1, 64, 512, (4 if mode == "csa" else 128), 16, 400
+    pos0 = N * m
+    k = 256 if mode == "csa" else 0
+    q = gen(43, "og.q", (bt, Tq, H, d))
+    kv = gen(43, "og.kv", (bt, N, d))
+    kv[:, :64] *= 0.01
+    win = gen(43, "og.win", (bt, pos0 + Tq - (pos0 - w + 1), d)) * 0.01
+    sk = normal_device(43, "og.sink", (H,), 1.0, "f32", DEV)
+    idx = torch.from_numpy(_random_idx(bt, Tq, pos0, m, N, k, 5)).to(DEV) if mode == "csa" else None
+    if idx is not None:
+        idx[..., :64] = torch.arange(64, device=DEV, dtype=idx.dtype)  # the first tile holds small entries
+        idx = torch.sort(idx, dim=-1).values
+    scale = 40.0 / np.sqrt(d)
+    md = B.CSA if mode == "csa" else B.HCA
+    kw = dict(k=k, rope_dims=0, apply_q_norm=False, scale=scale, return_lse=True)
+    o, lse = B.compressed_attn_prefill(md, q, kv, idx, win, pos0 - w + 1, sk, pos0, m, w, **kw)
+    od, lsed = B.compressed_attn_decode(md, q, kv, idx, win, pos0 - w + 1, sk, pos0, m, w, n_splits=3, **kw)
+    torch.cuda.synchronize()
+    ro, rl = O.attention(np64(q[0]), np64(kv[0]), np64(win[0]), pos0 - w + 1, pos0, m, w,
+                         idx=idx[0].cpu().numpy() if idx is not None else None, sink=np64(sk), scale=scale,
+                         apply_q_norm=False, rope_dims=0)
+    assert rl.max() - 0.0 > 64 / np.log2(np.e)  # the logits really do outgrow any early reference
+    for out, l in ((o, lse), (od, lsed)):
+        err = np.abs(np64(out[0]) - ro).max()
+        say(f"  max|o err| {err:.3g}")
+        assert err <= 2e-2
+        assert np.abs(np64(l[0]) - rl).max() <= 1e-1
 
 
 # ----------------------------------------------------------------------------- FP8 KV storage
