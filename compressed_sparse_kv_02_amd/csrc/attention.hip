@@ -115,18 +115,19 @@ __device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
 }
 
-// LDS row of the tile that holds logical key L (0..31). S^T = K Q^T gives lane
-// group g the logical keys 4g+i (tile 0) and 16+4g+i (tile 1); the transpose
-// read of group g then touches rows P(4g+e), e = 0..3. With 1040-byte rows
-// (row r starts at bank 4r mod 64), this placement makes the 16 rows of a
-// K-operand read and the 8 rows of a 32-lane transpose read fall on distinct
-// banks.
+// LDS row of the tile that holds logical key L (0..31): key n of the first half in
+// row 2n, key 16+n in row 2n+1. Row r of 1040 bytes starts at bank 4r of gfx950's
+// 128 (measured: conflicts follow this model, with 32 lanes per pass for 16- and
+// 8-byte reads). A K-operand read (lane (n, g): key n, 16 bytes at byte 16g) then
+// covers 4-bank groups 2n + g, all 32 distinct in a pass of g = 0, 1; the transpose
+// read of 32 lanes touches keys 4g + e, g = 0, 1, i.e. 8 even rows whose 32-byte
+// pieces start 8 banks apart. Both are free of bank conflicts (the counters read 0).
 __device__ __forceinline__ int key_row_of(int L) {
-  return (L & 16) | (2 * (L & 3) + 8 * ((L >> 2) & 1) + ((L >> 3) & 1));
+  return 2 * (L & 15) + (L >> 4);
 }
 // Inverse of key_row_of.
 __device__ __forceinline__ int key_of_row(int r) {
-  return (r & 16) | (8 * (r & 1) + 4 * ((r >> 3) & 1) + ((r >> 1) & 3));
+  return (r >> 1) + 16 * (r & 1);
 }
 
 // Logits of a query only grow the softmax reference when they exceed it by this
@@ -340,11 +341,11 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
 
     // S^T = K Q^T: s0 -> keys 4g+i, s1 -> keys 16+4g+i; column = head n
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* kp = &kt[buf][key_row_of(n) * ROWE + 8 * g];  // logical key n; 16+n is 16 rows on
+    const uint16_t* kp = &kt[buf][key_row_of(n) * ROWE + 8 * g];  // logical key n; 16+n is the next row
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kp + ks * 32);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kp + 16 * ROWE + ks * 32);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kp + ROWE + ks * 32);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[ks], s1, 0, 0, 0);
     }
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
     // O^T += V^T P^T: A = V^T via transpose reads (lane n of group g: keys 4g+e / 16+4g+e for
     // e = n/4, dims 16tt + 4(n%4) .. +3), B = P^T already in this lane (head n, 8 keys).
     const uint16_t* vp0 = &kt[buf][key_row_of(4 * g + (n >> 2)) * ROWE + 4 * (n & 3)];
-    const uint16_t* vp1 = vp0 + 16 * ROWE;
+    const uint16_t* vp1 = vp0 + ROWE;
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt) {
       const v4i16 lo4 = lds_read_tr16(vp0 + 16 * tt);
