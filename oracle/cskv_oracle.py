@@ -488,6 +488,53 @@ def attention(q, kv, win, win_pos0: int, pos0: int, m: int, w: int, idx=None, si
 
 
 # ---------------------------------------------------------------------------
+# Projections around the core attention ("Paper Breakdown: DeepSeek-V4",
+# section 4, CSA §2.3.1: low-rank indexer queries from a shared latent c_t^Q;
+# "MQA core attention + grouped output projection"; HCA §2.3.2: same MQA +
+# grouped projection). The pages give no shapes; the readings are named here.
+# ---------------------------------------------------------------------------
+
+def lowrank_proj(cq, W) -> np.ndarray:
+    """Query (or indexer-query) heads from the shared latent: out[t] = c^Q_t W.
+
+    Reading: both the attention queries and the indexer queries are one plain
+    product of the token's latent c^Q_t [r] with a weight [r, heads * dim]; the
+    per-head query RMSNorm and RoPE stay in the attention (they follow it).
+    """
+    return np.asarray(cq, dtype=F64) @ np.asarray(W, dtype=F64)
+
+
+def grouped_out_proj_mid(o, Wg) -> np.ndarray:
+    """First stage of the grouped output projection, per token:
+    u[t, g] = concat(o[t, h] for h in group g) @ Wg[g].
+
+    Reading: the H heads form G contiguous groups of H/G heads; each group's
+    concatenated outputs [(H/G) * d] have their own projection Wg[g] [(H/G) d, d_g].
+    o: [T, H, d]; Wg: [G, (H/G) d, d_g] -> u: [T, G, d_g].
+    """
+    o = np.asarray(o, dtype=F64)
+    Wg = np.asarray(Wg, dtype=F64)
+    T, H, d = o.shape
+    G = Wg.shape[0]
+    og = o.reshape(T, G, (H // G) * d)
+    return np.stack([og[:, g, :] @ Wg[g] for g in range(G)], axis=1)
+
+
+def grouped_out_proj(o, Wg, Wo, round_mid: bool = True) -> np.ndarray:
+    """Grouped output projection: y[t] = concat_g(u[t, g]) @ Wo, u from
+    grouped_out_proj_mid. Wo: [G d_g, D] -> y: [T, D].
+
+    round_mid: the intermediate u is a stored bf16 tensor on the GPU path, so it
+    is rounded to bf16 here too (a rounding point the kernels share).
+    """
+    u = grouped_out_proj_mid(o, Wg)
+    if round_mid:
+        u = round_bf16(u)
+    T = u.shape[0]
+    return u.reshape(T, -1) @ np.asarray(Wo, dtype=F64)
+
+
+# ---------------------------------------------------------------------------
 # Whole-layer drivers (compress -> [indexer -> top-k] -> attention)
 # ---------------------------------------------------------------------------
 

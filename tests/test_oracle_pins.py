@@ -486,3 +486,53 @@ def test_page_constants_fixture():
         g = json.load(f)
     assert g["csa_ratio_m"]["value"] == 4 and g["hca_ratio_m_prime"]["value"] == 128
     assert g["topk"]["value"] == 1024 and g["window"]["value"] == 128 and g["rope_dims"]["value"] == 64
+
+
+# ---------------------------------------------------------------- projections
+
+def test_lowrank_proj_brute_force():
+    # small integers: every product and sum is exact in fp64, so the triple loop must agree bit for bit
+    cq = rng.integers(-4, 5, size=(3, 5)).astype(np.float64)
+    W = rng.integers(-4, 5, size=(5, 7)).astype(np.float64)
+    ref = [[sum(cq[t, k] * W[k, n] for k in range(5)) for n in range(7)] for t in range(3)]
+    assert np.array_equal(O.lowrank_proj(cq, W), np.array(ref))
+
+
+def test_grouped_out_proj_hand_case():
+    # H = 4 heads of d = 1, G = 2 groups of 2 heads, d_g = 1: u[t, g] = o[t, 2g] Wg[g,0] + o[t, 2g+1] Wg[g,1]
+    o = np.array([[[1.0], [2.0], [3.0], [4.0]]])
+    Wg = np.array([[[10.0], [100.0]], [[1000.0], [10000.0]]])
+    u = O.grouped_out_proj_mid(o, Wg)
+    assert np.array_equal(u, np.array([[[210.0], [43000.0]]]))
+    Wo = np.array([[1.0, 2.0], [3.0, 5.0]])
+    y = O.grouped_out_proj(o, Wg, Wo, round_mid=False)
+    assert np.array_equal(y, np.array([[210.0 + 3 * 43000.0, 420.0 + 5 * 43000.0]]))
+
+
+def test_grouped_out_proj_equals_block_diagonal_dense():
+    # contiguous head groups with their own weights == one dense product with a block-diagonal
+    # weight; catches interleaved grouping, a transposed group weight or a wrong group order
+    from scipy.linalg import block_diag
+    T, H, d, G, dg = 5, 6, 4, 3, 7
+    o = rng.standard_normal((T, H, d))
+    Wg = rng.standard_normal((G, (H // G) * d, dg))
+    u = O.grouped_out_proj_mid(o, Wg)
+    dense = o.reshape(T, H * d) @ block_diag(*[Wg[g] for g in range(G)])
+    np.testing.assert_allclose(u.reshape(T, G * dg), dense, rtol=1e-13, atol=1e-13)
+    # G = 1 is a plain product
+    W1 = rng.standard_normal((1, H * d, dg))
+    np.testing.assert_allclose(O.grouped_out_proj_mid(o, W1)[:, 0], o.reshape(T, H * d) @ W1[0], rtol=1e-13)
+
+
+def test_grouped_out_proj_identity_weights_and_mid_rounding():
+    # identity group and output weights return the heads concatenated; the bf16 rounding of the
+    # intermediate is exact on bf16 inputs and changes a non-bf16 intermediate
+    T, H, d, G = 3, 4, 2, 2
+    o = O.round_bf16(rng.standard_normal((T, H, d)))
+    n = (H // G) * d
+    Wg = np.stack([np.eye(n)] * G)
+    y = O.grouped_out_proj(o, Wg, np.eye(G * n))
+    assert np.array_equal(y, o.reshape(T, H * d))
+    o2 = rng.standard_normal((T, H, d))
+    assert not np.array_equal(O.grouped_out_proj(o2, Wg, np.eye(G * n)),
+                              O.grouped_out_proj(o2, Wg, np.eye(G * n), round_mid=False))
