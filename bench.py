@@ -285,6 +285,67 @@ def kv_fp8_attention_rows(prefill, tp, decode, td, reps: int = 3):
     return res
 
 
+# Projection shapes. The pages give none: the latent rank follows the low-rank indexer-query
+# reading (r = 256); the output groups G = 8 of 8 heads, d_g = 1024 and the model width
+# D = 4096 are assumptions of this benchmark, named as such in its output.
+PROJ_R, PROJ_G, PROJ_DG, PROJ_D = 256, 8, 1024, 4096
+
+
+def projection_rows(prefill, reps: int = 3):
+    """The projections around the attention for the prefill chunk's tokens (batch x chunk):
+    attention queries c^Q W^Q, indexer queries c^Q W^QI, and the grouped output projection.
+    Seeded synthetic latents and weights; each call timed with HIP events on the launch stream."""
+    import torch
+    from compressed_sparse_kv_02_amd import binding as B
+    from compressed_sparse_kv_02_amd.synth import normal_device
+
+    L = prefill[0]
+    T = L.batch * L.T
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def row(ms, flops, nbytes):
+        tf = flops / (ms / 1e3) / 1e12
+        gb = nbytes / (ms / 1e3) / 1e9
+        mfma_bound = flops / PEAK_BF16_FLOPS >= nbytes / PEAK_HBM_BYTES
+        ent = {"avg_launch_ms": ms, "algorithmic_flops_per_launch": flops, "algorithmic_bytes_per_launch": nbytes,
+               "tflops": tf, "gbps": gb, "bound": "mfma" if mfma_bound else "hbm"}
+        ent["frac"] = tf / (PEAK_BF16_FLOPS / 1e12) if mfma_bound else gb / (PEAK_HBM_BYTES / 1e9)
+        return ent
+
+    r, G, dg, D = PROJ_R, PROJ_G, PROJ_DG, PROJ_D
+    cq = normal_device(61, "proj.cq", (T, r))
+    out = {"shapes": {"tokens": T, "latent_rank": r, "groups": G, "group_dim": dg, "model_dim": D,
+                      "assumed": "r, G, d_g and D are not on the pages"}}
+    for tag, n_out in (("query_proj", L.H * L.d), ("indexer_query_proj", L.HI * L.dI)):
+        W = normal_device(61, f"proj.{tag}", (r, n_out), r ** -0.5)
+        dst = torch.empty(T, n_out, dtype=torch.bfloat16, device=cq.device)
+        ms = timed(lambda: B.lowrank_proj(cq, W, out=dst))
+        out[tag] = row(ms, 2 * T * r * n_out, 2 * (T * r + r * n_out + T * n_out))
+        del W, dst
+    kin = (L.H // G) * L.d
+    o = normal_device(61, "proj.o", (T, L.H, L.d))
+    Wg = normal_device(61, "proj.Wg", (G, kin, dg), kin ** -0.5)
+    Wo = normal_device(61, "proj.Wo", (G * dg, D), (G * dg) ** -0.5)
+    mid = torch.empty(T, G, dg, dtype=torch.bfloat16, device=o.device)
+    y = torch.empty(T, D, dtype=torch.bfloat16, device=o.device)
+    ms = timed(lambda: B.grouped_out_proj(o, Wg, Wo, mid=mid, out=y))
+    fl = 2 * T * G * kin * dg + 2 * T * G * dg * D
+    by = 2 * (T * L.H * L.d + G * kin * dg + 2 * T * G * dg + G * dg * D + T * D)
+    out["grouped_out_proj"] = row(ms, fl, by)
+    out["kernel"] = "gemm_bf16 (128 x 128 tiles, v_mfma_f32_32x32x16_bf16)"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -417,7 +478,7 @@ def main():
         "roofline": roofline,
         "roofline_decode": roofline_dec,
         "cpu_baseline": None,
-        "next_rows": dict(lowp_indexer_rows(prefill, tp, decode, td),
+        "next_rows": dict(lowp_indexer_rows(prefill, tp, decode, td), projections=projection_rows(prefill),
                           kv_fp8_attention=kv_fp8_attention_rows(prefill, tp, decode, td)),
     }
     if not args.no_cpu_baseline:

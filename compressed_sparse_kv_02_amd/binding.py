@@ -25,7 +25,8 @@ EXPORTS = ("cskv_version", "cskv_status_string", "csa_compress", "hca_compress",
            "cskv_quantize_fp4", "indexer_scores_fp4", "indexer_topk_fp4",
            "cskv_quantize_kv_fp8", "compressed_attn_prefill_kv8", "compressed_attn_decode_kv8",
            "compressed_attn_prefill",
-           "cskv_decode_workspace_size", "compressed_attn_decode")
+           "cskv_decode_workspace_size", "compressed_attn_decode",
+           "cskv_lowrank_proj", "cskv_grouped_out_proj")
 
 _lib = None
 
@@ -55,6 +56,8 @@ _SIGS = {
     "compressed_attn_prefill": (_I, [_I, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
                                      _I, _P, _F, _I, _F, _F, _I, _P, _P, _I, _P]),
     "cskv_decode_workspace_size": (_Z, [_I, _L, _I, _I, _I]),
+    "cskv_lowrank_proj": (_I, [_P, _P, _P, _L, _L, _L, _I, _P]),
+    "cskv_grouped_out_proj": (_I, [_P, _P, _P, _P, _P, _L, _I, _I, _I, _L, _L, _I, _P]),
     "compressed_attn_decode": (_I, [_I, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
                                     _I, _P, _F, _I, _F, _F, _I, _I, _P, _Z, _P, _P, _I, _P]),
 }
@@ -364,3 +367,31 @@ def compressed_attn_decode(mode: int, q, kv, idx, win, win_pos0: int, sink, pos0
         _check("compressed_attn_decode", lib().compressed_attn_decode(
             *args, n_splits, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _dtype(q), _stream(q)))
     return (out, lse) if return_lse else out
+
+
+def lowrank_proj(cq, W, out=None):
+    """out [..., n_out] = cq [..., r] @ W [r, n_out] (bf16; the leading dims of cq are the tokens)."""
+    r, n_out = W.shape
+    T = cq.numel() // r
+    if out is None:
+        out = torch.empty(*cq.shape[:-1], n_out, dtype=cq.dtype, device=cq.device)
+    _check("cskv_lowrank_proj", lib().cskv_lowrank_proj(_ptr(cq), _ptr(W), _ptr(out), T, r, n_out,
+                                                        _dtype(cq), _stream(cq)))
+    return out
+
+
+def grouped_out_proj(o, Wg, Wo, mid=None, out=None, return_mid: bool = False):
+    """Grouped output projection of attention outputs o [..., H, d] with Wg [G, (H/G) d, dg] and
+    Wo [G dg, D] -> y [..., D] (and the bf16 intermediate mid [..., G, dg])."""
+    H, d = o.shape[-2], o.shape[-1]
+    G, _, dg = Wg.shape
+    D = Wo.shape[1]
+    T = o.numel() // (H * d)
+    lead = o.shape[:-2]
+    if mid is None:
+        mid = torch.empty(*lead, G, dg, dtype=o.dtype, device=o.device)
+    if out is None:
+        out = torch.empty(*lead, D, dtype=o.dtype, device=o.device)
+    _check("cskv_grouped_out_proj", lib().cskv_grouped_out_proj(
+        _ptr(o), _ptr(Wg), _ptr(Wo), _ptr(mid), _ptr(out), T, H, d, G, dg, D, _dtype(o), _stream(o)))
+    return (out, mid) if return_mid else out

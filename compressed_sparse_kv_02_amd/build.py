@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcskv.so")
-SOURCES = ["compress.hip", "indexer.hip", "indexer_lowp.hip", "topk.hip", "attention.hip", "abi.cpp"]
+SOURCES = ["compress.hip", "indexer.hip", "indexer_lowp.hip", "topk.hip", "attention.hip", "proj.hip", "abi.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

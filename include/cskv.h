@@ -337,6 +337,34 @@ int compressed_attn_decode_kv8(int mode, const void* q, const uint8_t* kv, const
                                int n_splits, void* workspace, size_t ws_bytes, void* out, float* lse,
                                void* stream);
 
+/* ------------------------------------------------------------------------
+ * Projections around the core attention ("Paper Breakdown: DeepSeek-V4",
+ * section 4, CSA §2.3.1: low-rank indexer queries from a latent c_t^Q shared
+ * with the attention queries; MQA core attention + grouped output projection;
+ * HCA §2.3.2: the same grouped projection). The pages give no shapes; both
+ * entry points take them as arguments. bf16 only (dtype CSKV_BF16), fp32
+ * accumulation, bf16 results (round to nearest even).
+ *
+ * cskv_lowrank_proj -- out [T, n_out] = cq [T, r] @ W [r, n_out], all
+ *   row-major. One call per projection: the attention queries (n_out = H * d,
+ *   read as [T, H, d]) and the indexer queries (n_out = H_I * d_I). The query
+ *   RMSNorm and RoPE are applied by the attention entry points. r a multiple
+ *   of 64, n_out of 8; T = 0 is a no-op.
+ * cskv_grouped_out_proj -- o [T, H, d] (the attention output) in G groups of
+ *   H/G contiguous heads: mid [T, G, dg] with mid[t, g] = concat(o[t, h] for
+ *   h in group g) @ Wg[g], Wg [G, (H/G) * d, dg]; then y [T, D] =
+ *   mid[t] (as [G * dg]) @ Wo [G * dg, D]. mid is a caller buffer of T * G *
+ *   dg bf16 values (it holds the rounded intermediate on return).
+ *   (H/G) * d and G * dg multiples of 64, dg and D multiples of 8.
+ * Pointers 16-byte aligned. Errors: CSKV_ERR_BAD_DTYPE for a dtype other than
+ * CSKV_BF16, CSKV_ERR_BAD_SHAPE for sizes outside the above, CSKV_ERR_INVALID_ARG
+ * for a null pointer, CSKV_ERR_MISALIGNED; all checked before any launch.
+ */
+int cskv_lowrank_proj(const void* cq, const void* W, void* out, int64_t T, int64_t r, int64_t n_out, int dtype,
+                      void* stream);
+int cskv_grouped_out_proj(const void* o, const void* Wg, const void* Wo, void* mid, void* y, int64_t T, int H,
+                          int d, int G, int64_t dg, int64_t D, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

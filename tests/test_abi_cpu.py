@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 21, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(L, n), n
     from compressed_sparse_kv_02_amd import binding
@@ -236,6 +236,31 @@ def test_attention_validation(L):
         assert call(Tq=0) == OK
         if fname.endswith("decode"):
             assert call(ns=300) == SHAPE
+
+
+def test_projection_validation(L):
+    f = L.cskv_lowrank_proj
+    assert f(P, P, P, 64, 256, 8192, 1, None) == DTYPE        # bf16 only
+    assert f(P, P, P, 64, 96, 8192, 0, None) == SHAPE         # r not a multiple of 64
+    assert f(P, P, P, 64, 256, 8190, 0, None) == SHAPE        # n_out not a multiple of 8
+    assert f(P, P, P, -1, 256, 8192, 0, None) == SHAPE
+    assert f(None, P, P, 64, 256, 8192, 0, None) == INVALID
+    assert f(P, P + 8, P, 64, 256, 8192, 0, None) == MISALIGNED
+    assert f(P, P, P, 0, 256, 8192, 0, None) == OK            # no tokens: nothing launched
+    g = L.cskv_grouped_out_proj
+    base = dict(o=P, Wg=P, Wo=P, mid=P, y=P, T=64, H=64, d=512, G=8, dg=1024, D=4096, dt=0, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return g(*a.values())
+    assert call(dt=1) == DTYPE
+    assert call(G=7) == SHAPE       # H not a multiple of G
+    assert call(d=32, H=8, G=8) == SHAPE   # (H/G) d = 32 not a multiple of 64
+    assert call(dg=1020) == SHAPE
+    assert call(D=4100) == SHAPE
+    assert call(mid=None) == INVALID
+    assert call(y=P + 2) == MISALIGNED
+    assert call(T=0) == OK
 
 
 def test_binding_refuses_cpu_tensors():

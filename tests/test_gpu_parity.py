@@ -694,3 +694,57 @@ def test_indexer_topk_matches_its_two_halves():
     torch.cuda.synchronize()
     assert B.indexer_workspace_bytes(bt, Tq, N, HI, k, B.BF16) < bt * Tq * B.score_ld(N) * 4  # it did chunk
     assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------------- projections
+
+def _gemm_bound(A, B, ref):
+    """Per-element bound for a bf16 product with fp32 accumulation and a bf16 result: one bf16
+    ulp of the exact value (the fp32 sum may sit across a rounding boundary) plus the fp32
+    summation error over K terms."""
+    K = A.shape[-1]
+    mag = np.abs(A) @ np.abs(B)
+    return 2.0 ** -8 * np.abs(ref) + K * 2.0 ** -24 * mag + 1e-30
+
+
+@pytest.mark.parametrize("T,r,n_out", [(300, 256, 8192), (37, 64, 136), (129, 1536, 1024)])
+def test_lowrank_proj(T, r, n_out):
+    say("lowrank_proj", T, r, n_out)
+    cq = gen(51, "lp.cq", (T, r))
+    W = gen(51, "lp.W", (r, n_out), std=r ** -0.5)
+    out = B.lowrank_proj(cq, W)
+    torch.cuda.synchronize()
+    a, w = np64(cq), np64(W)
+    ref = O.lowrank_proj(a, w)
+    err = np.abs(np64(out) - ref)
+    bound = _gemm_bound(a, w, ref)
+    say(f"  max err {err.max():.3g}, max err/bound {(err / bound).max():.3g}")
+    assert (err <= bound).all()
+
+
+@pytest.mark.parametrize("T,H,d,G,dg,D", [(70, 64, 128, 8, 256, 512), (200, 64, 512, 8, 1024, 4096),
+                                         (33, 16, 64, 4, 80, 136)])
+def test_grouped_out_proj(T, H, d, G, dg, D):
+    say("grouped_out_proj", T, H, d, G, dg, D)
+    o = gen(52, "gp.o", (T, H, d))
+    Wg = gen(52, "gp.Wg", (G, (H // G) * d, dg), std=((H // G) * d) ** -0.5)
+    Wo = gen(52, "gp.Wo", (G * dg, D), std=(G * dg) ** -0.5)
+    y, mid = B.grouped_out_proj(o, Wg, Wo, return_mid=True)
+    torch.cuda.synchronize()
+    o64, wg, wo = np64(o), np64(Wg), np64(Wo)
+    # stage 1 against the oracle, per group
+    ref_mid = O.grouped_out_proj_mid(o64, wg)
+    og = o64.reshape(T, G, (H // G) * d)
+    for g in range(G):
+        err = np.abs(np64(mid[:, g]) - ref_mid[:, g])
+        assert (err <= _gemm_bound(og[:, g], wg[g], ref_mid[:, g])).all(), g
+    # stage 2 on the GPU's own intermediate (identical inputs), against the oracle's final product
+    m64 = np64(mid)
+    ref_y = m64.reshape(T, G * dg) @ wo
+    err = np.abs(np64(y) - ref_y)
+    bound = _gemm_bound(m64.reshape(T, G * dg), wo, ref_y)
+    say(f"  y: max err {err.max():.3g}, max err/bound {(err / bound).max():.3g}")
+    assert (err <= bound).all()
+    # and the whole chain against the oracle end to end (bf16 intermediate on both sides)
+    full = O.grouped_out_proj(o64, wg, wo)
+    assert np.abs(np64(y) - full).max() <= 2e-2 * max(1.0, np.abs(full).max())
