@@ -10,7 +10,7 @@
 // Scores are compared through an order-preserving uint32 key, so the
 // selection is integer work and deterministic.
 //
-// Many rows (prefill): one 512-thread workgroup per row (two fit a compute
+// Many rows (prefill): one 512-thread workgroup per row (three fit a compute
 // unit). A sample of the row (128 runs of 32 consecutive entries) gives a
 // threshold that about 3k entries exceed; one vectorised pass, each wave over
 // its own contiguous share of the row, keeps those entries (in index order)
@@ -30,7 +30,7 @@ namespace cskv {
 // Exact top-k per row
 // ----------------------------------------------------------------------------
 constexpr int TOPK_THREADS = 512;
-constexpr int TOPK_CAP = 8192;      // candidate (key, index) pairs held in LDS
+constexpr int TOPK_CAP = 5632;      // candidate (key, index) pairs held in LDS: 53 KiB per workgroup, three per CU
 constexpr int TOPK_SAMPLES = 4096;     // sample of a long row, for the candidate threshold
 constexpr int TOPK_SAMPLE_RUNS = 128;  // ... taken as runs of 32 consecutive entries
 
@@ -313,10 +313,13 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
 //    dropped one, so the candidates hold the row's exact top-k. Otherwise the
 //    row falls back to the exact select over global memory.
 constexpr int TOPK_MAX_PARTS = 128;
-constexpr int64_t TOPK_SEL_STRIDE = (int64_t)TOPK_CAP * 8 + TOPK_MAX_PARTS * 16;
+// Part length and candidate capacity of the two-kernel route (few workgroups, so their LDS
+// size does not limit occupancy; larger than TOPK_CAP so that k up to 2048 still splits).
+constexpr int TOPK_SPLIT_CAP = 8192;
+constexpr int64_t TOPK_SEL_STRIDE = (int64_t)TOPK_SPLIT_CAP * 8 + TOPK_MAX_PARTS * 16;
 
 __global__ __launch_bounds__(TOPK_THREADS) void topk_part(IdxArgs a) {
-  __shared__ uint32_t ckey[TOPK_CAP];
+  __shared__ uint32_t ckey[TOPK_SPLIT_CAP];
   __shared__ TopkShared sh;
   const int tid = threadIdx.x;
   const int p = blockIdx.x;
@@ -326,8 +329,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_part(IdxArgs a) {
   if (V <= a.k) return;
   uint8_t* ws = a.sel_ws + ((int64_t)b * a.nrows + jr) * TOPK_SEL_STRIDE;
   uint32_t* wkey = reinterpret_cast<uint32_t*>(ws) + (int64_t)p * a.kp;
-  int32_t* widx = reinterpret_cast<int32_t*>(ws + (int64_t)TOPK_CAP * 4) + (int64_t)p * a.kp;
-  int4* rec = reinterpret_cast<int4*>(ws + (int64_t)TOPK_CAP * 8) + p;
+  int32_t* widx = reinterpret_cast<int32_t*>(ws + (int64_t)TOPK_SPLIT_CAP * 4) + (int64_t)p * a.kp;
+  int4* rec = reinterpret_cast<int4*>(ws + (int64_t)TOPK_SPLIT_CAP * 8) + p;
   const int64_t s0 = (int64_t)p * a.part_len;
   const int n = (int)(V - s0 < a.part_len ? (V - s0 > 0 ? V - s0 : 0) : a.part_len);
   if (n == 0) {
@@ -364,8 +367,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_part(IdxArgs a) {
 }
 
 __global__ __launch_bounds__(TOPK_THREADS) void topk_merge(IdxArgs a) {
-  __shared__ uint32_t ckey[TOPK_CAP];
-  __shared__ int32_t cidx[TOPK_CAP];
+  __shared__ uint32_t ckey[TOPK_SPLIT_CAP];
+  __shared__ int32_t cidx[TOPK_SPLIT_CAP];
   __shared__ int pcnt[TOPK_MAX_PARTS], poff[TOPK_MAX_PARTS];
   __shared__ TopkShared sh;
   const int tid = threadIdx.x;
@@ -380,8 +383,8 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge(IdxArgs a) {
   }
   const uint8_t* ws = a.sel_ws + ((int64_t)b * a.nrows + jr) * TOPK_SEL_STRIDE;
   const uint32_t* wkey = reinterpret_cast<const uint32_t*>(ws);
-  const int32_t* widx = reinterpret_cast<const int32_t*>(ws + (int64_t)TOPK_CAP * 4);
-  const int4* rec = reinterpret_cast<const int4*>(ws + (int64_t)TOPK_CAP * 8);
+  const int32_t* widx = reinterpret_cast<const int32_t*>(ws + (int64_t)TOPK_SPLIT_CAP * 4);
+  const int4* rec = reinterpret_cast<const int4*>(ws + (int64_t)TOPK_SPLIT_CAP * 8);
   const int P = (int)((V + a.part_len - 1) / a.part_len);
   const int4 r = tid < P ? rec[tid] : make_int4(0, 0, 0, 0);
   int n_cand;
@@ -419,7 +422,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge(IdxArgs a) {
 // ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
-// Parts for the two-kernel selection: rows of at least 4 parts of TOPK_CAP entries, and
+// Parts for the two-kernel selection: rows of at least 4 parts of TOPK_SPLIT_CAP entries, and
 // at most 64 rows in the call (more rows fill the GPU one workgroup per row).
 struct SplitPlan {
   int parts, kp;
@@ -427,10 +430,10 @@ struct SplitPlan {
 
 static bool plan_split(int64_t rows, int64_t vmax, int k, SplitPlan& sp) {
   if (rows > 64) return false;
-  const int64_t P = ceil_div(vmax, (int64_t)TOPK_CAP);
+  const int64_t P = ceil_div(vmax, (int64_t)TOPK_SPLIT_CAP);
   if (P < 4 || P > TOPK_MAX_PARTS) return false;
   int64_t kp = round_up(ceil_div(4 * (int64_t)k, P), (int64_t)64);
-  if (P * kp > TOPK_CAP) return false;
+  if (P * kp > TOPK_SPLIT_CAP) return false;
   sp.parts = (int)P;
   sp.kp = (int)kp;
   return true;
@@ -451,7 +454,7 @@ int launch_select(IdxArgs& a, int batch, void* sel_ws, size_t sel_bytes, hipStre
   const int64_t rows = (int64_t)batch * a.nrows;
   if (sel_ws && plan_split(rows, vmax, a.k, sp) && sel_bytes >= (size_t)(rows * TOPK_SEL_STRIDE)) {
     a.sel_ws = (uint8_t*)sel_ws;
-    a.part_len = TOPK_CAP;
+    a.part_len = TOPK_SPLIT_CAP;
     a.kp = sp.kp;
     hipLaunchKernelGGL(topk_part, dim3((unsigned)sp.parts, (unsigned)a.nrows, (unsigned)batch),
                        dim3(TOPK_THREADS), 0, st, a);
