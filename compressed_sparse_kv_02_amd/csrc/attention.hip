@@ -351,29 +351,37 @@ __global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
     }
     const int4 d0 = *reinterpret_cast<const int4*>(&kvq[buf][4 * g]);
     const int4 d1 = *reinterpret_cast<const int4*>(&kvq[buf][16 + 4 * g]);
-    float sv[8];
-    sv[0] = ((d0.x >> qi) & 1) ? s0[0] * a.scale_log2 : -INFINITY;
-    sv[1] = ((d0.y >> qi) & 1) ? s0[1] * a.scale_log2 : -INFINITY;
-    sv[2] = ((d0.z >> qi) & 1) ? s0[2] * a.scale_log2 : -INFINITY;
-    sv[3] = ((d0.w >> qi) & 1) ? s0[3] * a.scale_log2 : -INFINITY;
-    sv[4] = ((d1.x >> qi) & 1) ? s1[0] * a.scale_log2 : -INFINITY;
-    sv[5] = ((d1.y >> qi) & 1) ? s1[1] * a.scale_log2 : -INFINITY;
-    sv[6] = ((d1.z >> qi) & 1) ? s1[2] * a.scale_log2 : -INFINITY;
-    sv[7] = ((d1.w >> qi) & 1) ? s1[3] * a.scale_log2 : -INFINITY;
+    float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    // masking only where some key of the tile is invalid for this wave's query (tile edges)
+    const int vall = d0.x & d0.y & d0.z & d0.w & d1.x & d1.y & d1.z & d1.w;
+    if (__ballot(((vall >> qi) & 1) == 0) != 0) {
+      sv[0] = ((d0.x >> qi) & 1) ? sv[0] : -INFINITY;
+      sv[1] = ((d0.y >> qi) & 1) ? sv[1] : -INFINITY;
+      sv[2] = ((d0.z >> qi) & 1) ? sv[2] : -INFINITY;
+      sv[3] = ((d0.w >> qi) & 1) ? sv[3] : -INFINITY;
+      sv[4] = ((d1.x >> qi) & 1) ? sv[4] : -INFINITY;
+      sv[5] = ((d1.y >> qi) & 1) ? sv[5] : -INFINITY;
+      sv[6] = ((d1.z >> qi) & 1) ? sv[6] : -INFINITY;
+      sv[7] = ((d1.w >> qi) & 1) ? sv[7] : -INFINITY;
+    }
+    // sv holds raw dot products; base-2 logits are sv * scale_log2 (> 0, so the maximum commutes)
     float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
     mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
     mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
+    mb *= a.scale_log2;
     // lazy reference: move it only when a logit exceeds it by REF_SLACK
     const bool upd = mb > m_ref + REF_SLACK;
     float alpha = 1.f;
     if (upd) {
-      alpha = exp2f(m_ref - mb);  // 0 when the reference was -inf
+      alpha = __builtin_amdgcn_exp2f(m_ref - mb);  // 0 when the reference was -inf
       m_ref = mb;
     }
     float p[8], ps = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      p[i] = m_ref == -INFINITY ? 0.f : exp2f(sv[i] - m_ref);
+      // v_exp_f32 directly: arguments are <= REF_SLACK, and a result below the normal
+      // range (a weight under 2^-126 of the largest) flushes to zero
+      p[i] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.scale_log2, -m_ref));
       ps += p[i];
     }
     ps += __shfl_xor(ps, 16, 64);
