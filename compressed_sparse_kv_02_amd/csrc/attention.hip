@@ -138,8 +138,10 @@ constexpr float REF_SLACK = 8.0f;
 // power-of-two scale per entry) followed by the KVR RoPE dims in bf16; the loader widens
 // them to bf16 rows in LDS (exact: E4M3 times a power of two is a bf16 value), so the rest
 // of the kernel is unchanged. Window rows stay bf16. KVR < 0: bf16 entries.
-template <int D, int HW, int QG, int KVR>
-__global__ __launch_bounds__(HW * QG * 64) void attn_mfma(AttnArgs a) {
+// OCC = 2 asks the compiler for two workgroups per CU (at most 256 registers per lane):
+// CSA prefill then has two gathers in flight per CU, which pays for a few spills.
+template <int D, int HW, int QG, int KVR, int OCC = 1>
+__global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
   constexpr bool KV8 = KVR >= 0;
   constexpr int NW = HW * QG;
   constexpr int NT = NW * 64;
@@ -623,8 +625,16 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
 // ---------------------------------------------------------------------------- host
 template <int D, int HW, int QG, int KVR>
 static void launch_kvr(const AttnArgs& a, dim3 grid, hipStream_t st) {
-  if constexpr (KVR <= D)
+  if constexpr (KVR <= D) {
+    // one query per workgroup over bf16 entries, not split (CSA prefill): two per CU
+    if constexpr (D == 512 && HW == 4 && QG == 1 && KVR < 0) {
+      if (a.n_splits == 1) {
+        hipLaunchKernelGGL((attn_mfma<D, HW, QG, KVR, 2>), grid, dim3(HW * QG * 64), 0, st, a);
+        return;
+      }
+    }
     hipLaunchKernelGGL((attn_mfma<D, HW, QG, KVR>), grid, dim3(HW * QG * 64), 0, st, a);
+  }
 }
 
 // FP8 entries are compiled for RoPE widths 0, 16, 32 and 64 (validated before launch).
