@@ -123,12 +123,13 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
     }
   }
 
-  // Merge row groups in a fixed order (row group 0 first).
+  // Merge row groups in a fixed order (row group 0 first). Partials are stored channel-major
+  // (element v of thread t at v * NT + t), so each store and read touches consecutive words.
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
-    part[0][tid * VEC + v] = mx[v];
-    part[1][tid * VEC + v] = sm[v];
-    part[2][tid * VEC + v] = acc[v];
+    part[0][v * NT + tid] = mx[v];
+    part[1][v * NT + tid] = sm[v];
+    part[2][v * NT + tid] = acc[v];
   }
   __syncthreads();
 
@@ -138,10 +139,10 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
       float M = -INFINITY;
-      for (int q = 0; q < RG; ++q) M = fmaxf(M, part[0][(q * a.clp + g) * VEC + v]);
+      for (int q = 0; q < RG; ++q) M = fmaxf(M, part[0][v * NT + q * a.clp + g]);
       float S = 0.f, A = 0.f;
       for (int q = 0; q < RG; ++q) {
-        const int o = (q * a.clp + g) * VEC + v;
+        const int o = v * NT + q * a.clp + g;
         const float mq = part[0][o];
         if (mq == -INFINITY) continue;  // row group saw no rows
         const float sc = __expf(mq - M);
