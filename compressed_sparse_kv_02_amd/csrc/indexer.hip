@@ -25,21 +25,26 @@ namespace cskv {
 // ----------------------------------------------------------------------------
 
 // Prefill rows: 8 queries per workgroup, one per wave, sharing 256-key LDS tiles.
+// Each 32-key sub-block runs in two phases of KS/2 k-steps. A phase issues the
+// LDS reads of the next phase's B operands, then its own MFMAs, interleaved with
+// half of the previous sub-block's ReLU / weighted head-sum; scheduling barriers
+// keep the reads one phase (KS/2 x HT MFMAs) ahead of their use.
 template <int HT, int KS>
 __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
   constexpr int QB = 8;                // queries per workgroup (one per wave)
-  constexpr int KW = 1;                // waves that take different key blocks
-  constexpr int SUB = 8;               // 32-key sub-blocks per wave per tile
+  constexpr int SUB = 8;               // 32-key sub-blocks per tile (even)
   constexpr int DI = 16 * KS;
-  constexpr int TILE = KW * SUB * 32;  // keys per LDS tile
+  constexpr int KH = KS / 2;           // k-steps per phase
+  constexpr int TILE = SUB * 32;       // keys per LDS tile
   constexpr int ROW = DI + 8;          // padded LDS row (bf16), +16 bytes vs bank conflicts
   constexpr int CPR = DI / 8;          // 16-byte chunks per key row
   constexpr int CHUNKS = TILE * CPR;
   constexpr int CPT = (CHUNKS + 511) / 512;
+  static_assert(CHUNKS % 512 == 0, "whole chunks per thread");
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][TILE * ROW];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int qs = wave % QB, kl = wave / QB;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int qs = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.z;
   const int64_t qblk = (int64_t)gridDim.y - 1 - blockIdx.y;  // longest rows first
   const int64_t jr = qblk * QB + qs;                        // row within chunk
@@ -54,7 +59,8 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
   if (kbeg >= kend) return;  // uniform for the workgroup
   const int64_t vj = qvalid ? visible_entries(a.pos0 + j, a.m, a.N) : 0;
   const int nkeys = (int)(kend - kbeg);         // keys of this workgroup (< 2^31)
-  const int vrel = (int)((vj > kbeg ? vj : kbeg) - kbeg);  // visible keys of this query, relative
+  // visible keys of this query within this workgroup's span
+  const int vrel = (int)((vj < kbeg ? kbeg : (vj > kend ? kend : vj)) - kbeg);
 
   // A operands: lane holds head (lane % 32) of each 32-head tile, 8 dims per k-step.
   bf16x8 qa[HT][KS];
@@ -81,67 +87,101 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
   }
 
   const uint16_t* kbase = (const uint16_t*)a.KI + ((int64_t)b * a.N + kbeg) * DI;
-  float* srow = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS + kbeg;
+  float* srow = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS + kbeg + (lane & 31);
+  const bool storer = qvalid && lane < 32;
   const int ntiles = (nkeys + TILE - 1) / TILE;
 
   u32x4 pre[CPT];
   auto gload = [&](int t0) {
+    if (t0 + TILE <= nkeys) {  // whole tile in range (uniform)
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * 512;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ch < CHUNKS) {
-        const int s = t0 + ch / CPR;
-        if (s < nkeys) v = *reinterpret_cast<const u32x4*>(kbase + (int64_t)s * DI + (ch % CPR) * 8);
+      for (int c = 0; c < CPT; ++c) {
+        const int ch = tid + c * 512;
+        pre[c] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(t0 + ch / CPR) * DI + (ch % CPR) * 8);
       }
-      pre[c] = v;
+    } else {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int ch = tid + c * 512;
+        const int s = t0 + ch / CPR;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (s < nkeys) v = *reinterpret_cast<const u32x4*>(kbase + (int64_t)s * DI + (ch % CPR) * 8);
+        pre[c] = v;
+      }
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < CPT; ++c) {
       const int ch = tid + c * 512;
-      if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&kt[buf][(ch / CPR) * ROW + (ch % CPR) * 8]) = pre[c];
+      *reinterpret_cast<u32x4*>(&kt[buf][(ch / CPR) * ROW + (ch % CPR) * 8]) = pre[c];
     }
   };
-  auto mma = [&](const uint16_t* kp, f32x16 (&acc)[HT]) {
+  auto rdB = [&](const uint16_t* kp, int h, bf16x8 (&dst)[KH]) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(kp + ks * 16);
+    for (int i = 0; i < KH; ++i) dst[i] = *reinterpret_cast<const bf16x8*>(kp + (h * KH + i) * 16);
+  };
+  auto mmaH = [&](const bf16x8 (&bv)[KH], int h, f32x16 (&acc)[HT]) {
+#pragma unroll
+    for (int i = 0; i < KH; ++i) {
+      const int ks = h * KH + i;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
-        acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][ks], bv, ks == 0 ? f32x16{} : acc[ht], 0, 0, 0);
+        acc[ht] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ht][ks], bv[i], ks == 0 ? f32x16{} : acc[ht], 0, 0, 0);
     }
   };
-  // ReLU, head weights, sum over the 32 heads of each tile, then over tiles; lanes 0-31 store key lane%32.
-  auto epilogue = [&](const f32x16 (&acc)[HT], int s0) {
-    float part = 0.f;
+  // ReLU and head weights over accumulator entries [8h, 8h + 8) of every head tile
+  auto epiH = [&](const f32x16 (&acc)[HT], int h, float part) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) part = __builtin_fmaf(relu_bits(acc[ht][i]), wv[ht][i], part);
+      for (int i = 8 * h; i < 8 * h + 8; ++i) part = __builtin_fmaf(relu_bits(acc[ht][i]), wv[ht][i], part);
+    return part;
+  };
+  // sum of the two lane halves (the other 16 heads of each 32-head tile); lanes 0-31 store key lane%32
+  auto finish = [&](float part, int s0) {
     part += __shfl_xor(part, 32, 64);
-    const int s = s0 + (lane & 31);
-    if (qvalid && lane < 32 && s < nkeys) srow[s] = s < vrel ? part : -INFINITY;
+    if (s0 + 32 <= vrel) {
+      if (storer) srow[s0] = part;
+    } else if (storer && s0 + (lane & 31) < nkeys) {
+      srow[s0] = s0 + (lane & 31) < vrel ? part : -INFINITY;
+    }
   };
 
   gload(0);
   lstore(0);
   __syncthreads();
+  f32x16 acc[2][HT];
+  bf16x8 b0[KH], b1[KH];
   for (int it = 0; it < ntiles; ++it) {
     const int t0 = it * TILE;
     if (it + 1 < ntiles) gload(t0 + TILE);
-    const uint16_t* kp = &kt[it & 1][(kl * SUB * 32 + (lane & 31)) * ROW + 8 * (lane >> 5)];
-    f32x16 acc[2][HT];
-    mma(kp, acc[0]);
+    const uint16_t* kp = &kt[it & 1][(lane & 31) * ROW + 8 * (lane >> 5)];
+    rdB(kp, 0, b0);
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb) {
-      if (sb + 1 < SUB) mma(kp + (sb + 1) * 32 * ROW, acc[(sb + 1) & 1]);  // next sub-block's MFMAs first
-      epilogue(acc[sb & 1], t0 + (kl * SUB + sb) * 32);
+      // the previous sub-block (of this tile, or the last of the previous tile) is epilogued here
+      const bool prev = sb > 0 || it > 0;
+      const int sp = t0 + sb * 32 - 32;
+      // phase 0
+      rdB(kp + sb * 32 * ROW, 1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+      mmaH(b0, 0, acc[sb & 1]);
+      float part = 0.f;
+      if (prev) part = epiH(acc[(sb + 1) & 1], 0, 0.f);
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 1
+      if (sb + 1 < SUB) rdB(kp + (sb + 1) * 32 * ROW, 0, b0);
+      __builtin_amdgcn_sched_barrier(0);
+      mmaH(b1, 1, acc[sb & 1]);
+      if (prev) finish(epiH(acc[(sb + 1) & 1], 1, part), sp);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (it + 1 < ntiles) lstore((it + 1) & 1);
     __syncthreads();
   }
+  // last sub-block of the last tile
+  finish(epiH(acc[(SUB - 1) & 1], 1, epiH(acc[(SUB - 1) & 1], 0, 0.f)), ntiles * TILE - 32);
 }
 
 // Decode-shaped rows (fewer than 64 queries in the call): row_waves waves score
