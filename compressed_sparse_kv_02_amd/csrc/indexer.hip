@@ -87,8 +87,7 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
   }
 
   const uint16_t* kbase = (const uint16_t*)a.KI + ((int64_t)b * a.N + kbeg) * DI;
-  float* srow = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS + kbeg + (lane & 31);
-  const bool storer = qvalid && lane < 32;
+  float* rowp = a.scores + ((int64_t)b * a.rows_ws + (qvalid ? jr : 0)) * a.ldS + kbeg;
   const int ntiles = (nkeys + TILE - 1) / TILE;
 
   u32x4 pre[CPT];
@@ -138,14 +137,19 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
       for (int i = 8 * h; i < 8 * h + 8; ++i) part = __builtin_fmaf(relu_bits(acc[ht][i]), wv[ht][i], part);
     return part;
   };
-  // sum of the two lane halves (the other 16 heads of each 32-head tile); lanes 0-31 store key lane%32
+  // sum of the two lane halves (the other 16 heads of each 32-head tile); lanes 0-31 store key
+  // lane%32 through a buffer descriptor that covers this sub-block's keys of this row, so that the
+  // hardware drops the stores of keys past the span (and of a padding query) without branches
   auto finish = [&](float part, int s0) {
-    part += __shfl_xor(part, 32, 64);
-    if (s0 + 32 <= vrel) {
-      if (storer) srow[s0] = part;
-    } else if (storer && s0 + (lane & 31) < nkeys) {
-      srow[s0] = s0 + (lane & 31) < vrel ? part : -INFINITY;
+    {  // lanes 0-31 receive lanes 32-63
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+      part += __uint_as_float(sw[1]);
     }
+    const int left = nkeys - s0;
+    const int nrec = (qvalid && left > 0) ? 4 * (left < 32 ? left : 32) : 0;  // 0: all dropped
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(rowp + s0, (short)0, nrec, 0x00020000);
+    const float v = s0 + (lane & 31) < vrel ? part : -INFINITY;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, lane < 32 ? 4 * lane : 256, 0, 0);
   };
 
   gload(0);

@@ -696,6 +696,37 @@ def test_indexer_topk_matches_its_two_halves():
     assert torch.equal(a, b)
 
 
+
+@pytest.mark.parametrize("dtype,bt,Tq,N,HI,dI,pos0,m", [
+    ("bf16", 1, 77, 5000, 20, 64, 16000, 4),   # several key spans per row, partial last tiles
+    ("bf16", 2, 300, 400, 64, 128, 0, 4),      # one span, rows with no visible entry
+    ("bf16", 3, 5, 70000, 64, 128, 4 * 70000, 4),  # decode-shaped rows
+    ("f32", 1, 100, 128, 2, 32, 0, 4),
+])
+def test_indexer_scores_write_extent(dtype, bt, Tq, N, HI, dI, pos0, m):
+    # every visible entry gets a finite score; past V_t only -inf may be written, and nothing
+    # at or past the last row's V (the end of every swept key range) or past N is touched
+    say("indexer_scores write extent", dtype, bt, Tq, N, HI, dI, pos0, m)
+    qI = gen(23, "we.q", (bt, Tq, HI, dI), dtype)
+    KI = gen(23, "we.k", (bt, N, dI), dtype)
+    wI = uniform_device(23, "we.w", (bt, Tq, HI), DEV)
+    ld = B.score_ld(N) + 8
+    sc = torch.full((bt, Tq, ld), float("nan"), dtype=torch.float32, device=DEV)
+    B.indexer_scores(qI, wI, KI, pos0, m, scores=sc)
+    torch.cuda.synchronize()
+    sc = sc.cpu()
+    V = torch.tensor([O.visible(pos0 + r, m, N) for r in range(Tq)])
+    vend = int(V.max())
+    col = torch.arange(ld)
+    for b in range(bt):
+        x = sc[b]
+        vis = col[None, :] < V[:, None]
+        assert torch.isfinite(x[vis]).all(), f"b{b}: visible entry not written or not finite"
+        mid = (~vis) & (col[None, :] < vend)
+        assert (torch.isnan(x[mid]) | torch.isneginf(x[mid])).all(), f"b{b}: past V_t something other than -inf"
+        assert torch.isnan(x[:, vend:]).all(), f"b{b}: written at or past the end of the swept range"
+
+
 # ----------------------------------------------------------------------------- projections
 
 def _gemm_bound(A, B, ref):
