@@ -130,6 +130,37 @@ __device__ __forceinline__ int key_of_row(int r) {
   return (r >> 1) + 16 * (r & 1);
 }
 
+// Maximum / sum over the four 16-lane groups (lanes l, l^16, l^32, l^48) in every lane.
+// SWAP: through gfx950's row swaps on the vector ALU, so the partner values never leave
+// the register file and no LDS round trip sits in the softmax's dependency chain; each
+// swap hands every lane its own value and its partner's, combined in either order (max
+// and + commute), so the result has the same bits as the cross-lane reads of !SWAP,
+// which need two fewer registers (kernels at the register limit keep them).
+template <bool SWAP>
+__device__ __forceinline__ float group4_max(float x) {
+  if constexpr (SWAP) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+  } else {
+    x = fmaxf(x, __shfl_xor(x, 16, 64));
+    return fmaxf(x, __shfl_xor(x, 32, 64));
+  }
+}
+template <bool SWAP>
+__device__ __forceinline__ float group4_sum(float x) {
+  if constexpr (SWAP) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+  } else {
+    x += __shfl_xor(x, 16, 64);
+    return x + __shfl_xor(x, 32, 64);
+  }
+}
+
 // Logits of a query only grow the softmax reference when they exceed it by this
 // much (log2 units): the O/l rescale is then almost never needed, and P <= 2^8.
 constexpr float REF_SLACK = 8.0f;
@@ -368,9 +399,7 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
     }
     // sv holds raw dot products; base-2 logits are sv * scale_log2 (> 0, so the maximum commutes)
     float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-    mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-    mb *= a.scale_log2;
+    mb = group4_max<OCC == 1>(mb) * a.scale_log2;
     // lazy reference: move it only when a logit exceeds it by REF_SLACK
     const bool upd = mb > m_ref + REF_SLACK;
     float alpha = 1.f;
@@ -386,8 +415,7 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
       p[i] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.scale_log2, -m_ref));
       ps += p[i];
     }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
+    ps = group4_sum<OCC == 1>(ps);
     l_run = l_run * alpha + ps;
     if (__ballot(upd) != 0) {
 #pragma unroll
