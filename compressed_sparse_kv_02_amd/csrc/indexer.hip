@@ -13,7 +13,8 @@
 // K = dI), fused with the ReLU and the weighted head-sum in registers. A
 // workgroup of 8 waves holds QB queries (their q rows stay in registers as
 // MFMA A operands) and streams a span of keys through double-buffered LDS
-// tiles, so each key row fetched from HBM feeds QB queries. With QB = 1
+// tiles, copied straight from global memory into LDS (global_load_lds, no
+// staging registers), so each key row fetched from HBM feeds QB queries. With QB = 1
 // (decode) the 8 waves take different key blocks and many workgroups split
 // the key range. Scores go to a caller workspace as fp32 rows.
 #include "indexer.h"
@@ -36,12 +37,15 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
   constexpr int DI = 16 * KS;
   constexpr int KH = KS / 2;           // k-steps per phase
   constexpr int TILE = SUB * 32;       // keys per LDS tile
-  constexpr int ROW = DI + 8;          // padded LDS row (bf16), +16 bytes vs bank conflicts
   constexpr int CPR = DI / 8;          // 16-byte chunks per key row
-  constexpr int CHUNKS = TILE * CPR;
-  constexpr int CPT = (CHUNKS + 511) / 512;
-  static_assert(CHUNKS % 512 == 0, "whole chunks per thread");
-  __shared__ __attribute__((aligned(16))) uint16_t kt[2][TILE * ROW];
+  constexpr int RPI = 64 / CPR;        // key rows per direct-to-LDS copy (64 lanes x 16 bytes)
+  constexpr int IPW = 32 / RPI;        // copies per wave per tile (each wave copies 32 rows)
+  constexpr int SH = CPR == 16 ? 1 : CPR == 8 ? 2 : 3;  // log2(32 / CPR)
+  static_assert(SUB == 8 && CPR >= 4 && CPR <= 16, "tile shape");
+  // Unpadded rows; chunk c of row r sits at position c ^ sw(r), sw(r) = (r >> SH) % CPR, so the
+  // 32 rows of a 32-lane B read (one chunk each) hit 32 distinct 4-bank groups. Two arrays
+  // (not one [2][...]) let the compiler see that a copy into one never feeds reads of the other.
+  __shared__ __attribute__((aligned(16))) uint16_t kt0[TILE * DI], kt1[TILE * DI];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int qs = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -90,35 +94,28 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
   float* rowp = a.scores + ((int64_t)b * a.rows_ws + (qvalid ? jr : 0)) * a.ldS + kbeg;
   const int ntiles = (nkeys + TILE - 1) / TILE;
 
-  u32x4 pre[CPT];
-  auto gload = [&](int t0) {
-    if (t0 + TILE <= nkeys) {  // whole tile in range (uniform)
+  // direct-to-LDS copy of tile t0 into buf: wave w copies rows 32 w .. 32 w + 31; lane l of a
+  // copy lands at 16 l bytes past the copy's base, i.e. row l / CPR, position l % CPR, and
+  // fetches the chunk stored there. Rows past the span fetch row 0 (their scores are dropped).
+  auto dma = [&](int t0, uint16_t* buf) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int ch = tid + c * 512;
-        pre[c] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)(t0 + ch / CPR) * DI + (ch % CPR) * 8);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int ch = tid + c * 512;
-        const int s = t0 + ch / CPR;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (s < nkeys) v = *reinterpret_cast<const u32x4*>(kbase + (int64_t)s * DI + (ch % CPR) * 8);
-        pre[c] = v;
-      }
+    for (int i = 0; i < IPW; ++i) {
+      const int rr = 32 * qs + i * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ ((rr >> SH) % CPR);
+      const int s = t0 + rr < nkeys ? t0 + rr : 0;
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + (int64_t)s * DI + c * 8),
+                                       (__attribute__((address_space(3))) void*)(buf + (32 * qs + i * RPI) * DI), 16, 0,
+                                       0);
     }
   };
-  auto lstore = [&](int buf) {
+  // B operand of k-step ks for the lane's key row: chunk 2 ks + (lane / 32) at its swizzled
+  // position; bofs holds the lane's element offset of each k-step within a sub-block
+  int bofs[KS];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * 512;
-      *reinterpret_cast<u32x4*>(&kt[buf][(ch / CPR) * ROW + (ch % CPR) * 8]) = pre[c];
-    }
-  };
+  for (int ks = 0; ks < KS; ++ks) bofs[ks] = (lane & 31) * DI + (((2 * ks + (lane >> 5)) ^ (((lane & 31) >> SH) % CPR)) * 8);
   auto rdB = [&](const uint16_t* kp, int h, bf16x8 (&dst)[KH]) {
 #pragma unroll
-    for (int i = 0; i < KH; ++i) dst[i] = *reinterpret_cast<const bf16x8*>(kp + (h * KH + i) * 16);
+    for (int i = 0; i < KH; ++i) dst[i] = *reinterpret_cast<const bf16x8*>(kp + bofs[h * KH + i]);
   };
   auto mmaH = [&](const bf16x8 (&bv)[KH], int h, f32x16 (&acc)[HT]) {
 #pragma unroll
@@ -152,15 +149,17 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, lane < 32 ? 4 * lane : 256, 0, 0);
   };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  // wait for this wave's copies, then a workgroup barrier (every copy of the tile has landed and
+  // every wave is done with the other buffer)
+  auto wait_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);  // every counter at zero: the compiler's wait tracking sees it
+    __syncthreads();
+  };
   f32x16 acc[2][HT];
   bf16x8 b0[KH], b1[KH];
-  for (int it = 0; it < ntiles; ++it) {
+  auto tile = [&](int it, const uint16_t* kb) {
     const int t0 = it * TILE;
-    if (it + 1 < ntiles) gload(t0 + TILE);
-    const uint16_t* kp = &kt[it & 1][(lane & 31) * ROW + 8 * (lane >> 5)];
+    const uint16_t* kp = kb;
     rdB(kp, 0, b0);
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb) {
@@ -168,22 +167,32 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
       const bool prev = sb > 0 || it > 0;
       const int sp = t0 + sb * 32 - 32;
       // phase 0
-      rdB(kp + sb * 32 * ROW, 1, b1);
+      rdB(kp + sb * 32 * DI, 1, b1);
       __builtin_amdgcn_sched_barrier(0);
       mmaH(b0, 0, acc[sb & 1]);
       float part = 0.f;
       if (prev) part = epiH(acc[(sb + 1) & 1], 0, 0.f);
       __builtin_amdgcn_sched_barrier(0);
       // phase 1
-      if (sb + 1 < SUB) rdB(kp + (sb + 1) * 32 * ROW, 0, b0);
+      if (sb + 1 < SUB) rdB(kp + (sb + 1) * 32 * DI, 0, b0);
       __builtin_amdgcn_sched_barrier(0);
       mmaH(b1, 1, acc[sb & 1]);
       if (prev) finish(epiH(acc[(sb + 1) & 1], 1, part), sp);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (it + 1 < ntiles) lstore((it + 1) & 1);
-    __syncthreads();
+  };
+  dma(0, kt0);
+  wait_barrier();
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    dma((it + 1) * TILE, kt1);
+    tile(it, kt0);
+    wait_barrier();
+    dma((it + 2 < ntiles ? it + 2 : it) * TILE, kt0);  // unconditional (a join would cost a full wait)
+    tile(it + 1, kt1);
+    wait_barrier();
   }
+  if (it < ntiles) tile(it, kt0);
   // last sub-block of the last tile
   finish(epiH(acc[(SUB - 1) & 1], 1, epiH(acc[(SUB - 1) & 1], 0, 0.f)), ntiles * TILE - 32);
 }
