@@ -15,9 +15,11 @@
 //    workgroup into LDS (angles formed in fp64).
 //  * The key list -- selected (CSA) or visible (HCA) compressed entries, then
 //    window rows -- is gathered 32 rows at a time into a double-buffered LDS
-//    tile; one register-staged prefetch overlaps the next tile's loads with
-//    this tile's math (the CSA index list is staged in LDS first, so row
-//    addresses never wait on a global load). K = V: one tile serves both
+//    tile; the next tile's loads overlap this tile's math, staged through
+//    registers, or, in the CSA prefill build (two workgroups per CU), copied
+//    straight into LDS (global_load_lds, one 1 KiB row per wave instruction),
+//    which frees the 32 staging registers (the CSA index list is staged in
+//    LDS first, so row addresses never wait on a global load). K = V: one tile serves both
 //    products. Keys sit in LDS rows by a fixed permutation that keeps both
 //    the K-operand reads and the transpose reads free of bank conflicts.
 //  * S^T = K Q^T (v_mfma_f32_16x16x32_bf16) leaves each lane the logits of
@@ -170,7 +172,8 @@ constexpr float REF_SLACK = 8.0f;
 // them to bf16 rows in LDS (exact: E4M3 times a power of two is a bf16 value), so the rest
 // of the kernel is unchanged. Window rows stay bf16. KVR < 0: bf16 entries.
 // OCC = 2 asks the compiler for two workgroups per CU (at most 256 registers per lane):
-// CSA prefill then has two gathers in flight per CU, which pays for a few spills.
+// CSA prefill then has two gathers in flight per CU. Its tiles are copied straight into
+// LDS, so it needs no staging registers (no spills) and affords the row-swap softmax.
 template <int D, int HW, int QG, int KVR, int OCC = 1>
 __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
   constexpr bool KV8 = KVR >= 0;
@@ -184,8 +187,10 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
   static_assert(CPR % TPK == 0, "loader mapping");
   constexpr int CPT = CPR / TPK;     // chunks per loader thread per tile
   constexpr int MAXPAIRS = D / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t kt[2][32 * ROWE];
-  __shared__ __attribute__((aligned(16))) int kvq[2][32];  // logical key -> bit q: valid for query q
+  // double-buffered key tiles as two separately declared arrays: with direct-to-LDS copies
+  // the compiler then sees that a copy into one buffer never feeds reads of the other
+  __shared__ __attribute__((aligned(16))) uint16_t kt0[32 * ROWE], kt1[32 * ROWE];
+  __shared__ __attribute__((aligned(16))) int kvq0[32], kvq1[32];  // logical key -> bit q: valid for query q
   __shared__ float rope_cs[QG][MAXPAIRS][2];
   __shared__ int idx_s[CSKV_MAX_TOPK];  // CSA: the query's selected entries, staged once
 
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
     }
     pre_ok = ok;
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](uint16_t* ktb, int* kvqb) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int oc = c0 + TPK * i;
@@ -358,23 +363,55 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
         v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c23, pre_sc, false));
         v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c23, pre_sc, true));
       }
-      *reinterpret_cast<u32x4*>(&kt[buf][kr * ROWE + oc * 8]) = v;
+      *reinterpret_cast<u32x4*>(&ktb[kr * ROWE + oc * 8]) = v;
     }
-    if (c0 == 0) kvq[buf][key_of_row(kr)] = pre_ok;
+    if (c0 == 0) kvqb[key_of_row(kr)] = pre_ok;
+  };
+  // bf16 entries of 512 dims: one key row is one 1 KiB wave copy straight into LDS
+  // (global_load_lds_dwordx4, lane l -> bytes 16 l .. 16 l + 15 of the row), so no staging
+  // registers. Wave w copies LDS rows w, w + NW, ...; an absent key copies a window row
+  // (finite data; its validity bits are 0, so its weight is exactly 0).
+  constexpr bool DMA = KVR < 0 && D == 512 && OCC == 2;
+  auto dma = [&](int64_t blk, uint16_t* ktb, int* kvqb) {
+#pragma unroll
+    for (int i = 0; i < 32 / NW; ++i) {
+      const int rr = wave + i * NW;
+      const int L = key_of_row(rr);
+      const int64_t u = blk * 32 + L;
+      const uint16_t* src = (const uint16_t*)a.win + wbase * D;
+      int ok = 0;
+      if (u < n_comp) {
+        const int64_t s_ = csa ? (int64_t)idx_s[u] : u;
+        if (s_ >= 0 && s_ < a.N) {
+          src = kvb + s_ * D;
+#pragma unroll
+          for (int q = 0; q < QG; ++q) ok |= (csa || s_ < vis_q[q]) ? (1 << q) : 0;
+        }
+      } else if (u < n_tot) {
+        const int64_t pos = lo + (u - n_comp);
+        int64_t wr = wr_lo + (u - n_comp);
+        if (wr >= a.W) wr -= a.W;
+        src = (const uint16_t*)a.win + (wbase + wr) * D;
+#pragma unroll
+        for (int q = 0; q < QG; ++q) ok |= (pos >= t_q[q] - a.w + 1 && pos <= t_q[q]) ? (1 << q) : 0;
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(src + lane * 8),
+                                       (__attribute__((address_space(3))) void*)(&ktb[rr * ROWE]), 16, 0, 0);
+      if (lane == 0) kvqb[L] = ok;
+    }
+  };
+  // every copy of the tile has landed and every wave is done with the other buffer; the
+  // explicit full wait is visible to the compiler's wait tracking (one in inline asm is not)
+  auto wait_barrier = [&]() {
+    if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
 
-  if (blk0 < blk1) {
-    gload(blk0);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int64_t blk = blk0; blk < blk1; ++blk) {
-    const int buf = (int)((blk - blk0) & 1);
-    if (blk + 1 < blk1) gload(blk + 1);
-
+  // one key tile: S^T, online softmax, O^T update, from buffer (ktb, kvqb)
+  auto tile = [&](const uint16_t* ktb, const int* kvqb) {
     // S^T = K Q^T: s0 -> keys 4g+i, s1 -> keys 16+4g+i; column = head n
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-    const uint16_t* kp = &kt[buf][key_row_of(n) * ROWE + 8 * g];  // logical key n; 16+n is the next row
+    const uint16_t* kp = &ktb[key_row_of(n) * ROWE + 8 * g];  // logical key n; 16+n is the next row
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kp + ks * 32);
@@ -382,8 +419,8 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qb[ks], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qb[ks], s1, 0, 0, 0);
     }
-    const int4 d0 = *reinterpret_cast<const int4*>(&kvq[buf][4 * g]);
-    const int4 d1 = *reinterpret_cast<const int4*>(&kvq[buf][16 + 4 * g]);
+    const int4 d0 = *reinterpret_cast<const int4*>(&kvqb[4 * g]);
+    const int4 d1 = *reinterpret_cast<const int4*>(&kvqb[16 + 4 * g]);
     float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
     // masking only where some key of the tile is invalid for this wave's query (tile edges)
     const int vall = d0.x & d0.y & d0.z & d0.w & d1.x & d1.y & d1.z & d1.w;
@@ -399,7 +436,7 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
     }
     // sv holds raw dot products; base-2 logits are sv * scale_log2 (> 0, so the maximum commutes)
     float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mb = group4_max<OCC == 1>(mb) * a.scale_log2;
+    mb = group4_max<OCC == 1 || DMA>(mb) * a.scale_log2;
     // lazy reference: move it only when a logit exceeds it by REF_SLACK
     const bool upd = mb > m_ref + REF_SLACK;
     float alpha = 1.f;
@@ -415,7 +452,7 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
       p[i] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.scale_log2, -m_ref));
       ps += p[i];
     }
-    ps = group4_sum<OCC == 1>(ps);
+    ps = group4_sum<OCC == 1 || DMA>(ps);
     l_run = l_run * alpha + ps;
     if (__ballot(upd) != 0) {
 #pragma unroll
@@ -430,7 +467,7 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
 
     // O^T += V^T P^T: A = V^T via transpose reads (lane n of group g: keys 4g+e / 16+4g+e for
     // e = n/4, dims 16tt + 4(n%4) .. +3), B = P^T already in this lane (head n, 8 keys).
-    const uint16_t* vp0 = &kt[buf][key_row_of(4 * g + (n >> 2)) * ROWE + 4 * (n & 3)];
+    const uint16_t* vp0 = &ktb[key_row_of(4 * g + (n >> 2)) * ROWE + 4 * (n & 3)];
     const uint16_t* vp1 = vp0 + ROWE;
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt) {
@@ -439,8 +476,35 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
       const v4i16 av[2] = {lo4, hi4};
       o[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, o[tt], 0, 0, 0);
     }
-    if (blk + 1 < blk1) lstore(buf ^ 1);
+  };
+  if constexpr (DMA) {
+    if (blk0 < blk1) dma(blk0, kt0, kvq0);
+    wait_barrier();
+    // tile pairs: buffer 0 holds the even tiles of the range, buffer 1 the odd ones
+    for (int64_t blk = blk0; blk < blk1; blk += 2) {
+      if (blk + 1 < blk1) dma(blk + 1, kt1, kvq1);
+      tile(kt0, kvq0);
+      wait_barrier();
+      if (blk + 1 < blk1) {
+        if (blk + 2 < blk1) dma(blk + 2, kt0, kvq0);
+        tile(kt1, kvq1);
+        wait_barrier();
+      }
+    }
+  } else {
+    // register-staged: the next tile's rows are loaded into registers during this tile
+    if (blk0 < blk1) {
+      gload(blk0);
+      lstore(kt0, kvq0);
+    }
     __syncthreads();
+    for (int64_t blk = blk0; blk < blk1; ++blk) {
+      const bool odd = ((blk - blk0) & 1) != 0;
+      if (blk + 1 < blk1) gload(blk + 1);
+      tile(odd ? kt1 : kt0, odd ? kvq1 : kvq0);
+      if (blk + 1 < blk1) lstore(odd ? kt0 : kt1, odd ? kvq0 : kvq1);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: lane holds O[head n][16tt + 4g + i]
