@@ -11,7 +11,7 @@
 // selection is integer work and deterministic.
 //
 // Many rows (prefill): one 512-thread workgroup per row (three fit a compute
-// unit). A sample of the row (128 runs of 32 consecutive entries) gives a
+// unit). A sample of the row (64 runs of 32 consecutive entries) gives a
 // threshold that about 3k entries exceed; one vectorised pass, each wave over
 // its own contiguous share of the row, keeps those entries (in index order)
 // in LDS, an exact 3-pass radix
@@ -31,8 +31,8 @@ namespace cskv {
 // ----------------------------------------------------------------------------
 constexpr int TOPK_THREADS = 512;
 constexpr int TOPK_CAP = 5632;      // candidate (key, index) pairs held in LDS: 53 KiB per workgroup, three per CU
-constexpr int TOPK_SAMPLES = 4096;     // sample of a long row, for the candidate threshold
-constexpr int TOPK_SAMPLE_RUNS = 128;  // ... taken as runs of 32 consecutive entries
+constexpr int TOPK_SAMPLES = 2048;     // sample of a long row, for the candidate threshold
+constexpr int TOPK_SAMPLE_RUNS = 64;   // ... taken as runs of 32 consecutive entries
 
 // Exclusive prefix sum over the workgroup; also returns the total.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total) {
@@ -197,12 +197,12 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
     radix_select([&](int64_t s) { return samp[s]; }, TOPK_SAMPLES, r, sh, tau0, need0);
     __syncthreads();  // the sample (aliasing cidx) is consumed
     // one pass: keep key >= tau0 in index order. Wave w scans its own contiguous
-    // sixteenth of the row (4 consecutive entries per lane per 256-entry chunk, UNR
+    // eighth of the row (4 consecutive entries per lane per 256-entry chunk, UNR
     // chunks loaded before any is scanned) and appends to its own LDS segment of SEG
     // slots with a wave-level prefix sum: no workgroup barrier inside the pass.
     constexpr int NWAVE = TOPK_THREADS / 64;
     constexpr int SEG = TOPK_CAP / NWAVE;
-    constexpr int UNR = 4;
+    constexpr int UNR = 6;
     const int lane = tid & 63, wave = tid >> 6;
     const int64_t len = ((V + NWAVE - 1) / NWAVE + 3) & ~(int64_t)3;  // a multiple of 4
     const int64_t lo = wave * len;
