@@ -364,6 +364,8 @@ def _random_idx(bt, Tq, pos0, m, N, k, seed):
     ("bf16", "hca", 2, 41, 300, 128 * 250, 128, 0, 128, 64, 512, 64, True, True),
     ("bf16", "csa", 1, 37, 90, 0, 4, 256, 16, 64, 512, 64, True, False),
     ("bf16", "csa", 2, 9, 400, 4 * 390, 4, 64, 128, 64, 512, 64, False, True),
+    ("bf16", "csa", 1, 20, 200, 4 * 150, 4, 16, 8, 64, 512, 64, True, True),   # one key tile (16 + 8 keys)
+    ("bf16", "csa", 2, 10, 300, 4 * 290, 4, 64, 16, 64, 512, 64, False, True),  # three key tiles (64 + 16 keys)
 ])
 def test_attention_prefill(dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink):
     say("attention", dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink)
