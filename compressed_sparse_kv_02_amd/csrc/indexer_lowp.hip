@@ -20,11 +20,12 @@
 // are correctly rounded fp32.
 //
 // The scoring kernels follow the bf16 ones: 8 queries per workgroup sharing
-// 256-key LDS tiles for prefill; for decode, interleaved 32-key blocks per
-// wave with coalesced loads turned into the MFMA layout through per-wave LDS
-// rows. A key row is dI bytes; each lane holds one contiguous half of it
-// (the K dimension permuted identically in A and B: lane half h, k-step ks
-// holds bytes h*dI/2 + 32*ks .. +32).
+// 256-key LDS tiles copied straight from global memory for prefill; for
+// decode, interleaved 32-key blocks per wave with coalesced loads turned into
+// the MFMA layout through per-wave LDS rows. A key row is DI bytes (dI for
+// E4M3, dI/2 for E2M1); each lane holds one contiguous half of it (the K
+// dimension permuted identically in A and B: lane half h, k-step ks holds
+// bytes h*DI/2 + OB*ks .. + OB, OB = 32 bytes for E4M3, 16 for E2M1).
 #include "indexer.h"
 
 namespace cskv {
@@ -164,25 +165,35 @@ __device__ __forceinline__ void load_query_lowp(const IdxArgs& a, int b, int64_t
   }
 }
 
-// Prefill rows: 8 queries per workgroup (one per wave) sharing 256-key LDS tiles.
+// Prefill rows: 8 queries per workgroup (one per wave) sharing 256-key LDS tiles, copied
+// straight from global memory into LDS (global_load_lds, no staging registers) as in the bf16
+// kernel: unpadded rows, chunk c of row r at position c ^ ((r >> SH) % CPR), so the 32 rows of a
+// 32-lane B read (one 16-byte chunk each) hit 32 distinct 4-bank groups. The key scales travel
+// the same way (4 bytes per lane). Each 32-key sub-block reads the next one's B operands first,
+// then issues its MFMAs beside the previous sub-block's ReLU / weighted head-sum.
 template <int FMT, int HT, int KS8>
 __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
-  constexpr int QB = 8;
-  constexpr int SUB = 8;               // 32-key sub-blocks per wave per tile
+  constexpr int QB = 8;                // queries per workgroup (one per wave)
+  constexpr int SUB = 8;               // 32-key sub-blocks per tile (even)
   constexpr int TILE = SUB * 32;
   constexpr int DI = 64 * KS8 * LowP<FMT>::BITS / 8;  // bytes per key row
-  constexpr int OB = LowP<FMT>::OB;
-  constexpr int ROW = DI + 16;         // padded LDS row, against bank conflicts
-  constexpr int CPR = DI / 16;
-  constexpr int CHUNKS = TILE * CPR;
-  constexpr int CPT = (CHUNKS + 511) / 512;
-  __shared__ __attribute__((aligned(16))) uint8_t kt[2][TILE * ROW];
-  __shared__ float ksc[2][TILE];
+  constexpr int OB = LowP<FMT>::OB;    // operand bytes per lane per k-step
+  constexpr int CPO = OB / 16;         // 16-byte chunks per operand
+  constexpr int CPR = DI / 16;         // 16-byte chunks per key row
+  constexpr int RPI = 64 / CPR;        // key rows per direct-to-LDS copy (64 lanes x 16 bytes)
+  constexpr int IPW = 32 / RPI;        // copies per wave per tile (each wave copies 32 rows)
+  constexpr int SH = CPR == 16 ? 1 : CPR == 8 ? 2 : CPR == 4 ? 3 : 4;  // log2(32 / CPR)
+  static_assert(TILE == 32 * QB && CPR >= 2 && CPR <= 16 && IPW >= 1, "tile shape");
+  // two arrays per buffer kind (not [2][...]): the compiler then sees that a copy into one
+  // never feeds reads of the other. Scales: wave w copies keys 32 w + (lane % 32) to 64 w + lane.
+  __shared__ __attribute__((aligned(16))) uint8_t kt0[TILE * DI], kt1[TILE * DI];
+  __shared__ float ks0[2 * TILE], ks1[2 * TILE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int qs = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.z;
   const int64_t qblk = (int64_t)gridDim.y - 1 - blockIdx.y;  // longest rows first
-  const int64_t jr = qblk * QB + wave;
+  const int64_t jr = qblk * QB + qs;
   const bool qvalid = jr < a.nrows;
   const int64_t j = a.row0 + (qvalid ? jr : 0);
   int64_t jl = qblk * QB + QB - 1;
@@ -194,7 +205,8 @@ __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
   if (kbeg >= kend) return;  // uniform for the workgroup
   const int64_t vj = qvalid ? visible_entries(a.pos0 + j, a.m, a.N) : 0;
   const int nkeys = (int)(kend - kbeg);
-  const int vrel = (int)((vj > kbeg ? vj : kbeg) - kbeg);
+  // visible keys of this query within this workgroup's span
+  const int vrel = (int)((vj < kbeg ? kbeg : (vj > kend ? kend : vj)) - kbeg);
 
   i32x8 qa[HT][KS8];
   float wv[HT][16];
@@ -202,71 +214,106 @@ __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
 
   const uint8_t* kbase = (const uint8_t*)a.KI + ((int64_t)b * a.N + kbeg) * DI;
   const float* kscale = a.k_scale + (int64_t)b * a.N + kbeg;
-  float* srow = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS + kbeg;
+  float* rowp = a.scores + ((int64_t)b * a.rows_ws + (qvalid ? jr : 0)) * a.ldS + kbeg;
   const int ntiles = (nkeys + TILE - 1) / TILE;
 
-  u32x4 pre[CPT];
-  float pre_s = 0.f;
-  auto gload = [&](int t0) {
+  // direct-to-LDS copy of tile t0: wave w copies rows 32 w .. 32 w + 31 (lane l of a copy lands
+  // 16 l bytes past its base: row l / CPR, position l % CPR) and their scales. Rows past the span
+  // fetch row 0 (their scores are dropped).
+  auto dma = [&](int t0, uint8_t* buf, float* sbuf) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * 512;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ch < CHUNKS) {
-        const int s = t0 + ch / CPR;
-        if (s < nkeys) v = *reinterpret_cast<const u32x4*>(kbase + (int64_t)s * DI + (ch % CPR) * 16);
-      }
-      pre[c] = v;
+    for (int i = 0; i < IPW; ++i) {
+      const int rr = 32 * qs + i * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ ((rr >> SH) % CPR);
+      const int s = t0 + rr < nkeys ? t0 + rr : 0;
+      __builtin_amdgcn_global_load_lds((const void*)(kbase + (int64_t)s * DI + c * 16),
+                                       (__attribute__((address_space(3))) void*)(buf + (32 * qs + i * RPI) * DI), 16,
+                                       0, 0);
     }
-    if (tid < TILE) pre_s = t0 + tid < nkeys ? kscale[t0 + tid] : 0.f;
+    const int ss = t0 + 32 * qs + (lane & 31);
+    __builtin_amdgcn_global_load_lds((const void*)(kscale + (ss < nkeys ? ss : 0)),
+                                     (__attribute__((address_space(3))) void*)(sbuf + 64 * qs), 4, 0, 0);
   };
-  auto lstore = [&](int buf) {
+  // B operand of k-step ks for the lane's key row (lane half h holds bytes h DI/2 + OB ks .. + OB):
+  // its CPO chunks at their swizzled positions; bofs holds their byte offsets within a sub-block
+  int bofs[KS8][CPO];
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + c * 512;
-      if (ch < CHUNKS) *reinterpret_cast<u32x4*>(&kt[buf][(ch / CPR) * ROW + (ch % CPR) * 16]) = pre[c];
-    }
-    if (tid < TILE) ksc[buf][tid] = pre_s;
-  };
-  auto mma = [&](const uint8_t* kp, f32x16 (&acc)[HT]) {
+  for (int ks = 0; ks < KS8; ++ks)
+#pragma unroll
+    for (int q = 0; q < CPO; ++q)
+      bofs[ks][q] = (lane & 31) * DI + ((((lane >> 5) * (CPR / 2) + ks * CPO + q) ^ (((lane & 31) >> SH) % CPR)) * 16);
+  auto rdB = [&](const uint8_t* kp, i32x8 (&dst)[KS8]) {
 #pragma unroll
     for (int ks = 0; ks < KS8; ++ks) {
-      const i32x8 bv = load_op<FMT>(kp + OB * ks);
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_lowp<FMT>(qa[ht][ks], bv, ks == 0 ? f32x16{} : acc[ht]);
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(kp + bofs[ks][0]);
+      if constexpr (CPO == 2) {
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(kp + bofs[ks][CPO - 1]);
+        dst[ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      } else {
+        dst[ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+      }
     }
   };
-  // ReLU, folded head weights, head sum; lanes 0-31 scale by their key's ks and store.
-  auto epilogue = [&](const f32x16 (&acc)[HT], int sub0, int t0, int buf) {
+  auto mma = [&](const i32x8 (&bv)[KS8], f32x16 (&acc)[HT]) {
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks)
+#pragma unroll
+      for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_lowp<FMT>(qa[ht][ks], bv[ks], ks == 0 ? f32x16{} : acc[ht]);
+  };
+  // ReLU, folded head weights, head sum, the other lane half (the other 16 heads of each 32-head
+  // tile), the key scale; lanes 0-31 store key lane%32 through a buffer descriptor that covers this
+  // sub-block's keys of this row, so the hardware drops stores past the span (and of a padding
+  // query) without branches
+  auto finish = [&](const f32x16 (&acc)[HT], int s0, float sc) {
     float part = 0.f;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
       for (int i = 0; i < 16; ++i) part = __builtin_fmaf(relu_bits(acc[ht][i]), wv[ht][i], part);
-    part += __shfl_xor(part, 32, 64);
-    const int kt_i = sub0 + (lane & 31);  // key within the tile
-    const int s = t0 + kt_i;
-    if (qvalid && lane < 32 && s < nkeys) srow[s] = s < vrel ? part * ksc[buf][kt_i] : -INFINITY;
+    {  // lanes 0-31 receive lanes 32-63
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part), __float_as_uint(part), false, false);
+      part += __uint_as_float(sw[1]);
+    }
+    const int left = nkeys - s0;
+    const int nrec = (qvalid && left > 0) ? 4 * (left < 32 ? left : 32) : 0;  // 0: all dropped
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(rowp + s0, (short)0, nrec, 0x00020000);
+    const float v = s0 + (lane & 31) < vrel ? part * sc : -INFINITY;
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, lane < 32 ? 4 * lane : 256, 0, 0);
   };
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int it = 0; it < ntiles; ++it) {
+  auto wait_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0);  // every counter at zero: the compiler's wait tracking sees it
+    __syncthreads();
+  };
+  f32x16 acc[2][HT];
+  i32x8 bv[2][KS8];
+  float sc[2];  // scales of the keys of the current and previous sub-block
+  auto tile = [&](int it, const uint8_t* kb, const float* sb_) {
     const int t0 = it * TILE;
-    const int buf = it & 1;
-    if (it + 1 < ntiles) gload(t0 + TILE);
-    const uint8_t* kp = &kt[buf][(lane & 31) * ROW + (DI / 2) * (lane >> 5)];
-    f32x16 acc[2][HT];
-    mma(kp, acc[0]);
+    rdB(kb, bv[0]);
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb) {
-      if (sb + 1 < SUB) mma(kp + (sb + 1) * 32 * ROW, acc[(sb + 1) & 1]);  // next sub-block's MFMAs first
-      epilogue(acc[sb & 1], sb * 32, t0, buf);
+      const bool prev = sb > 0 || it > 0;
+      if (sb + 1 < SUB) rdB(kb + (sb + 1) * 32 * DI, bv[(sb + 1) & 1]);
+      sc[sb & 1] = sb_[64 * sb + lane];  // lanes 32-63 read the same scales as lanes 0-31
+      __builtin_amdgcn_sched_barrier(0);
+      mma(bv[sb & 1], acc[sb & 1]);
+      if (prev) finish(acc[(sb + 1) & 1], t0 + sb * 32 - 32, sc[(sb + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (it + 1 < ntiles) lstore(buf ^ 1);
-    __syncthreads();
+  };
+  dma(0, kt0, ks0);
+  wait_barrier();
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    dma((it + 1) * TILE, kt1, ks1);
+    tile(it, kt0, ks0);
+    wait_barrier();
+    dma((it + 2 < ntiles ? it + 2 : it) * TILE, kt0, ks0);  // unconditional (a join would cost a full wait)
+    tile(it + 1, kt1, ks1);
+    wait_barrier();
   }
+  if (it < ntiles) tile(it, kt0, ks0);
+  finish(acc[(SUB - 1) & 1], ntiles * TILE - 32, sc[(SUB - 1) & 1]);  // last sub-block of the last tile
 }
 
 // Decode-shaped rows: row_waves waves per query row, wave r taking the 32-key

@@ -212,6 +212,7 @@ def _fp8_case(bt, Tq, N, HI, dI, seed):
     (1, 77, 5000, 20, 64, 16000, 4, 100),             # dI 64, HI not a multiple of 32
     (3, 5, 70000, 64, 128, 4 * 70000, 4, 1024),       # decode route (streaming waves), two-kernel top-k
     (1, 2, 3000, 128, 128, 3000 * 4 - 2, 4, 2048),    # 128 heads, max k
+    (1, 1024, 7000, 64, 128, 4 * 7000 - 1024, 4, 512),  # spans of 3 and 4 key tiles, partial last tiles
 ])
 def test_indexer_fp8(bt, Tq, N, HI, dI, pos0, m, k):
     """FP8 scores and top-k against the oracle on its own quantisation of the same raw inputs."""
@@ -286,6 +287,7 @@ def _unpack(packed_row):
     (1, 77, 5000, 20, 64, 16000, 4, 100),             # dI 64, HI not a multiple of 32
     (3, 5, 70000, 64, 128, 4 * 70000, 4, 1024),       # decode route, two-kernel top-k
     (1, 2, 3000, 128, 128, 3000 * 4 - 2, 4, 2048),    # 128 heads, max k
+    (1, 1024, 7000, 64, 128, 4 * 7000 - 1024, 4, 512),  # spans of 3 and 4 key tiles, partial last tiles
 ])
 def test_indexer_fp4(bt, Tq, N, HI, dI, pos0, m, k):
     """FP4 scores and top-k against the oracle on its own quantisation. E2M1 dot products are exact,
@@ -704,17 +706,28 @@ def test_indexer_topk_matches_its_two_halves():
     ("bf16", 2, 300, 400, 64, 128, 0, 4),      # one span, rows with no visible entry
     ("bf16", 3, 5, 70000, 64, 128, 4 * 70000, 4),  # decode-shaped rows
     ("f32", 1, 100, 128, 2, 32, 0, 4),
+    ("fp8", 1, 1024, 7000, 64, 128, 4 * 7000 - 1024, 4),  # spans of 3 and 4 key tiles
+    ("fp8", 2, 300, 400, 20, 64, 0, 4),
+    ("fp4", 1, 1024, 7000, 64, 128, 4 * 7000 - 1024, 4),
+    ("fp4", 1, 77, 5000, 20, 64, 16000, 4),    # 32-byte key rows
+    ("fp4", 3, 5, 70000, 64, 128, 4 * 70000, 4),
 ])
 def test_indexer_scores_write_extent(dtype, bt, Tq, N, HI, dI, pos0, m):
     # every visible entry gets a finite score; past V_t only -inf may be written, and nothing
     # at or past the last row's V (the end of every swept key range) or past N is touched
     say("indexer_scores write extent", dtype, bt, Tq, N, HI, dI, pos0, m)
-    qI = gen(23, "we.q", (bt, Tq, HI, dI), dtype)
-    KI = gen(23, "we.k", (bt, N, dI), dtype)
+    lowp = dtype in ("fp8", "fp4")
+    qI = gen(23, "we.q", (bt, Tq, HI, dI), "bf16" if lowp else dtype)
+    KI = gen(23, "we.k", (bt, N, dI), "bf16" if lowp else dtype)
     wI = uniform_device(23, "we.w", (bt, Tq, HI), DEV)
     ld = B.score_ld(N) + 8
     sc = torch.full((bt, Tq, ld), float("nan"), dtype=torch.float32, device=DEV)
-    B.indexer_scores(qI, wI, KI, pos0, m, scores=sc)
+    if lowp:
+        qz, fn = (B.quantize_fp8, B.indexer_scores_fp8) if dtype == "fp8" else (B.quantize_fp4, B.indexer_scores_fp4)
+        (qc, qs), (kc, ks) = qz(qI), qz(KI)
+        fn(qc, qs, wI, kc, ks, pos0, m, scores=sc)
+    else:
+        B.indexer_scores(qI, wI, KI, pos0, m, scores=sc)
     torch.cuda.synchronize()
     sc = sc.cpu()
     V = torch.tensor([O.visible(pos0 + r, m, N) for r in range(Tq)])
