@@ -377,6 +377,56 @@ def indexer_scores_fp4(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: i
 
 
 # ---------------------------------------------------------------------------
+# FP4 indexer with block scales ("Paper Breakdown: DeepSeek-V4", "Efficiency
+# (§2.3.4)": FP4 indexer QK path in V4). Reading: the block scales are those
+# of the OCP Microscaling (MX) formats, the published standard for FP4 with
+# shared scales: blocks of 32 consecutive values along dI share one E8M0
+# scale (a power of two, 2**(code - 127)); the shared exponent is
+# floor(log2(amax)) - 2 (2 = the exponent of E2M1's largest value, 6 =
+# 1.5 * 2**2), and each value is stored as E2M1(x / scale) rounded to
+# nearest, ties to even, saturating at +-6. An all-zero block takes scale
+# code 0 and zero codes; exponents below -127 are clamped to code 0.
+# ---------------------------------------------------------------------------
+
+MX_BLOCK = 32
+E2M1_EMAX = 2
+
+
+def mx_scale_codes(amax) -> np.ndarray:
+    """E8M0 code of each block's shared scale from its largest magnitude (fp32 values)."""
+    a = np.asarray(amax, dtype=F64)
+    _, ex = np.frexp(a)                       # a = f * 2**ex, f in [0.5, 1): floor(log2 a) = ex - 1
+    e = ex.astype(np.int64) - 1 - E2M1_EMAX
+    return np.where(a > 0, np.clip(e + 127, 0, 254), 0).astype(np.uint8)
+
+
+def quantize_rows_mxfp4(x) -> Tuple[np.ndarray, np.ndarray]:
+    """MX-FP4 codes (unpacked, one per element) and E8M0 scale codes ([..., dim / 32]) of fp32 rows."""
+    x32 = np.asarray(x, dtype=np.float32)
+    d = x32.shape[-1]
+    assert d % MX_BLOCK == 0
+    xb = x32.reshape(x32.shape[:-1] + (d // MX_BLOCK, MX_BLOCK)).astype(F64)
+    amax = np.abs(xb).max(axis=-1)
+    sc = mx_scale_codes(amax)
+    y = xb / np.exp2(sc.astype(F64) - 127)[..., None]   # exact: a power-of-two divisor
+    codes = np.where((amax > 0)[..., None], e2m1_encode(y), np.uint8(0)).astype(np.uint8)
+    return codes.reshape(x32.shape), sc
+
+
+def dequantize_mxfp4(codes, scales) -> np.ndarray:
+    c = np.asarray(codes)
+    d = c.shape[-1]
+    v = e2m1_decode(c).reshape(c.shape[:-1] + (d // MX_BLOCK, MX_BLOCK))
+    v = v * np.exp2(np.asarray(scales, dtype=F64) - 127)[..., None]
+    return v.reshape(c.shape)
+
+
+def indexer_scores_mxfp4(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int) -> np.ndarray:
+    """Indexer scores on MX-FP4 rows: the plain indexer on the dequantised values."""
+    return indexer_scores(dequantize_mxfp4(q_codes, q_scales), wI, dequantize_mxfp4(k_codes, k_scales), pos0, m)
+
+
+# ---------------------------------------------------------------------------
 # FP8 KV storage ("Paper Breakdown: DeepSeek-V4", "Efficiency (§2.3.4)": V4
 # stores the KV cache as FP8 for the non-RoPE dims and BF16 for the RoPE dims).
 # Readings: the FP8 part is OCP E4M3 with one scale per entry; the scale is a

@@ -450,6 +450,61 @@ def test_indexer_fp4_reduces_to_plain_indexer():
                        O.indexer_scores(q, w, k, pos0=80, m=4) * ks[None, :], rtol=1e-13, atol=0)
 
 
+# ---------------------------------------------------------------- MX-FP4 (E2M1 + E8M0 block scales) indexer
+
+def test_mxfp4_hand_blocks():
+    x = np.zeros((3, 64), dtype=np.float32)
+    # block 0: amax 6 = 1.5 * 2**2 -> shared exponent 0 (code 127), values exact or rounded to even
+    x[0, :6] = [6.0, -3.0, 0.5, 0.25, 1.25, 5.0]
+    # block 1: amax 0.3 -> floor(log2 0.3) = -2 -> exponent -4 (code 123), scale 1/16
+    x[0, 32:35] = [0.3, -0.2, 0.01]
+    # row 1: block 0 all zero; block 1 amax 1000 -> floor(log2) = 9 -> exponent 7 (code 134)
+    x[1, 40:42] = [1000.0, 100.0]
+    # row 2: tiny values: amax 2**-130 -> exponent -132 clamps to code 0 (scale 2**-127), values round to 0
+    x[2, 0] = 2.0 ** -130
+    codes, sc = O.quantize_rows_mxfp4(x)
+    assert sc.tolist() == [[127, 123], [0, 134], [0, 0]]
+    assert codes[0, :6].tolist() == [7, 8 | 5, 1, 0, 2, 6]     # 0.25 and 1.25 tie to the even code; 5 -> 4
+    assert codes[0, 32:35].tolist() == [6, 8 | 5, 0]           # 4.8 -> 4, -3.2 -> -3, 0.16 -> 0
+    assert codes[1, 40:42].tolist() == [7, 2]                  # 1000/128 = 7.8 saturates to 6; 100/128 = 0.78 -> 1
+    assert (codes[1, :32] == 0).all() and codes[2, 0] == 0
+    deq = O.dequantize_mxfp4(codes, sc)
+    assert deq[0, :6].tolist() == [6.0, -3.0, 0.5, 0.0, 1.0, 4.0]
+    assert deq[0, 32:35].tolist() == [0.25, -0.1875, 0.0]
+    assert deq[1, 40:42].tolist() == [768.0, 128.0]
+
+
+def test_mxfp4_scale_is_the_standard_exponent():
+    # over random blocks: the largest magnitude sits in [4, 8) scale units, every value within
+    # half of the widest E2M1 step (2 scale units between 4 and 6) or saturated at 6 units
+    x = (rng.standard_normal((50, 128)) * np.exp2(rng.integers(-20, 20, (50, 1)))).astype(np.float32)
+    codes, sc = O.quantize_rows_mxfp4(x)
+    xb = x.reshape(50, 4, 32).astype(np.float64)
+    X = np.exp2(sc.astype(np.float64) - 127)
+    r = np.abs(xb).max(axis=-1) / X
+    assert ((r >= 4) & (r < 8)).all()
+    deq = O.dequantize_mxfp4(codes, sc).reshape(50, 4, 32)
+    err = np.abs(deq - xb)
+    assert (err <= np.maximum(X[..., None], np.abs(xb) - 6 * X[..., None])).all()  # half a 2-unit step, or saturated
+    assert (np.abs(deq) <= 6 * X[..., None]).all()
+
+
+def test_indexer_mxfp4_reduces_to_plain_indexer():
+    v = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float64)
+    q = rng.choice(np.concatenate([v, -v]), (4, 3, 64))
+    k = rng.choice(np.concatenate([v, -v]), (30, 64))
+    w = rng.uniform(0, 1, (4, 3))
+    qc, kc = O.e2m1_encode(q), O.e2m1_encode(k)
+    one_q, one_k = np.full((4, 3, 2), 127, np.uint8), np.full((30, 2), 127, np.uint8)
+    assert np.array_equal(O.indexer_scores_mxfp4(qc, one_q, w, kc, one_k, pos0=80, m=4),
+                          O.indexer_scores(q, w, k, pos0=80, m=4))
+    # scaling block 1 of every key by 2**3 is the plain indexer on keys whose second half is 8x
+    ks = one_k.copy(); ks[:, 1] = 130
+    k2 = k.copy(); k2[:, 32:] *= 8
+    assert np.array_equal(O.indexer_scores_mxfp4(qc, one_q, w, kc, ks, pos0=80, m=4),
+                          O.indexer_scores(q, w, k2, pos0=80, m=4))
+
+
 # ---------------------------------------------------------------- FP8 + BF16 KV storage
 
 def test_kv_scale_exponent_is_the_smallest_that_fits():
