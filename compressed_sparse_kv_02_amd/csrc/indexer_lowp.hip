@@ -19,6 +19,15 @@
 // scale = amax / MAX, MAX = 448 (E4M3) or 6 (E2M1); the quotient and product
 // are correctly rounded fp32.
 //
+// MX-FP4 (the same E2M1 codes with block scales, as in the OCP Microscaling
+// formats): every 32 consecutive values of a row share one E8M0 scale
+// 2^(code - 127), the shared exponent being floor(log2 amax) - 2 over the
+// block (E2M1's largest value is 1.5 * 2^2); codes = E2M1(x / scale). The
+// scaled MFMA applies them in hardware: with the K permutation below, lane
+// half h at k-step ks holds block 2h + ks of its row (dI = 128), so each
+// lane passes its row's 4 scale bytes shifted by 16 h and the instruction
+// selects byte ks. Only the head weight multiplies the ReLU; no key scale.
+//
 // The scoring kernels follow the bf16 ones: 8 queries per workgroup sharing
 // 256-key LDS tiles copied straight from global memory for prefill; for
 // decode, interleaved 32-key blocks per wave with coalesced loads turned into
@@ -123,6 +132,44 @@ __global__ __launch_bounds__(256) void quantize_fp4_kernel(const T* x, int64_t r
   if (lane == 0) scales[r] = amax > 0.f ? __fdiv_rn(amax, 6.f) : 0.f;
 }
 
+// MX-FP4 rows: one wave per row, dim % 32 == 0, dim <= 1024. Lane groups of 8 (4 values each)
+// cover one 32-value block; codes packed as in quantize_fp4_kernel, one E8M0 byte per block.
+template <typename T>
+__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const T* x, int64_t rows, int dim, uint8_t* codes,
+                                                            uint8_t* scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const T* xr = x + r * dim;
+  const int nc = dim / 4;  // 4-value chunks: lane takes chunks lane, lane + 64, ...; 8 chunks per block
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = lane + 64 * q;
+    if (64 * q >= nc) break;  // uniform: whole 64-chunk passes only (nc is a multiple of 8)
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (c < nc) load_vec<T, 4>(xr + 4 * c, v);
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+    int code = 0;
+    if (amax > 0.f) {
+      int ex;
+      (void)frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
+      code = min(max(ex - 1 - 2 + 127, 0), 254);
+    }
+    const float inv = ldexpf(1.f, 127 - code);  // 1 / scale, exact
+    if (c < nc) {
+      uint32_t w = 0;
+      if (amax > 0.f)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w |= e2m1_code(v[e] * inv) << (4 * e);
+      *reinterpret_cast<uint16_t*>(codes + r * (dim / 2) + 2 * c) = (uint16_t)w;
+      if ((c & 7) == 0) scales[r * (dim / 32) + c / 8] = (uint8_t)code;
+    }
+  }
+}
+
 // MFMA operand: 32 values = 32 bytes (E4M3) or 16 bytes (E2M1, upper registers unused).
 template <int FMT>
 __device__ __forceinline__ i32x8 load_op(const uint8_t* p) {
@@ -141,10 +188,21 @@ __device__ __forceinline__ f32x16 mfma_lowp(const i32x8& a, const i32x8& b, cons
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, 0, 0, 0);
 }
 
-// Query operands (A) and folded head weights (w * qs) of query j; lane holds head lane%32 of each tile.
-template <int FMT, int HT, int KS8>
+// Block-scaled product (MX): scale bytes ks of sa (A row) and sb (B column) apply to this k-step.
+template <int FMT, int KS>
+__device__ __forceinline__ f32x16 mfma_mx(const i32x8& a, const i32x8& b, const f32x16& c, uint32_t sa, uint32_t sb) {
+  if constexpr (KS == 0)
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, (int)sa, 0, (int)sb);
+  else
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 1, (int)sa, 1, (int)sb);
+}
+
+// Query operands (A) and head weights of query j; lane holds head lane%32 of each tile. Row
+// scales (MX = false) are folded into the weights (w * qs); MX block scales go to qsx: the
+// head row's 4 scale bytes shifted to this lane half's two blocks.
+template <int FMT, int HT, int KS8, bool MX>
 __device__ __forceinline__ void load_query_lowp(const IdxArgs& a, int b, int64_t j, bool qvalid, int lane,
-                                                i32x8 (&qa)[HT][KS8], float (&wv)[HT][16]) {
+                                                i32x8 (&qa)[HT][KS8], float (&wv)[HT][16], uint32_t (&qsx)[HT]) {
   constexpr int DI = 64 * KS8 * LowP<FMT>::BITS / 8;  // bytes per row
   constexpr int OB = LowP<FMT>::OB;
   const uint8_t* qp = (const uint8_t*)a.qI + ((int64_t)b * a.Tq + j) * a.HI * DI + (DI / 2) * (lane >> 5);
@@ -156,11 +214,12 @@ __device__ __forceinline__ void load_query_lowp(const IdxArgs& a, int b, int64_t
 #pragma unroll
     for (int ks = 0; ks < KS8; ++ks)
       qa[ht][ks] = (qvalid && h < a.HI) ? load_op<FMT>(qp + (int64_t)h * DI + OB * ks) : i32x8{};
+    qsx[ht] = MX && qvalid && h < a.HI ? __float_as_uint(sp[h]) >> (16 * (lane >> 5)) : 0x7f7f7f7fu;
     // accumulator rows held by this lane: 8*(i/4) + 4*(lane/32) + i%4
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int hh = ht * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      wv[ht][i] = (qvalid && hh < a.HI) ? wp[hh] * sp[hh] : 0.f;
+      wv[ht][i] = (qvalid && hh < a.HI) ? (MX ? wp[hh] : wp[hh] * sp[hh]) : 0.f;
     }
   }
 }
@@ -171,7 +230,7 @@ __device__ __forceinline__ void load_query_lowp(const IdxArgs& a, int b, int64_t
 // 32-lane B read (one 16-byte chunk each) hit 32 distinct 4-bank groups. The key scales travel
 // the same way (4 bytes per lane). Each 32-key sub-block reads the next one's B operands first,
 // then issues its MFMAs beside the previous sub-block's ReLU / weighted head-sum.
-template <int FMT, int HT, int KS8>
+template <int FMT, int HT, int KS8, bool MX>
 __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
   constexpr int QB = 8;                // queries per workgroup (one per wave)
   constexpr int SUB = 8;               // 32-key sub-blocks per tile (even)
@@ -184,6 +243,7 @@ __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
   constexpr int IPW = 32 / RPI;        // copies per wave per tile (each wave copies 32 rows)
   constexpr int SH = CPR == 16 ? 1 : CPR == 8 ? 2 : CPR == 4 ? 3 : 4;  // log2(32 / CPR)
   static_assert(TILE == 32 * QB && CPR >= 2 && CPR <= 16 && IPW >= 1, "tile shape");
+  static_assert(!MX || (FMT == FMT_E2M1 && KS8 == 2), "MX: E2M1, dI = 128 (4 scale bytes per row)");
   // two arrays per buffer kind (not [2][...]): the compiler then sees that a copy into one
   // never feeds reads of the other. Scales: wave w copies keys 32 w + (lane % 32) to 64 w + lane.
   __shared__ __attribute__((aligned(16))) uint8_t kt0[TILE * DI], kt1[TILE * DI];
@@ -210,10 +270,11 @@ __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
 
   i32x8 qa[HT][KS8];
   float wv[HT][16];
-  load_query_lowp<FMT, HT, KS8>(a, b, j, qvalid, lane, qa, wv);
+  uint32_t qsx[HT];
+  load_query_lowp<FMT, HT, KS8, MX>(a, b, j, qvalid, lane, qa, wv, qsx);
 
   const uint8_t* kbase = (const uint8_t*)a.KI + ((int64_t)b * a.N + kbeg) * DI;
-  const float* kscale = a.k_scale + (int64_t)b * a.N + kbeg;
+  const float* kscale = a.k_scale + (int64_t)b * a.N + kbeg;  // MX: 4 scale bytes per key
   float* rowp = a.scores + ((int64_t)b * a.rows_ws + (qvalid ? jr : 0)) * a.ldS + kbeg;
   const int ntiles = (nkeys + TILE - 1) / TILE;
 
@@ -254,11 +315,17 @@ __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
       }
     }
   };
-  auto mma = [&](const i32x8 (&bv)[KS8], f32x16 (&acc)[HT]) {
+  auto mma = [&](const i32x8 (&bv)[KS8], f32x16 (&acc)[HT], uint32_t kx) {
 #pragma unroll
-    for (int ks = 0; ks < KS8; ++ks)
+    for (int ht = 0; ht < HT; ++ht) {
+      if constexpr (MX) {
+        acc[ht] = mfma_mx<FMT, 0>(qa[ht][0], bv[0], f32x16{}, qsx[ht], kx);
+        acc[ht] = mfma_mx<FMT, 1>(qa[ht][1], bv[1], acc[ht], qsx[ht], kx);
+      } else {
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_lowp<FMT>(qa[ht][ks], bv[ks], ks == 0 ? f32x16{} : acc[ht]);
+        for (int ks = 0; ks < KS8; ++ks) acc[ht] = mfma_lowp<FMT>(qa[ht][ks], bv[ks], ks == 0 ? f32x16{} : acc[ht]);
+      }
+    }
   };
   // ReLU, folded head weights, head sum, the other lane half (the other 16 heads of each 32-head
   // tile), the key scale; lanes 0-31 store key lane%32 through a buffer descriptor that covers this
@@ -277,7 +344,7 @@ __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
     const int left = nkeys - s0;
     const int nrec = (qvalid && left > 0) ? 4 * (left < 32 ? left : 32) : 0;  // 0: all dropped
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(rowp + s0, (short)0, nrec, 0x00020000);
-    const float v = s0 + (lane & 31) < vrel ? part * sc : -INFINITY;
+    const float v = s0 + (lane & 31) < vrel ? (MX ? part : part * sc) : -INFINITY;
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, lane < 32 ? 4 * lane : 256, 0, 0);
   };
   auto wait_barrier = [&]() {
@@ -286,17 +353,23 @@ __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
   };
   f32x16 acc[2][HT];
   i32x8 bv[2][KS8];
-  float sc[2];  // scales of the keys of the current and previous sub-block
+  float sc[2];     // scales of the keys of the current and previous sub-block
+  uint32_t kx[2];  // MX: scale bytes of the current and next sub-block's keys, shifted to the lane half
+  auto rdX = [&](const float* sb_, int sb) { return __float_as_uint(sb_[64 * sb + lane]) >> (16 * (lane >> 5)); };
   auto tile = [&](int it, const uint8_t* kb, const float* sb_) {
     const int t0 = it * TILE;
     rdB(kb, bv[0]);
+    if constexpr (MX) kx[0] = rdX(sb_, 0);
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb) {
       const bool prev = sb > 0 || it > 0;
-      if (sb + 1 < SUB) rdB(kb + (sb + 1) * 32 * DI, bv[(sb + 1) & 1]);
-      sc[sb & 1] = sb_[64 * sb + lane];  // lanes 32-63 read the same scales as lanes 0-31
+      if (sb + 1 < SUB) {
+        rdB(kb + (sb + 1) * 32 * DI, bv[(sb + 1) & 1]);
+        if constexpr (MX) kx[(sb + 1) & 1] = rdX(sb_, sb + 1);
+      }
+      if constexpr (!MX) sc[sb & 1] = sb_[64 * sb + lane];  // lanes 32-63 read the same scales as lanes 0-31
       __builtin_amdgcn_sched_barrier(0);
-      mma(bv[sb & 1], acc[sb & 1]);
+      mma(bv[sb & 1], acc[sb & 1], kx[sb & 1]);
       if (prev) finish(acc[(sb + 1) & 1], t0 + sb * 32 - 32, sc[(sb + 1) & 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -319,7 +392,7 @@ __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
 // Decode-shaped rows: row_waves waves per query row, wave r taking the 32-key
 // blocks r, r + row_waves, ...; each block loaded with coalesced 16-byte loads
 // one block ahead and turned into the MFMA layout through the wave's own LDS rows.
-template <int FMT, int HT, int KS8>
+template <int FMT, int HT, int KS8, bool MX>
 __global__ __launch_bounds__(256) void indexer_score_lowp_stream(IdxArgs a) {
   constexpr int DI = 64 * KS8 * LowP<FMT>::BITS / 8;  // bytes per key row
   constexpr int OB = LowP<FMT>::OB;
@@ -340,7 +413,8 @@ __global__ __launch_bounds__(256) void indexer_score_lowp_stream(IdxArgs a) {
 
   i32x8 qa[HT][KS8];
   float wv[HT][16];
-  load_query_lowp<FMT, HT, KS8>(a, b, j, true, lane, qa, wv);
+  uint32_t qsx[HT];
+  load_query_lowp<FMT, HT, KS8, MX>(a, b, j, true, lane, qa, wv, qsx);
 
   uint8_t* my = kst[wave];
   const uint8_t* kb0 = (const uint8_t*)a.KI + (int64_t)b * a.N * DI;
@@ -375,11 +449,22 @@ __global__ __launch_bounds__(256) void indexer_score_lowp_stream(IdxArgs a) {
     }
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     f32x16 acc[HT];
+    if constexpr (MX) {
+      const uint32_t kx = __float_as_uint(sc) >> (16 * half);  // the key's 4 scale bytes, this half's blocks
+      const i32x8 b0 = load_op<FMT>(my + kl * RS + (DI / 2) * half);
+      const i32x8 b1 = load_op<FMT>(my + kl * RS + (DI / 2) * half + OB);
 #pragma unroll
-    for (int ks = 0; ks < KS8; ++ks) {
-      const i32x8 bv = load_op<FMT>(my + kl * RS + (DI / 2) * half + OB * ks);
+      for (int ht = 0; ht < HT; ++ht) {
+        acc[ht] = mfma_mx<FMT, 0>(qa[ht][0], b0, f32x16{}, qsx[ht], kx);
+        acc[ht] = mfma_mx<FMT, 1>(qa[ht][1], b1, acc[ht], qsx[ht], kx);
+      }
+    } else {
 #pragma unroll
-      for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_lowp<FMT>(qa[ht][ks], bv, ks == 0 ? f32x16{} : acc[ht]);
+      for (int ks = 0; ks < KS8; ++ks) {
+        const i32x8 bv = load_op<FMT>(my + kl * RS + (DI / 2) * half + OB * ks);
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma_lowp<FMT>(qa[ht][ks], bv, ks == 0 ? f32x16{} : acc[ht]);
+      }
     }
     float part = 0.f;
 #pragma unroll
@@ -388,7 +473,7 @@ __global__ __launch_bounds__(256) void indexer_score_lowp_stream(IdxArgs a) {
       for (int i = 0; i < 16; ++i) part = __builtin_fmaf(relu_bits(acc[ht][i]), wv[ht][i], part);
     part += __shfl_xor(part, 32, 64);
     const int64_t s = key_of(blk);
-    if (lane < 32 && s < vj) srow[s] = part * sc;
+    if (lane < 32 && s < vj) srow[s] = MX ? part : part * sc;
   };
 
 #pragma unroll
@@ -407,27 +492,30 @@ __global__ __launch_bounds__(256) void indexer_score_lowp_stream(IdxArgs a) {
 // ----------------------------------------------------------------------------
 static constexpr int64_t LOWP_STREAM_WAVES = 4096;  // decode scoring: waves over the whole call
 
-template <int FMT, int HT, int KS8, bool STREAM>
+template <int FMT, int HT, int KS8, bool STREAM, bool MX>
 static void launch_lowp(const IdxArgs& a, dim3 grid, hipStream_t st) {
   if constexpr (STREAM)
-    hipLaunchKernelGGL((indexer_score_lowp_stream<FMT, HT, KS8>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((indexer_score_lowp_stream<FMT, HT, KS8, MX>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((indexer_score_lowp_mfma<FMT, HT, KS8>), grid, dim3(512), 0, st, a);
+    hipLaunchKernelGGL((indexer_score_lowp_mfma<FMT, HT, KS8, MX>), grid, dim3(512), 0, st, a);
 }
 
-template <int FMT, bool STREAM>
+template <int FMT, bool STREAM, bool MX = false>
 static bool dispatch_lowp(int ht, int ks8, const IdxArgs& a, dim3 grid, hipStream_t st) {
-  if (ks8 == 1) {
-    switch (ht) {
-      case 1: launch_lowp<FMT, 1, 1, STREAM>(a, grid, st); return true;
-      case 2: launch_lowp<FMT, 2, 1, STREAM>(a, grid, st); return true;
-      case 4: launch_lowp<FMT, 4, 1, STREAM>(a, grid, st); return true;
+  if constexpr (!MX) {
+    if (ks8 == 1) {
+      switch (ht) {
+        case 1: launch_lowp<FMT, 1, 1, STREAM, false>(a, grid, st); return true;
+        case 2: launch_lowp<FMT, 2, 1, STREAM, false>(a, grid, st); return true;
+        case 4: launch_lowp<FMT, 4, 1, STREAM, false>(a, grid, st); return true;
+      }
     }
-  } else if (ks8 == 2) {
+  }
+  if (ks8 == 2) {
     switch (ht) {
-      case 1: launch_lowp<FMT, 1, 2, STREAM>(a, grid, st); return true;
-      case 2: launch_lowp<FMT, 2, 2, STREAM>(a, grid, st); return true;
-      case 4: launch_lowp<FMT, 4, 2, STREAM>(a, grid, st); return true;
+      case 1: launch_lowp<FMT, 1, 2, STREAM, MX>(a, grid, st); return true;
+      case 2: launch_lowp<FMT, 2, 2, STREAM, MX>(a, grid, st); return true;
+      case 4: launch_lowp<FMT, 4, 2, STREAM, MX>(a, grid, st); return true;
     }
   }
   return false;
@@ -457,7 +545,10 @@ int launch_scores_lowp(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st)
     grid = dim3((unsigned)(a.row_waves / 4), (unsigned)a.nrows, (unsigned)batch);
   }
   bool ok;
-  if (dtype == CSKV_FP4)
+  if (dtype == CSKV_MXFP4)
+    ok = qb == 8 ? dispatch_lowp<FMT_E2M1, false, true>(ht, ks8, a, grid, st)
+                 : dispatch_lowp<FMT_E2M1, true, true>(ht, ks8, a, grid, st);
+  else if (dtype == CSKV_FP4)
     ok = qb == 8 ? dispatch_lowp<FMT_E2M1, false>(ht, ks8, a, grid, st) : dispatch_lowp<FMT_E2M1, true>(ht, ks8, a, grid, st);
   else
     ok = qb == 8 ? dispatch_lowp<FMT_E4M3, false>(ht, ks8, a, grid, st) : dispatch_lowp<FMT_E4M3, true>(ht, ks8, a, grid, st);
@@ -465,11 +556,12 @@ int launch_scores_lowp(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st)
   return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
 }
 
-static int check_lowp_shape(int batch, int64_t Tq, int64_t N, int HI, int dI, int64_t pos0, int m) {
+static int check_lowp_shape(int batch, int64_t Tq, int64_t N, int HI, int dI, int64_t pos0, int m, int dtype) {
   if (batch < 0 || Tq < 0 || N < 0 || pos0 < 0 || m < 1) return CSKV_ERR_BAD_SHAPE;
   if (HI < 1 || HI > CSKV_MAX_HEADS) return CSKV_ERR_BAD_SHAPE;
   if (N > ((int64_t)1 << 31) - 64) return CSKV_ERR_BAD_SHAPE;
   if (dI != 64 && dI != 128) return CSKV_ERR_UNSUPPORTED;
+  if (dtype == CSKV_MXFP4 && dI != 128) return CSKV_ERR_UNSUPPORTED;  // 4 scale bytes per row
   return CSKV_OK;
 }
 
@@ -499,10 +591,28 @@ static int quantize_rows(int fmt, const void* x, int64_t rows, int dim, int dtyp
   return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
 }
 
+static int quantize_rows_mx(const void* x, int64_t rows, int dim, int dtype, uint8_t* codes, uint8_t* scales,
+                            void* stream) {
+  if (dtype != CSKV_BF16 && dtype != CSKV_F32) return CSKV_ERR_BAD_DTYPE;
+  if (rows < 0 || dim < 32 || dim % 32 != 0 || dim > 1024) return CSKV_ERR_BAD_SHAPE;
+  if (ceil_div(rows, (int64_t)4) > 0x7fffffff) return CSKV_ERR_BAD_SHAPE;
+  if (rows == 0) return CSKV_OK;
+  if (!x || !codes || !scales) return CSKV_ERR_INVALID_ARG;
+  if (!aligned16(x, codes, scales)) return CSKV_ERR_MISALIGNED;
+  dim3 grid((unsigned)ceil_div(rows, (int64_t)4));
+  hipStream_t st = (hipStream_t)stream;
+  if (dtype == CSKV_BF16)
+    hipLaunchKernelGGL(quantize_mxfp4_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)x, rows, dim, codes, scales);
+  else
+    hipLaunchKernelGGL(quantize_mxfp4_kernel<float>, grid, dim3(256), 0, st, (const float*)x, rows, dim, codes,
+                       scales);
+  return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+}
+
 static int scores_lowp(int dtype, const uint8_t* qI, const float* q_scale, const float* wI, const uint8_t* KI,
                        const float* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI, int64_t pos0, int m,
                        float* scores, int64_t ld, void* stream) {
-  int st = check_lowp_shape(batch, Tq, N, HI, dI, pos0, m);
+  int st = check_lowp_shape(batch, Tq, N, HI, dI, pos0, m, dtype);
   if (st) return st;
   if (ld < N || ld % 4 != 0) return CSKV_ERR_BAD_SHAPE;
   if (batch == 0 || Tq == 0) return CSKV_OK;
@@ -519,7 +629,7 @@ static int scores_lowp(int dtype, const uint8_t* qI, const float* q_scale, const
 static int topk_lowp(int dtype, const uint8_t* qI, const float* q_scale, const float* wI, const uint8_t* KI,
                      const float* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI, int64_t pos0, int m,
                      int k, int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream) {
-  int st = check_lowp_shape(batch, Tq, N, HI, dI, pos0, m);
+  int st = check_lowp_shape(batch, Tq, N, HI, dI, pos0, m, dtype);
   if (st) return st;
   if (k < 1) return CSKV_ERR_BAD_SHAPE;
   if (k > CSKV_MAX_TOPK) return CSKV_ERR_UNSUPPORTED;
@@ -596,4 +706,26 @@ extern "C" int indexer_topk_fp4(const uint8_t* qI, const float* q_scale, const f
                                 void* stream) {
   return topk_lowp(CSKV_FP4, qI, q_scale, wI, KI, k_scale, batch, Tq, N, HI, dI, pos0, m, k, out_idx, workspace,
                    ws_bytes, stream);
+}
+
+// MX-FP4: the scale arrays hold 4 E8M0 bytes per row (dI = 128); the kernels read them as one
+// 32-bit word per row through the fp32 scale slots of the argument block.
+extern "C" int cskv_quantize_mxfp4(const void* x, int64_t rows, int dim, int dtype, uint8_t* codes, uint8_t* scales,
+                                   void* stream) {
+  return quantize_rows_mx(x, rows, dim, dtype, codes, scales, stream);
+}
+
+extern "C" int indexer_scores_mxfp4(const uint8_t* qI, const uint8_t* q_scale, const float* wI, const uint8_t* KI,
+                                    const uint8_t* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                                    int64_t pos0, int m, float* scores, int64_t ld, void* stream) {
+  return scores_lowp(CSKV_MXFP4, qI, (const float*)q_scale, wI, KI, (const float*)k_scale, batch, Tq, N, HI, dI,
+                     pos0, m, scores, ld, stream);
+}
+
+extern "C" int indexer_topk_mxfp4(const uint8_t* qI, const uint8_t* q_scale, const float* wI, const uint8_t* KI,
+                                  const uint8_t* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                                  int64_t pos0, int m, int k, int32_t* out_idx, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+  return topk_lowp(CSKV_MXFP4, qI, (const float*)q_scale, wI, KI, (const float*)k_scale, batch, Tq, N, HI, dI, pos0,
+                   m, k, out_idx, workspace, ws_bytes, stream);
 }

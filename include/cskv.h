@@ -61,7 +61,8 @@ enum {
 };
 
 enum { CSKV_BF16 = 0, CSKV_F32 = 1, CSKV_FP8 = 2 /* E4M3 codes, fp32 row scales */,
-       CSKV_FP4 = 3 /* E2M1 codes, two per byte, fp32 row scales */ };
+       CSKV_FP4 = 3 /* E2M1 codes, two per byte, fp32 row scales */,
+       CSKV_MXFP4 = 4 /* E2M1 codes, two per byte, one E8M0 scale per 32 values */ };
 enum { CSKV_MODE_CSA = 0, CSKV_MODE_HCA = 1 };
 
 #define CSKV_MAX_TOPK 2048
@@ -245,6 +246,43 @@ int indexer_topk_fp4(const uint8_t* qI, const float* q_scale, const float* wI, c
                      const float* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
                      int64_t pos0, int m, int k, int32_t* out_idx, void* workspace, size_t ws_bytes,
                      void* stream);
+
+/*
+ * MX-FP4 lightning indexer -- the FP4 indexer of [PB §2.3.4] with block
+ * scales, in the layout of the OCP Microscaling (MX) formats: every 32
+ * consecutive values of a row share one E8M0 scale byte (value
+ * 2^(code - 127)); the values are the E2M1 codes of cskv_quantize_fp4.
+ *
+ * cskv_quantize_mxfp4 -- per 32-value block: amax = max |x| (x as fp32),
+ *   code = clamp(floor(log2 amax) - 2 + 127, 0, 254) (0 for an all-zero
+ *   block), codes = E2M1(x * 2^(127 - code)) (nearest, ties to the even
+ *   code, saturating at +-6).
+ *   x : [rows, dim] bf16 or fp32 (dtype), dim % 32 == 0, dim <= 1024
+ *   codes : [rows, dim / 2] bytes, scales : [rows, dim / 32] bytes;
+ *   caller-owned device buffers, 16-byte aligned.
+ * indexer_scores_mxfp4 / indexer_topk_mxfp4 -- indexer_scores / indexer_topk on
+ *   MX-FP4 rows:
+ *   I[t, s] = sum_h wI[t,h] * max(0, q[t,h,:] . k[s,:])
+ *   with q, k the decoded rows (code value times its block's scale), the
+ *   block scales applied by v_mfma_scale_f32_32x32x64_f8f6f4. Each block's
+ *   sum of E2M1 products is exact; the matrix core may truncate when it
+ *   adds blocks of different scales (about one fp32 ulp of the dot product),
+ *   then the head sum rounds in fp32.
+ *   qI : [batch, Tq, HI, 64] bytes, q_scale : [batch, Tq, HI, 4] bytes
+ *   KI : [batch, N, 64] bytes,      k_scale : [batch, N, 4] bytes
+ *   dI = 128 only (CSKV_ERR_UNSUPPORTED otherwise); other arguments, limits
+ *   and outputs as in indexer_scores / indexer_topk; the workspace of
+ *   indexer_topk_mxfp4 is cskv_indexer_workspace_size(..., CSKV_MXFP4) bytes.
+ */
+int cskv_quantize_mxfp4(const void* x, int64_t rows, int dim, int dtype, uint8_t* codes, uint8_t* scales,
+                        void* stream);
+int indexer_scores_mxfp4(const uint8_t* qI, const uint8_t* q_scale, const float* wI, const uint8_t* KI,
+                         const uint8_t* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                         int64_t pos0, int m, float* scores, int64_t ld, void* stream);
+int indexer_topk_mxfp4(const uint8_t* qI, const uint8_t* q_scale, const float* wI, const uint8_t* KI,
+                       const uint8_t* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                       int64_t pos0, int m, int k, int32_t* out_idx, void* workspace, size_t ws_bytes,
+                       void* stream);
 
 /*
  * compressed_attn_prefill -- MQA core attention over compressed entries,

@@ -196,3 +196,27 @@ def key_rounding_band(qI_row: np.ndarray, wI_row: np.ndarray, ik_new_exact: Opti
     else:
         u = np.abs(ik_new_exact).max(axis=0) * 2.0 ** -21
     return float(np.sum(np.abs(wI_row)[:, None] * np.abs(qI_row) * u[None, :]))
+
+
+def mxfp4_score_bound(q_codes, q_scales, w_row, k_codes, k_scales, V: int) -> np.ndarray:
+    """Bound on |I_gpu - I| for one query's MX-FP4 scores over keys 0..V-1.
+
+    Each 32-value block's sum of E2M1 products is a multiple of 1/4 below
+    32 * 36 and exact in fp32; an in-bounds probe of
+    v_mfma_scale_f32_32x32x64_f8f6f4 showed the instruction adding the two
+    scaled block sums of one k-step with up to one fp32 ulp of truncation,
+    and the second k-step adds to that in fp32. So each head's dot product is
+    off by at most 3 * 2**-23 * A[h, s], A = sum over blocks of |scaled block
+    sum|; ReLU is 1-Lipschitz and the fp32 head sum adds at most
+    HI * 2**-24 * sum_h |w_h dot_h|:
+      B[s] = sum_h |w_h| (3 * 2**-23 A[h, s] + HI * 2**-24 |dot_h[s]|)
+    """
+    dq = O.dequantize_mxfp4(q_codes, q_scales)          # [HI, dI]
+    dk = O.dequantize_mxfp4(k_codes[:V], k_scales[:V])  # [V, dI]
+    HI, dI = dq.shape
+    nb = dI // O.MX_BLOCK
+    blk = np.einsum("hbk,sbk->shb", dq.reshape(HI, nb, -1), dk.reshape(V, nb, -1))  # [V, HI, blocks]
+    A = np.abs(blk).sum(axis=2)
+    dot = np.abs(blk.sum(axis=2))
+    w = np.abs(np.asarray(w_row, dtype=np.float64))
+    return (3 * 2.0 ** -23 * A + HI * 2.0 ** -24 * dot) @ w

@@ -13,6 +13,7 @@ from compressed_sparse_kv_02_amd import binding as B
 from compressed_sparse_kv_02_amd import layer as LY
 from compressed_sparse_kv_02_amd.synth import normal_device, uniform_device
 from tests.parity_utils import (assert_storage_close, check_topk_row, check_topk_row_bounded, fp8_score_bound,
+                                mxfp4_score_bound,
                                 key_rounding_band, np64, oracle_layer)
 
 pytestmark = pytest.mark.gpu
@@ -316,6 +317,67 @@ def test_indexer_fp4(bt, Tq, N, HI, dI, pos0, m, k):
             assert np.abs(sc[b, r, :V] - I[:V]).max() <= 1e-5 * np.abs(I[:V]).max(), (b, r)
             n_band += check_topk_row(idx[b, r], I, V, k, what=f"b{b} r{r}")
     say("  tie-band differences:", n_band)
+
+
+@pytest.mark.parametrize("dtype,rows,dim", [("bf16", 300, 128), ("f32", 77, 1024), ("bf16", 5, 32)])
+def test_quantize_mxfp4(dtype, rows, dim):
+    """MX-FP4 codes and E8M0 block scales bit-exact against the oracle, with zero, tiny, huge and
+    saturating blocks among normal ones."""
+    say("quantize_mxfp4", dtype, rows, dim)
+    x = gen(35, "mx.x", (rows, dim), dtype).float()
+    x = x * torch.exp2(torch.arange(rows, device=DEV, dtype=torch.float32) % 41 - 20)[:, None]
+    x[0, :32] = 0.0                       # all-zero block
+    if rows > 2:
+        x[1, :32] = 2.0 ** -130           # exponent below -127: clamped scale, codes round to 0
+        x[2, :32] = 3.0e30                # large exponent
+        x[2, 5] = -0.0
+    x = x.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+    codes, sc = B.quantize_mxfp4(x)
+    torch.cuda.synchronize()
+    oc, osc = O.quantize_rows_mxfp4(np64(x).astype(np.float32))
+    assert np.array_equal(sc.cpu().numpy(), osc)
+    assert np.array_equal(_unpack(codes.cpu().numpy()), oc)
+
+
+@pytest.mark.parametrize("bt,Tq,N,HI,pos0,m,k", [
+    (2, 300, 2000, 64, 4 * 2000 - 300, 4, 256),        # prefill route, ragged tail
+    (1, 1024, 7000, 64, 4 * 7000 - 1024, 4, 512),      # spans of 3 and 4 key tiles
+    (1, 77, 5000, 20, 16000, 4, 100),                  # HI not a multiple of 32
+    (3, 5, 70000, 64, 4 * 70000, 4, 1024),             # decode route, two-kernel top-k
+    (1, 2, 3000, 128, 3000 * 4 - 2, 4, 2048),          # 128 heads, max k
+])
+def test_indexer_mxfp4(bt, Tq, N, HI, pos0, m, k):
+    """MX-FP4 scores within the derived bound of the oracle on its own quantisation (dI = 128);
+    top-k exact outside the bound."""
+    say("indexer mxfp4", bt, Tq, N, HI, pos0, m, k)
+    dI = 128
+    qI = gen(37, "mx.q", (bt, Tq, HI, dI))
+    KI = gen(37, "mx.k", (bt, N, dI))
+    wI = uniform_device(37, "mx.w", (bt, Tq, HI), DEV)
+    qc, qs = B.quantize_mxfp4(qI)
+    kc, ks = B.quantize_mxfp4(KI)
+    sc = B.indexer_scores_mxfp4(qc, qs, wI, kc, ks, pos0, m)
+    idx = B.indexer_topk_mxfp4(qc, qs, wI, kc, ks, pos0, m, k)
+    torch.cuda.synchronize()
+    sc, idx = sc.cpu().numpy(), idx.cpu().numpy()
+    rows = range(Tq) if Tq <= 80 else sorted(set(np.linspace(0, Tq - 1, 40).astype(int)) | {0, Tq - 1})
+    n_band, worst = 0, 0.0
+    for b in range(bt):
+        okc, oks = O.quantize_rows_mxfp4(np64(KI[b]).astype(np.float32))
+        assert np.array_equal(okc, _unpack(kc[b].cpu().numpy())) and np.array_equal(oks, ks[b].cpu().numpy())
+        for r in rows:
+            oqc, oqs = O.quantize_rows_mxfp4(np64(qI[b, r]).astype(np.float32))
+            I = O.indexer_scores_mxfp4(oqc[None], oqs[None], np64(wI[b, r:r + 1]), okc, oks, pos0 + r, m)[0]
+            V = O.visible(pos0 + r, m, N)
+            if V == 0:
+                continue
+            bound = mxfp4_score_bound(oqc, oqs, np64(wI[b, r]), okc, oks, V)
+            err = np.abs(sc[b, r, :V] - I[:V])
+            assert (err <= bound).all(), (b, r, float((err / bound).max()))
+            worst = max(worst, float((err / bound).max()))
+            n_band += check_topk_row_bounded(idx[b, r], I, bound, V, k, what=f"b{b} r{r}")
+    say(f"  undecided entries: {n_band}; largest error / bound: {worst:.3g}")
+
 
 
 def test_indexer_fp4_decode_1m():
@@ -711,19 +773,22 @@ def test_indexer_topk_matches_its_two_halves():
     ("fp4", 1, 1024, 7000, 64, 128, 4 * 7000 - 1024, 4),
     ("fp4", 1, 77, 5000, 20, 64, 16000, 4),    # 32-byte key rows
     ("fp4", 3, 5, 70000, 64, 128, 4 * 70000, 4),
+    ("mxfp4", 1, 1024, 7000, 64, 128, 4 * 7000 - 1024, 4),
+    ("mxfp4", 3, 5, 70000, 20, 128, 4 * 70000, 4),
 ])
 def test_indexer_scores_write_extent(dtype, bt, Tq, N, HI, dI, pos0, m):
     # every visible entry gets a finite score; past V_t only -inf may be written, and nothing
     # at or past the last row's V (the end of every swept key range) or past N is touched
     say("indexer_scores write extent", dtype, bt, Tq, N, HI, dI, pos0, m)
-    lowp = dtype in ("fp8", "fp4")
+    lowp = dtype in ("fp8", "fp4", "mxfp4")
     qI = gen(23, "we.q", (bt, Tq, HI, dI), "bf16" if lowp else dtype)
     KI = gen(23, "we.k", (bt, N, dI), "bf16" if lowp else dtype)
     wI = uniform_device(23, "we.w", (bt, Tq, HI), DEV)
     ld = B.score_ld(N) + 8
     sc = torch.full((bt, Tq, ld), float("nan"), dtype=torch.float32, device=DEV)
     if lowp:
-        qz, fn = (B.quantize_fp8, B.indexer_scores_fp8) if dtype == "fp8" else (B.quantize_fp4, B.indexer_scores_fp4)
+        qz, fn = {"fp8": (B.quantize_fp8, B.indexer_scores_fp8), "fp4": (B.quantize_fp4, B.indexer_scores_fp4),
+                  "mxfp4": (B.quantize_mxfp4, B.indexer_scores_mxfp4)}[dtype]
         (qc, qs), (kc, ks) = qz(qI), qz(KI)
         fn(qc, qs, wI, kc, ks, pos0, m, scores=sc)
     else:
