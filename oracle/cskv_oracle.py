@@ -385,45 +385,71 @@ def indexer_scores_fp4(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: i
 # floor(log2(amax)) - 2 (2 = the exponent of E2M1's largest value, 6 =
 # 1.5 * 2**2), and each value is stored as E2M1(x / scale) rounded to
 # nearest, ties to even, saturating at +-6. An all-zero block takes scale
-# code 0 and zero codes; exponents below -127 are clamped to code 0.
+# code 0 and zero codes; exponents below -127 are clamped to code 0. MX-FP8
+# (the FP8 setting with the same block scales) stores E4M3 values with the
+# shared exponent floor(log2(amax)) - 8.
 # ---------------------------------------------------------------------------
 
 MX_BLOCK = 32
-E2M1_EMAX = 2
+E2M1_EMAX = 2   # E2M1's largest value 6 = 1.5 * 2**2
+E4M3_EMAX = 8   # E4M3's largest value 448 = 1.75 * 2**8 (MX-FP8, the same layout with E4M3 values)
 
 
-def mx_scale_codes(amax) -> np.ndarray:
+def mx_scale_codes(amax, emax: int = E2M1_EMAX) -> np.ndarray:
     """E8M0 code of each block's shared scale from its largest magnitude (fp32 values)."""
     a = np.asarray(amax, dtype=F64)
     _, ex = np.frexp(a)                       # a = f * 2**ex, f in [0.5, 1): floor(log2 a) = ex - 1
-    e = ex.astype(np.int64) - 1 - E2M1_EMAX
+    e = ex.astype(np.int64) - 1 - emax
     return np.where(a > 0, np.clip(e + 127, 0, 254), 0).astype(np.uint8)
 
 
-def quantize_rows_mxfp4(x) -> Tuple[np.ndarray, np.ndarray]:
-    """MX-FP4 codes (unpacked, one per element) and E8M0 scale codes ([..., dim / 32]) of fp32 rows."""
+def _quantize_rows_mx(x, emax: int, encode) -> Tuple[np.ndarray, np.ndarray]:
     x32 = np.asarray(x, dtype=np.float32)
     d = x32.shape[-1]
     assert d % MX_BLOCK == 0
     xb = x32.reshape(x32.shape[:-1] + (d // MX_BLOCK, MX_BLOCK)).astype(F64)
     amax = np.abs(xb).max(axis=-1)
-    sc = mx_scale_codes(amax)
+    sc = mx_scale_codes(amax, emax)
     y = xb / np.exp2(sc.astype(F64) - 127)[..., None]   # exact: a power-of-two divisor
-    codes = np.where((amax > 0)[..., None], e2m1_encode(y), np.uint8(0)).astype(np.uint8)
+    codes = np.where((amax > 0)[..., None], encode(y), np.uint8(0)).astype(np.uint8)
     return codes.reshape(x32.shape), sc
 
 
-def dequantize_mxfp4(codes, scales) -> np.ndarray:
+def _dequantize_mx(codes, scales, decode) -> np.ndarray:
     c = np.asarray(codes)
     d = c.shape[-1]
-    v = e2m1_decode(c).reshape(c.shape[:-1] + (d // MX_BLOCK, MX_BLOCK))
+    v = decode(c).reshape(c.shape[:-1] + (d // MX_BLOCK, MX_BLOCK))
     v = v * np.exp2(np.asarray(scales, dtype=F64) - 127)[..., None]
     return v.reshape(c.shape)
+
+
+def quantize_rows_mxfp4(x) -> Tuple[np.ndarray, np.ndarray]:
+    """MX-FP4 codes (unpacked, one per element) and E8M0 scale codes ([..., dim / 32]) of fp32 rows."""
+    return _quantize_rows_mx(x, E2M1_EMAX, e2m1_encode)
+
+
+def dequantize_mxfp4(codes, scales) -> np.ndarray:
+    return _dequantize_mx(codes, scales, e2m1_decode)
 
 
 def indexer_scores_mxfp4(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int) -> np.ndarray:
     """Indexer scores on MX-FP4 rows: the plain indexer on the dequantised values."""
     return indexer_scores(dequantize_mxfp4(q_codes, q_scales), wI, dequantize_mxfp4(k_codes, k_scales), pos0, m)
+
+
+def quantize_rows_mxfp8(x) -> Tuple[np.ndarray, np.ndarray]:
+    """MX-FP8 codes (E4M3, one byte per element) and E8M0 scale codes ([..., dim / 32]) of fp32 rows:
+    shared exponent floor(log2 amax) - 8, values E4M3(x / scale), nearest even, saturating at 448."""
+    return _quantize_rows_mx(x, E4M3_EMAX, e4m3_encode)
+
+
+def dequantize_mxfp8(codes, scales) -> np.ndarray:
+    return _dequantize_mx(codes, scales, e4m3_decode)
+
+
+def indexer_scores_mxfp8(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int) -> np.ndarray:
+    """Indexer scores on MX-FP8 rows: the plain indexer on the dequantised values."""
+    return indexer_scores(dequantize_mxfp8(q_codes, q_scales), wI, dequantize_mxfp8(k_codes, k_scales), pos0, m)
 
 
 # ---------------------------------------------------------------------------

@@ -505,6 +505,28 @@ def test_indexer_mxfp4_reduces_to_plain_indexer():
                           O.indexer_scores(q, w, k2, pos0=80, m=4))
 
 
+def test_mxfp8_hand_blocks_and_range():
+    x = np.zeros((2, 64), dtype=np.float32)
+    x[0, :4] = [448.0, -1.0, 300.0, 0.0]     # amax 448 = 1.75 * 2**8 -> shared exponent 0 (code 127)
+    x[0, 32:34] = [3.0, 0.001]               # amax 3 -> floor(log2 3) = 1 -> exponent -7 (code 120): 3 -> 384
+    x[1, :2] = [1e-3, -5e-4]                 # floor(log2 1e-3) = -10 -> exponent -18 (code 109)
+    codes, sc = O.quantize_rows_mxfp8(x)
+    assert sc.tolist() == [[127, 120], [109, 0]]
+    deq = O.dequantize_mxfp8(codes, sc)
+    assert deq[0, :4].tolist() == [448.0, -1.0, 288.0, 0.0]            # 300 -> 288 (E4M3 step 32 there)
+    assert deq[0, 32] == 3.0 and deq[0, 33] == 0.0009765625              # 0.128 units -> 0.125 units
+    assert abs(deq[1, 0] - 1e-3) <= 2.0 ** -18 * 16 and (deq[1, 32:] == 0).all()
+    # random blocks: the largest magnitude lies in [256, 512) scale units, saturating at 448
+    xr = (rng.standard_normal((40, 128)) * np.exp2(rng.integers(-20, 20, (40, 1)))).astype(np.float32)
+    c, s = O.quantize_rows_mxfp8(xr)
+    r = np.abs(xr.reshape(40, 4, 32)).max(axis=-1) / np.exp2(s.astype(np.float64) - 127)
+    assert ((r >= 256) & (r < 512)).all()
+    d = O.dequantize_mxfp8(c, s).reshape(40, 4, 32)
+    X = np.exp2(s.astype(np.float64) - 127)[..., None]
+    xb = xr.reshape(40, 4, 32).astype(np.float64)
+    assert (np.abs(d - xb) <= np.maximum(16 * X, np.abs(xb) - 448 * X)).all()   # half a 32-unit step, or saturated
+
+
 # ---------------------------------------------------------------- FP8 + BF16 KV storage
 
 def test_kv_scale_exponent_is_the_smallest_that_fits():
