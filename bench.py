@@ -193,8 +193,8 @@ def cpu_baseline(prefill, decode, tp, td, budget_s: float):
 
 
 def lowp_indexer_rows(prefill, tp, decode, td, reps: int = 3):
-    """Low-precision indexer scoring (FP8 E4M3, FP4 E2M1 with row scales, MX-FP4: E2M1 with one
-    E8M0 scale per 32 values) on the timed step's CSA inputs. Per key row the scales take 4 bytes
+    """Low-precision indexer scoring (FP8 E4M3, FP4 E2M1 with row scales; MX-FP4 / MX-FP8: the same
+    values with one E8M0 scale per 32) on the timed step's CSA inputs. Per key row the scales take 4 bytes
     in every format (one fp32, or four E8M0 bytes at dI = 128).
 
     The indexer keys and queries of prefill layer 0 and of the decode CSA layer
@@ -218,7 +218,8 @@ def lowp_indexer_rows(prefill, tp, decode, td, reps: int = 3):
     out = {}
     for fmt, quant, score, peak, bits in (("fp8", B.quantize_fp8, B.indexer_scores_fp8, PEAK_FP8_FLOPS, 8),
                                           ("fp4", B.quantize_fp4, B.indexer_scores_fp4, PEAK_FP4_FLOPS, 4),
-                                          ("mxfp4", B.quantize_mxfp4, B.indexer_scores_mxfp4, PEAK_FP4_FLOPS, 4)):
+                                          ("mxfp4", B.quantize_mxfp4, B.indexer_scores_mxfp4, PEAK_FP4_FLOPS, 4),
+                                          ("mxfp8", B.quantize_mxfp8, B.indexer_scores_mxfp8, PEAK_FP8_FLOPS, 8)):
         res = {}
         for tag, L, t in (("prefill", prefill[0], tp[0]), ("decode", decode[0], td[0])):
             kc, ks = quant(t["cache.ik"])

@@ -17,13 +17,14 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcskv.so")
 
-BF16, F32, FP8, FP4, MXFP4 = 0, 1, 2, 3, 4
+BF16, F32, FP8, FP4, MXFP4, MXFP8 = 0, 1, 2, 3, 4, 5
 CSA, HCA = 0, 1
 EXPORTS = ("cskv_version", "cskv_status_string", "csa_compress", "hca_compress",
            "cskv_indexer_workspace_size", "indexer_topk", "indexer_scores", "topk_select",
            "cskv_topk_workspace_size", "cskv_quantize_fp8", "indexer_scores_fp8", "indexer_topk_fp8",
            "cskv_quantize_fp4", "indexer_scores_fp4", "indexer_topk_fp4",
            "cskv_quantize_mxfp4", "indexer_scores_mxfp4", "indexer_topk_mxfp4",
+           "cskv_quantize_mxfp8", "indexer_scores_mxfp8", "indexer_topk_mxfp8",
            "cskv_quantize_kv_fp8", "compressed_attn_prefill_kv8", "compressed_attn_decode_kv8",
            "compressed_attn_prefill",
            "cskv_decode_workspace_size", "compressed_attn_decode",
@@ -52,6 +53,9 @@ _SIGS = {
     "cskv_quantize_mxfp4": (_I, [_P, _L, _I, _I, _P, _P, _P]),
     "indexer_scores_mxfp4": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _P, _L, _P]),
     "indexer_topk_mxfp4": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _I, _P, _P, _Z, _P]),
+    "cskv_quantize_mxfp8": (_I, [_P, _L, _I, _I, _P, _P, _P]),
+    "indexer_scores_mxfp8": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _P, _L, _P]),
+    "indexer_topk_mxfp8": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _I, _P, _P, _Z, _P]),
     "cskv_quantize_kv_fp8": (_I, [_P, _I, _L, _I, _I, _I, _P, _P, _L, _P]),
     "compressed_attn_prefill_kv8": (_I, [_I, _P, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
                                          _I, _P, _F, _I, _F, _F, _I, _P, _P, _P]),
@@ -211,7 +215,7 @@ def topk_select(scores, N: int, pos0: int, m: int, k: int, out=None, workspace=N
     return out
 
 
-_LOWP = {FP8: ("fp8", 1), FP4: ("fp4", 2), MXFP4: ("mxfp4", 2)}  # name suffix, values per byte
+_LOWP = {FP8: ("fp8", 1), FP4: ("fp4", 2), MXFP4: ("mxfp4", 2), MXFP8: ("mxfp8", 1)}  # name suffix, values per byte
 
 
 def _quantize(x, fmt):
@@ -235,16 +239,27 @@ def quantize_fp4(x) -> Tuple[torch.Tensor, torch.Tensor]:
     return _quantize(x, FP4)
 
 
+def _quantize_mx(x, fmt):
+    suffix, per_byte = _LOWP[fmt]
+    dim = x.shape[-1]
+    rows = x.numel() // dim if dim else 0
+    codes = torch.empty(*x.shape[:-1], dim // per_byte, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(*x.shape[:-1], dim // 32, dtype=torch.uint8, device=x.device)
+    name = f"cskv_quantize_{suffix}"
+    _check(name, getattr(lib(), name)(_ptr(x), rows, dim, _dtype(x), _ptr(codes), _ptr(scales), _stream(x)))
+    return codes, scales
+
+
 def quantize_mxfp4(x) -> Tuple[torch.Tensor, torch.Tensor]:
     """MX-FP4 rows of x (bf16 or fp32): E2M1 codes, two per byte ([..., dim / 2] uint8), and one
     E8M0 scale byte per 32 values ([..., dim / 32] uint8)."""
-    dim = x.shape[-1]
-    rows = x.numel() // dim if dim else 0
-    codes = torch.empty(*x.shape[:-1], dim // 2, dtype=torch.uint8, device=x.device)
-    scales = torch.empty(*x.shape[:-1], dim // 32, dtype=torch.uint8, device=x.device)
-    _check("cskv_quantize_mxfp4", lib().cskv_quantize_mxfp4(_ptr(x), rows, dim, _dtype(x), _ptr(codes), _ptr(scales),
-                                                            _stream(x)))
-    return codes, scales
+    return _quantize_mx(x, MXFP4)
+
+
+def quantize_mxfp8(x) -> Tuple[torch.Tensor, torch.Tensor]:
+    """MX-FP8 rows of x (bf16 or fp32): E4M3 codes ([..., dim] uint8) and one E8M0 scale byte per
+    32 values ([..., dim / 32] uint8)."""
+    return _quantize_mx(x, MXFP8)
 
 
 def _scores_lowp(fmt, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, scores):
@@ -422,3 +437,14 @@ def indexer_topk_mxfp4(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: i
                        workspace=None) -> torch.Tensor:
     """Top-k compressed entries per query from MX-FP4 rows: [batch, Tq, k] int32, ascending, -1 padded."""
     return _topk_lowp(MXFP4, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, k, out, workspace)
+
+
+def indexer_scores_mxfp8(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int, scores=None) -> torch.Tensor:
+    """Indexer scores on MX-FP8 rows (dI = 128): [batch, Tq, ld] fp32 (valid for s < V_t)."""
+    return _scores_lowp(MXFP8, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, scores)
+
+
+def indexer_topk_mxfp8(q_codes, q_scales, wI, k_codes, k_scales, pos0: int, m: int, k: int, out=None,
+                       workspace=None) -> torch.Tensor:
+    """Top-k compressed entries per query from MX-FP8 rows: [batch, Tq, k] int32, ascending, -1 padded."""
+    return _topk_lowp(MXFP8, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, k, out, workspace)

@@ -19,14 +19,17 @@
 // scale = amax / MAX, MAX = 448 (E4M3) or 6 (E2M1); the quotient and product
 // are correctly rounded fp32.
 //
-// MX-FP4 (the same E2M1 codes with block scales, as in the OCP Microscaling
-// formats): every 32 consecutive values of a row share one E8M0 scale
-// 2^(code - 127), the shared exponent being floor(log2 amax) - 2 over the
-// block (E2M1's largest value is 1.5 * 2^2); codes = E2M1(x / scale). The
-// scaled MFMA applies them in hardware: with the K permutation below, lane
-// half h at k-step ks holds block 2h + ks of its row (dI = 128), so each
-// lane passes its row's 4 scale bytes shifted by 16 h and the instruction
-// selects byte ks. Only the head weight multiplies the ReLU; no key scale.
+// MX-FP4 / MX-FP8 (the same E2M1 / E4M3 codes with block scales, as in the
+// OCP Microscaling formats): every 32 consecutive values of a row share one
+// E8M0 scale 2^(code - 127), the shared exponent being floor(log2 amax) - 2
+// (E2M1's largest value is 1.5 * 2^2) or - 8 (E4M3: 1.75 * 2^8) over the
+// block; codes = FMT(x / scale). The scaled MFMA applies them in hardware
+// (dI = 128, 4 scale bytes per row): for E2M1 each lane's 16 operand bytes
+// are one block (lane half h at k-step ks holds block 2h + ks), for E4M3 a
+// block is bytes 16q .. 16q+15 of lanes l and l + 32 (block 2 ks + q), see
+// op_off; each lane passes its row's scale bytes shifted so that the
+// instruction's byte select picks the block. Only the head weight multiplies
+// the ReLU; no key scale.
 //
 // The scoring kernels follow the bf16 ones: 8 queries per workgroup sharing
 // 256-key LDS tiles copied straight from global memory for prefill; for
@@ -132,11 +135,13 @@ __global__ __launch_bounds__(256) void quantize_fp4_kernel(const T* x, int64_t r
   if (lane == 0) scales[r] = amax > 0.f ? __fdiv_rn(amax, 6.f) : 0.f;
 }
 
-// MX-FP4 rows: one wave per row, dim % 32 == 0, dim <= 1024. Lane groups of 8 (4 values each)
-// cover one 32-value block; codes packed as in quantize_fp4_kernel, one E8M0 byte per block.
-template <typename T>
-__global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const T* x, int64_t rows, int dim, uint8_t* codes,
-                                                            uint8_t* scales) {
+// MX rows (E2M1 or E4M3 values): one wave per row, dim % 32 == 0, dim <= 1024. Lane groups of 8
+// (4 values each) cover one 32-value block; codes as in quantize_fp4_kernel / quantize_fp8_kernel,
+// one E8M0 byte per block; shared exponent floor(log2 amax) - EMAX, EMAX = 2 (E2M1) or 8 (E4M3).
+template <typename T, int FMT>
+__global__ __launch_bounds__(256) void quantize_mx_kernel(const T* x, int64_t rows, int dim, uint8_t* codes,
+                                                         uint8_t* scales) {
+  constexpr int EMAX = FMT == FMT_E2M1 ? 2 : 8;
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
@@ -156,15 +161,22 @@ __global__ __launch_bounds__(256) void quantize_mxfp4_kernel(const T* x, int64_t
     if (amax > 0.f) {
       int ex;
       (void)frexpf(amax, &ex);  // amax = f 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
-      code = min(max(ex - 1 - 2 + 127, 0), 254);
+      code = min(max(ex - 1 - EMAX + 127, 0), 254);
     }
     const float inv = ldexpf(1.f, 127 - code);  // 1 / scale, exact
     if (c < nc) {
       uint32_t w = 0;
-      if (amax > 0.f)
+      if constexpr (FMT == FMT_E2M1) {
+        if (amax > 0.f)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w |= e2m1_code(v[e] * inv) << (4 * e);
-      *reinterpret_cast<uint16_t*>(codes + r * (dim / 2) + 2 * c) = (uint16_t)w;
+          for (int e = 0; e < 4; ++e) w |= e2m1_code(v[e] * inv) << (4 * e);
+        *reinterpret_cast<uint16_t*>(codes + r * (dim / 2) + 2 * c) = (uint16_t)w;
+      } else {
+        if (amax > 0.f)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w |= e4m3_code(v[e] * inv) << (8 * e);
+        *reinterpret_cast<uint32_t*>(codes + r * dim + 4 * c) = w;
+      }
       if ((c & 7) == 0) scales[r * (dim / 32) + c / 8] = (uint8_t)code;
     }
   }
@@ -188,13 +200,42 @@ __device__ __forceinline__ f32x16 mfma_lowp(const i32x8& a, const i32x8& b, cons
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, 0, 0, 0);
 }
 
-// Block-scaled product (MX): scale bytes ks of sa (A row) and sb (B column) apply to this k-step.
+// Byte offset within a row of the q-th 16-byte chunk of the operand that lane half h holds at
+// k-step ks. Plain rows: one contiguous half row per lane half (h DI/2 + OB ks + 16 q). MX-FP8: the
+// matrix core forms each 32-value scale block of a k-step from bytes 16q .. 16q+15 of lane l and of
+// lane l + 32 (in-bounds probe on gfx950), so those hold values 64 ks + 32 q + 16 h .. +15 of the
+// row: block q of k-step ks is the row's block 2 ks + q. (E2M1 blocks are one lane's 16 bytes.)
+template <int FMT, int KS8, bool MX>
+__device__ __forceinline__ int op_off(int h, int ks, int q) {
+  constexpr int DI = 64 * KS8 * LowP<FMT>::BITS / 8;
+  if constexpr (MX && FMT == FMT_E4M3) return 64 * ks + 32 * q + 16 * h;
+  else return h * (DI / 2) + LowP<FMT>::OB * ks + 16 * q;
+}
+
+template <int FMT, int KS8, bool MX>
+__device__ __forceinline__ i32x8 load_op_at(const uint8_t* row, int h, int ks) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(row + op_off<FMT, KS8, MX>(h, ks, 0));
+  if constexpr (FMT == FMT_E2M1) {
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, 0, 0, 0, 0};
+  } else {
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(row + op_off<FMT, KS8, MX>(h, ks, 1));
+    return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  }
+}
+
+// MX scale bytes of a row (4 bytes, dI = 128) as one lane's scale operand: E2M1 lane half h holds
+// blocks 2h + ks (shift 16 h, byte select ks); E4M3 lane half h supplies block 2 ks + h (shift 8 h,
+// byte select 2 ks).
+template <int FMT>
+__device__ __forceinline__ uint32_t mx_scale_word(uint32_t bytes, int h) {
+  return bytes >> ((FMT == FMT_E2M1 ? 16 : 8) * h);
+}
+
+// Block-scaled product (MX) at k-step KS; sa, sb from mx_scale_word.
 template <int FMT, int KS>
 __device__ __forceinline__ f32x16 mfma_mx(const i32x8& a, const i32x8& b, const f32x16& c, uint32_t sa, uint32_t sb) {
-  if constexpr (KS == 0)
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 0, (int)sa, 0, (int)sb);
-  else
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, 1, (int)sa, 1, (int)sb);
+  constexpr int SEL = FMT == FMT_E2M1 ? KS : 2 * KS;
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT, FMT, SEL, (int)sa, SEL, (int)sb);
 }
 
 // Query operands (A) and head weights of query j; lane holds head lane%32 of each tile. Row
@@ -205,7 +246,7 @@ __device__ __forceinline__ void load_query_lowp(const IdxArgs& a, int b, int64_t
                                                 i32x8 (&qa)[HT][KS8], float (&wv)[HT][16], uint32_t (&qsx)[HT]) {
   constexpr int DI = 64 * KS8 * LowP<FMT>::BITS / 8;  // bytes per row
   constexpr int OB = LowP<FMT>::OB;
-  const uint8_t* qp = (const uint8_t*)a.qI + ((int64_t)b * a.Tq + j) * a.HI * DI + (DI / 2) * (lane >> 5);
+  const uint8_t* qp = (const uint8_t*)a.qI + ((int64_t)b * a.Tq + j) * a.HI * DI;
   const float* wp = a.wI + ((int64_t)b * a.Tq + j) * a.HI;
   const float* sp = a.q_scale + ((int64_t)b * a.Tq + j) * a.HI;
 #pragma unroll
@@ -213,8 +254,8 @@ __device__ __forceinline__ void load_query_lowp(const IdxArgs& a, int b, int64_t
     const int h = ht * 32 + (lane & 31);
 #pragma unroll
     for (int ks = 0; ks < KS8; ++ks)
-      qa[ht][ks] = (qvalid && h < a.HI) ? load_op<FMT>(qp + (int64_t)h * DI + OB * ks) : i32x8{};
-    qsx[ht] = MX && qvalid && h < a.HI ? __float_as_uint(sp[h]) >> (16 * (lane >> 5)) : 0x7f7f7f7fu;
+      qa[ht][ks] = (qvalid && h < a.HI) ? load_op_at<FMT, KS8, MX>(qp + (int64_t)h * DI, lane >> 5, ks) : i32x8{};
+    qsx[ht] = MX && qvalid && h < a.HI ? mx_scale_word<FMT>(__float_as_uint(sp[h]), lane >> 5) : 0x7f7f7f7fu;
     // accumulator rows held by this lane: 8*(i/4) + 4*(lane/32) + i%4
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -243,7 +284,7 @@ __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
   constexpr int IPW = 32 / RPI;        // copies per wave per tile (each wave copies 32 rows)
   constexpr int SH = CPR == 16 ? 1 : CPR == 8 ? 2 : CPR == 4 ? 3 : 4;  // log2(32 / CPR)
   static_assert(TILE == 32 * QB && CPR >= 2 && CPR <= 16 && IPW >= 1, "tile shape");
-  static_assert(!MX || (FMT == FMT_E2M1 && KS8 == 2), "MX: E2M1, dI = 128 (4 scale bytes per row)");
+  static_assert(!MX || KS8 == 2, "MX: dI = 128 (4 scale bytes per row)");
   // two arrays per buffer kind (not [2][...]): the compiler then sees that a copy into one
   // never feeds reads of the other. Scales: wave w copies keys 32 w + (lane % 32) to 64 w + lane.
   __shared__ __attribute__((aligned(16))) uint8_t kt0[TILE * DI], kt1[TILE * DI];
@@ -302,7 +343,7 @@ __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
   for (int ks = 0; ks < KS8; ++ks)
 #pragma unroll
     for (int q = 0; q < CPO; ++q)
-      bofs[ks][q] = (lane & 31) * DI + ((((lane >> 5) * (CPR / 2) + ks * CPO + q) ^ (((lane & 31) >> SH) % CPR)) * 16);
+      bofs[ks][q] = (lane & 31) * DI + (((op_off<FMT, KS8, MX>(lane >> 5, ks, q) / 16) ^ (((lane & 31) >> SH) % CPR)) * 16);
   auto rdB = [&](const uint8_t* kp, i32x8 (&dst)[KS8]) {
 #pragma unroll
     for (int ks = 0; ks < KS8; ++ks) {
@@ -355,7 +396,7 @@ __global__ __launch_bounds__(512) void indexer_score_lowp_mfma(IdxArgs a) {
   i32x8 bv[2][KS8];
   float sc[2];     // scales of the keys of the current and previous sub-block
   uint32_t kx[2];  // MX: scale bytes of the current and next sub-block's keys, shifted to the lane half
-  auto rdX = [&](const float* sb_, int sb) { return __float_as_uint(sb_[64 * sb + lane]) >> (16 * (lane >> 5)); };
+  auto rdX = [&](const float* sb_, int sb) { return mx_scale_word<FMT>(__float_as_uint(sb_[64 * sb + lane]), lane >> 5); };
   auto tile = [&](int it, const uint8_t* kb, const float* sb_) {
     const int t0 = it * TILE;
     rdB(kb, bv[0]);
@@ -450,9 +491,9 @@ __global__ __launch_bounds__(256) void indexer_score_lowp_stream(IdxArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     f32x16 acc[HT];
     if constexpr (MX) {
-      const uint32_t kx = __float_as_uint(sc) >> (16 * half);  // the key's 4 scale bytes, this half's blocks
-      const i32x8 b0 = load_op<FMT>(my + kl * RS + (DI / 2) * half);
-      const i32x8 b1 = load_op<FMT>(my + kl * RS + (DI / 2) * half + OB);
+      const uint32_t kx = mx_scale_word<FMT>(__float_as_uint(sc), half);  // the key's 4 scale bytes
+      const i32x8 b0 = load_op_at<FMT, KS8, MX>(my + kl * RS, half, 0);
+      const i32x8 b1 = load_op_at<FMT, KS8, MX>(my + kl * RS, half, 1);
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht) {
         acc[ht] = mfma_mx<FMT, 0>(qa[ht][0], b0, f32x16{}, qsx[ht], kx);
@@ -548,6 +589,9 @@ int launch_scores_lowp(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st)
   if (dtype == CSKV_MXFP4)
     ok = qb == 8 ? dispatch_lowp<FMT_E2M1, false, true>(ht, ks8, a, grid, st)
                  : dispatch_lowp<FMT_E2M1, true, true>(ht, ks8, a, grid, st);
+  else if (dtype == CSKV_MXFP8)
+    ok = qb == 8 ? dispatch_lowp<FMT_E4M3, false, true>(ht, ks8, a, grid, st)
+                 : dispatch_lowp<FMT_E4M3, true, true>(ht, ks8, a, grid, st);
   else if (dtype == CSKV_FP4)
     ok = qb == 8 ? dispatch_lowp<FMT_E2M1, false>(ht, ks8, a, grid, st) : dispatch_lowp<FMT_E2M1, true>(ht, ks8, a, grid, st);
   else
@@ -561,7 +605,7 @@ static int check_lowp_shape(int batch, int64_t Tq, int64_t N, int HI, int dI, in
   if (HI < 1 || HI > CSKV_MAX_HEADS) return CSKV_ERR_BAD_SHAPE;
   if (N > ((int64_t)1 << 31) - 64) return CSKV_ERR_BAD_SHAPE;
   if (dI != 64 && dI != 128) return CSKV_ERR_UNSUPPORTED;
-  if (dtype == CSKV_MXFP4 && dI != 128) return CSKV_ERR_UNSUPPORTED;  // 4 scale bytes per row
+  if ((dtype == CSKV_MXFP4 || dtype == CSKV_MXFP8) && dI != 128) return CSKV_ERR_UNSUPPORTED;  // 4 scale bytes per row
   return CSKV_OK;
 }
 
@@ -591,8 +635,8 @@ static int quantize_rows(int fmt, const void* x, int64_t rows, int dim, int dtyp
   return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
 }
 
-static int quantize_rows_mx(const void* x, int64_t rows, int dim, int dtype, uint8_t* codes, uint8_t* scales,
-                            void* stream) {
+static int quantize_rows_mx(int fmt, const void* x, int64_t rows, int dim, int dtype, uint8_t* codes,
+                            uint8_t* scales, void* stream) {
   if (dtype != CSKV_BF16 && dtype != CSKV_F32) return CSKV_ERR_BAD_DTYPE;
   if (rows < 0 || dim < 32 || dim % 32 != 0 || dim > 1024) return CSKV_ERR_BAD_SHAPE;
   if (ceil_div(rows, (int64_t)4) > 0x7fffffff) return CSKV_ERR_BAD_SHAPE;
@@ -601,11 +645,21 @@ static int quantize_rows_mx(const void* x, int64_t rows, int dim, int dtype, uin
   if (!aligned16(x, codes, scales)) return CSKV_ERR_MISALIGNED;
   dim3 grid((unsigned)ceil_div(rows, (int64_t)4));
   hipStream_t st = (hipStream_t)stream;
-  if (dtype == CSKV_BF16)
-    hipLaunchKernelGGL(quantize_mxfp4_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)x, rows, dim, codes, scales);
-  else
-    hipLaunchKernelGGL(quantize_mxfp4_kernel<float>, grid, dim3(256), 0, st, (const float*)x, rows, dim, codes,
-                       scales);
+  if (fmt == FMT_E2M1) {
+    if (dtype == CSKV_BF16)
+      hipLaunchKernelGGL((quantize_mx_kernel<bf16, FMT_E2M1>), grid, dim3(256), 0, st, (const bf16*)x, rows, dim, codes,
+                         scales);
+    else
+      hipLaunchKernelGGL((quantize_mx_kernel<float, FMT_E2M1>), grid, dim3(256), 0, st, (const float*)x, rows, dim,
+                         codes, scales);
+  } else {
+    if (dtype == CSKV_BF16)
+      hipLaunchKernelGGL((quantize_mx_kernel<bf16, FMT_E4M3>), grid, dim3(256), 0, st, (const bf16*)x, rows, dim, codes,
+                         scales);
+    else
+      hipLaunchKernelGGL((quantize_mx_kernel<float, FMT_E4M3>), grid, dim3(256), 0, st, (const float*)x, rows, dim,
+                         codes, scales);
+  }
   return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
 }
 
@@ -712,7 +766,27 @@ extern "C" int indexer_topk_fp4(const uint8_t* qI, const float* q_scale, const f
 // 32-bit word per row through the fp32 scale slots of the argument block.
 extern "C" int cskv_quantize_mxfp4(const void* x, int64_t rows, int dim, int dtype, uint8_t* codes, uint8_t* scales,
                                    void* stream) {
-  return quantize_rows_mx(x, rows, dim, dtype, codes, scales, stream);
+  return quantize_rows_mx(FMT_E2M1, x, rows, dim, dtype, codes, scales, stream);
+}
+
+extern "C" int cskv_quantize_mxfp8(const void* x, int64_t rows, int dim, int dtype, uint8_t* codes, uint8_t* scales,
+                                   void* stream) {
+  return quantize_rows_mx(FMT_E4M3, x, rows, dim, dtype, codes, scales, stream);
+}
+
+extern "C" int indexer_scores_mxfp8(const uint8_t* qI, const uint8_t* q_scale, const float* wI, const uint8_t* KI,
+                                    const uint8_t* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                                    int64_t pos0, int m, float* scores, int64_t ld, void* stream) {
+  return scores_lowp(CSKV_MXFP8, qI, (const float*)q_scale, wI, KI, (const float*)k_scale, batch, Tq, N, HI, dI,
+                     pos0, m, scores, ld, stream);
+}
+
+extern "C" int indexer_topk_mxfp8(const uint8_t* qI, const uint8_t* q_scale, const float* wI, const uint8_t* KI,
+                                  const uint8_t* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                                  int64_t pos0, int m, int k, int32_t* out_idx, void* workspace, size_t ws_bytes,
+                                  void* stream) {
+  return topk_lowp(CSKV_MXFP8, qI, (const float*)q_scale, wI, KI, (const float*)k_scale, batch, Tq, N, HI, dI, pos0,
+                   m, k, out_idx, workspace, ws_bytes, stream);
 }
 
 extern "C" int indexer_scores_mxfp4(const uint8_t* qI, const uint8_t* q_scale, const float* wI, const uint8_t* KI,

@@ -62,7 +62,8 @@ enum {
 
 enum { CSKV_BF16 = 0, CSKV_F32 = 1, CSKV_FP8 = 2 /* E4M3 codes, fp32 row scales */,
        CSKV_FP4 = 3 /* E2M1 codes, two per byte, fp32 row scales */,
-       CSKV_MXFP4 = 4 /* E2M1 codes, two per byte, one E8M0 scale per 32 values */ };
+       CSKV_MXFP4 = 4 /* E2M1 codes, two per byte, one E8M0 scale per 32 values */,
+       CSKV_MXFP8 = 5 /* E4M3 codes, one E8M0 scale per 32 values */ };
 enum { CSKV_MODE_CSA = 0, CSKV_MODE_HCA = 1 };
 
 #define CSKV_MAX_TOPK 2048
@@ -280,6 +281,32 @@ int indexer_scores_mxfp4(const uint8_t* qI, const uint8_t* q_scale, const float*
                          const uint8_t* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
                          int64_t pos0, int m, float* scores, int64_t ld, void* stream);
 int indexer_topk_mxfp4(const uint8_t* qI, const uint8_t* q_scale, const float* wI, const uint8_t* KI,
+                       const uint8_t* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                       int64_t pos0, int m, int k, int32_t* out_idx, void* workspace, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * MX-FP8 lightning indexer -- the FP8 setting of [PB §2.3.4] with the same
+ * block scales: E4M3 values (one byte each), one E8M0 scale byte per 32.
+ *
+ * cskv_quantize_mxfp8 -- as cskv_quantize_mxfp4 with E4M3 values and
+ *   code = clamp(floor(log2 amax) - 8 + 127, 0, 254) (E4M3's largest value
+ *   is 1.75 * 2^8); codes = E4M3(x * 2^(127 - code)) (nearest, ties to the
+ *   even code, saturating at +-448).
+ *   codes : [rows, dim] bytes, scales : [rows, dim / 32] bytes.
+ * indexer_scores_mxfp8 / indexer_topk_mxfp8 -- as the MX-FP4 calls on E4M3
+ *   rows: qI : [batch, Tq, HI, 128], KI : [batch, N, 128] bytes; scales as
+ *   for MX-FP4. E4M3 products are summed as in indexer_scores_fp8 (groups of
+ *   8 on a grid 2^-13 below the group's largest), then scaled per block. The
+ *   workspace of indexer_topk_mxfp8 is
+ *   cskv_indexer_workspace_size(..., CSKV_MXFP8) bytes.
+ */
+int cskv_quantize_mxfp8(const void* x, int64_t rows, int dim, int dtype, uint8_t* codes, uint8_t* scales,
+                        void* stream);
+int indexer_scores_mxfp8(const uint8_t* qI, const uint8_t* q_scale, const float* wI, const uint8_t* KI,
+                         const uint8_t* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
+                         int64_t pos0, int m, float* scores, int64_t ld, void* stream);
+int indexer_topk_mxfp8(const uint8_t* qI, const uint8_t* q_scale, const float* wI, const uint8_t* KI,
                        const uint8_t* k_scale, int batch, int64_t Tq, int64_t N, int HI, int dI,
                        int64_t pos0, int m, int k, int32_t* out_idx, void* workspace, size_t ws_bytes,
                        void* stream);

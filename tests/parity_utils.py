@@ -85,17 +85,33 @@ def fp8_score_bound(q_codes, q_scales, w_row, k_codes, k_scales, V: int) -> np.n
       B[s] = ks[s] * sum_h |w_h qs_h| * (7 * 2**-13 * sum_g Qmax[h,g] Kmax[s,g]
                                         + 2**-20 * (|dq_h| . |dk_s|) + 2**-17 * |dq_h . dk_s|)
     """
-    dq = O.e4m3_decode(q_codes)                 # [HI, dI]
-    dk = O.e4m3_decode(k_codes[:V])             # [V, dI]
+    return e4m3_group_bound(O.e4m3_decode(q_codes), O.e4m3_decode(k_codes[:V]),
+                            np.asarray(w_row, dtype=np.float64) * np.asarray(q_scales, dtype=np.float64),
+                            np.asarray(k_scales[:V], dtype=np.float64))
+
+
+def mxfp8_score_bound(q_codes, q_scales, w_row, k_codes, k_scales, V: int) -> np.ndarray:
+    """Bound on |I_gpu - I| for one query's MX-FP8 scores over keys 0..V-1: the FP8 group model
+    (fp8_score_bound) on the decoded rows, whose 8-value groups lie inside one 32-value block and so
+    share one scale (the grid moves with it); the block-sum additions (at most an fp32 ulp each,
+    measured for the block-scaled instruction) fall under its 2**-20 * sum |products| term."""
+    dq = O.dequantize_mxfp8(q_codes, q_scales)
+    dk = O.dequantize_mxfp8(k_codes[:V], k_scales[:V])
+    return e4m3_group_bound(dq, dk, np.asarray(w_row, dtype=np.float64), np.ones(V))
+
+
+def e4m3_group_bound(dq, dk, wq, ks) -> np.ndarray:
+    """The FP8 error model of fp8_score_bound on decoded rows dq [HI, dI], dk [V, dI], head factors
+    wq [HI] (weight times row scale) and key factors ks [V]."""
+    V = dk.shape[0]
     HI, dI = dq.shape
     qmax = np.abs(dq).reshape(HI, dI // 8, 8).max(axis=2)
     kmax = np.abs(dk).reshape(V, dI // 8, 8).max(axis=2)
     gm = kmax @ qmax.T                          # [V, HI]
     ab = np.abs(dk) @ np.abs(dq).T
     dot = np.abs(dk @ dq.T)
-    wq = np.abs(np.asarray(w_row, dtype=np.float64) * np.asarray(q_scales, dtype=np.float64))  # [HI]
     per = 7 * 2.0 ** -13 * gm + 2.0 ** -20 * ab + 2.0 ** -17 * dot
-    return np.asarray(k_scales[:V], dtype=np.float64) * (per @ wq)
+    return np.asarray(ks, dtype=np.float64) * (per @ np.abs(np.asarray(wq, dtype=np.float64)))
 
 
 def check_topk_row_bounded(gpu_row: np.ndarray, scores: np.ndarray, bound: np.ndarray, V: int, k: int,

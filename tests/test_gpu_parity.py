@@ -13,7 +13,7 @@ from compressed_sparse_kv_02_amd import binding as B
 from compressed_sparse_kv_02_amd import layer as LY
 from compressed_sparse_kv_02_amd.synth import normal_device, uniform_device
 from tests.parity_utils import (assert_storage_close, check_topk_row, check_topk_row_bounded, fp8_score_bound,
-                                mxfp4_score_bound,
+                                mxfp4_score_bound, mxfp8_score_bound,
                                 key_rounding_band, np64, oracle_layer)
 
 pytestmark = pytest.mark.gpu
@@ -319,11 +319,12 @@ def test_indexer_fp4(bt, Tq, N, HI, dI, pos0, m, k):
     say("  tie-band differences:", n_band)
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
 @pytest.mark.parametrize("dtype,rows,dim", [("bf16", 300, 128), ("f32", 77, 1024), ("bf16", 5, 32)])
-def test_quantize_mxfp4(dtype, rows, dim):
+def test_quantize_mx(fmt, dtype, rows, dim):
     """MX-FP4 codes and E8M0 block scales bit-exact against the oracle, with zero, tiny, huge and
     saturating blocks among normal ones."""
-    say("quantize_mxfp4", dtype, rows, dim)
+    say("quantize", fmt, dtype, rows, dim)
     x = gen(35, "mx.x", (rows, dim), dtype).float()
     x = x * torch.exp2(torch.arange(rows, device=DEV, dtype=torch.float32) % 41 - 20)[:, None]
     x[0, :32] = 0.0                       # all-zero block
@@ -332,11 +333,12 @@ def test_quantize_mxfp4(dtype, rows, dim):
         x[2, :32] = 3.0e30                # large exponent
         x[2, 5] = -0.0
     x = x.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
-    codes, sc = B.quantize_mxfp4(x)
+    codes, sc = (B.quantize_mxfp4 if fmt == "mxfp4" else B.quantize_mxfp8)(x)
     torch.cuda.synchronize()
-    oc, osc = O.quantize_rows_mxfp4(np64(x).astype(np.float32))
+    oc, osc = (O.quantize_rows_mxfp4 if fmt == "mxfp4" else O.quantize_rows_mxfp8)(np64(x).astype(np.float32))
     assert np.array_equal(sc.cpu().numpy(), osc)
-    assert np.array_equal(_unpack(codes.cpu().numpy()), oc)
+    got = codes.cpu().numpy()
+    assert np.array_equal(_unpack(got) if fmt == "mxfp4" else got, oc)
 
 
 @pytest.mark.parametrize("bt,Tq,N,HI,pos0,m,k", [
@@ -346,32 +348,38 @@ def test_quantize_mxfp4(dtype, rows, dim):
     (3, 5, 70000, 64, 4 * 70000, 4, 1024),             # decode route, two-kernel top-k
     (1, 2, 3000, 128, 3000 * 4 - 2, 4, 2048),          # 128 heads, max k
 ])
-def test_indexer_mxfp4(bt, Tq, N, HI, pos0, m, k):
-    """MX-FP4 scores within the derived bound of the oracle on its own quantisation (dI = 128);
-    top-k exact outside the bound."""
-    say("indexer mxfp4", bt, Tq, N, HI, pos0, m, k)
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_indexer_mx(fmt, bt, Tq, N, HI, pos0, m, k):
+    """MX-FP4 / MX-FP8 scores within the derived bound of the oracle on its own quantisation
+    (dI = 128); top-k exact outside the bound."""
+    say("indexer", fmt, bt, Tq, N, HI, pos0, m, k)
+    qz, score, topk = ((B.quantize_mxfp4, B.indexer_scores_mxfp4, B.indexer_topk_mxfp4) if fmt == "mxfp4" else
+                       (B.quantize_mxfp8, B.indexer_scores_mxfp8, B.indexer_topk_mxfp8))
+    oqz, oscore, obound = ((O.quantize_rows_mxfp4, O.indexer_scores_mxfp4, mxfp4_score_bound) if fmt == "mxfp4" else
+                           (O.quantize_rows_mxfp8, O.indexer_scores_mxfp8, mxfp8_score_bound))
+    unpack = _unpack if fmt == "mxfp4" else (lambda a: a)
     dI = 128
     qI = gen(37, "mx.q", (bt, Tq, HI, dI))
     KI = gen(37, "mx.k", (bt, N, dI))
     wI = uniform_device(37, "mx.w", (bt, Tq, HI), DEV)
-    qc, qs = B.quantize_mxfp4(qI)
-    kc, ks = B.quantize_mxfp4(KI)
-    sc = B.indexer_scores_mxfp4(qc, qs, wI, kc, ks, pos0, m)
-    idx = B.indexer_topk_mxfp4(qc, qs, wI, kc, ks, pos0, m, k)
+    qc, qs = qz(qI)
+    kc, ks = qz(KI)
+    sc = score(qc, qs, wI, kc, ks, pos0, m)
+    idx = topk(qc, qs, wI, kc, ks, pos0, m, k)
     torch.cuda.synchronize()
     sc, idx = sc.cpu().numpy(), idx.cpu().numpy()
     rows = range(Tq) if Tq <= 80 else sorted(set(np.linspace(0, Tq - 1, 40).astype(int)) | {0, Tq - 1})
     n_band, worst = 0, 0.0
     for b in range(bt):
-        okc, oks = O.quantize_rows_mxfp4(np64(KI[b]).astype(np.float32))
-        assert np.array_equal(okc, _unpack(kc[b].cpu().numpy())) and np.array_equal(oks, ks[b].cpu().numpy())
+        okc, oks = oqz(np64(KI[b]).astype(np.float32))
+        assert np.array_equal(okc, unpack(kc[b].cpu().numpy())) and np.array_equal(oks, ks[b].cpu().numpy())
         for r in rows:
-            oqc, oqs = O.quantize_rows_mxfp4(np64(qI[b, r]).astype(np.float32))
-            I = O.indexer_scores_mxfp4(oqc[None], oqs[None], np64(wI[b, r:r + 1]), okc, oks, pos0 + r, m)[0]
+            oqc, oqs = oqz(np64(qI[b, r]).astype(np.float32))
+            I = oscore(oqc[None], oqs[None], np64(wI[b, r:r + 1]), okc, oks, pos0 + r, m)[0]
             V = O.visible(pos0 + r, m, N)
             if V == 0:
                 continue
-            bound = mxfp4_score_bound(oqc, oqs, np64(wI[b, r]), okc, oks, V)
+            bound = obound(oqc, oqs, np64(wI[b, r]), okc, oks, V)
             err = np.abs(sc[b, r, :V] - I[:V])
             assert (err <= bound).all(), (b, r, float((err / bound).max()))
             worst = max(worst, float((err / bound).max()))
@@ -775,12 +783,14 @@ def test_indexer_topk_matches_its_two_halves():
     ("fp4", 3, 5, 70000, 64, 128, 4 * 70000, 4),
     ("mxfp4", 1, 1024, 7000, 64, 128, 4 * 7000 - 1024, 4),
     ("mxfp4", 3, 5, 70000, 20, 128, 4 * 70000, 4),
+    ("mxfp8", 1, 1024, 7000, 64, 128, 4 * 7000 - 1024, 4),
+    ("mxfp8", 3, 5, 70000, 20, 128, 4 * 70000, 4),
 ])
 def test_indexer_scores_write_extent(dtype, bt, Tq, N, HI, dI, pos0, m):
     # every visible entry gets a finite score; past V_t only -inf may be written, and nothing
     # at or past the last row's V (the end of every swept key range) or past N is touched
     say("indexer_scores write extent", dtype, bt, Tq, N, HI, dI, pos0, m)
-    lowp = dtype in ("fp8", "fp4", "mxfp4")
+    lowp = dtype in ("fp8", "fp4", "mxfp4", "mxfp8")
     qI = gen(23, "we.q", (bt, Tq, HI, dI), "bf16" if lowp else dtype)
     KI = gen(23, "we.k", (bt, N, dI), "bf16" if lowp else dtype)
     wI = uniform_device(23, "we.w", (bt, Tq, HI), DEV)
@@ -788,7 +798,8 @@ def test_indexer_scores_write_extent(dtype, bt, Tq, N, HI, dI, pos0, m):
     sc = torch.full((bt, Tq, ld), float("nan"), dtype=torch.float32, device=DEV)
     if lowp:
         qz, fn = {"fp8": (B.quantize_fp8, B.indexer_scores_fp8), "fp4": (B.quantize_fp4, B.indexer_scores_fp4),
-                  "mxfp4": (B.quantize_mxfp4, B.indexer_scores_mxfp4)}[dtype]
+                  "mxfp4": (B.quantize_mxfp4, B.indexer_scores_mxfp4),
+                  "mxfp8": (B.quantize_mxfp8, B.indexer_scores_mxfp8)}[dtype]
         (qc, qs), (kc, ks) = qz(qI), qz(KI)
         fn(qc, qs, wI, kc, ks, pos0, m, scores=sc)
     else:
