@@ -186,6 +186,31 @@ def test_fp8_indexer_validation(L):
     assert L.cskv_indexer_workspace_size(1, 64, 1000, 64, 1024, 3) >= 64 * 1000 * 4
 
 
+def test_mx_indexer_validation(L):
+    for fmt in ("mxfp4", "mxfp8"):
+        q = getattr(L, f"cskv_quantize_{fmt}")
+        assert q(P, 10, 128, 2, P, P, None) == DTYPE     # input must be bf16 or fp32
+        assert q(P, 10, 48, 0, P, P, None) == SHAPE      # dim % 32 (one scale per 32 values)
+        assert q(P, 10, 2048, 0, P, P, None) == SHAPE    # dim > 1024
+        assert q(P, 10, 128, 0, P, None, None) == INVALID
+        assert q(P, 10, 128, 0, P, P + 4, None) == MISALIGNED
+        assert q(P, 0, 128, 0, P, P, None) == OK
+        s = getattr(L, f"indexer_scores_{fmt}")
+        base = dict(q=P, qs=P, w=P, k=P, ks=P, batch=1, Tq=4, N=1000, HI=64, dI=128, pos0=0, m=4, sc=P, ld=1024,
+                    st=None)
+        for kw, want in ((dict(dI=64), UNSUPPORTED),   # 4 scale bytes per row: dI = 128 only
+                         (dict(HI=0), SHAPE), (dict(ld=999), SHAPE), (dict(qs=None), INVALID),
+                         (dict(ks=P + 4), MISALIGNED), (dict(Tq=0), OK)):
+            assert s(*dict(base, **kw).values()) == want, (fmt, kw)
+        t = getattr(L, f"indexer_topk_{fmt}")
+        tb = dict(q=P, qs=P, w=P, k=P, ks=P, batch=1, Tq=64, N=1000, HI=64, dI=128, pos0=0, m=4, kk=1024, out=P,
+                  ws=P, wsb=1 << 40, st=None)
+        for kw, want in ((dict(kk=4096), UNSUPPORTED), (dict(ws=None), WS), (dict(dI=64), UNSUPPORTED)):
+            assert t(*dict(tb, **kw).values()) == want, (fmt, kw)
+    assert L.cskv_indexer_workspace_size(1, 64, 1000, 64, 1024, 4) >= 64 * 1000 * 4
+    assert L.cskv_indexer_workspace_size(1, 64, 1000, 64, 1024, 5) >= 64 * 1000 * 4
+
+
 def test_kv8_validation(L):
     q = L.cskv_quantize_kv_fp8
     assert q(P, 1, 4, 512, 64, 2, P, P, 0, None) == DTYPE
