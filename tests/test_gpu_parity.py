@@ -410,6 +410,35 @@ def test_indexer_fp4_decode_1m():
     say("  fp4 vs bf16 selection overlap per row:", [round(o, 3) for o in overlap])
 
 
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+def test_indexer_mx_decode_1m(fmt):
+    """MX top-k at the decode shape (batch 8 x 262144 keys at position 2^20, k = 1024), exact outside
+    the derived score bound; two calls give identical indices."""
+    say("indexer", fmt, "decode 1M: batch 8, 262144 keys")
+    N, pos0 = 262144, 1 << 20
+    qI = gen(8, "mxd.q", (8, 1, 64, 128))
+    KI = gen(8, "mxd.k", (8, N, 128))
+    wI = uniform_device(8, "mxd.w", (8, 1, 64), DEV)
+    qz, topk = (B.quantize_mxfp4, B.indexer_topk_mxfp4) if fmt == "mxfp4" else (B.quantize_mxfp8, B.indexer_topk_mxfp8)
+    oqz, oscore, obound = ((O.quantize_rows_mxfp4, O.indexer_scores_mxfp4, mxfp4_score_bound) if fmt == "mxfp4" else
+                           (O.quantize_rows_mxfp8, O.indexer_scores_mxfp8, mxfp8_score_bound))
+    qc, qs = qz(qI)
+    kc, ks = qz(KI)
+    idx = topk(qc, qs, wI, kc, ks, pos0, 4, 1024)
+    idx2 = topk(qc, qs, wI, kc, ks, pos0, 4, 1024)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+    idx = idx.cpu().numpy()
+    n_band = 0
+    for b in range(8):
+        okc, oks = oqz(np64(KI[b]).astype(np.float32))
+        oqc, oqs = oqz(np64(qI[b, 0]).astype(np.float32))
+        I = oscore(oqc[None], oqs[None], np64(wI[b]), okc, oks, pos0, 4)[0]
+        n_band += check_topk_row_bounded(idx[b, 0], I, obound(oqc, oqs, np64(wI[b, 0]), okc, oks, N), N, 1024,
+                                         what=f"b{b}")
+    say("  undecided entries:", n_band)
+
+
 # ----------------------------------------------------------------------------- attention
 
 def _random_idx(bt, Tq, pos0, m, N, k, seed):
