@@ -552,6 +552,9 @@ def attention(q, kv, win, win_pos0: int, pos0: int, m: int, w: int, idx=None, si
             sel = [int(s) for s in idx[j] if 0 <= s < N]
             comp = kv[sel]
         lo = max(0, t - w + 1)
+        if lo < win_pos0 or t - win_pos0 >= win.shape[0]:
+            raise ValueError(f"window rows at positions {win_pos0}..{win_pos0 + win.shape[0] - 1} "
+                             f"do not cover query {t}'s window {lo}..{t}")
         wrows = win[lo - win_pos0:t - win_pos0 + 1]
         keys = np.concatenate([comp, wrows], axis=0)
         qt = prepare_query(q[j], t, apply_q_norm, q_norm_w, eps, rope_dims, rope_base)

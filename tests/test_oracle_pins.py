@@ -94,6 +94,29 @@ def test_csa_chunk_with_tail_equals_full():
     assert np.allclose(part, full[cut // m:], atol=1e-13)
 
 
+def test_entry_rope_position_is_first_token_of_its_block():
+    # One rotated pair (rope_dims = c = 2, so theta_0 = 1) and a raw entry of [1, 0]: the stored
+    # entry is [cos p, sin p], p the entry's rotary position, which must be the first token of its
+    # own block, pos0 + m * i. CSA: a-row 0 of each block takes all the weight and holds [1, 0].
+    m, n, pos0 = 4, 5, 4 * 37
+    Ca = np.tile([[1.0, 0.0], [0.0, 3.0], [0.0, 3.0], [0.0, 3.0]], (n, 1))
+    Za = np.tile([[50.0, 50.0], [0.0, 0.0], [0.0, 0.0], [0.0, 0.0]], (n, 1))
+    Zb = np.full((n * m, 2), -50.0)
+    out = O.csa_compress(Ca, np.zeros_like(Ca), Za, Zb, np.zeros((2 * m, 2)), m, pos0=pos0,
+                         prev_Cb=np.zeros((m, 2)), prev_Zb=np.full((m, 2), -50.0), rope_dims=2)
+    p = pos0 + m * np.arange(n)
+    assert np.allclose(out, np.stack([np.cos(p), np.sin(p)], axis=1), atol=1e-12)
+    # HCA with uniform weights over a block of identical rows [1, 0]: entry i at pos0 + m' i
+    mh, pos0h = 8, 8 * 11
+    out = O.hca_compress(np.tile([1.0, 0.0], (3 * mh, 1)), None, None, mh, pos0=pos0h, rope_dims=2)
+    p = pos0h + mh * np.arange(3)
+    assert np.allclose(out, np.stack([np.cos(p), np.sin(p)], axis=1), atol=1e-12)
+    # window rows (m' = 1), normed ([2, 0] has RMS sqrt 2) and each turned at its own position
+    out = O.prepare_window(np.tile([2.0, 0.0], (4, 1)), 1000, eps=0.0, rope_dims=2)
+    p = 1000 + np.arange(4)
+    assert np.allclose(out, math.sqrt(2.0) * np.stack([np.cos(p), np.sin(p)], axis=1), atol=1e-12)
+
+
 def test_hca_hand_closed_form_and_m1_identity():
     C = np.array([[1.0, -2.0], [3.0, 4.0]])
     Z = np.array([[0.0, 0.0], [math.log(3.0), 0.0]])
@@ -117,6 +140,9 @@ def test_hca_uniform_is_block_mean():
 
 def test_rmsnorm_closed_form_and_unit_rms():
     assert np.allclose(O.rmsnorm(np.array([3.0, 4.0]), eps=0.0), [3 / math.sqrt(12.5), 4 / math.sqrt(12.5)])
+    # eps joins the mean square under the root: mean 12.5 + 0.5 = 13
+    assert np.allclose(O.rmsnorm(np.array([3.0, 4.0]), eps=0.5), [3 / math.sqrt(13.0), 4 / math.sqrt(13.0)],
+                       rtol=0, atol=1e-15)
     X = rng.normal(size=(10, 64)) * 5
     Y = O.rmsnorm(X, eps=0.0)
     assert np.allclose(np.sqrt((Y * Y).mean(axis=-1)), 1.0, atol=1e-13)
@@ -307,6 +333,78 @@ def test_attention_output_derotation_is_relative():
         outs.append((O.rope(o, np.full(H, -t), dr), lse))
     assert np.allclose(outs[0][0], outs[1][0], atol=1e-9)
     assert np.allclose(outs[0][1], outs[1][1], atol=1e-9)
+
+
+def test_attention_self_key_closed_form_with_rope_and_window_offset():
+    # One visible key: the window row of the query's own token (w = 1), in a window buffer that
+    # starts at position win_pos0 = 5, with RoPE on every dim and the output de-rotated. The raw
+    # row x has entries +-1, so with eps = 0 its RMSNorm is x itself. The stored row is
+    # e = RoPE_t(x); the query (head 0: 5x, head 1: -x/2, normed to x and -x) becomes +-RoPE_t(x), so its logit is
+    # +-scale * |x|^2 = +-scale * d whatever t is, and since the value is the key itself the output
+    # is sigma(l - z) * e, which de-rotated by -t is sigma(l - z) * x. A query turned at another position, a window
+    # read that ignores win_pos0, or an output turned forward instead of back all break it.
+    r = np.random.default_rng(11)
+    d, scale = 8, 0.3
+    t, win_pos0 = 9, 5
+    x = r.choice([-1.0, 1.0], size=d)
+    raw = r.normal(size=(t - win_pos0 + 1, d))
+    raw[-1] = x
+    win = O.prepare_window(raw, win_pos0, eps=0.0, rope_dims=d)
+    q = np.stack([5 * x, -x / 2])[None]                       # [1, 2, d]: RMSNorm gives x and -x
+    z = np.array([0.4, -0.7])
+    o, lse = O.attention(q, np.zeros((0, d)), win, win_pos0, pos0=t, m=4, w=1, sink=z, scale=scale,
+                         eps=0.0, rope_dims=d, rope_on_output=True)
+    ell = np.array([scale * d, -scale * d])
+    sig = 1.0 / (1.0 + np.exp(z - ell))
+    assert np.allclose(o[0], sig[:, None] * x[None, :], atol=1e-12)
+    assert np.allclose(lse[0], np.logaddexp(z, ell), atol=1e-12)
+    # without de-rotation the output is the stored (rotated) row itself
+    o2, _ = O.attention(q, np.zeros((0, d)), win, win_pos0, pos0=t, m=4, w=1, sink=z, scale=scale,
+                        eps=0.0, rope_dims=d, rope_on_output=False)
+    assert np.allclose(o2[0], sig[:, None] * win[-1][None, :], atol=1e-12)
+    assert not np.allclose(win[-1], x)
+
+
+def test_attention_shift_invariance_through_oracle_caches():
+    # Build one CSA layer twice from the same raw streams, once at positions 0.. and once shifted
+    # by delta (a multiple of m): compressed entries and window rows come from the oracle's own
+    # compressor and window preparation, the shifted cache holds delta/m extra entries in front
+    # and the selected indices move with it. With the output de-rotated, every output and lse
+    # must be unchanged: only relative positions may matter. Rows are compared from t = w - 1 on
+    # (before that the unshifted window is cut at position 0); the shifted window buffer starts at
+    # position delta + w - 1 - (w - 1) = delta, so a window read that ignores win_pos0 fails.
+    r = np.random.default_rng(12)
+    m, c, T, H, dr, w, k = 4, 16, 40, 3, 8, 6, 5
+    delta = 4 * 1021
+    Ca, Cb, Za, Zb = (r.normal(size=(T, c)) for _ in range(4))
+    Bz = r.normal(size=(2 * m, c))
+    raw_win = r.normal(size=(T, c))
+    q = r.normal(size=(T, H, c))
+    sink = r.normal(size=H)
+    idx = np.full((T, k), -1)
+    for j in range(T):
+        V = O.visible(j, m, T // m)
+        sel = np.sort(r.permutation(V)[:k])
+        idx[j, :len(sel)] = sel
+    res = []
+    for shift in (0, delta):
+        ent = O.csa_compress(Ca, Cb, Za, Zb, Bz, m, pos0=shift, apply_norm=True, rope_dims=dr)
+        kv = np.concatenate([r.normal(size=(shift // m, c)), ent])
+        win = O.prepare_window(raw_win, shift, rope_dims=dr)
+        idx_s = np.where(idx >= 0, idx + shift // m, -1)
+        rows = range(w - 1, T)
+        res.append(O.attention(q, kv, win, shift, pos0=shift, m=m, w=w, idx=idx_s, sink=sink,
+                               rope_dims=dr, rope_on_output=True, rows=rows))
+    assert np.allclose(res[0][0], res[1][0], atol=1e-9)
+    assert np.allclose(res[0][1], res[1][1], atol=1e-9)
+    # and the pin is not vacuous: without de-rotation the two outputs differ
+    raw = [O.attention(q, np.concatenate([r.normal(size=(s // m, c)),
+                                          O.csa_compress(Ca, Cb, Za, Zb, Bz, m, pos0=s, apply_norm=True,
+                                                         rope_dims=dr)]),
+                       O.prepare_window(raw_win, s, rope_dims=dr), s, pos0=s, m=m, w=w,
+                       idx=np.where(idx >= 0, idx + s // m, -1), sink=sink, rope_dims=dr,
+                       rope_on_output=False, rows=[T - 1])[0] for s in (0, delta)]
+    assert not np.allclose(raw[0], raw[1], atol=1e-3)
 
 
 def test_decode_row_equals_prefill_row():
@@ -505,6 +603,27 @@ def test_indexer_mxfp4_reduces_to_plain_indexer():
                           O.indexer_scores(q, w, k2, pos0=80, m=4))
 
 
+def test_indexer_mxfp8_reduces_to_plain_indexer():
+    # small integers are exact E4M3 values; with every scale code 127 (2**0) the MX-FP8 scores are
+    # the plain indexer's on those integers, and a scale code of 130 on a block is that block x 8
+    ints = np.array([0, 1, 2, 3, 4, 5, 6, 7, 8, 10, 12, 16], dtype=np.float64)
+    q = rng.choice(np.concatenate([ints, -ints]), (4, 3, 128))
+    k = rng.choice(np.concatenate([ints, -ints]), (30, 128))
+    w = rng.uniform(0, 1, (4, 3))
+    qc, kc = O.e4m3_encode(q), O.e4m3_encode(k)
+    one_q, one_k = np.full((4, 3, 4), 127, np.uint8), np.full((30, 4), 127, np.uint8)
+    assert np.array_equal(O.indexer_scores_mxfp8(qc, one_q, w, kc, one_k, pos0=80, m=4),
+                          O.indexer_scores(q, w, k, pos0=80, m=4))
+    ks = one_k.copy(); ks[:, 2] = 130
+    k2 = k.copy(); k2[:, 64:96] *= 8
+    assert np.array_equal(O.indexer_scores_mxfp8(qc, one_q, w, kc, ks, pos0=80, m=4),
+                          O.indexer_scores(q, w, k2, pos0=80, m=4))
+    qs = one_q.copy(); qs[:, :, 0] = 125
+    q2 = q.copy(); q2[:, :, :32] /= 4
+    assert np.array_equal(O.indexer_scores_mxfp8(qc, qs, w, kc, one_k, pos0=80, m=4),
+                          O.indexer_scores(q2, w, k, pos0=80, m=4))
+
+
 def test_mxfp8_hand_blocks_and_range():
     x = np.zeros((2, 64), dtype=np.float32)
     x[0, :4] = [448.0, -1.0, 300.0, 0.0]     # amax 448 = 1.75 * 2**8 -> shared exponent 0 (code 127)
@@ -556,6 +675,10 @@ def test_kv_fp8_roundtrip_and_errors():
     g = np.concatenate([grid, np.zeros((5, r))], axis=1)
     c2, r2, s2 = O.quantize_kv_fp8(g, r)
     assert np.array_equal(O.dequantize_kv_fp8(c2, r2, s2), g)
+    # the RoPE dims are stored in bf16 (8 significant bits): 1 + 2**-10 -> 1, 1 + 3 * 2**-9 -> 1 + 2**-7
+    h = np.zeros((1, 32)); h[0, 0] = 1.0; h[0, 16:18] = [1 + 2.0 ** -10, 1 + 3 * 2.0 ** -9]
+    _, r3, _ = O.quantize_kv_fp8(h, 16)
+    assert r3[0, :2].tolist() == [1.0, 1 + 2.0 ** -7] and (r3[0, 2:] == 0).all()
 
 
 def test_page_constants_fixture():
