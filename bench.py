@@ -346,7 +346,7 @@ def projection_rows(prefill, reps: int = 3):
     fl = 2 * T * G * kin * dg + 2 * T * G * dg * D
     by = 2 * (T * L.H * L.d + G * kin * dg + 2 * T * G * dg + G * dg * D + T * D)
     out["grouped_out_proj"] = row(ms, fl, by)
-    out["kernel"] = "gemm_bf16 (128 x 128 tiles, v_mfma_f32_32x32x16_bf16)"
+    out["kernel"] = "gemm_bf16 (256 x 256 tiles, v_mfma_f32_32x32x16_bf16)"
     return out
 
 

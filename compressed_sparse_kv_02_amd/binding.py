@@ -109,6 +109,20 @@ def _ptr(t: Optional[torch.Tensor]):
     return t.data_ptr()
 
 
+def _need(cond: bool, msg: str) -> None:
+    """Raise before any library call when a caller buffer cannot hold what the call writes."""
+    if not cond:
+        raise CskvError(msg)
+
+
+def _check_append(name: str, out: torch.Tensor, batch: int, width: int, out_row0: int, n_new: int) -> None:
+    """out [batch, cap, width]: rows out_row0 .. out_row0 + n_new - 1 of every sequence must exist."""
+    _need(out.dim() == 3 and out.shape[0] == batch and out.shape[2] == width,
+          f"{name}: out must be [batch={batch}, cap, {width}], got {tuple(out.shape)}")
+    _need(0 <= out_row0 and out_row0 + n_new <= out.shape[1],
+          f"{name}: rows {out_row0} .. {out_row0 + n_new - 1} do not fit a cache of {out.shape[1]} rows")
+
+
 def _dtype(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return BF16
@@ -132,6 +146,8 @@ def csa_compress(Ca, Cb, Za, Zb, B, m: int, pos0: int = 0, prev_Cb=None, prev_Zb
     batch, T, c = Ca.shape
     if out is None:
         out = torch.empty(batch, T // m, c, dtype=Ca.dtype, device=Ca.device)
+    _need(out.dtype == Ca.dtype, "csa_compress: out must have the streams' dtype")
+    _check_append("csa_compress", out, batch, c, out_row0, T // m if m > 0 else 0)
     _ptr(out)
     ptr = out.data_ptr() + out_row0 * c * out.element_size()
     _check("csa_compress", lib().csa_compress(
@@ -151,6 +167,8 @@ def hca_compress(C, Z=None, B=None, m: int = 128, pos0: int = 0, apply_norm: boo
     batch, T, c = C.shape
     if out is None:
         out = torch.empty(batch, T // m, c, dtype=C.dtype, device=C.device)
+    _need(out.dtype == C.dtype, "hca_compress: out must have the stream's dtype")
+    _check_append("hca_compress", out, batch, c, out_row0, T // m if m > 0 else 0)
     _ptr(out)
     ptr = out.data_ptr() + out_row0 * c * out.element_size()
     _check("hca_compress", lib().hca_compress(
@@ -170,6 +188,7 @@ def indexer_topk(qI, wI, KI, pos0: int, m: int, k: int, out=None, workspace=None
     dt = _dtype(qI)
     if out is None:
         out = torch.empty(batch, Tq, k, dtype=torch.int32, device=qI.device)
+    _check_idx("indexer_topk", out, batch, Tq, k)
     need = indexer_workspace_bytes(batch, Tq, N, HI, k, dt)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=qI.device)
@@ -177,6 +196,17 @@ def indexer_topk(qI, wI, KI, pos0: int, m: int, k: int, out=None, workspace=None
         _ptr(qI), _ptr(wI), _ptr(KI), batch, Tq, N, HI, dI, pos0, m, k, _ptr(out), _ptr(workspace),
         workspace.numel(), dt, _stream(qI)))
     return out
+
+
+def _check_scores(name: str, scores: torch.Tensor, batch: int, Tq: int, N: int) -> None:
+    _need(scores.dtype == torch.float32 and scores.dim() == 3 and tuple(scores.shape[:2]) == (batch, Tq)
+          and scores.shape[2] >= N, f"{name}: scores must be fp32 [{batch}, {Tq}, >= {N}], got "
+          f"{scores.dtype} {tuple(scores.shape)}")
+
+
+def _check_idx(name: str, out: torch.Tensor, batch: int, Tq: int, k: int) -> None:
+    _need(out.dtype == torch.int32 and tuple(out.shape) == (batch, Tq, k),
+          f"{name}: out must be int32 [{batch}, {Tq}, {k}], got {out.dtype} {tuple(out.shape)}")
 
 
 def score_ld(N: int) -> int:
@@ -190,6 +220,7 @@ def indexer_scores(qI, wI, KI, pos0: int, m: int, scores=None) -> torch.Tensor:
     N = KI.shape[1]
     if scores is None:
         scores = torch.empty(batch, Tq, score_ld(N), dtype=torch.float32, device=qI.device)
+    _check_scores("indexer_scores", scores, batch, Tq, N)
     _check("indexer_scores", lib().indexer_scores(
         _ptr(qI), _ptr(wI), _ptr(KI), batch, Tq, N, HI, dI, pos0, m, _ptr(scores), scores.shape[-1],
         _dtype(qI), _stream(qI)))
@@ -209,6 +240,8 @@ def topk_select(scores, N: int, pos0: int, m: int, k: int, out=None, workspace=N
     batch, Tq, ld = scores.shape
     if out is None:
         out = torch.empty(batch, Tq, k, dtype=torch.int32, device=scores.device)
+    _check_scores("topk_select", scores, batch, Tq, N)
+    _check_idx("topk_select", out, batch, Tq, k)
     ws, nbytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
     _check("topk_select", lib().topk_select(_ptr(scores), ld, batch, Tq, N, pos0, m, k, _ptr(out), ws, nbytes,
                                             _stream(scores)))
@@ -269,6 +302,7 @@ def _scores_lowp(fmt, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, scores)
     if scores is None:
         scores = torch.empty(batch, Tq, score_ld(N), dtype=torch.float32, device=q_codes.device)
     name = f"indexer_scores_{suffix}"
+    _check_scores(name, scores, batch, Tq, N)
     _check(name, getattr(lib(), name)(
         _ptr(q_codes), _ptr(q_scales), _ptr(wI), _ptr(k_codes), _ptr(k_scales), batch, Tq, N, HI, db * per_byte,
         pos0, m, _ptr(scores), scores.shape[-1], _stream(q_codes)))
@@ -281,6 +315,7 @@ def _topk_lowp(fmt, q_codes, q_scales, wI, k_codes, k_scales, pos0, m, k, out, w
     N = k_codes.shape[1]
     if out is None:
         out = torch.empty(batch, Tq, k, dtype=torch.int32, device=q_codes.device)
+    _check_idx(f"indexer_topk_{suffix}", out, batch, Tq, k)
     need = indexer_workspace_bytes(batch, Tq, N, HI, k, fmt)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_codes.device)
@@ -326,8 +361,15 @@ def quantize_kv_fp8(x, rope_dims: int, out=None, scales=None, out_row0: int = 0)
     batch, n, d = x.shape
     rb = kv_fp8_row_bytes(d, rope_dims)
     if out is None:
+        _need(scales is None, "quantize_kv_fp8: scales given without out")
         out = torch.empty(batch, n, rb, dtype=torch.uint8, device=x.device)
         scales = torch.empty(batch, n, dtype=torch.float32, device=x.device)
+    _need(scales is not None, "quantize_kv_fp8: out given without scales")
+    _need(out.dtype == torch.uint8 and scales.dtype == torch.float32, "quantize_kv_fp8: out uint8, scales fp32")
+    _check_append("quantize_kv_fp8", out, batch, rb, out_row0, n)
+    _need(scales.dim() == 2 and tuple(scales.shape) == (batch, out.shape[1]),
+          f"quantize_kv_fp8: scales must be [{batch}, {out.shape[1]}], got {tuple(scales.shape)}")
+    _ptr(out), _ptr(scales)
     cap = out.shape[1]
     _check("cskv_quantize_kv_fp8", lib().cskv_quantize_kv_fp8(
         _ptr(x), batch, n, d, rope_dims, _dtype(x), out.data_ptr() + out_row0 * rb,
@@ -344,7 +386,14 @@ def _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_n
         out = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty(batch, Tq, H, dtype=torch.float32, device=q.device)
+    _need(out.shape == q.shape and out.dtype == q.dtype, f"attention: out must match q {tuple(q.shape)} {q.dtype}")
+    _need(lse is None or (lse.dtype == torch.float32 and tuple(lse.shape) == (batch, Tq, H)),
+          f"attention: lse must be fp32 [{batch}, {Tq}, {H}]")
+    _need(kv.dim() == 3 and kv.shape[0] == batch and win.dim() == 3 and win.shape[0] == batch
+          and win.shape[2] == d, "attention: kv [batch, N, .] and win [batch, W, d] expected")
     if mode == CSA:
+        _need(idx is not None and idx.dim() == 3 and tuple(idx.shape[:2]) == (batch, Tq)
+              and idx.dtype == torch.int32, f"attention (CSA): idx must be int32 [{batch}, {Tq}, k]")
         k = idx.shape[2]
     args = (mode, _ptr(q), _ptr(kv), _ptr(idx), _ptr(win), win_pos0, W, _ptr(sink), batch, Tq, N, pos0,
             m, k, w, H, d, int(apply_q_norm), _ptr(q_norm_w), eps, rope_dims, rope_base, scale,

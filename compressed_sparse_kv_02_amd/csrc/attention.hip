@@ -906,21 +906,31 @@ extern "C" int compressed_attn_prefill_kv8(int mode, const void* q, const uint8_
 // Splits per query: about one workgroup per compute unit (256) over the whole call, at
 // least 4 key tiles each. Every split costs a query prologue and an fp32 partial of
 // H x d written and merged, so more splits than CUs only add traffic.
+// Automatic split count: about one workgroup per CU over the call (256 / queries), at least 4 key
+// tiles per split, at most 256. Without the key count this is bounded by the first term alone.
+static int64_t auto_splits_bound(int batch, int64_t Tq) {
+  int64_t s = (256 + batch * Tq - 1) / (batch * Tq);
+  return s > 256 ? 256 : (s < 1 ? 1 : s);
+}
+
 static int decode_splits(int batch, int64_t Tq, int64_t max_k, int n_splits) {
   if (n_splits > 0) return n_splits;
   const int64_t nblk = (max_k + 31) / 32;
-  int64_t s = (256 + batch * Tq - 1) / (batch * Tq);
+  int64_t s = auto_splits_bound(batch, Tq);
   const int64_t cap = (nblk + 3) / 4;
   if (s > cap) s = cap;
-  if (s > 256) s = 256;
   if (s < 1) s = 1;
   return (int)s;
 }
 
+static size_t decode_partial_bytes(int batch, int64_t Tq, int S, int H, int d) {
+  return S > 1 ? (size_t)batch * Tq * S * H * ((size_t)d + 2) * 4 : 0;
+}
+
 extern "C" size_t cskv_decode_workspace_size(int batch, int64_t Tq, int H, int d, int n_splits) {
-  if (batch <= 0 || Tq <= 0) return 0;
-  const int s = n_splits > 0 ? n_splits : 256;
-  return (size_t)batch * Tq * s * H * ((size_t)d + 2) * 4 + 256;
+  if (batch <= 0 || Tq <= 0 || H <= 0 || d <= 0 || n_splits < 0 || n_splits > 256) return 0;
+  const int S = n_splits > 0 ? n_splits : (int)auto_splits_bound(batch, Tq);
+  return decode_partial_bytes(batch, Tq, S, H, d);
 }
 
 static int attn_decode_impl(int mode, const void* q, const void* kv, const float* kv_scale, const int32_t* idx,
@@ -946,7 +956,7 @@ static int attn_decode_impl(int mode, const void* q, const void* kv, const float
     if (!dispatch_attn(a, batch, s)) return CSKV_ERR_UNSUPPORTED;
     return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
   }
-  const size_t need = (size_t)batch * Tq * S * H * ((size_t)d + 2) * 4;
+  const size_t need = decode_partial_bytes(batch, Tq, S, H, d);
   if (!workspace || ws_bytes < need) return CSKV_ERR_WORKSPACE;
   if (!aligned16(workspace)) return CSKV_ERR_MISALIGNED;
   a.n_splits = S;

@@ -355,9 +355,15 @@ int compressed_attn_prefill(int mode, const void* q, const void* kv, const int32
  * writes a partial (max, sum, weighted sum) to the workspace and a merge
  * kernel combines the splits in a fixed order. Arguments as in
  * compressed_attn_prefill, plus:
- *   n_splits  : 0 = choose from the shape; else 1 .. 256 splits per query
- *   workspace : cskv_decode_workspace_size(...) bytes of device memory
+ *   n_splits  : 0 = choose from the shape (S = min(ceil(256 / (batch * Tq)),
+ *               ceil(key tiles / 4), 256), a key tile being 32 keys); else
+ *               1 .. 256 splits per query
+ *   workspace : cskv_decode_workspace_size(...) bytes of device memory: the
+ *               fp32 partials, batch * Tq * S * H * (d + 2) * 4 bytes when
+ *               S > 1 and nothing (0 bytes, NULL allowed) when S = 1. With
+ *               n_splits = 0 the size covers the largest automatic S.
  * Any n_splits gives the same result up to fp32 rounding of the merge.
+ * cskv_decode_workspace_size returns 0 for arguments the call would reject.
  */
 size_t cskv_decode_workspace_size(int batch, int64_t Tq, int H, int d, int n_splits);
 int compressed_attn_decode(int mode, const void* q, const void* kv, const int32_t* idx,

@@ -12,6 +12,10 @@ import numpy as np
 from oracle import cskv_oracle as O
 
 
+class ParityCount(UserWarning):
+    """How many rows an end-to-end parity check compared, and how (shown in pytest's summary)."""
+
+
 def np64(t) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
@@ -100,6 +104,28 @@ def mxfp8_score_bound(q_codes, q_scales, w_row, k_codes, k_scales, V: int) -> np
     return e4m3_group_bound(dq, dk, np.asarray(w_row, dtype=np.float64), np.ones(V))
 
 
+def fp8_refined_bound(q_codes, q_scales, w_row, k_codes, k_scales, V: int, k: int, scores,
+                      cap: int = 8192) -> np.ndarray:
+    """fp8_score_bound, taken product by product (e4m3_product_bound) for the entries near the k-th
+    score whose top-k membership depends on it."""
+    b = fp8_score_bound(q_codes, q_scales, w_row, k_codes, k_scales, V)
+    dq = O.e4m3_decode(q_codes)
+    wq = np.asarray(w_row, dtype=np.float64) * np.asarray(q_scales, dtype=np.float64)
+    kc, ks = np.asarray(k_codes), np.asarray(k_scales, dtype=np.float64)
+    return refine_bound_near_kth(scores, b, V, k, lambda ix: e4m3_product_bound(dq, O.e4m3_decode(kc[ix]), wq, ks[ix]),
+                                 cap)
+
+
+def mxfp8_refined_bound(q_codes, q_scales, w_row, k_codes, k_scales, V: int, k: int, scores,
+                        cap: int = 8192) -> np.ndarray:
+    """mxfp8_score_bound, taken product by product for the entries near the k-th score."""
+    b = mxfp8_score_bound(q_codes, q_scales, w_row, k_codes, k_scales, V)
+    dq = O.dequantize_mxfp8(q_codes, q_scales)
+    kc, ks = np.asarray(k_codes), np.asarray(k_scales)
+    return refine_bound_near_kth(scores, b, V, k, lambda ix: e4m3_product_bound(
+        dq, O.dequantize_mxfp8(kc[ix], ks[ix]), w_row, np.ones(ix.size)), cap)
+
+
 def e4m3_group_bound(dq, dk, wq, ks) -> np.ndarray:
     """The FP8 error model of fp8_score_bound on decoded rows dq [HI, dI], dk [V, dI], head factors
     wq [HI] (weight times row scale) and key factors ks [V]."""
@@ -112,6 +138,72 @@ def e4m3_group_bound(dq, dk, wq, ks) -> np.ndarray:
     dot = np.abs(dk @ dq.T)
     per = 7 * 2.0 ** -13 * gm + 2.0 ** -20 * ab + 2.0 ** -17 * dot
     return np.asarray(ks, dtype=np.float64) * (per @ np.abs(np.asarray(wq, dtype=np.float64)))
+
+
+def e4m3_product_bound(dq, dk, wq, ks, chunk: int = 512) -> np.ndarray:
+    """The group model of fp8_score_bound taken product by product, for the keys in dk.
+
+    Each E4M3 x E4M3 product is exact in float64. In a group of 8 products the
+    grid is 2**(E - 13), E = floor(log2) of the group's largest |product|; a
+    product on that grid loses nothing, and one off it loses less than the
+    grid step: its remainder r below the grid when bits are cut toward zero,
+    g - r when cut toward minus infinity, at most g / 2 when rounded, so
+    max(r, g - r) covers all three. The fp32 sums of the group sums and of the
+    heads add the same 2**-20 * sum |products| + 2**-17 * |dot| as before.
+    dq [HI, dI], dk [n, dI] decoded rows, wq [HI] head factors, ks [n] key
+    factors; returns [n].
+    """
+    dq = np.asarray(dq, dtype=np.float64)
+    dk = np.asarray(dk, dtype=np.float64)
+    HI, dI = dq.shape
+    aw = np.abs(np.asarray(wq, dtype=np.float64))
+    out = np.empty(dk.shape[0])
+    for a in range(0, dk.shape[0], chunk):
+        kk = dk[a:a + chunk]
+        n = kk.shape[0]
+        P = np.abs(kk[:, None, :] * dq[None, :, :]).reshape(n, HI, dI // 8, 8)
+        gm = P.max(axis=-1, keepdims=True)
+        _, ex = np.frexp(gm)                                   # gm = f * 2**ex, f in [0.5, 1)
+        g = np.ldexp(1.0, ex - 14)                             # 2**(E - 13), E = ex - 1
+        r = np.fmod(P, g)
+        per = np.where(r > 0, np.maximum(r, g - r), 0.0).sum(axis=(-1, -2))   # [n, HI]
+        ab = np.abs(kk) @ np.abs(dq).T
+        dot = np.abs(kk @ dq.T)
+        out[a:a + n] = (per + 2.0 ** -20 * ab + 2.0 ** -17 * dot) @ aw
+    return np.asarray(ks, dtype=np.float64) * out
+
+
+def refine_bound_near_kth(scores, bound, V: int, k: int, product_bound, cap: int = 16384) -> np.ndarray:
+    """Tighten a per-entry bound where the top-k decision depends on it.
+
+    Entries whose interval [s - b, s + b] meets the span of the still-undecided
+    entries (see check_topk_row_bounded) get product_bound(indices) instead,
+    when smaller; at most `cap` of them, nearest the k-th score. Both bounds
+    hold for every entry, so the result does too.
+    """
+    b = np.array(bound[:V], dtype=np.float64)
+    if V <= k:
+        return b
+    s = np.asarray(scores[:V], dtype=np.float64)
+    und = undecided_mask(s, b, k)
+    if not und.any():
+        return b
+    lo, hi = (s - b)[und].min(), (s + b)[und].max()
+    near = np.nonzero((s + b >= lo) & (s - b <= hi))[0]
+    if near.size > cap:
+        Ik = np.sort(s)[::-1][k - 1]
+        near = near[np.argsort(np.abs(s[near] - Ik))[:cap]]
+    b[near] = np.minimum(b[near], product_bound(near))
+    return b
+
+
+def undecided_mask(s, b, k: int) -> np.ndarray:
+    """Entries that the bounds leave undecided: some k others may beat them, yet not k surely do."""
+    V = s.shape[0]
+    lo, hi = s - b, s + b
+    n_reach = V - np.searchsorted(np.sort(hi), lo, side="left") - 1
+    n_above = V - np.searchsorted(np.sort(lo), hi, side="right")
+    return ~((n_reach < k) | (n_above >= k))
 
 
 def check_topk_row_bounded(gpu_row: np.ndarray, scores: np.ndarray, bound: np.ndarray, V: int, k: int,
@@ -158,8 +250,15 @@ def oracle_layer(L, t, b: int, rows: Iterable[int]):
     h = lambda name: np64(t[name][b])
     opt = lambda name: np64(t[name][b]) if name in t else None
     rows = list(rows)
-    kv = h("cache.kv")
-    ik = h("cache.ik") if L.kind == "csa" else None
+    def cache(name, n_valid):
+        # rows past n_valid are written by the call itself (and recomputed below); never read them
+        full = t[name][b]
+        a = np.zeros(tuple(full.shape), dtype=np.float64)
+        a[:n_valid] = np64(full[:n_valid])
+        return a
+
+    kv = cache("cache.kv", L.n_cached)
+    ik = cache("cache.ik", L.n_cached) if L.kind == "csa" else None
     extras = {}
     if L.n_new:
         if L.kind == "csa":
@@ -174,7 +273,7 @@ def oracle_layer(L, t, b: int, rows: Iterable[int]):
             new = O.hca_compress(h("kv.C"), h("kv.Z"), np64(t["kv.B"]), L.m, L.pos0, apply_norm=True,
                                  rope_dims=L.rope_dims)
             kv[L.n_cached:] = rnd(new)
-    win = h("win")
+    win = cache("win", L.win_cached)
     win[L.win_cached:] = rnd(O.prepare_window(h("win_raw"), L.pos0, rope_dims=L.rope_dims))
     sink = np64(t["sink"])
     idx = np.full((L.T, L.k), -1, dtype=np.int64) if L.kind == "csa" else None

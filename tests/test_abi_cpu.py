@@ -294,3 +294,48 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 8, 64)
     with pytest.raises(binding.CskvError):
         binding.hca_compress(x, m=1)
+
+
+def test_binding_rejects_appends_past_the_cache():
+    # the extent checks run before any device access, so CPU tensors reach them
+    import torch
+    from compressed_sparse_kv_02_amd import binding
+    x = torch.zeros(2, 16, 64)
+    B = torch.zeros(8, 64)
+    cache = torch.zeros(2, 10, 64)
+    for row0 in (-1, 7, 10):                       # 16 / 4 = 4 new rows: rows 7..10 overflow a 10-row cache
+        with pytest.raises(binding.CskvError, match="do not fit"):
+            binding.csa_compress(x, x, x, x, B, 4, out=cache, out_row0=row0)
+    with pytest.raises(binding.CskvError, match="do not fit"):
+        binding.hca_compress(x, None, None, 4, out=cache, out_row0=7)
+    with pytest.raises(binding.CskvError, match="out must be"):
+        binding.hca_compress(x, None, None, 4, out=torch.zeros(1, 10, 64))   # wrong batch
+    with pytest.raises(binding.CskvError, match="dtype"):
+        binding.hca_compress(x, None, None, 4, out=torch.zeros(2, 10, 64, dtype=torch.bfloat16))
+    with pytest.raises(binding.CskvError, match="without scales"):
+        binding.quantize_kv_fp8(torch.zeros(2, 4, 64), 16, out=torch.zeros(2, 10, 80, dtype=torch.uint8))
+    with pytest.raises(binding.CskvError, match="do not fit"):
+        binding.quantize_kv_fp8(torch.zeros(2, 4, 64), 16, out=torch.zeros(2, 10, 80, dtype=torch.uint8),
+                                scales=torch.zeros(2, 10), out_row0=8)
+    # in range: the device check is what fails on the CPU
+    with pytest.raises(binding.CskvError, match="not on the GPU"):
+        binding.csa_compress(x, x, x, x, B, 4, out=cache, out_row0=6)
+
+
+def test_decode_workspace_size_follows_the_split_policy(L):
+    f = L.cskv_decode_workspace_size
+    per = lambda b, tq, s, H=64, d=512: b * tq * s * H * (d + 2) * 4
+    # automatic splits: at most ceil(256 / (batch * Tq)), nothing when that is one split
+    assert f(8, 1, 64, 512, 0) == per(8, 1, 32)
+    assert f(1, 1, 64, 512, 0) == per(1, 1, 256)
+    assert f(3, 1, 64, 512, 0) == per(3, 1, 86)
+    assert f(2, 4096, 64, 512, 0) == 0 and f(256, 1, 64, 512, 0) == 0
+    assert f(8, 1, 64, 512, 1) == 0
+    assert f(8, 1, 64, 512, 7) == per(8, 1, 7)
+    # arguments the call rejects size to 0
+    assert f(8, 1, 64, 512, 257) == 0 and f(8, 1, 64, 512, -1) == 0 and f(0, 1, 64, 512, 0) == 0
+    # a decode call with too small a workspace fails validation before any launch
+    a = dict(mode=1, q=P, kv=P, idx=None, win=P, wp0=0, W=128, sink=None, batch=8, Tq=1, N=8192,
+             pos0=1 << 20, m=128, k=0, w=128, H=64, d=512, qn=1, qnw=None, eps=1e-6, rd=64, rb=1e4,
+             sc=0.0, ro=1, ns=0, ws=P, wsb=f(8, 1, 64, 512, 0) - 1, out=P, lse=None, dt=0, st=None)
+    assert L.compressed_attn_decode(*a.values()) == WS

@@ -3,6 +3,7 @@ same seeded inputs. Stage tests feed both sides generator-made inputs for
 every stage; end-to-end tests run the whole layer on both sides."""
 import dataclasses
 import math
+import warnings
 
 import numpy as np
 import pytest
@@ -12,9 +13,9 @@ from oracle import cskv_oracle as O
 from compressed_sparse_kv_02_amd import binding as B
 from compressed_sparse_kv_02_amd import layer as LY
 from compressed_sparse_kv_02_amd.synth import normal_device, uniform_device
-from tests.parity_utils import (assert_storage_close, check_topk_row, check_topk_row_bounded, fp8_score_bound,
-                                mxfp4_score_bound, mxfp8_score_bound,
-                                key_rounding_band, np64, oracle_layer)
+from tests.parity_utils import (assert_storage_close, check_topk_row, check_topk_row_bounded, fp8_refined_bound,
+                                fp8_score_bound, mxfp4_score_bound, mxfp8_refined_bound, mxfp8_score_bound,
+                                key_rounding_band, np64, oracle_layer, ParityCount)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -224,7 +225,7 @@ def test_indexer_fp8(bt, Tq, N, HI, dI, pos0, m, k):
     torch.cuda.synchronize()
     sc, idx = sc.cpu().numpy(), idx.cpu().numpy()
     rows = range(Tq) if Tq <= 80 else sorted(set(np.linspace(0, Tq - 1, 40).astype(int)) | {0, Tq - 1})
-    n_band, worst = 0, 0.0
+    n_band, worst, worst_ref = 0, 0.0, 0.0
     for b in range(bt):
         okc, oks = O.quantize_rows_fp8(np64(KI[b]).astype(np.float32))
         assert np.array_equal(okc, kc[b].cpu().numpy())
@@ -234,12 +235,17 @@ def test_indexer_fp8(bt, Tq, N, HI, dI, pos0, m, k):
             V = O.visible(pos0 + r, m, N)
             if V == 0:
                 continue
-            bound = fp8_score_bound(oqc, oqs, np64(wI[b, r]), okc, oks, V)
+            cheap = fp8_score_bound(oqc, oqs, np64(wI[b, r]), okc, oks, V)
+            bound = fp8_refined_bound(oqc, oqs, np64(wI[b, r]), okc, oks, V, k, I)
             err = np.abs(sc[b, r, :V] - I[:V])
             assert (err <= bound).all(), (b, r, float((err / bound).max()))
             worst = max(worst, float((err / bound).max()))
+            ref = bound < cheap
+            if ref.any():
+                worst_ref = max(worst_ref, float((err[ref] / bound[ref]).max()))
             n_band += check_topk_row_bounded(idx[b, r], I, bound, V, k, what=f"b{b} r{r}")
-    say(f"  undecided entries: {n_band}; largest error / bound: {worst:.3g}")
+    say(f"  undecided entries: {n_band}; largest error / bound: {worst:.3g} "
+        f"(over the entries bounded product by product: {worst_ref:.3g})")
 
 
 def test_indexer_fp8_decode_1m():
@@ -255,7 +261,7 @@ def test_indexer_fp8_decode_1m():
         okc, oks = O.quantize_rows_fp8(np64(KI[b]).astype(np.float32))
         oqc, oqs = O.quantize_rows_fp8(np64(qI[b, 0]).astype(np.float32))
         I = O.indexer_scores_fp8(oqc[None], oqs[None], np64(wI[b]), okc, oks, pos0, 4)[0]
-        bound = fp8_score_bound(oqc, oqs, np64(wI[b, 0]), okc, oks, N)
+        bound = fp8_refined_bound(oqc, oqs, np64(wI[b, 0]), okc, oks, N, 1024, I)
         und = check_topk_row_bounded(idx[b, 0], I, bound, N, 1024, what=f"b{b}")
         overlap.append(len(set(idx[b, 0].tolist()) & set(ref[b, 0].tolist())) / 1024)
         say(f"  b{b}: undecided entries {und}")
@@ -379,7 +385,8 @@ def test_indexer_mx(fmt, bt, Tq, N, HI, pos0, m, k):
             V = O.visible(pos0 + r, m, N)
             if V == 0:
                 continue
-            bound = obound(oqc, oqs, np64(wI[b, r]), okc, oks, V)
+            bound = (obound(oqc, oqs, np64(wI[b, r]), okc, oks, V) if fmt == "mxfp4" else
+                     mxfp8_refined_bound(oqc, oqs, np64(wI[b, r]), okc, oks, V, k, I))
             err = np.abs(sc[b, r, :V] - I[:V])
             assert (err <= bound).all(), (b, r, float((err / bound).max()))
             worst = max(worst, float((err / bound).max()))
@@ -434,8 +441,9 @@ def test_indexer_mx_decode_1m(fmt):
         okc, oks = oqz(np64(KI[b]).astype(np.float32))
         oqc, oqs = oqz(np64(qI[b, 0]).astype(np.float32))
         I = oscore(oqc[None], oqs[None], np64(wI[b]), okc, oks, pos0, 4)[0]
-        n_band += check_topk_row_bounded(idx[b, 0], I, obound(oqc, oqs, np64(wI[b, 0]), okc, oks, N), N, 1024,
-                                         what=f"b{b}")
+        bound = (obound(oqc, oqs, np64(wI[b, 0]), okc, oks, N) if fmt == "mxfp4" else
+                 mxfp8_refined_bound(oqc, oqs, np64(wI[b, 0]), okc, oks, N, 1024, I))
+        n_band += check_topk_row_bounded(idx[b, 0], I, bound, N, 1024, what=f"b{b}")
     say("  undecided entries:", n_band)
 
 
@@ -615,14 +623,36 @@ def test_decode_splits_and_prefill_agree(mode):
 
 # ----------------------------------------------------------------------------- whole layers
 
+def _attend_row(L, t, b, r, sel):
+    """The GPU attention of query row r of sequence b over the selection `sel` (an oracle top-k row),
+    on the caches and window rows the layer call left on the GPU."""
+    kv = t.get("post.cache.kv", t["cache.kv"])[b:b + 1]
+    win = t.get("post.win", t["win"])[b:b + 1]
+    q = t["q"][b:b + 1, r:r + 1].contiguous()
+    idx = torch.from_numpy(np.asarray(sel, dtype=np.int32)).to(DEV).reshape(1, 1, -1)
+    kw = dict(k=L.k, rope_dims=L.rope_dims, rope_on_output=True, return_lse=True)
+    if L.decode:
+        o, l = B.compressed_attn_decode(B.CSA, q, kv, idx, win, L.win_pos0, t["sink"], L.pos0 + r, L.m, L.w,
+                                        n_splits=L.n_splits, **kw)
+    else:
+        o, l = B.compressed_attn_prefill(B.CSA, q, kv, idx, win, L.win_pos0, t["sink"], L.pos0 + r, L.m, L.w, **kw)
+    torch.cuda.synchronize()
+    return np64(o[0, 0]), np64(l[0, 0])
+
+
 def _check_layer(L, t, rows_per_seq, atol, max_band_rows=0.25):
+    """Every sampled row is compared. Where the GPU's top-k differs from the oracle's inside the tie
+    band (both are valid selections), the GPU attention is run again for that row on the oracle's
+    selection and compared with the oracle's output, so no row goes unchecked and no GPU output
+    feeds the oracle."""
     out, lse = t["out"], t["lse"]
     gidx = t["idx"].cpu().numpy() if L.kind == "csa" else None
-    compared = skipped = 0
+    compared = alt = 0
     for b in range(L.batch):
         rows = rows_per_seq(L)
         o, l, idx, ex = oracle_layer(L, t, b, rows)
         for n, r in enumerate(rows):
+            go, gl = np64(out[b, r]), np64(lse[b, r])
             if L.kind == "csa":
                 I = ex["scores"][r]
                 V = O.visible(L.pos0 + r, L.m, L.N)
@@ -630,23 +660,28 @@ def _check_layer(L, t, rows_per_seq, atol, max_band_rows=0.25):
                 band += key_rounding_band(np64(t["qI"][b, r]), np64(t["wI"][b, r]), ex.get("ik_new_exact"), L.dtype)
                 check_topk_row(gidx[b, r], I, V, L.k, band=band, what=f"b{b} r{r}")
                 if not np.array_equal(gidx[b, r], idx[r]):
-                    skipped += 1
-                    continue
-            err = np.abs(np64(out[b, r]) - o[n]).max()
+                    go, gl = _attend_row(L, t, b, r, idx[r])
+                    alt += 1
+            err = np.abs(go - o[n]).max()
             assert err <= atol, f"{L.name} b{b} row {r}: max err {err:.3g}"
-            assert np.abs(np64(lse[b, r]) - l[n]).max() <= 5 * atol
+            assert np.abs(gl - l[n]).max() <= 5 * atol
             compared += 1
-    say(f"  {L.name}: compared {compared} rows, {skipped} rows with a near-tie selection difference")
-    assert skipped <= max_band_rows * (compared + skipped)
+    msg = (f"{L.name}: {compared} rows compared, {alt} of them (GPU top-k != oracle's inside the tie band) "
+           f"on the oracle's selection")
+    say("  " + msg)
+    warnings.warn(ParityCount(msg))
+    assert alt <= max_band_rows * compared
 
 
 def _run(L):
-    """Run the layer; return its inputs with the caches and window as they were before the call."""
+    """Run the layer; return its inputs with the caches and window as they were before the call
+    (and, under "post.", as the call left them)."""
     t = LY.make_inputs(L)
     pre = {k: t[k].clone() for k in ("cache.kv", "cache.ik", "win") if k in t}
     LY.run_layer(L, t)
     torch.cuda.synchronize()
     res = dict(t)
+    res.update({f"post.{k}": t[k] for k in pre})
     res.update(pre)
     return res
 
