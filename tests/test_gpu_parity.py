@@ -244,8 +244,10 @@ def test_indexer_fp8(bt, Tq, N, HI, dI, pos0, m, k):
             if ref.any():
                 worst_ref = max(worst_ref, float((err[ref] / bound[ref]).max()))
             n_band += check_topk_row_bounded(idx[b, r], I, bound, V, k, what=f"b{b} r{r}")
-    say(f"  undecided entries: {n_band}; largest error / bound: {worst:.3g} "
-        f"(over the entries bounded product by product: {worst_ref:.3g})")
+    msg = (f"fp8 {bt}x{Tq}x{N} k={k}: undecided entries {n_band}; largest error / bound {worst:.3g} "
+           f"(entries bounded product by product: {worst_ref:.3g})")
+    say("  " + msg)
+    warnings.warn(ParityCount(msg))
 
 
 def test_indexer_fp8_decode_1m():
@@ -256,16 +258,18 @@ def test_indexer_fp8_decode_1m():
     ref = B.indexer_topk(qI, wI, KI, pos0, 4, 1024)   # the bf16 selection, for the overlap figure only
     torch.cuda.synchronize()
     idx, ref = idx.cpu().numpy(), ref.cpu().numpy()
-    overlap = []
+    overlap, und = [], []
     for b in range(8):
         okc, oks = O.quantize_rows_fp8(np64(KI[b]).astype(np.float32))
         oqc, oqs = O.quantize_rows_fp8(np64(qI[b, 0]).astype(np.float32))
         I = O.indexer_scores_fp8(oqc[None], oqs[None], np64(wI[b]), okc, oks, pos0, 4)[0]
         bound = fp8_refined_bound(oqc, oqs, np64(wI[b, 0]), okc, oks, N, 1024, I)
-        und = check_topk_row_bounded(idx[b, 0], I, bound, N, 1024, what=f"b{b}")
+        und.append(check_topk_row_bounded(idx[b, 0], I, bound, N, 1024, what=f"b{b}"))
         overlap.append(len(set(idx[b, 0].tolist()) & set(ref[b, 0].tolist())) / 1024)
-        say(f"  b{b}: undecided entries {und}")
-    say("  fp8 vs bf16 selection overlap per row:", [round(o, 3) for o in overlap])
+    msg = (f"fp8 decode 1M: undecided entries per row {und}; fp8 vs bf16 selection overlap "
+           f"{[round(o, 3) for o in overlap]}")
+    say("  " + msg)
+    warnings.warn(ParityCount(msg))
 
 
 # ----------------------------------------------------------------------------- FP4 (E2M1) indexer
@@ -391,7 +395,9 @@ def test_indexer_mx(fmt, bt, Tq, N, HI, pos0, m, k):
             assert (err <= bound).all(), (b, r, float((err / bound).max()))
             worst = max(worst, float((err / bound).max()))
             n_band += check_topk_row_bounded(idx[b, r], I, bound, V, k, what=f"b{b} r{r}")
-    say(f"  undecided entries: {n_band}; largest error / bound: {worst:.3g}")
+    msg = f"{fmt} {bt}x{Tq}x{N} k={k}: undecided entries {n_band}; largest error / bound {worst:.3g}"
+    say("  " + msg)
+    warnings.warn(ParityCount(msg))
 
 
 
@@ -444,7 +450,9 @@ def test_indexer_mx_decode_1m(fmt):
         bound = (obound(oqc, oqs, np64(wI[b, 0]), okc, oks, N) if fmt == "mxfp4" else
                  mxfp8_refined_bound(oqc, oqs, np64(wI[b, 0]), okc, oks, N, 1024, I))
         n_band += check_topk_row_bounded(idx[b, 0], I, bound, N, 1024, what=f"b{b}")
-    say("  undecided entries:", n_band)
+    msg = f"{fmt} decode 1M: undecided entries over 8 rows {n_band}"
+    say("  " + msg)
+    warnings.warn(ParityCount(msg))
 
 
 # ----------------------------------------------------------------------------- attention
