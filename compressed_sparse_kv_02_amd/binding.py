@@ -27,7 +27,7 @@ EXPORTS = ("cskv_version", "cskv_status_string", "csa_compress", "hca_compress",
            "cskv_quantize_mxfp8", "indexer_scores_mxfp8", "indexer_topk_mxfp8",
            "cskv_quantize_kv_fp8", "compressed_attn_prefill_kv8", "compressed_attn_decode_kv8",
            "compressed_attn_prefill",
-           "cskv_decode_workspace_size", "compressed_attn_decode",
+           "cskv_decode_workspace_size", "compressed_attn_decode", "compressed_attn_decode_noalloc",
            "cskv_lowrank_proj", "cskv_grouped_out_proj")
 
 _lib = None
@@ -64,6 +64,8 @@ _SIGS = {
     "compressed_attn_prefill": (_I, [_I, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
                                      _I, _P, _F, _I, _F, _F, _I, _P, _P, _I, _P]),
     "cskv_decode_workspace_size": (_Z, [_I, _L, _I, _I, _I]),
+    "compressed_attn_decode_noalloc": (_I, [_I, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
+                                            _I, _P, _F, _I, _F, _F, _I, _I, _P, _P, _I, _P]),
     "cskv_lowrank_proj": (_I, [_P, _P, _P, _L, _L, _L, _I, _P]),
     "cskv_grouped_out_proj": (_I, [_P, _P, _P, _P, _P, _L, _I, _I, _I, _L, _L, _I, _P]),
     "compressed_attn_decode": (_I, [_I, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
@@ -447,6 +449,25 @@ def compressed_attn_decode(mode: int, q, kv, idx, win, win_pos0: int, sink, pos0
         _check("compressed_attn_decode", lib().compressed_attn_decode(
             *args, n_splits, _ptr(workspace), workspace.numel(), _ptr(out), _ptr(lse), _dtype(q), _stream(q)))
     return (out, lse) if return_lse else out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def compressed_attn_decode_noalloc(mode: int, q, kv, idx, win, win_pos0: int, sink, pos0: int, m: int, w: int,
+                                   out, lse=None, k: int = 0, apply_q_norm: bool = True, q_norm_w=None,
+                                   eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 10000.0,
+                                   scale: float = 0.0, rope_on_output: bool = True, n_splits: int = 0):
+    """compressed_attn_decode without a workspace: the split partials use the library's static
+    per-GPU scratch (NOALLOC_SCRATCH_BYTES, held from the library's first use on a GPU to the end of
+    the process), so the call allocates no device memory; `out` (and `lse`, if wanted) are the
+    caller's. Calls that overlap on one GPU race on the shared scratch."""
+    _need(out is not None, "compressed_attn_decode_noalloc: out must be given (the call allocates nothing)")
+    args, out, lse = _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_norm,
+                                  q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output, out, lse, False)
+    _check("compressed_attn_decode_noalloc", lib().compressed_attn_decode_noalloc(
+        *args, n_splits, _ptr(out), _ptr(lse), _dtype(q), _stream(q)))
+    return out
 
 
 def lowrank_proj(cq, W, out=None):

@@ -35,6 +35,9 @@
 //    merge kernel combines splits in a fixed order, adds the sink, de-rotates.
 // fp32 kernel: plain vector-ALU online softmax, one workgroup per
 // (query, head); it serves the fp32 mode.
+#include <atomic>
+#include <mutex>
+
 #include "device_common.h"
 #include "abi_common.h"
 
@@ -205,7 +208,6 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
   const int64_t jl = (jb + QG < a.Tq ? jb + QG : a.Tq) - 1;  // last query of the tile
   const int64_t j = jb + qi < a.Tq ? jb + qi : jl;
   const bool qvalid = jb + qi < a.Tq;
-  const int64_t t = a.pos0 + j;
   const int h = hw * 16 + n;
   const bool hvalid = qvalid && h < a.H;
   const int split = blockIdx.y;
@@ -933,6 +935,22 @@ extern "C" size_t cskv_decode_workspace_size(int batch, int64_t Tq, int H, int d
   return decode_partial_bytes(batch, Tq, S, H, d);
 }
 
+// Split-K launch: S splits write fp32 partials into `part` (S > 1: decode_partial_bytes of
+// it), then attn_merge combines them; S = 1 runs the single-pass kernel and needs no partials.
+static int launch_decode(AttnArgs& a, int batch, int S, void* part, hipStream_t s) {
+  if (S == 1) {
+    if (!dispatch_attn(a, batch, s)) return CSKV_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+  }
+  a.n_splits = S;
+  a.part_o = (float*)part;
+  a.part_ml = a.part_o + (size_t)batch * a.Tq * S * a.H * a.D;
+  if (!dispatch_attn(a, batch, s)) return CSKV_ERR_UNSUPPORTED;
+  if (hipGetLastError() != hipSuccess) return CSKV_ERR_HIP;
+  hipLaunchKernelGGL((attn_merge<bf16>), dim3((unsigned)(batch * a.Tq), (unsigned)a.H), dim3(256), 0, s, a);
+  return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+}
+
 static int attn_decode_impl(int mode, const void* q, const void* kv, const float* kv_scale, const int32_t* idx,
                             const void* win, int64_t win_pos0, int64_t W, const float* sink, int batch,
                             int64_t Tq, int64_t N, int64_t pos0, int m, int k, int w, int H, int d,
@@ -952,20 +970,12 @@ static int attn_decode_impl(int mode, const void* q, const void* kv, const float
   hipStream_t s = (hipStream_t)stream;
   if (dtype == CSKV_F32) return launch_f32(a, batch, s);
   const int S = decode_splits(batch, Tq, max_keys(mode, Tq, N, pos0, m, k, w), n_splits);
-  if (S == 1) {
-    if (!dispatch_attn(a, batch, s)) return CSKV_ERR_UNSUPPORTED;
-    return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+  if (S > 1) {
+    const size_t need = decode_partial_bytes(batch, Tq, S, H, d);
+    if (!workspace || ws_bytes < need) return CSKV_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return CSKV_ERR_MISALIGNED;
   }
-  const size_t need = decode_partial_bytes(batch, Tq, S, H, d);
-  if (!workspace || ws_bytes < need) return CSKV_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return CSKV_ERR_MISALIGNED;
-  a.n_splits = S;
-  a.part_o = (float*)workspace;
-  a.part_ml = a.part_o + (size_t)batch * Tq * S * H * d;
-  if (!dispatch_attn(a, batch, s)) return CSKV_ERR_UNSUPPORTED;
-  if (hipGetLastError() != hipSuccess) return CSKV_ERR_HIP;
-  hipLaunchKernelGGL((attn_merge<bf16>), dim3((unsigned)(batch * Tq), (unsigned)H), dim3(256), 0, s, a);
-  return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+  return launch_decode(a, batch, S, workspace, s);
 }
 
 extern "C" int compressed_attn_decode(int mode, const void* q, const void* kv, const int32_t* idx,
@@ -993,4 +1003,82 @@ extern "C" int compressed_attn_decode_kv8(int mode, const void* q, const uint8_t
   return attn_decode_impl(mode, q, kv, N > 0 ? kv_scale : nullptr, idx, win, win_pos0, W, sink, batch, Tq, N,
                           pos0, m, k, w, H, d, apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale,
                           rope_on_output, n_splits, workspace, ws_bytes, out, lse, CSKV_BF16, stream);
+}
+
+// ---------------------------------------------------------------------------- allocation-free decode
+// compressed_attn_decode for callers that cannot allocate device memory: the split partials
+// live in `scratch`, a file-scope device array of CSKV_NOALLOC_SCRATCH_BYTES. Each GPU the
+// library runs on holds its own copy until the process ends; its device address is looked up
+// once per device (hipGetSymbolAddress, with that device current) and only that address is
+// handed to kernels -- in host code the array's name is a host-side stand-in, not a device
+// address. Every call on a GPU shares that GPU's array, so calls that overlap on one GPU
+// (different streams, or host threads) race on it. The partials need no clearing: every split
+// writes its whole partial, an empty split included.
+static __device__ __align__(256) unsigned char scratch[CSKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+std::atomic<void*> scratch_addr[kMaxDevices];
+
+// Device address of this device's `scratch`, for the device that `stream` runs on.
+int scratch_address(hipStream_t stream, void** addr) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return CSKV_ERR_HIP;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd;
+    if (hipStreamGetDevice(stream, &sd) != hipSuccess) return CSKV_ERR_HIP;
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return CSKV_ERR_UNSUPPORTED;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    p = scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (dev != cur && hipSetDevice(dev) != hipSuccess) return CSKV_ERR_HIP;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (dev != cur && hipSetDevice(cur) != hipSuccess) return CSKV_ERR_HIP;
+      if (e != hipSuccess || !p) return CSKV_ERR_HIP;
+      scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *addr = p;
+  return CSKV_OK;
+}
+}  // namespace
+
+extern "C" int compressed_attn_decode_noalloc(int mode, const void* q, const void* kv, const int32_t* idx,
+                                              const void* win, int64_t win_pos0, int64_t W, const float* sink,
+                                              int batch, int64_t Tq, int64_t N, int64_t pos0, int m, int k, int w,
+                                              int H, int d, int apply_q_norm, const float* q_norm_w, float eps,
+                                              int rope_dims, float rope_base, float scale, int rope_on_output,
+                                              int n_splits, void* out, float* lse, int dtype, void* stream) {
+  int st = validate_attn(mode, q, kv, idx, win, win_pos0, W, sink, batch, Tq, N, pos0, m, k, w, H, d,
+                         apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale, out, lse, dtype);
+  if (st) return st;
+  if (n_splits < 0 || n_splits > 256) return CSKV_ERR_BAD_SHAPE;
+  if (batch == 0 || Tq == 0) return CSKV_OK;
+  int S = 1;
+  if (dtype == CSKV_BF16) {
+    S = decode_splits(batch, Tq, max_keys(mode, Tq, N, pos0, m, k, w), n_splits);
+    const size_t per_split = decode_partial_bytes(batch, Tq, 2, H, d) / 2;
+    if (S > 1 && decode_partial_bytes(batch, Tq, S, H, d) > CSKV_NOALLOC_SCRATCH_BYTES) {
+      if (n_splits > 0) return CSKV_ERR_WORKSPACE;  // an explicit split count beyond the scratch
+      const size_t fit = CSKV_NOALLOC_SCRATCH_BYTES / per_split;
+      S = fit >= 2 ? (int)fit : 1;
+    }
+  }
+  AttnArgs a = make_args(mode, q, kv, idx, win, win_pos0, W, sink, Tq, N, pos0, m, k, w, H, d,
+                         apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output,
+                         out, lse);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == CSKV_F32) return launch_f32(a, batch, s);
+  void* part = nullptr;
+  if (S > 1) {
+    st = scratch_address(s, &part);
+    if (st) return st;
+  }
+  return launch_decode(a, batch, S, part, s);
 }

@@ -375,6 +375,33 @@ int compressed_attn_decode(int mode, const void* q, const void* kv, const int32_
                            int dtype, void* stream);
 
 /*
+ * compressed_attn_decode_noalloc -- compressed_attn_decode for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. There is no workspace argument;
+ * the call itself allocates nothing (no hipMalloc / hipFree). The split
+ * partials live in a static device buffer of CSKV_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends.
+ *   n_splits : 0 = the automatic split count of compressed_attn_decode,
+ *              lowered if need be so that the partials fit the buffer (down
+ *              to one split, which needs none); an explicit 1 .. 256 whose
+ *              partials (batch * Tq * n_splits * H * (d + 2) * 4 bytes) exceed
+ *              the buffer returns CSKV_ERR_WORKSPACE before any launch.
+ *   other arguments, limits and results as in compressed_attn_decode (bf16
+ *   or f32; with the same split count the output is bit-identical).
+ * Every call on one GPU shares that GPU's buffer: calls that overlap on one
+ * GPU (other streams, other host threads) race and must be serialised by
+ * the caller. The first call on a device looks the buffer's address up
+ * (hipGetSymbolAddress); a failure there returns CSKV_ERR_HIP.
+ */
+#define CSKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int compressed_attn_decode_noalloc(int mode, const void* q, const void* kv, const int32_t* idx,
+                                   const void* win, int64_t win_pos0, int64_t W, const float* sink,
+                                   int batch, int64_t Tq, int64_t N, int64_t pos0, int m, int k, int w,
+                                   int H, int d, int apply_q_norm, const float* q_norm_w, float eps,
+                                   int rope_dims, float rope_base, float scale, int rope_on_output,
+                                   int n_splits, void* out, float* lse, int dtype, void* stream);
+
+/*
  * FP8 KV storage [PB §2.3.4 "Efficiency": KV storage FP8 for the non-RoPE
  * dims, BF16 for the RoPE dims]. A stored entry is the E4M3 codes of its
  * first d - rope_dims values (x * 2^-e, e the smallest integer with

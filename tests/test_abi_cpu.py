@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 29, names
+    assert len(names) == 30, names
     for n in names:
         assert hasattr(L, n), n
     from compressed_sparse_kv_02_amd import binding
@@ -339,3 +339,23 @@ def test_decode_workspace_size_follows_the_split_policy(L):
              pos0=1 << 20, m=128, k=0, w=128, H=64, d=512, qn=1, qnw=None, eps=1e-6, rd=64, rb=1e4,
              sc=0.0, ro=1, ns=0, ws=P, wsb=f(8, 1, 64, 512, 0) - 1, out=P, lse=None, dt=0, st=None)
     assert L.compressed_attn_decode(*a.values()) == WS
+
+
+def test_decode_noalloc_rejects_explicit_splits_beyond_its_scratch(L):
+    from compressed_sparse_kv_02_amd import binding
+    f = L.compressed_attn_decode_noalloc
+    a = dict(mode=1, q=P, kv=P, idx=None, win=P, wp0=0, W=128, sink=None, batch=8, Tq=1, N=8192,
+             pos0=1 << 20, m=128, k=0, w=128, H=64, d=512, qn=1, qnw=None, eps=1e-6, rd=64, rb=1e4,
+             sc=0.0, ro=1, ns=256, out=P, lse=None, dt=0, st=None)
+    # 8 x 256 splits x 64 heads x 514 x 4 bytes = 269 MB of partials > 64 MiB: refused before any HIP call
+    assert 8 * 256 * 64 * 514 * 4 > binding.NOALLOC_SCRATCH_BYTES
+    assert f(*a.values()) == WS
+    assert f(*dict(a, ns=257).values()) == SHAPE
+    assert f(*dict(a, dt=5).values()) == DTYPE
+    assert f(*dict(a, out=None).values()) == INVALID
+    assert f(*dict(a, q=P + 8).values()) == MISALIGNED
+    # the binding refuses to allocate an output for it
+    import torch
+    with pytest.raises(binding.CskvError, match="out must be given"):
+        binding.compressed_attn_decode_noalloc(1, torch.zeros(1, 1, 4, 64), torch.zeros(1, 8, 64), None,
+                                               torch.zeros(1, 4, 64), 0, None, 3, 1, 4, out=None)
