@@ -15,8 +15,11 @@ resident in HBM when timing starts.
 Prints one JSON line. `roofline` covers the dominant kernel, the bf16 MFMA
 indexer scoring of the prefill CSA layers, timed with HIP events on its
 stream over the timed region; `roofline_decode` does the same for the
-HBM-bound decode scoring. `cpu_baseline` times the CPU oracle on a bounded
-sample of the same workload on this host's cores.
+HBM-bound decode scoring, `roofline_decode_step` for the whole decode step
+and `decode_attention` for its two attention calls. `configs` times the
+single-layer prefill configurations (HCA 16K, CSA 64K) outside the step.
+`cpu_baseline` times the CPU oracle on a bounded sample of the same
+workload on this host's cores.
 """
 from __future__ import annotations
 
@@ -121,12 +124,66 @@ def indexer_flops(L) -> float:
 
 
 def decode_score_bytes(L) -> float:
-    # indexer keys read once, queries + weights, fp32 score rows written
-    return L.batch * (L.N * L.dI * 2 + L.HI * L.dI * 2 + L.HI * 4 + L.N * 4)
+    """The decode scoring's own bytes: indexer keys read once, queries and head weights (the
+    fp32 score rows it hands to the top-k are a by-product of splitting the step, not counted)."""
+    return L.batch * (L.N * L.dI * 2 + L.HI * L.dI * 2 + L.HI * 4)
+
+
+def decode_step_bytes(decode) -> float:
+    """Algorithmic HBM bytes of one decode step (every layer of `decode`), each byte once: queries
+    and outputs, the new token's raw and prepared window row, the w window rows, lse; CSA: indexer
+    keys, indexer queries and weights, the k selected entries and their indices; HCA: every
+    visible entry."""
+    tot = 0
+    for L in decode:
+        e, b = 2, L.batch
+        tot += b * (2 * L.H * L.d * e + 2 * L.d * e + L.w * L.d * e + L.H * 4)
+        if L.kind == "csa":
+            tot += b * (L.N * L.dI * e + L.HI * L.dI * e + L.HI * 4 + L.k * L.d * e + 2 * L.k * 4)
+        else:
+            tot += b * min(L.N, (L.pos0 + 1) // L.m) * L.d * e
+    return tot
+
+
+def attn_pairs(L) -> int:
+    """(query, key) pairs of the layer call's attention: selected (CSA, at most k) or visible (HCA)
+    compressed entries plus the window rows, summed over queries."""
+    tot = 0
+    for j in range(L.T):
+        t = L.pos0 + j
+        V = min(L.N, (t + 1) // L.m)
+        tot += (min(L.k, V) if L.kind == "csa" else V) + min(L.w, t + 1)
+    return tot * L.batch
+
+
+def attn_flops(L) -> float:
+    return 4.0 * L.H * L.d * attn_pairs(L)   # S = Q K^T and O = P V, 2 H d each per pair
+
+
+def prefill_layer_bytes(L) -> float:
+    """Algorithmic HBM bytes of one prefill layer call read or written once: queries, outputs, lse,
+    raw and prepared window rows, compressor streams and new entries; CSA adds the indexer streams,
+    indexer queries and weights, the indexer keys and the selected indices. The gathered entry rows
+    of the attention are counted once per distinct entry (the cache), not per gather."""
+    e, b, T = 2, L.batch, L.T
+    tot = b * T * (2 * L.H * L.d * e + L.H * 4 + 3 * L.d * e)
+    if L.kind == "csa":
+        tot += b * T * 4 * (L.d + L.dI) * e + b * (L.n_new + L.N) * (L.d + L.dI) * e
+        tot += b * T * (L.HI * L.dI * e + L.HI * 4 + L.k * 4)
+    else:
+        tot += b * T * 2 * L.d * e + b * (L.n_new + L.N) * L.d * e
+    return tot
 
 
 def cpu_baseline(prefill, decode, tp, td, budget_s: float):
-    """Time the CPU oracle on a bounded sample: whole-chunk compression plus a few query rows."""
+    """Time the CPU oracle on a bounded sample of the step's workload.
+
+    Prefill: per layer, the whole chunk's compression and window rows for sequence 0 (amortised
+    over the chunk's tokens), then query rows drawn from a seeded stratified order (the chunk's
+    first rows, block and window edges, then a shuffle) until the layer's share of the budget is
+    spent (at least 4 rows). Decode: every one of the 8 sequences' tokens through both layers.
+    The rate weights the per-token times by the step's prefill and decode token counts.
+    """
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import cskv_oracle as O
@@ -134,20 +191,17 @@ def cpu_baseline(prefill, decode, tp, td, budget_s: float):
     def np64(t):
         return t.detach().float().cpu().numpy().astype(np.float64)
 
-    def layer_rows(L, t, rows, compress: bool):
-        b = 0
+    def layer_inputs(L, t, b):
         kv = np64(t["cache.kv"][b])
         ik = np64(t["cache.ik"][b]) if L.kind == "csa" else None
         win = np64(t["win"][b])
         h = {k: np64(v[b]) for k, v in t.items() if k.split(".")[-1] in ("Ca", "Cb", "Za", "Zb", "C", "Z",
                                                                           "prevCb", "prevZb") and v.dim() == 3}
         hb = {k: np64(v) for k, v in t.items() if k.endswith(".B")}
-        q = {r: np64(t["q"][b, r:r + 1]) for r in rows}
-        qI = {r: (np64(t["qI"][b, r:r + 1]), np64(t["wI"][b, r:r + 1])) for r in rows} if L.kind == "csa" else {}
-        raw = np64(t["win_raw"][b])
-        sink = np64(t["sink"])
-        t0 = time.perf_counter()
-        if compress and L.n_new:
+        return kv, ik, win, h, hb
+
+    def compress(L, t, b, kv, ik, win, h, hb):
+        if L.n_new:
             if L.kind == "csa":
                 kv[L.n_cached:] = O.csa_compress(h["kv.Ca"], h["kv.Cb"], h["kv.Za"], h["kv.Zb"], hb["kv.B"], L.m,
                                                  L.pos0, h.get("kv.prevCb"), h.get("kv.prevZb"), True,
@@ -157,39 +211,126 @@ def cpu_baseline(prefill, decode, tp, td, budget_s: float):
             else:
                 kv[L.n_cached:] = O.hca_compress(h["kv.C"], h["kv.Z"], hb["kv.B"], L.m, L.pos0, True,
                                                  rope_dims=L.rope_dims)
-            win[L.win_cached:] = O.prepare_window(raw, L.pos0, rope_dims=L.rope_dims)
-        t_comp = time.perf_counter() - t0
-        t0 = time.perf_counter()
-        for r in rows:
-            idx = None
-            if L.kind == "csa":
-                I = O.indexer_scores(qI[r][0], qI[r][1], ik, L.pos0 + r, L.m)[0]
-                idx = O.topk_row(I, O.visible(L.pos0 + r, L.m, L.N), L.k)[None]
-            O.attention(q[r], kv, win, L.win_pos0, L.pos0 + r, L.m, L.w, idx=idx, sink=sink,
-                        rope_dims=L.rope_dims)
-        return t_comp, time.perf_counter() - t0
+        win[L.win_cached:] = O.prepare_window(np64(t["win_raw"][b]), L.pos0, rope_dims=L.rope_dims)
 
-    # prefill: per-sequence chunk compression amortised over the chunk's tokens, plus n rows
-    n_pre = 4 if budget_s >= 10 else 2
-    rows = [0, 1365, 2730, 4095][:n_pre]
-    per_tok_pre = 0.0
+    def row(L, t, b, r, kv, ik, win, sink):
+        q = np64(t["q"][b, r:r + 1])
+        idx = None
+        if L.kind == "csa":
+            I = O.indexer_scores(np64(t["qI"][b, r:r + 1]), np64(t["wI"][b, r:r + 1]), ik, L.pos0 + r, L.m)[0]
+            idx = O.topk_row(I, O.visible(L.pos0 + r, L.m, L.N), L.k)[None]
+        O.attention(q, kv, win, L.win_pos0, L.pos0 + r, L.m, L.w, idx=idx, sink=sink, rope_dims=L.rope_dims)
+
+    share = budget_s * 0.8 / len(prefill)
+    per_tok_pre, n_rows = 0.0, []
     for L, t in zip(prefill, tp):
-        tc, tr = layer_rows(L, t, rows, compress=True)
-        per_tok_pre += tc / L.T + tr / len(rows)
-    per_tok_dec = 0.0
+        kv, ik, win, h, hb = layer_inputs(L, t, 0)
+        sink = np64(t["sink"])
+        t0 = time.perf_counter()
+        compress(L, t, 0, kv, ik, win, h, hb)
+        per_tok_pre += (time.perf_counter() - t0) / L.T
+        order = [0, 1, 3, 4, L.m - 1, L.m, L.w - 1, L.w, L.T - 1]
+        order += [int(r) for r in np.random.default_rng(5).permutation(L.T) if r not in order]
+        spent, n = 0.0, 0
+        for r in order:
+            t0 = time.perf_counter()
+            row(L, t, 0, r, kv, ik, win, sink)
+            spent += time.perf_counter() - t0
+            n += 1
+            if n >= 4 and spent >= share:
+                break
+        per_tok_pre += spent / n
+        n_rows.append(n)
+    per_tok_dec, n_dec_rows = 0.0, 0
     for L, t in zip(decode, td):
-        tc, tr = layer_rows(L, t, [0], compress=True)  # decode: prepares the new token's window row
-        per_tok_dec += tc + tr
+        spent = 0.0
+        for b in range(L.batch):
+            kv, ik, win, h, hb = layer_inputs(L, t, b)
+            t0 = time.perf_counter()
+            compress(L, t, b, kv, ik, win, h, hb)     # the new token's window row
+            row(L, t, b, 0, kv, ik, win, np64(t["sink"]))
+            spent += time.perf_counter() - t0
+        per_tok_dec += spent / L.batch
+        n_dec_rows += L.batch
     n_pre_tok = prefill[0].batch * prefill[0].T
     n_dec_tok = decode[0].batch
     value = (n_pre_tok + n_dec_tok) / (n_pre_tok * per_tok_pre + n_dec_tok * per_tok_dec)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": value, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": (f"sequence 0: whole-chunk compression of all 4 prefill layers amortised over the "
-                       f"chunk, plus {len(rows)} query rows through the 4-layer stack and 1 decode token "
-                       f"through the CSA+HCA decode layers; per-token times weighted by the step's "
+            "sample": (f"sequence 0 of the prefill chunk: whole-chunk compression and window rows of each of "
+                       f"the 4 layers amortised over the chunk, plus {n_rows} query rows per layer (stratified, "
+                       f"as many as a {budget_s:.0f} s budget allows); all {decode[0].batch} decode tokens "
+                       f"through the CSA and HCA decode layers; per-token times weighted by the step's "
                        f"{n_pre_tok} prefill + {n_dec_tok} decode tokens"),
+            "rows_timed": {"prefill_per_layer": n_rows, "decode": n_dec_rows},
             "seconds_per_prefill_token": per_tok_pre, "seconds_per_decode_token": per_tok_dec}
+
+
+PHASES = ("compress", "score", "topk", "attend")
+
+
+def run_phases(L, t, rec=None, ev=None):
+    """One layer call, phase by phase (compression + window rows, indexer scores, top-k,
+    attention); with `rec`, each phase is bracketed by HIP events on the launch stream."""
+    from compressed_sparse_kv_02_amd import layer as LY
+    for name, fn in zip(PHASES, (LY.compress_step, LY.score_step, LY.topk_step, LY.attend_step)):
+        if rec is None:
+            fn(L, t)
+        else:
+            a, b = ev(), ev()
+            a.record()
+            fn(L, t)
+            b.record()
+            rec.setdefault(name, []).append((a, b))
+
+
+def mean_ms(pairs) -> float:
+    return sum(a.elapsed_time(b) for a, b in pairs) / len(pairs) if pairs else 0.0
+
+
+def prefill_config_rows(reps: int = 3):
+    """The two single-layer prefill configurations, each a whole layer call (compression, window
+    rows, scoring, top-k, attention), timed phase by phase with HIP events: HCA prefill of 16384
+    tokens (32 heads, m' = 128; HBM-bound) and CSA prefill of 65536 tokens (64 heads, k = 1024,
+    rank-256 indexer queries; the indexer and the attention against the bf16 matrix peak)."""
+    import torch
+    from compressed_sparse_kv_02_amd import layer as LY
+
+    out = {}
+    for name, L in (("hca_prefill_16k", LY.hca_prefill_16k()), ("csa_prefill_64k", LY.csa_prefill_64k())):
+        t = LY.make_inputs(L)
+        run_phases(L, t)
+        torch.cuda.synchronize()
+        pool, rec = [], {}
+
+        def ev():
+            e = torch.cuda.Event(enable_timing=True)
+            pool.append(e)
+            return e
+        for _ in range(reps):
+            run_phases(L, t, rec, ev)
+        torch.cuda.synchronize()
+        ph = {k: mean_ms(v) for k, v in rec.items()}
+        total = sum(ph.values())
+        by = prefill_layer_bytes(L)
+        af, pairs = attn_flops(L), attn_pairs(L)
+        ent = {"layer": f"{L.kind} batch {L.batch} x {L.T} tokens, {L.H} heads x {L.d}, m={L.m}, window {L.w}"
+                        + (f", k={L.k}, indexer {L.HI} x {L.dI}" if L.kind == "csa" else ""),
+               "ms_per_call": total, "query_tokens_per_s": L.batch * L.T / (total / 1e3), "phases_ms": ph,
+               "hbm": {"algorithmic_bytes": by, "achieved_GBps": by / (total / 1e3) / 1e9,
+                       "frac": by / (total / 1e3) / PEAK_HBM_BYTES},
+               "attention": {"algorithmic_flops": af, "tflops": af / (ph["attend"] / 1e3) / 1e12,
+                             "frac_mfma": af / (ph["attend"] / 1e3) / PEAK_BF16_FLOPS,
+                             "gathered_rows_bytes": pairs * L.d * 2,
+                             "gather_GBps": pairs * L.d * 2 / (ph["attend"] / 1e3) / 1e9}}
+        if L.kind == "csa":
+            fl = indexer_flops(L)
+            ent["indexer"] = {"algorithmic_flops": fl, "tflops": fl / (ph["score"] / 1e3) / 1e12,
+                              "frac_mfma": fl / (ph["score"] / 1e3) / PEAK_BF16_FLOPS}
+        out[name] = ent
+        del t
+        torch.cuda.empty_cache()
+    return out
 
 
 def lowp_indexer_rows(prefill, tp, decode, td, reps: int = 3):
@@ -357,6 +498,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-configs", action="store_true", help="skip the 16K HCA and 64K CSA prefill lines")
+    ap.add_argument("--no-next-rows", action="store_true", help="skip the low-precision / projection lines")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB copy (counter calibration for --write-traffic)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -390,40 +533,19 @@ def main():
         return e
 
     def step(rec=None):
-        marks = {}
-        for L, t in zip(prefill, tp):
-            LY.compress_step(L, t)
-            if L.kind == "csa" and rec is not None:
-                a, b = ev(), ev()
-                a.record()
-                LY.score_step(L, t)
-                b.record()
-                rec["pre_score"].append((a, b))
-            else:
-                LY.score_step(L, t)
-            LY.topk_step(L, t)
-            LY.attend_step(L, t)
+        for i, (L, t) in enumerate(zip(prefill, tp)):
+            run_phases(L, t, None if rec is None else rec["pre"][i], ev)
         if rec is not None:
             m = ev()
             m.record()
             rec["mid"].append(m)
-        for L, t in zip(decode, td):
-            LY.compress_step(L, t)
-            if L.kind == "csa" and rec is not None:
-                a, b = ev(), ev()
-                a.record()
-                LY.score_step(L, t)
-                b.record()
-                rec["dec_score"].append((a, b))
-            else:
-                LY.score_step(L, t)
-            LY.topk_step(L, t)
-            LY.attend_step(L, t)
+        for i, (L, t) in enumerate(zip(decode, td)):
+            run_phases(L, t, None if rec is None else rec["dec"][i], ev)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    rec = {"pre_score": [], "dec_score": [], "mid": []}
+    rec = {"pre": [{} for _ in prefill], "dec": [{} for _ in decode], "mid": []}
     starts = []
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -448,8 +570,13 @@ def main():
     n_pre = prefill[0].batch * prefill[0].T
     n_dec = decode[0].batch
     value = (n_pre + n_dec) / (ms / 1e3)
+    phases = {
+        "prefill": [dict(layer=f"{L.kind}{i}", **{k: mean_ms(v) for k, v in r.items()})
+                    for i, (L, r) in enumerate(zip(prefill, rec["pre"]))],
+        "decode": [dict(layer=L.kind, **{k: mean_ms(v) for k, v in r.items()}) for L, r in zip(decode, rec["dec"])],
+    }
 
-    score_ms = sum(a.elapsed_time(b) for a, b in rec["pre_score"]) / len(rec["pre_score"])
+    score_ms = mean_ms([p for L, r in zip(prefill, rec["pre"]) if L.kind == "csa" for p in r["score"]])
     fl = indexer_flops(prefill[0])
     achieved = fl / (score_ms / 1e3) / 1e12
     tr = load_traffic() or {}
@@ -458,7 +585,7 @@ def main():
                 "frac": achieved * 1e12 / PEAK_BF16_FLOPS, "traffic": traffic,
                 "kernel": "indexer_score_mfma<2,8> (prefill CSA layers)", "avg_launch_ms": score_ms,
                 "algorithmic_flops_per_launch": fl}
-    dscore_ms = sum(a.elapsed_time(b) for a, b in rec["dec_score"]) / len(rec["dec_score"])
+    dscore_ms = mean_ms(rec["dec"][0]["score"])
     db = decode_score_bytes(decode[0])
     dach = db / (dscore_ms / 1e3) / 1e9
     dtraffic = tr.get("indexer_score_mfma_decode", {}).get("hbm_bytes_per_launch")
@@ -466,6 +593,19 @@ def main():
                     "frac": dach * 1e9 / PEAK_HBM_BYTES, "traffic": dtraffic,
                     "kernel": "indexer_score_stream<2,8> (decode CSA layer)", "avg_launch_ms": dscore_ms,
                     "algorithmic_bytes_per_launch": db}
+    sb = decode_step_bytes(decode)
+    roofline_step = {"bound": "hbm", "achieved": sb / (dec_ms / 1e3) / 1e9, "peak": PEAK_HBM_BYTES / 1e9,
+                     "unit": "GB/s", "frac": sb / (dec_ms / 1e3) / PEAK_HBM_BYTES, "ms": dec_ms,
+                     "algorithmic_bytes": sb,
+                     "what": "the whole decode step (window rows, scoring, top-k, CSA and HCA attention)"}
+    dattn = {}
+    for L, r in zip(decode, rec["dec"]):
+        e = 2
+        keys = min(L.k, L.N) if L.kind == "csa" else min(L.N, (L.pos0 + 1) // L.m)
+        by = L.batch * ((keys + L.w) * L.d * e + 2 * L.H * L.d * e + L.H * 4)
+        am = mean_ms(r["attend"])
+        dattn[L.kind] = {"bound": "hbm", "ms": am, "algorithmic_bytes": by,
+                         "achieved_GBps": by / (am / 1e3) / 1e9, "frac": by / (am / 1e3) / PEAK_HBM_BYTES}
 
     out = {
         "metric": METRIC, "value": value, "unit": "query-tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -478,13 +618,19 @@ def main():
                    "decode": "batch 8 x 1 token at pos 1048576, CSA (262144 entries, k=1024) + HCA (8192)",
                    "query_tokens_per_step": n_pre + n_dec},
         "parts": {"prefill_ms": pre_ms, "prefill_query_tokens_per_s": n_pre / (pre_ms / 1e3),
-                  "decode_ms": dec_ms, "decode_query_tokens_per_s": n_dec / (dec_ms / 1e3)},
+                  "decode_ms": dec_ms, "decode_query_tokens_per_s": n_dec / (dec_ms / 1e3),
+                  "phases_ms": phases},
         "roofline": roofline,
         "roofline_decode": roofline_dec,
+        "roofline_decode_step": roofline_step,
+        "decode_attention": dattn,
         "cpu_baseline": None,
-        "next_rows": dict(lowp_indexer_rows(prefill, tp, decode, td), projections=projection_rows(prefill),
-                          kv_fp8_attention=kv_fp8_attention_rows(prefill, tp, decode, td)),
     }
+    if not args.no_configs:
+        out["configs"] = prefill_config_rows()
+    if not args.no_next_rows:
+        out["next_rows"] = dict(lowp_indexer_rows(prefill, tp, decode, td), projections=projection_rows(prefill),
+                                kv_fp8_attention=kv_fp8_attention_rows(prefill, tp, decode, td))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(prefill, decode, tp, td, args.cpu_budget)
     print(json.dumps(out), flush=True)

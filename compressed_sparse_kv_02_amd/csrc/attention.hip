@@ -720,8 +720,10 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
 template <int D, int HW, int QG, int KVR>
 static void launch_kvr(const AttnArgs& a, dim3 grid, hipStream_t st) {
   if constexpr (KVR <= D) {
-    // one query per workgroup over bf16 entries, not split (CSA prefill): two per CU
-    if constexpr (D == 512 && HW == 4 && QG == 1 && KVR < 0) {
+    // 256-thread workgroups over bf16 entries, not split (CSA prefill with 64 heads, HCA prefill
+    // with up to 32 heads and two queries per workgroup): two per CU, so the compiler keeps each
+    // lane within 256 registers; built for one per CU they took twice that and ran alone on the CU
+    if constexpr (D == 512 && HW * QG == 4 && KVR < 0) {
       if (a.n_splits == 1) {
         hipLaunchKernelGGL((attn_mfma<D, HW, QG, KVR, 2>), grid, dim3(HW * QG * 64), 0, st, a);
         return;

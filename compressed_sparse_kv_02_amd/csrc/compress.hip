@@ -5,14 +5,27 @@
 // a-stream rows of block i -- under one per-channel softmax of Z + B.
 // HCA compressor (§2.3.2): entry i pools the m' rows of block i of one stream.
 // Both are followed by optional RMSNorm over the channels and RoPE on the
-// last rope_dims channels (§2.3.3) at the entry's position.
+// last rope_dims channels (§2.3.3) at the entry's position. m' = 1 prepares
+// raw sliding-window rows: the softmax over one row is the row itself.
 //
-// One workgroup (256 threads) builds one entry of one sequence. Threads are
-// laid out as [row group][channel group]: a channel group is VEC contiguous
-// channels (one 16-byte load per row), row groups split the block's rows.
-// Each thread keeps an online softmax (max, sum, weighted sum) per channel;
-// the row groups are merged through LDS in a fixed order, so the result is
-// deterministic. The kernel is HBM-streaming: every input byte is read once.
+// The softmax is per channel, over the entry's rows, so a lane that owns a
+// few channels needs nothing from other lanes until the RMSNorm. Three
+// kernels, all HBM-streaming (every input byte read once):
+//  * rows (one row per entry): a group of lanes per row, each lane 8 (bf16)
+//    or 4 (fp32) channels per 16-byte load, several rows' loads in flight per
+//    group; RMSNorm's sum of squares is a butterfly over the group's lanes.
+//  * pool (2..32 rows per entry, e.g. CSA with m = 4): a group of lanes per
+//    entry keeps an online softmax (max, sum, weighted sum) per channel in
+//    registers over the entry's rows, loaded four rows at a time.
+//  * block (more than 32 rows, e.g. HCA with m' = 128): a workgroup per
+//    entry, its waves take interleaved rows, and one wave merges their
+//    partial softmaxes from LDS in wave order.
+// No kernel uses an atomic; every reduction has a fixed order, so results
+// are deterministic. Rotary angles: each lane forms r = base^(-2/rope_dims)
+// once (fp64) and the pair angles theta_j = r^j by products, then the
+// angle pos * theta_j is reduced modulo 2 pi in fp64 before an fp32 sincos.
+#include <algorithm>
+
 #include "device_common.h"
 #include "abi_common.h"
 
@@ -33,164 +46,337 @@ struct CompressArgs {
   int csa;  // 1: two streams, overlapped; 0: one stream
   int apply_norm, rope_dims;
   float eps, rope_base;
-  int clp;  // channel groups per row group (power of two)
+  int lpe;    // lanes per entry (power of two <= 64)
+  int batch;  // sequences (the row and pool kernels stride over batch * n_out entries)
 };
 
-template <typename T, int VEC>
-__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
-  constexpr int NT = 256;
-  __shared__ float part[3][NT * VEC];
-  __shared__ float red[NT / 64];
-
-  const int entry = blockIdx.x;
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int CL = a.c / VEC;
-  const int g = tid % a.clp;
-  const int rg = tid / a.clp;
-  const int RG = NT / a.clp;
-  const bool active = g < CL;
-  const int ch0 = g * VEC;
-  const int64_t seq = (int64_t)b * a.T * a.c;
-
-  float mx[VEC], sm[VEC], acc[VEC];
-#pragma unroll
-  for (int v = 0; v < VEC; ++v) {
-    mx[v] = -INFINITY;
-    sm[v] = 0.f;
-    acc[v] = 0.f;
+// Rotary angle of pair j: theta_j = r^j with r = base^(-2/rope_dims), by binary powering (fp64).
+__device__ __forceinline__ double rope_theta(double r, int j) {
+  double t = 1.0, x = r;
+  for (int e = j; e > 0; e >>= 1) {
+    if (e & 1) t *= x;
+    x *= x;
   }
+  return t;
+}
 
-  // Rows of this entry's softmax: CSA: [b-half (m rows, if present), a-half (m rows)];
-  // HCA: the m rows of block `entry`.
-  const int m = a.m;
-  bool has_b = false;
-  if (a.csa) has_b = entry > 0 || a.prev_Cb != nullptr;
-  const int nrows = a.csa ? (has_b ? 2 * m : m) : m;
-  const int first = a.csa ? (has_b ? 0 : m) : 0;  // logical row index of the first row
+__device__ __forceinline__ void rope_apply(double theta, int64_t pos, float& x0, float& x1) {
+  const double inv_two_pi = 0.15915494309189533576888376337251;
+  const double two_pi = 6.283185307179586476925286766559;
+  double ang = (double)pos * theta;
+  ang = __builtin_fma(-two_pi, rint(ang * inv_two_pi), ang);  // |ang| <= pi (+ rounding)
+  float sn, cs;
+  sincosf((float)ang, &sn, &cs);
+  const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
+  x0 = y0;
+  x1 = y1;
+}
 
-  if (active) {
-    for (int r = first + rg; r < first + nrows; r += RG) {
-      const T* cp;
-      const T* zp;
-      const T* bp = nullptr;
-      if (a.csa) {
-        const int p = r % m;
-        if (r < m) {  // b-half: block entry-1 (or previous chunk's tail)
-          if (entry > 0) {
-            const int64_t row = (int64_t)(entry - 1) * m + p;
-            cp = (const T*)a.Cb + seq + row * a.c;
-            zp = (const T*)a.Zb + seq + row * a.c;
-          } else {
-            cp = (const T*)a.prev_Cb + ((int64_t)b * m + p) * a.c;
-            zp = (const T*)a.prev_Zb + ((int64_t)b * m + p) * a.c;
-          }
-          bp = (const T*)a.B + (int64_t)p * a.c;
-        } else {
-          const int64_t row = (int64_t)entry * m + p;
-          cp = (const T*)a.Ca + seq + row * a.c;
-          zp = (const T*)a.Za + seq + row * a.c;
-          bp = (const T*)a.B + (int64_t)(m + p) * a.c;
-        }
-      } else {
-        const int64_t row = (int64_t)entry * m + r;
-        cp = (const T*)a.Ca + seq + row * a.c;
-        zp = a.Za ? (const T*)a.Za + seq + row * a.c : nullptr;
-        bp = a.B ? (const T*)a.B + (int64_t)r * a.c : nullptr;
-      }
-      float cv[VEC], zv[VEC], bv[VEC];
-      load_vec<T, VEC>(cp + ch0, cv);
-      if (zp) {
-        load_vec<T, VEC>(zp + ch0, zv);
-      } else {
+// Per-lane rotary table: theta of each pair (channels ch, ch + 1) in this lane's channel groups,
+// 0 where the pair is not rotated (ch < c - rope_dims; a group may straddle that boundary).
+template <int VEC, int CPL>
+__device__ __forceinline__ void rope_table(const CompressArgs& a, int gi, int LPE, double (&th)[CPL][VEC / 2]) {
+  const int rstart = a.c - a.rope_dims;
+  const bool any = a.rope_dims > 0 && (gi + LPE * (CPL - 1)) * VEC + VEC > rstart;
+  const double r = any ? pow((double)a.rope_base, -2.0 / (double)a.rope_dims) : 0.0;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) zv[v] = 0.f;
-      }
-      if (bp) {
-        load_vec<T, VEC>(bp + ch0, bv);
+  for (int cg = 0; cg < CPL; ++cg) {
+    const int ch0 = (gi + LPE * cg) * VEC;
+    const int jf = (ch0 >= rstart ? ch0 - rstart : 0) >> 1;  // first rotated pair of the group
+    double t = (any && ch0 + VEC > rstart) ? rope_theta(r, jf) : 0.0;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) zv[v] += bv[v];
-      }
-#pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        const float nm = fmaxf(mx[v], zv[v]);
-        const float sc = __expf(mx[v] - nm);  // exp(-inf) = 0 on the first row
-        const float e = __expf(zv[v] - nm);
-        sm[v] = sm[v] * sc + e;
-        acc[v] = acc[v] * sc + e * cv[v];
-        mx[v] = nm;
-      }
+    for (int p = 0; p < VEC / 2; ++p) {
+      const bool rot = ch0 + 2 * p >= rstart;
+      th[cg][p] = rot ? t : 0.0;
+      if (rot) t *= r;
     }
   }
+}
 
-  // Merge row groups in a fixed order (row group 0 first). Partials are stored channel-major
-  // (element v of thread t at v * NT + t), so each store and read touches consecutive words.
+// Entry epilogue for a lane group of LPE lanes holding y[cg][v] = channel (gi + LPE cg) VEC + v:
+// RMSNorm over the c channels, RoPE at `pos` on the last rope_dims channels, store to `op`.
+template <typename T, int VEC, int CPL>
+__device__ __forceinline__ void finish_entry(const CompressArgs& a, float (&y)[CPL][VEC], int gi, int LPE,
+                                             const double (&th)[CPL][VEC / 2], int64_t pos, T* op) {
+  const int groups = a.c / VEC;
+  if (a.apply_norm) {
+    float ss = 0.f;
+#pragma unroll
+    for (int cg = 0; cg < CPL; ++cg)
+      if (gi + LPE * cg < groups)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) ss += y[cg][v] * y[cg][v];
+    for (int o = LPE >> 1; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float inv = rsqrtf(ss / (float)a.c + a.eps);
+#pragma unroll
+    for (int cg = 0; cg < CPL; ++cg) {
+      const int ch0 = (gi + LPE * cg) * VEC;
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) y[cg][v] *= inv * (a.norm_w && ch0 < a.c ? a.norm_w[ch0 + v] : 1.f);
+    }
+  }
+  const int rstart = a.c - a.rope_dims;
+#pragma unroll
+  for (int cg = 0; cg < CPL; ++cg) {
+    const int ch0 = (gi + LPE * cg) * VEC;
+    if (gi + LPE * cg >= groups) continue;
+    if (a.rope_dims > 0 && ch0 + VEC > rstart) {
+#pragma unroll
+      for (int p = 0; p < VEC / 2; ++p)
+        if (ch0 + 2 * p >= rstart) rope_apply(th[cg][p], pos, y[cg][2 * p], y[cg][2 * p + 1]);
+    }
+    store_vec<T, VEC>(op + ch0, y[cg]);
+  }
+}
+
+// Rows of entry e of sequence b: CSA [b-half (m rows, when present), a-half (m rows)];
+// HCA the m rows of block e. Returns the pointers of logical row r.
+template <typename T>
+__device__ __forceinline__ void entry_row(const CompressArgs& a, int b, int64_t e, int r, const T*& cp,
+                                          const T*& zp, const T*& bp) {
+  const int m = a.m;
+  const int64_t seq = (int64_t)b * a.T * a.c;
+  if (a.csa) {
+    const int p = r % m;
+    if (r < m) {  // b-half: block e-1 (or the previous chunk's tail)
+      if (e > 0) {
+        const int64_t row = (e - 1) * m + p;
+        cp = (const T*)a.Cb + seq + row * a.c;
+        zp = (const T*)a.Zb + seq + row * a.c;
+      } else {
+        cp = (const T*)a.prev_Cb + ((int64_t)b * m + p) * a.c;
+        zp = (const T*)a.prev_Zb + ((int64_t)b * m + p) * a.c;
+      }
+      bp = (const T*)a.B + (int64_t)p * a.c;
+    } else {
+      const int64_t row = e * m + p;
+      cp = (const T*)a.Ca + seq + row * a.c;
+      zp = (const T*)a.Za + seq + row * a.c;
+      bp = (const T*)a.B + (int64_t)(m + p) * a.c;
+    }
+  } else {
+    const int64_t row = e * m + r;
+    cp = (const T*)a.Ca + seq + row * a.c;
+    zp = a.Za ? (const T*)a.Za + seq + row * a.c : nullptr;
+    bp = a.B ? (const T*)a.B + (int64_t)r * a.c : nullptr;
+  }
+}
+
+__device__ __forceinline__ void entry_rows(const CompressArgs& a, int64_t e, int& first, int& nrows) {
+  const bool has_b = a.csa && (e > 0 || a.prev_Cb != nullptr);
+  nrows = a.csa ? (has_b ? 2 * a.m : a.m) : a.m;
+  first = a.csa ? (has_b ? 0 : a.m) : 0;
+}
+
+template <int VEC>
+__device__ __forceinline__ void softmax_step(float (&mx)[VEC], float (&sm)[VEC], float (&acc)[VEC],
+                                             const float (&zv)[VEC], const float (&cv)[VEC]) {
 #pragma unroll
   for (int v = 0; v < VEC; ++v) {
-    part[0][v * NT + tid] = mx[v];
-    part[1][v * NT + tid] = sm[v];
-    part[2][v * NT + tid] = acc[v];
+    const float nm = fmaxf(mx[v], zv[v]);
+    const float sc = __expf(mx[v] - nm);  // exp(-inf) = 0 on the first row
+    const float e = __expf(zv[v] - nm);
+    sm[v] = sm[v] * sc + e;
+    acc[v] = acc[v] * sc + e * cv[v];
+    mx[v] = nm;
   }
-  __syncthreads();
+}
 
-  float y[VEC];
-  float ss = 0.f;
-  if (rg == 0 && active) {
+// One row per entry (m = 1): the softmax over a single row is that row. A lane group takes
+// EPL rows per pass, all loads issued before any use.
+template <typename T, int VEC, int CPL, int EPL>
+__global__ __launch_bounds__(256) void compress_rows_kernel(CompressArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int LPE = a.lpe, gi = lane & (LPE - 1), gpw = 64 / LPE;
+  const int groups = a.c / VEC;
+  const int64_t task0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * gpw + lane / LPE;
+  const int64_t ntask = (int64_t)gridDim.x * 4 * gpw;
+  const int64_t n_tot = (int64_t)a.n_out * a.batch;
+  double th[CPL][VEC / 2];
+  rope_table<VEC, CPL>(a, gi, LPE, th);
+  for (int64_t t = task0 * EPL; t < n_tot; t += ntask * EPL) {
+    float y[EPL][CPL][VEC];
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+      const int64_t el = t + q < n_tot ? t + q : n_tot - 1;
+      const int b = (int)(el / a.n_out);
+      const int64_t e = el % a.n_out;
+      const T* cp = (const T*)a.Ca + ((int64_t)b * a.T + e) * a.c;
+#pragma unroll
+      for (int cg = 0; cg < CPL; ++cg) {
+        const int g = gi + LPE * cg;
+        if (g < groups) load_vec<T, VEC>(cp + g * VEC, y[q][cg]);
+        else
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) y[q][cg][v] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < EPL; ++q) {
+      if (t + q >= n_tot) break;
+      const int b = (int)((t + q) / a.n_out);
+      const int64_t e = (t + q) % a.n_out;
+      finish_entry<T, VEC, CPL>(a, y[q], gi, LPE, th, a.pos0 + e,
+                                (T*)a.out + ((int64_t)b * a.out_ld + e) * a.c);
+    }
+  }
+}
+
+// 2 .. 32 rows per entry: a lane group per entry, online softmax in registers, rows four at a time.
+template <typename T, int VEC, int CPL>
+__global__ __launch_bounds__(256) void compress_pool_kernel(CompressArgs a) {
+  constexpr int RB = 4;
+  const int lane = threadIdx.x & 63;
+  const int LPE = a.lpe, gi = lane & (LPE - 1), gpw = 64 / LPE;
+  const int groups = a.c / VEC;
+  const int64_t task0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * gpw + lane / LPE;
+  const int64_t ntask = (int64_t)gridDim.x * 4 * gpw;
+  const int64_t n_tot = (int64_t)a.n_out * a.batch;
+  double th[CPL][VEC / 2];
+  rope_table<VEC, CPL>(a, gi, LPE, th);
+  for (int64_t el = task0; el < n_tot; el += ntask) {
+    const int b = (int)(el / a.n_out);
+    const int64_t e = el % a.n_out;
+    int first, nrows;
+    entry_rows(a, e, first, nrows);
+    float mx[CPL][VEC], sm[CPL][VEC], acc[CPL][VEC];
+#pragma unroll
+    for (int cg = 0; cg < CPL; ++cg)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        mx[cg][v] = -INFINITY;
+        sm[cg][v] = 0.f;
+        acc[cg][v] = 0.f;
+      }
+    for (int r0 = 0; r0 < nrows; r0 += RB) {
+      float cv[RB][CPL][VEC], zv[RB][CPL][VEC];
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        const int r = first + (r0 + i < nrows ? r0 + i : nrows - 1);
+        const T *cp, *zp, *bp;
+        entry_row<T>(a, b, e, r, cp, zp, bp);
+#pragma unroll
+        for (int cg = 0; cg < CPL; ++cg) {
+          const int g = gi + LPE * cg < groups ? gi + LPE * cg : groups - 1;
+          load_vec<T, VEC>(cp + g * VEC, cv[i][cg]);
+          if (zp) {
+            load_vec<T, VEC>(zp + g * VEC, zv[i][cg]);
+          } else {
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) zv[i][cg][v] = 0.f;
+          }
+          if (bp) {
+            float bv[VEC];
+            load_vec<T, VEC>(bp + g * VEC, bv);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) zv[i][cg][v] += bv[v];
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        if (r0 + i >= nrows) break;
+#pragma unroll
+        for (int cg = 0; cg < CPL; ++cg) softmax_step<VEC>(mx[cg], sm[cg], acc[cg], zv[i][cg], cv[i][cg]);
+      }
+    }
+    float y[CPL][VEC];
+#pragma unroll
+    for (int cg = 0; cg < CPL; ++cg)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) y[cg][v] = acc[cg][v] / sm[cg][v];
+    finish_entry<T, VEC, CPL>(a, y, gi, LPE, th, a.pos0 + e * a.m, (T*)a.out + ((int64_t)b * a.out_ld + e) * a.c);
+  }
+}
+
+// More than 32 rows per entry: a workgroup of NW waves per entry; wave w takes rows w, w + NW,
+// ...; wave 0 merges the partial softmaxes in wave order and finishes the entry.
+template <typename T, int VEC, int CPL, int NW>
+__global__ __launch_bounds__(NW * 64) void compress_block_kernel(CompressArgs a) {
+  constexpr int W = CPL * VEC;  // floats per lane
+  __shared__ __attribute__((aligned(16))) float part[3][NW][64 * W];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int groups = a.c / VEC;
+  const int64_t e = blockIdx.x;
+  const int b = blockIdx.y;
+  int first, nrows;
+  entry_rows(a, e, first, nrows);
+  float mx[CPL][VEC], sm[CPL][VEC], acc[CPL][VEC];
+#pragma unroll
+  for (int cg = 0; cg < CPL; ++cg)
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
-      float M = -INFINITY;
-      for (int q = 0; q < RG; ++q) M = fmaxf(M, part[0][v * NT + q * a.clp + g]);
-      float S = 0.f, A = 0.f;
-      for (int q = 0; q < RG; ++q) {
-        const int o = v * NT + q * a.clp + g;
-        const float mq = part[0][o];
-        if (mq == -INFINITY) continue;  // row group saw no rows
-        const float sc = __expf(mq - M);
-        S += part[1][o] * sc;
-        A += part[2][o] * sc;
-      }
-      y[v] = A / S;
-      ss += y[v] * y[v];
+      mx[cg][v] = -INFINITY;
+      sm[cg][v] = 0.f;
+      acc[cg][v] = 0.f;
     }
-  }
-
-  if (a.apply_norm) {
-    // Block reduction of the sum of squares (fixed order over waves).
-    float w = wave_sum(ss);
-    if ((tid & 63) == 0) red[tid >> 6] = w;
-    __syncthreads();
-    float tot = 0.f;
+  constexpr int RB = 4;
+  for (int r0 = wave; r0 < nrows; r0 += NW * RB) {
+    float cv[RB][CPL][VEC], zv[RB][CPL][VEC];
 #pragma unroll
-    for (int q = 0; q < NT / 64; ++q) tot += red[q];
-    const float inv = rsqrtf(tot / (float)a.c + a.eps);
-    if (rg == 0 && active) {
+    for (int i = 0; i < RB; ++i) {
+      const int rr = r0 + i * NW;
+      const int r = first + (rr < nrows ? rr : r0);
+      const T *cp, *zp, *bp;
+      entry_row<T>(a, b, e, r, cp, zp, bp);
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) {
-        const float gmul = a.norm_w ? a.norm_w[ch0 + v] : 1.f;
-        y[v] = y[v] * inv * gmul;
-      }
-    }
-  }
-
-  if (rg == 0 && active) {
-    const int rstart = a.c - a.rope_dims;
-    if (a.rope_dims > 0 && ch0 + VEC > rstart) {
-      const int64_t pos = a.pos0 + (int64_t)entry * m;
+      for (int cg = 0; cg < CPL; ++cg) {
+        const int g = lane + 64 * cg < groups ? lane + 64 * cg : groups - 1;
+        load_vec<T, VEC>(cp + g * VEC, cv[i][cg]);
+        if (zp) {
+          load_vec<T, VEC>(zp + g * VEC, zv[i][cg]);
+        } else {
 #pragma unroll
-      for (int v = 0; v < VEC; v += 2) {
-        const int ch = ch0 + v;
-        if (ch >= rstart) {
-          float cs, sn;
-          rope_cos_sin(pos, (ch - rstart) >> 1, a.rope_dims, a.rope_base, &cs, &sn);
-          const float x0 = y[v], x1 = y[v + 1];
-          y[v] = x0 * cs - x1 * sn;
-          y[v + 1] = x0 * sn + x1 * cs;
+          for (int v = 0; v < VEC; ++v) zv[i][cg][v] = 0.f;
+        }
+        if (bp) {
+          float bv[VEC];
+          load_vec<T, VEC>(bp + g * VEC, bv);
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) zv[i][cg][v] += bv[v];
         }
       }
     }
-    T* op = (T*)a.out + ((int64_t)b * a.out_ld + entry) * a.c + ch0;
-    store_vec<T, VEC>(op, y);
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      if (r0 + i * NW >= nrows) break;
+#pragma unroll
+      for (int cg = 0; cg < CPL; ++cg) softmax_step<VEC>(mx[cg], sm[cg], acc[cg], zv[i][cg], cv[i][cg]);
+    }
   }
+#pragma unroll
+  for (int cg = 0; cg < CPL; ++cg)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      part[0][wave][lane * W + cg * VEC + v] = mx[cg][v];
+      part[1][wave][lane * W + cg * VEC + v] = sm[cg][v];
+      part[2][wave][lane * W + cg * VEC + v] = acc[cg][v];
+    }
+  __syncthreads();
+  if (wave != 0) return;
+  double th[CPL][VEC / 2];
+  rope_table<VEC, CPL>(a, lane, 64, th);
+  float y[CPL][VEC];
+#pragma unroll
+  for (int cg = 0; cg < CPL; ++cg)
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      const int o = lane * W + cg * VEC + v;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, part[0][w][o]);
+      float S = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = part[0][w][o];
+        if (mw == -INFINITY) continue;  // the wave saw no rows
+        const float sc = __expf(mw - M);
+        S += part[1][w][o] * sc;
+        A += part[2][w][o] * sc;
+      }
+      y[cg][v] = A / S;
+    }
+  finish_entry<T, VEC, CPL>(a, y, lane, 64, th, a.pos0 + e * a.m, (T*)a.out + ((int64_t)b * a.out_ld + e) * a.c);
 }
 
 // FP8 KV storage of compressed entries ("Paper Breakdown: DeepSeek-V4", §2.3.4
@@ -252,18 +438,42 @@ __global__ __launch_bounds__(256) void quantize_kv_fp8_kernel(const T* x, int64_
   if (lane == 0) scales[(int64_t)b * out_ld + r] = ldexpf(1.f, e);
 }
 
+template <typename T, int VEC, int CPL>
+static void launch_compress_t(CompressArgs& a, int batch, hipStream_t st) {
+  const int groups = a.c / VEC;
+  int lpe = 1;
+  while (lpe < groups && lpe < 64) lpe <<= 1;
+  a.lpe = lpe;
+  const int rows = a.csa ? 2 * a.m : a.m;
+  const int64_t n_tot = (int64_t)a.n_out * batch;
+  const int gpw = 64 / lpe;
+  if (rows > 32) {
+    constexpr int NW = 64 / (CPL * VEC) >= 4 ? 64 / (CPL * VEC) : 4;
+    hipLaunchKernelGGL((compress_block_kernel<T, VEC, CPL, NW>), dim3((unsigned)a.n_out, (unsigned)batch),
+                       dim3(NW * 64), 0, st, a);
+    return;
+  }
+  // the row and pool kernels take entries (b, e) as one index over batch * n_out, grid-strided
+  a.batch = batch;
+  const int epl = rows == 1 ? 4 : 1;
+  const int64_t waves = ceil_div(ceil_div(n_tot, epl), gpw);
+  const int64_t wgs = std::min<int64_t>(ceil_div(waves, 4), 2048);
+  if (rows == 1)
+    hipLaunchKernelGGL((compress_rows_kernel<T, VEC, CPL, 4>), dim3((unsigned)wgs), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((compress_pool_kernel<T, VEC, CPL>), dim3((unsigned)wgs), dim3(256), 0, st, a);
+}
+
 static int launch_compress(CompressArgs& a, int batch, int dtype, hipStream_t st) {
   if (a.n_out == 0 || batch == 0) return CSKV_OK;
-  const int VEC = dtype == CSKV_BF16 ? 8 : 4;
-  const int CL = a.c / VEC;
-  int clp = 1;
-  while (clp < CL) clp <<= 1;
-  a.clp = clp;
-  dim3 grid(a.n_out, batch), block(256);
-  if (dtype == CSKV_BF16)
-    hipLaunchKernelGGL((compress_kernel<bf16, 8>), grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL((compress_kernel<float, 4>), grid, block, 0, st, a);
+  if (dtype == CSKV_BF16) {
+    if (a.c <= 512) launch_compress_t<bf16, 8, 1>(a, batch, st);
+    else launch_compress_t<bf16, 8, 2>(a, batch, st);
+  } else {
+    if (a.c <= 256) launch_compress_t<float, 4, 1>(a, batch, st);
+    else if (a.c <= 512) launch_compress_t<float, 4, 2>(a, batch, st);
+    else launch_compress_t<float, 4, 4>(a, batch, st);
+  }
   return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
 }
 

@@ -27,17 +27,23 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
 
 
 def assert_storage_close(gpu: np.ndarray, exact: np.ndarray, dtype: str, what: str, rtol_f32=1e-5):
-    """bf16: within one bf16 ulp of the exact (fp64) value.
+    """bf16: within one bf16 ulp of the exact (fp64) value, plus 2**-17 of the RMS of its row.
 
     f32: within 1e-5 of (|x| + RMS of its row). A compressed entry is a
     weighted sum of up to m' rows; its fp32 rounding error scales with the
     magnitude of the summed terms, i.e. the row's scale, not with the
-    (possibly cancelled) element itself.
+    (possibly cancelled) element itself. In bf16 the final rounding adds at
+    most half an ulp of the result; the fp32 error before it (a few dozen
+    fp32 ulps of the row's scale, 2**-17 ~ 64 * 2**-23) matters only where a
+    channel's weighted sum cancels to far below the terms (about one element
+    in 4e5 on N(0,1) streams).
     """
     err = np.abs(gpu - exact)
     if dtype == "bf16":
-        bad = err > bf16_ulp(exact) * (1 + 1e-9)
-        assert not bad.any(), f"{what}: {bad.sum()} of {bad.size} elements beyond 1 bf16 ulp, max err {err.max():.3g}"
+        rms = np.sqrt(np.mean(exact * exact, axis=-1, keepdims=True))
+        bad = err > bf16_ulp(exact) * (1 + 1e-9) + 2.0 ** -17 * rms
+        assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} elements beyond 1 bf16 ulp + 2^-17 row rms, "
+                               f"max err {err.max():.3g}")
     else:
         rms = np.sqrt(np.mean(exact * exact, axis=-1, keepdims=True))
         bad = err > rtol_f32 * (np.abs(exact) + rms)

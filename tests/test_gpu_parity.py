@@ -36,7 +36,8 @@ def gen(seed, name, shape, dtype="bf16", std=1.0):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("c,m,T,pos0,norm,rope", [
     (64, 4, 203, 0, True, 16), (512, 4, 1000, 0, True, 64), (128, 4, 77, 96, False, 0),
-    (512, 4, 64, 4096, True, 64), (32 * 8, 2, 9, 0, True, 8), (64, 1, 33, 0, False, 0)])
+    (512, 4, 64, 4096, True, 64), (32 * 8, 2, 9, 0, True, 8), (64, 1, 33, 0, False, 0),
+    (96, 4, 130, 8, True, 6), (512, 20, 100, 40, True, 64)])
 def test_csa_compress(dtype, c, m, T, pos0, norm, rope):
     say("csa_compress", dtype, c, m, T, pos0, norm, rope)
     bt = 2
@@ -57,7 +58,8 @@ def test_csa_compress(dtype, c, m, T, pos0, norm, rope):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("c,m,T,pos0,withZ,norm,rope", [
     (512, 128, 300, 0, True, True, 64), (512, 128, 1024, 128 * 7, True, True, 64), (64, 16, 50, 0, False, True, 16),
-    (512, 1, 37, 1000, False, True, 64), (128, 1, 5, 0, True, False, 0), (512, 4096, 4096, 0, True, True, 64)])
+    (512, 1, 37, 1000, False, True, 64), (128, 1, 5, 0, True, False, 0), (512, 4096, 4096, 0, True, True, 64),
+    (1024, 1, 9, 3, False, True, 10), (1024, 64, 200, 128, True, True, 64), (40, 8, 100, 16, True, True, 2)])
 def test_hca_compress(dtype, c, m, T, pos0, withZ, norm, rope):
     say("hca_compress", dtype, c, m, T, pos0, withZ, norm, rope)
     bt = 2
