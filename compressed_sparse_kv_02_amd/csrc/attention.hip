@@ -58,6 +58,7 @@ struct AttnArgs {
   int64_t Tq, N, pos0, win_pos0, W;
   int m, k, w, H, D, mode, apply_q_norm, rope_dims, rope_on_output, n_splits;
   float eps, rope_base, scale_log2;
+  RopeTable rope;  // theta of the first rotary pairs (host fp64)
 };
 
 __device__ __forceinline__ int64_t visible_n(int64_t t, int m, int64_t N) {
@@ -549,47 +550,72 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
   }
 }
 
-// Merge split partials in split order, add the sink, normalise, de-rotate.
+// Merge split partials in split order, add the sink, normalise, de-rotate. One workgroup per
+// (query, head): thread s reads split s's (max, sum), the maximum and the weighted sum are
+// block reductions in a fixed order, and each thread sums its two output dims over the splits
+// with eight partial loads in flight.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
   __shared__ float wsplit[256];
+  __shared__ float red[4];
   __shared__ float scal[2];
   const int64_t row = blockIdx.x;  // b*Tq + j
   const int h = blockIdx.y;
   const int D = a.D;
   const int S = a.n_splits;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t j = row % a.Tq;
   const int64_t t = a.pos0 + j;
   const float* pm = a.part_ml + (row * S * a.H) * 2;
-  if (threadIdx.x == 0) {
-    const float z = a.sink ? a.sink[h] * 1.4426950408889634f : -INFINITY;
-    float M = z;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, pm[(s * a.H + h) * 2]);
-    float lt = (z == -INFINITY) ? 0.f : exp2f(z - M);
-    for (int s = 0; s < S; ++s) {
-      const float ms = pm[(s * a.H + h) * 2];
-      const float w = ms == -INFINITY ? 0.f : exp2f(ms - M);
-      wsplit[s] = w;
-      lt += w * pm[(s * a.H + h) * 2 + 1];
-    }
+  const float z = a.sink ? a.sink[h] * 1.4426950408889634f : -INFINITY;
+  float ms = -INFINITY, ls = 0.f;
+  if (tid < S) {
+    ms = pm[(tid * a.H + h) * 2];
+    ls = pm[(tid * a.H + h) * 2 + 1];
+  }
+  float M = wave_max(ms);
+  if (lane == 0) red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])), z);
+  const float w = (tid < S && ms != -INFINITY) ? exp2f(ms - M) : 0.f;
+  wsplit[tid] = w;
+  float lw = wave_sum(w * ls);
+  __syncthreads();  // red[] read above by every thread before it is reused
+  if (lane == 0) red[wave] = lw;
+  __syncthreads();
+  if (tid == 0) {
+    const float lt = ((red[0] + red[1]) + (red[2] + red[3])) + (z == -INFINITY ? 0.f : exp2f(z - M));
     scal[0] = lt > 0.f ? 1.f / lt : 0.f;
     if (a.lse) a.lse[row * a.H + h] = (M + log2f(lt)) * 0.6931471805599453f;
   }
   __syncthreads();
   const float inv = scal[0];
   const int rstart = D - a.rope_dims;
-  for (int d = 2 * threadIdx.x; d < D; d += 2 * blockDim.x) {
+  for (int d = 2 * tid; d < D; d += 2 * blockDim.x) {
+    const float* po = a.part_o + (row * S * a.H + h) * (int64_t)D + d;
+    const int64_t sstride = (int64_t)a.H * D;
     float x0 = 0.f, x1 = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float* po = a.part_o + ((row * S + s) * a.H + h) * (int64_t)D + d;
-      x0 += po[0] * wsplit[s];
-      x1 += po[1] * wsplit[s];
+    int s = 0;
+    for (; s + 8 <= S; s += 8) {
+      float2 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float2*>(po + (s + u) * sstride);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        x0 += v[u].x * wsplit[s + u];
+        x1 += v[u].y * wsplit[s + u];
+      }
+    }
+    for (; s < S; ++s) {
+      const float2 v = *reinterpret_cast<const float2*>(po + s * sstride);
+      x0 += v.x * wsplit[s];
+      x1 += v.y * wsplit[s];
     }
     x0 *= inv;
     x1 *= inv;
     if (a.rope_on_output && a.rope_dims > 0 && d >= rstart) {
       float cs, sn;
-      rope_cos_sin(-t, (d - rstart) >> 1, a.rope_dims, a.rope_base, &cs, &sn);
+      rope_cos_sin_t(a.rope, -t, (d - rstart) >> 1, a.rope_dims, a.rope_base, &cs, &sn);
       const float y0 = x0 * cs - x1 * sn, y1 = x0 * sn + x1 * cs;
       x0 = y0;
       x1 = y1;
@@ -645,7 +671,7 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
   const int rstart = D - a.rope_dims;
   for (int d = rstart + 2 * tid; a.rope_dims > 0 && d < D; d += 512) {
     float cs, sn;
-    rope_cos_sin(t, (d - rstart) >> 1, a.rope_dims, a.rope_base, &cs, &sn);
+    rope_cos_sin_t(a.rope, t, (d - rstart) >> 1, a.rope_dims, a.rope_base, &cs, &sn);
     const float x0 = qs[d], x1 = qs[d + 1];
     qs[d] = x0 * cs - x1 * sn;
     qs[d + 1] = x0 * sn + x1 * cs;
@@ -706,7 +732,7 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
   __syncthreads();
   for (int d = rstart + 2 * tid; a.rope_on_output && a.rope_dims > 0 && d < D; d += 512) {
     float cs, sn;
-    rope_cos_sin(-t, (d - rstart) >> 1, a.rope_dims, a.rope_base, &cs, &sn);
+    rope_cos_sin_t(a.rope, -t, (d - rstart) >> 1, a.rope_dims, a.rope_base, &cs, &sn);
     const float x0 = qs[d], x1 = qs[d + 1];
     qs[d] = x0 * cs - x1 * sn;
     qs[d + 1] = x0 * sn + x1 * cs;
@@ -842,6 +868,7 @@ static AttnArgs make_args(int mode, const void* q, const void* kv, const int32_t
   a.m = m; a.k = k; a.w = w; a.H = H; a.D = d; a.mode = mode; a.apply_q_norm = apply_q_norm;
   a.rope_dims = rope_dims; a.rope_on_output = rope_on_output; a.n_splits = 1;
   a.eps = eps; a.rope_base = rope_base;
+  fill_rope_table(a.rope, rope_base, rope_dims);
   const float sc = scale > 0.f ? scale : 1.0f / sqrtf((float)d);
   a.scale_log2 = sc * 1.4426950408889634f;
   return a;

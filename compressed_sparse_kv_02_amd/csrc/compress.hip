@@ -21,9 +21,9 @@
 //    entry, its waves take interleaved rows, and one wave merges their
 //    partial softmaxes from LDS in wave order.
 // No kernel uses an atomic; every reduction has a fixed order, so results
-// are deterministic. Rotary angles: each lane forms r = base^(-2/rope_dims)
-// once (fp64) and the pair angles theta_j = r^j by products, then the
-// angle pos * theta_j is reduced modulo 2 pi in fp64 before an fp32 sincos.
+// are deterministic. Rotary angles: each lane takes theta_j = base^(-2j/rope_dims)
+// from the host's fp64 table (kernel argument), and the angle pos * theta_j
+// is reduced modulo 2 pi in fp64 before an fp32 sincos.
 #include <algorithm>
 
 #include "device_common.h"
@@ -48,17 +48,8 @@ struct CompressArgs {
   float eps, rope_base;
   int lpe;    // lanes per entry (power of two <= 64)
   int batch;  // sequences (the row and pool kernels stride over batch * n_out entries)
+  RopeTable rope;  // theta of the first rotary pairs (host fp64)
 };
-
-// Rotary angle of pair j: theta_j = r^j with r = base^(-2/rope_dims), by binary powering (fp64).
-__device__ __forceinline__ double rope_theta(double r, int j) {
-  double t = 1.0, x = r;
-  for (int e = j; e > 0; e >>= 1) {
-    if (e & 1) t *= x;
-    x *= x;
-  }
-  return t;
-}
 
 __device__ __forceinline__ void rope_apply(double theta, int64_t pos, float& x0, float& x1) {
   const double inv_two_pi = 0.15915494309189533576888376337251;
@@ -77,18 +68,14 @@ __device__ __forceinline__ void rope_apply(double theta, int64_t pos, float& x0,
 template <int VEC, int CPL>
 __device__ __forceinline__ void rope_table(const CompressArgs& a, int gi, int LPE, double (&th)[CPL][VEC / 2]) {
   const int rstart = a.c - a.rope_dims;
-  const bool any = a.rope_dims > 0 && (gi + LPE * (CPL - 1)) * VEC + VEC > rstart;
-  const double r = any ? pow((double)a.rope_base, -2.0 / (double)a.rope_dims) : 0.0;
 #pragma unroll
   for (int cg = 0; cg < CPL; ++cg) {
     const int ch0 = (gi + LPE * cg) * VEC;
-    const int jf = (ch0 >= rstart ? ch0 - rstart : 0) >> 1;  // first rotated pair of the group
-    double t = (any && ch0 + VEC > rstart) ? rope_theta(r, jf) : 0.0;
 #pragma unroll
     for (int p = 0; p < VEC / 2; ++p) {
-      const bool rot = ch0 + 2 * p >= rstart;
-      th[cg][p] = rot ? t : 0.0;
-      if (rot) t *= r;
+      const int ch = ch0 + 2 * p;
+      th[cg][p] = (a.rope_dims > 0 && ch >= rstart && ch < a.c)
+                      ? rope_theta_of(a.rope, (ch - rstart) >> 1, a.rope_dims, a.rope_base) : 0.0;
     }
   }
 }
@@ -455,11 +442,15 @@ static void launch_compress_t(CompressArgs& a, int batch, hipStream_t st) {
   }
   // the row and pool kernels take entries (b, e) as one index over batch * n_out, grid-strided
   a.batch = batch;
-  const int epl = rows == 1 ? 4 : 1;
+  // window rows: four per lane group in flight for long calls; one each when the call is short
+  // (decode), so that the rows' dependent epilogues run in parallel groups
+  const int epl = rows == 1 && n_tot > 4096 ? 4 : 1;
   const int64_t waves = ceil_div(ceil_div(n_tot, epl), gpw);
   const int64_t wgs = std::min<int64_t>(ceil_div(waves, 4), 2048);
-  if (rows == 1)
+  if (rows == 1 && epl == 4)
     hipLaunchKernelGGL((compress_rows_kernel<T, VEC, CPL, 4>), dim3((unsigned)wgs), dim3(256), 0, st, a);
+  else if (rows == 1)
+    hipLaunchKernelGGL((compress_rows_kernel<T, VEC, CPL, 1>), dim3((unsigned)wgs), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((compress_pool_kernel<T, VEC, CPL>), dim3((unsigned)wgs), dim3(256), 0, st, a);
 }
@@ -516,6 +507,7 @@ extern "C" int csa_compress(const void* Ca, const void* Cb, const void* Za, cons
   a.prev_Cb = prev_Cb; a.prev_Zb = prev_Zb; a.out = out; a.norm_w = norm_w;
   a.T = T; a.pos0 = pos0; a.out_ld = out_ld; a.c = c; a.m = m; a.n_out = (int)n_out; a.csa = 1;
   a.apply_norm = apply_norm; a.rope_dims = rope_dims; a.eps = eps; a.rope_base = rope_base;
+  fill_rope_table(a.rope, rope_base, rope_dims);
   return launch_compress(a, batch, dtype, (hipStream_t)stream);
 }
 
@@ -538,6 +530,7 @@ extern "C" int hca_compress(const void* C, const void* Z, const void* B, int bat
   a.Ca = C; a.Za = Z; a.B = B; a.out = out; a.norm_w = norm_w;
   a.T = T; a.pos0 = pos0; a.out_ld = out_ld; a.c = c; a.m = m; a.n_out = (int)n_out; a.csa = 0;
   a.apply_norm = apply_norm; a.rope_dims = rope_dims; a.eps = eps; a.rope_base = rope_base;
+  fill_rope_table(a.rope, rope_base, rope_dims);
   return launch_compress(a, batch, dtype, (hipStream_t)stream);
 }
 

@@ -128,15 +128,42 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Rotary angle for pair j of a rope_dims-wide block at position pos:
-// pos * base^(-2j/rope_dims), formed and reduced in fp64 so that positions up
-// to 2^20 and beyond keep full fp32 accuracy in cos/sin.
-__device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, int rope_dims, float base, float* c,
-                                             float* s) {
+// Rotary pair angles theta_j = base^(-2j / rope_dims) of the first ROPE_TABLE pairs, formed on
+// the host in fp64 and passed in the kernel arguments, so that kernels evaluate no fp64 power
+// (a long dependent chain) for RoPE widths up to 2 * ROPE_TABLE; wider ones fall back to it.
+constexpr int ROPE_TABLE = 64;
+struct RopeTable {
+  double th[ROPE_TABLE];
+};
+
+__host__ inline void fill_rope_table(RopeTable& t, float base, int rope_dims) {
+  for (int j = 0; j < ROPE_TABLE; ++j)
+    t.th[j] = (rope_dims > 0 && j < rope_dims / 2) ? __builtin_pow((double)base, -2.0 * j / (double)rope_dims) : 0.0;
+}
+
+__device__ __forceinline__ double rope_theta_of(const RopeTable& t, int j, int rope_dims, float base) {
+  return j < ROPE_TABLE ? t.th[j] : pow((double)base, -2.0 * j / (double)rope_dims);
+}
+
+// Rotary angle for pair j of a rope_dims-wide block at position pos: pos * base^(-2j/rope_dims),
+// formed and reduced in fp64 on the device (kernels at their register limit use this form: the
+// table lookup below changed their register allocation).
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, int j, int rope_dims, float base, float* c, float* s) {
   const double theta = pow((double)base, -2.0 * j / (double)rope_dims);
   double a = (double)pos * theta;
   const double two_pi = 6.283185307179586476925286766559;
   a = a - two_pi * rint(a / two_pi);  // |a| <= pi, exact to ~1e-16 relative of pos * theta
+  sincosf((float)a, s, c);
+}
+
+// cos / sin of pos * theta_j, the angle reduced modulo 2 pi in fp64 (positions to 2^20 and beyond
+// keep full fp32 accuracy).
+__device__ __forceinline__ void rope_cos_sin_t(const RopeTable& t, int64_t pos, int j, int rope_dims, float base,
+                                               float* c, float* s) {
+  const double inv_two_pi = 0.15915494309189533576888376337251;
+  const double two_pi = 6.283185307179586476925286766559;
+  double a = (double)pos * rope_theta_of(t, j, rope_dims, base);
+  a = __builtin_fma(-two_pi, rint(a * inv_two_pi), a);
   sincosf((float)a, s, c);
 }
 

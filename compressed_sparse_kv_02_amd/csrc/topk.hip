@@ -57,6 +57,41 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wsum, int& total
   return pre + incl - v;
 }
 
+// Exclusive prefix count of a flag over the workgroup (ballots and popcounts: no shuffle chain);
+// also returns the total.
+__device__ __forceinline__ int block_exclusive_count(bool f, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t m = __ballot(f);
+  const int before = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[wave] = __popcll(m);
+  __syncthreads();
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < TOPK_THREADS / 64; ++w) {
+    const int x = wsum[w];
+    if (w < wave) pre += x;
+    tot += x;
+  }
+  __syncthreads();
+  total = tot;
+  return pre + before;
+}
+
+// Four consecutive entries per lane, in lane order: how many flagged entries precede this lane's
+// first one in the wave, and how many the wave holds (four ballots, no shuffle chain).
+__device__ __forceinline__ void wave_count4(const bool (&fl)[4], int& before, int& tot) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  before = 0;
+  tot = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint64_t m = __ballot(fl[e]);
+    before += __popcll(m & below);
+    tot += __popcll(m);
+  }
+}
+
 struct TopkShared {
   int hist[2048];
   int wsum[TOPK_THREADS / 64];
@@ -117,13 +152,13 @@ __device__ void ordered_pick(KeyAt key_at, Emit emit, int64_t n, uint32_t tau, i
     const int64_t s = base + tid;
     uint32_t key = 0;
     if (s < n) key = key_at(s);
-    const int gt = (s < n && key > tau) ? 1 : 0;
-    const int eq = (s < n && key == tau) ? 1 : 0;
+    const bool gt = s < n && key > tau;
+    const bool eq = s < n && key == tau;
     int eq_tot;
-    const int eq_rank = block_exclusive_scan(eq, sh.wsum, eq_tot);
-    const int sel = gt | (eq && (eq_taken + eq_rank) < need ? 1 : 0);
+    const int eq_rank = block_exclusive_count(eq, sh.wsum, eq_tot);
+    const bool sel = gt || (eq && (eq_taken + eq_rank) < need);
     int sel_tot;
-    const int pos = block_exclusive_scan(sel, sh.wsum, sel_tot);
+    const int pos = block_exclusive_count(sel, sh.wsum, sel_tot);
     if (sel) emit(written + pos, s);
     eq_taken += eq_tot;
     written += sel_tot;
@@ -223,22 +258,18 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
         const int64_t s0 = base + u * 256 + 4 * lane;
         const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
         uint32_t kk4[4];
-        int f = 0;
+        bool fl[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           kk4[e] = score_key(vv[e]);
-          if (s0 + e < hi && kk4[e] >= tau0) ++f;
+          fl[e] = s0 + e < hi && kk4[e] >= tau0;
         }
-        int incl = f;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int t = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += t;
-        }
-        int pos = cnt + incl - f;
+        int before, tot;
+        wave_count4(fl, before, tot);
+        int pos = cnt + before;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (s0 + e < hi && kk4[e] >= tau0) {
+          if (fl[e]) {
             if (pos < SEG) {
               wkey[pos] = kk4[e];
               widx[pos] = (int32_t)(s0 + e);
@@ -246,7 +277,7 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_select(IdxArgs a) {
             ++pos;
           }
         }
-        cnt += __shfl(incl, 63, 64);
+        cnt += tot;
       }
     }
     if (lane == 0) sh.wcnt[wave] = cnt;
@@ -419,6 +450,254 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge(IdxArgs a) {
                tau, need, sh);
 }
 
+// Few long rows of at most BM_MAX_BLOCKS blocks of 32 entries (decode at 1M context: 8 rows of
+// 262144): selection through block maxima.
+//  * topk_blockmax (many workgroups): the largest key of every block of 32 entries of the row
+//    (entries past V count as absent) goes to the row's workspace.
+//  * topk_bm_select (one workgroup per row): tau_b = a lower bound of the k-th largest block
+//    maximum (0 when the row has at most k blocks). Each block maximum is an entry's key, so at
+//    least k entries reach tau_b: the k-th largest key of the row is >= tau_b, and every entry
+//    at or above it sits in a block whose maximum is >= tau_b. The entries >= tau_b of those
+//    blocks (about k of them on continuous scores) are gathered in index order, and the exact
+//    top-k among them (radix select + in-order pick) is the row's exact top-k, ties included.
+//    Should they overflow LDS (many equal scores), the row falls back to the exact select over
+//    global memory.
+constexpr int BM_MAX_BLOCKS = 8192;
+constexpr int BM_CAP = 8192;  // gathered candidates held in LDS
+
+__global__ __launch_bounds__(256) void topk_blockmax(IdxArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t jr = blockIdx.y;
+  const int b = blockIdx.z;
+  const int64_t V = visible_entries(a.pos0 + a.row0 + jr, a.m, a.N);
+  if (V <= a.k) return;
+  const int nb = (int)((V + 31) / 32);
+  const float* row = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
+  uint32_t* bm = reinterpret_cast<uint32_t*>(a.sel_ws + ((int64_t)b * a.nrows + jr) * TOPK_SEL_STRIDE);
+  // this workgroup: blocks [256 x, 256 x + 256); wave w: 64 of them, 8 per load (8 lanes per block)
+  const int blk0 = blockIdx.x * 256 + wave * 64;
+  float4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t e0 = (int64_t)(blk0 + 8 * i) * 32 + 4 * lane;  // rows are padded to 64 entries
+    v[i] = e0 < V ? *reinterpret_cast<const float4*>(row + e0) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t e0 = (int64_t)(blk0 + 8 * i) * 32 + 4 * lane;
+    const float vv[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t mk = 0;  // absent entries: below every score's key
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e0 + e < V) mk = max(mk, score_key(vv[e]));
+    mk = max(mk, (uint32_t)__shfl_xor((int)mk, 1, 64));
+    mk = max(mk, (uint32_t)__shfl_xor((int)mk, 2, 64));
+    mk = max(mk, (uint32_t)__shfl_xor((int)mk, 4, 64));
+    const int blk = blk0 + 8 * i + (lane >> 3);
+    if ((lane & 7) == 0 && blk < nb) bm[blk] = mk;
+  }
+}
+
+// A lower bound of the kk-th largest of the keys held 16 per thread (bk; 0 = absent), 1 <= kk <=
+// the number present. The keys between the smallest and the largest present key share every bit
+// above the highest bit in which those two differ (hb), so one 2048-bin histogram of the 11 bits
+// below and at hb spreads them (few collisions on the same LDS counter); the lower edge of the bin
+// that holds the kk-th largest is <= it, and within 2^(hb - 10) of it.
+__device__ uint32_t kth_lower_bound(const uint32_t (&bk)[16], int kk, TopkShared& sh) {
+  constexpr int NWAVE = TOPK_THREADS / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t mx = 0u, mn = 0xffffffffu;
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if (bk[q]) {
+      mx = max(mx, bk[q]);
+      mn = min(mn, bk[q]);
+    }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+  }
+  if (lane == 0) {
+    sh.wsum[wave] = (int)mx;
+    sh.wcnt[wave] = (int)mn;
+  }
+  for (int i = tid; i < 2048; i += TOPK_THREADS) sh.hist[i] = 0;
+  __syncthreads();
+  mx = 0u;
+  mn = 0xffffffffu;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    mx = max(mx, (uint32_t)sh.wsum[w]);
+    mn = min(mn, (uint32_t)sh.wcnt[w]);
+  }
+  if (mx == mn) return mx;  // one distinct key: it is the kk-th largest
+  const int hb = 31 - __clz(mx ^ mn);
+  const int shift = hb >= 10 ? hb - 10 : 0;
+  const uint32_t high = hb >= 31 ? 0u : (mx >> (hb + 1)) << (hb + 1);  // the shared bits above hb
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if (bk[q]) atomicAdd(&sh.hist[(bk[q] >> shift) & 2047u], 1);
+  __syncthreads();
+  constexpr int BPT = 2048 / TOPK_THREADS;
+  int cnt[BPT], loc = 0;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    cnt[q] = sh.hist[2047 - (tid * BPT + q)];
+    loc += cnt[q];
+  }
+  int total;
+  int above = block_exclusive_scan(loc, sh.wsum, total);
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    if (above < kk && kk <= above + cnt[q]) sh.sel_bin = 2047 - (tid * BPT + q);
+    above += cnt[q];
+  }
+  __syncthreads();
+  const uint32_t lb = high | ((uint32_t)sh.sel_bin << shift);
+  __syncthreads();
+  return lb;
+}
+
+__global__ __launch_bounds__(TOPK_THREADS) void topk_bm_select(IdxArgs a) {
+  static_assert(BM_MAX_BLOCKS == 16 * TOPK_THREADS, "16 block maxima per thread");
+  __shared__ int32_t cblk[BM_MAX_BLOCKS];
+  __shared__ uint32_t ckey[BM_CAP];
+  __shared__ int32_t cidx[BM_CAP];
+  __shared__ TopkShared sh;
+  constexpr int NWAVE = TOPK_THREADS / 64;
+  constexpr int SEG = BM_CAP / NWAVE;
+  constexpr int GB = 16;  // gather loads in flight per lane (8 blocks of 32 entries per wave load)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t jr = blockIdx.x;
+  const int b = blockIdx.y;
+  const int k = a.k;
+  int32_t* out = a.out + ((int64_t)b * a.Tq + a.row0 + jr) * k;
+  const int64_t V = visible_entries(a.pos0 + a.row0 + jr, a.m, a.N);
+  if (V <= k) {
+    for (int i = tid; i < k; i += TOPK_THREADS) out[i] = i < V ? i : -1;
+    return;
+  }
+  const float* row = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
+  const uint32_t* bm = reinterpret_cast<const uint32_t*>(a.sel_ws + ((int64_t)b * a.nrows + jr) * TOPK_SEL_STRIDE);
+  const int nb = (int)((V + 31) / 32);
+  // thread t holds block maxima 16 t .. 16 t + 15 (4 vector loads; past nb: absent)
+  uint32_t bk[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint4 v = *reinterpret_cast<const uint4*>(bm + 16 * tid + 4 * q);
+    bk[4 * q] = v.x;
+    bk[4 * q + 1] = v.y;
+    bk[4 * q + 2] = v.z;
+    bk[4 * q + 3] = v.w;
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if (16 * tid + q >= nb) bk[q] = 0u;
+  // tau_b <= the kb-th largest block maximum (0: every block, when the row has at most k blocks)
+  const int kb = k < nb ? k : nb;
+  const uint32_t tau_b = kb == nb ? 0u : kth_lower_bound(bk, kb, sh);
+  // candidate blocks (maximum >= tau_b) in index order
+  int f = 0;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) f += (16 * tid + q < nb && bk[q] >= tau_b) ? 1 : 0;
+  int n_cb;
+  int pos = block_exclusive_scan(f, sh.wsum, n_cb);
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+    if (16 * tid + q < nb && bk[q] >= tau_b) cblk[pos++] = 16 * tid + q;
+  __syncthreads();
+  // gather the entries >= tau_b of the candidate blocks: wave w takes candidate blocks
+  // [c0, c1), 8 per wave load (8 lanes per block, 4 entries per lane, so lane order is index
+  // order), GB loads issued before any is used, and appends to its own LDS segment
+  const int L = (n_cb + NWAVE - 1) / NWAVE;
+  const int c0 = wave * L, c1 = c0 + L < n_cb ? c0 + L : n_cb;
+  uint32_t* wkey = ckey + wave * SEG;
+  int32_t* widx = cidx + wave * SEG;
+  int cnt = 0;
+  for (int c = c0; c < c1; c += 8 * GB) {
+    float4 v[GB];
+    int64_t e0[GB];
+#pragma unroll
+    for (int u = 0; u < GB; ++u) {
+      const int cc = c + 8 * u + (lane >> 3);
+      e0[u] = cc < c1 ? (int64_t)cblk[cc] * 32 + 4 * (lane & 7) : V;
+      v[u] = e0[u] < V ? *reinterpret_cast<const float4*>(row + e0[u]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < GB; ++u) {
+      const float vv[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t kk4[4];
+      bool fl[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kk4[e] = score_key(vv[e]);
+        fl[e] = e0[u] + e < V && kk4[e] >= tau_b;
+      }
+      int before, tot;
+      wave_count4(fl, before, tot);
+      int p = cnt + before;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (fl[e]) {
+          if (p < SEG) {
+            wkey[p] = kk4[e];
+            widx[p] = (int32_t)(e0[u] + e);
+          }
+          ++p;
+        }
+      }
+      cnt += tot;
+    }
+  }
+  if (lane == 0) sh.wcnt[wave] = cnt;
+  __syncthreads();
+  int cw[NWAVE], off[NWAVE], total = 0;
+  bool overflow = false;
+#pragma unroll
+  for (int w = 0; w < NWAVE; ++w) {
+    cw[w] = sh.wcnt[w];
+    off[w] = total;
+    total += cw[w];
+    overflow |= cw[w] > SEG;
+  }
+  if (overflow || total < k) {  // (total >= k always holds without overflow)
+    select_row_global(row, V, k, out, sh);
+    return;
+  }
+  // segments -> one contiguous list in index order
+  constexpr int SPT = BM_CAP / TOPK_THREADS;
+  uint32_t kr[SPT];
+  int32_t ir[SPT];
+  int dst[SPT];
+#pragma unroll
+  for (int q = 0; q < SPT; ++q) {
+    const int slot = q * TOPK_THREADS + tid;
+    const int w = slot / SEG, e = slot - w * SEG;
+    dst[q] = -1;
+#pragma unroll
+    for (int ww = 0; ww < NWAVE; ++ww)
+      if (ww == w && e < cw[ww]) dst[q] = off[ww] + e;
+    if (dst[q] >= 0) {
+      kr[q] = ckey[slot];
+      ir[q] = cidx[slot];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < SPT; ++q)
+    if (dst[q] >= 0) {
+      ckey[dst[q]] = kr[q];
+      cidx[dst[q]] = ir[q];
+    }
+  __syncthreads();
+  uint32_t tau;
+  int need;
+  radix_select([&](int64_t s) { return ckey[s]; }, total, k, sh, tau, need);
+  ordered_pick([&](int64_t s) { return ckey[s]; }, [&](int p, int64_t s) { out[p] = cidx[s]; }, total, tau, need,
+               sh);
+}
+
 // ----------------------------------------------------------------------------
 // Host side
 // ----------------------------------------------------------------------------
@@ -452,7 +731,15 @@ int launch_select(IdxArgs& a, int batch, void* sel_ws, size_t sel_bytes, hipStre
   if (vmax > a.N) vmax = a.N;
   SplitPlan sp;
   const int64_t rows = (int64_t)batch * a.nrows;
-  if (sel_ws && plan_split(rows, vmax, a.k, sp) && sel_bytes >= (size_t)(rows * TOPK_SEL_STRIDE)) {
+  const bool ws_ok = sel_ws && plan_split(rows, vmax, a.k, sp) && sel_bytes >= (size_t)(rows * TOPK_SEL_STRIDE);
+  if (ws_ok && ceil_div(vmax, (int64_t)32) <= BM_MAX_BLOCKS) {
+    static_assert((int64_t)BM_MAX_BLOCKS * 4 <= TOPK_SEL_STRIDE, "block maxima fit a row's workspace");
+    a.sel_ws = (uint8_t*)sel_ws;
+    hipLaunchKernelGGL(topk_blockmax, dim3((unsigned)ceil_div(ceil_div(vmax, (int64_t)32), (int64_t)256),
+                                           (unsigned)a.nrows, (unsigned)batch),
+                       dim3(256), 0, st, a);
+    hipLaunchKernelGGL(topk_bm_select, dim3((unsigned)a.nrows, (unsigned)batch), dim3(TOPK_THREADS), 0, st, a);
+  } else if (ws_ok) {
     a.sel_ws = (uint8_t*)sel_ws;
     a.part_len = TOPK_SPLIT_CAP;
     a.kp = sp.kp;

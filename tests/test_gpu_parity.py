@@ -155,10 +155,14 @@ def test_indexer_decode_1m_full():
     ("descending", 1, 1, 100000, 1024),  # the top-k sits in the first part: fallback route
     ("ties", 2, 2, 65536, 2048),      # 16 distinct values: ties across parts
     ("equal", 1, 1, 40000, 100),      # one value: the first k indices
+    ("normal", 8, 1, 262144, 1024),   # the decode shape: block maxima, 8192 blocks per row
+    ("normal", 1, 2, 40000, 1024),    # 1250 blocks: the candidate blocks are most of the row
+    ("normal", 1, 2, 300000, 1024),   # more than 8192 blocks: parts + merge
 ])
 def test_topk_split_route(kind, bt, Tq, N, k):
-    """Few long rows go through the two-kernel route (parts + merge); it must equal the
-    one-workgroup-per-row route and the oracle's top-k exactly (same fp32 scores on both sides)."""
+    """Few long rows go through a several-workgroups-per-row route (block maxima up to 8192 blocks of
+    32 entries, parts + merge beyond); it must equal the one-workgroup-per-row route and the oracle's
+    top-k exactly (same fp32 scores on both sides)."""
     say("topk split route", kind, bt, Tq, N, k)
     ld = B.score_ld(N)
     if kind == "normal":
