@@ -38,24 +38,26 @@ PEAK_FP8_FLOPS = 5.0e15
 PEAK_FP4_FLOPS = 10.1e15
 PEAK_HBM_BYTES = 8.0e12
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-# Sources whose kernels the stored counter figures describe; a change to any of
-# them makes those figures stale (reported as null).
-TRAFFIC_SOURCES = ("compressed_sparse_kv_02_amd/csrc/indexer.hip", "compressed_sparse_kv_02_amd/csrc/indexer.h",
-                   "compressed_sparse_kv_02_amd/csrc/device_common.h")
+# The stored counter figures describe the kernels built from these sources; a change to any of
+# them makes the figures stale (reported as null).
+CSRC = os.path.join("compressed_sparse_kv_02_amd", "csrc")
 COPY_PROBE_BYTES = 1 << 30   # plain copy used to calibrate FETCH_SIZE / WRITE_SIZE
+CU_COUNT, SIMD_PER_CU, XCD_COUNT = 256, 4, 8
 
 
 def sources_digest() -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in TRAFFIC_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+    d = os.path.join(ROOT, CSRC)
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
 def load_traffic():
-    """Stored HBM bytes per launch of the scoring kernels, or None when absent or stale."""
+    """Stored per-kernel counter figures, or None when absent or stale."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
@@ -65,50 +67,93 @@ def load_traffic():
     return tr
 
 
-def write_traffic(fetch_csv: str, write_csv: str) -> None:
-    """Turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, WRITE_SIZE, KiB per
-    dispatch) of `bench.py --copy-probe` into HBM bytes per launch of the scoring kernels.
+def traffic_of(tr, kernel: str):
+    """HBM bytes per launch of the stored kernel entry whose name starts with `kernel` (most dispatches)."""
+    if not tr:
+        return None
+    ents = [e for e in tr.get("kernels", []) if e["kernel"].startswith(kernel)]
+    if not ents:
+        return None
+    return max(ents, key=lambda e: e["dispatches"]).get("hbm_bytes_per_launch")
 
-    Each counter is scaled by bytes / counter of the calibration copy (a fp32 negation of
-    COPY_PROBE_BYTES in, COPY_PROBE_BYTES out), so the figures are in the units the copy
-    defines: bytes that crossed from HBM (or the memory-side cache) into L2 and back.
+
+def write_traffic(fetch_csv: str, write_csv: str, mfma_csv=None) -> None:
+    """Turn rocprofv3 --pmc counter_collection.csv files of `bench.py --copy-probe` into per-kernel
+    figures: HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, KiB per dispatch) and, from a third
+    run with SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE, the matrix cores' busy share.
+
+    Each byte counter is scaled by bytes / counter of the calibration copy (a fp32 negation of
+    COPY_PROBE_BYTES in, COPY_PROBE_BYTES out), so the figures are in the units the copy defines:
+    bytes that crossed from HBM (or the memory-side cache) into L2 and back. GRBM_GUI_ACTIVE is
+    summed over the XCDs and SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs, so the busy share is
+    busy / (GUI / XCDs * CUs * SIMDs per CU); GUI / XCDs over the dispatch's duration is its clock.
     """
     import csv
+    import re
     import statistics
 
-    def per_kernel(path, counter):
+    def short(n):
+        return re.sub(r"\(.*$", "", re.sub(r"^void ", "", n)).replace("cskv::", "")
+
+    def per_kernel(path):
         vals = {}
         with open(path) as f:
             for r in csv.DictReader(f):
-                if r["Counter_Name"] != counter:
-                    continue
-                vals.setdefault((r["Kernel_Name"], int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+                key = (short(r["Kernel_Name"]), int(r["Grid_Size"]))
+                ent = vals.setdefault(key, {})
+                ent.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                ent.setdefault("_dur_" + r["Counter_Name"], []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9)
         return vals
 
     out = {"sources_sha256": sources_digest(), "copy_probe_bytes": COPY_PROBE_BYTES}
-    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
-        vals = per_kernel(path, counter)
-        copy = [v for (name, grid), vs in vals.items() if "neg_kernel" in name for v in vs]
-        assert copy, f"no calibration copy dispatch in {path}"
-        kib = statistics.median(copy)
-        factor = COPY_PROBE_BYTES / (kib * 1024.0)
-        out[f"{counter}_copy_kib"] = kib
-        out[f"{counter}_factor"] = factor
-        for tag, tmpl in (("prefill", "indexer_score_mfma<2, 8>"), ("decode", "indexer_score_stream<2, 8>")):
-            vs = [v for (name, grid), xs in vals.items() if tmpl in name for v in xs]
-            assert vs, f"no {tmpl} dispatch in {path}"
-            ent = out.setdefault(f"indexer_score_mfma_{tag}", {})
-            ent[f"{counter}_kib_mean"] = statistics.mean(vs)
-            ent[f"{counter}_dispatches"] = len(vs)
-            ent[f"{counter}_bytes"] = statistics.mean(vs) * 1024.0 * factor
-    for tag in ("prefill", "decode"):
-        ent = out[f"indexer_score_mfma_{tag}"]
-        ent["hbm_bytes_per_launch"] = ent["FETCH_SIZE_bytes"] + ent["WRITE_SIZE_bytes"]
+    runs = {"FETCH_SIZE": per_kernel(fetch_csv), "WRITE_SIZE": per_kernel(write_csv)}
+    for counter, vals in runs.items():
+        copy = [v for (name, grid), cs in vals.items() if "neg_kernel" in name for v in cs.get(counter, [])]
+        assert copy, f"no calibration copy dispatch for {counter}"
+        out[f"{counter}_factor"] = COPY_PROBE_BYTES / (statistics.median(copy) * 1024.0)
+    mf = per_kernel(mfma_csv) if mfma_csv else {}
+    kernels = []
+    ours = ("attn_", "indexer_", "topk_", "compress_", "gemm_", "quantize_")
+    keys = sorted({k for run in runs.values() for k in run if k[0].startswith(ours)})
+    for key in keys:
+        ent = {"kernel": key[0], "grid": key[1]}
+        for counter, vals in runs.items():
+            vs = vals.get(key, {}).get(counter)
+            if vs:
+                ent[f"{counter}_bytes"] = statistics.mean(vs) * 1024.0 * out[f"{counter}_factor"]
+                ent["dispatches"] = len(vs)
+        if "FETCH_SIZE_bytes" in ent and "WRITE_SIZE_bytes" in ent:
+            ent["hbm_bytes_per_launch"] = ent["FETCH_SIZE_bytes"] + ent["WRITE_SIZE_bytes"]
+        m = mf.get(key, {})
+        if m.get("SQ_VALU_MFMA_BUSY_CYCLES") and m.get("GRBM_GUI_ACTIVE"):
+            gui = statistics.mean(m["GRBM_GUI_ACTIVE"]) / XCD_COUNT
+            ent["mfma_busy"] = statistics.mean(m["SQ_VALU_MFMA_BUSY_CYCLES"]) / (gui * CU_COUNT * SIMD_PER_CU)
+            ent["clock_ghz"] = gui / statistics.mean(m["_dur_GRBM_GUI_ACTIVE"]) / 1e9
+            ent["duration_us_under_counters"] = statistics.mean(m["_dur_GRBM_GUI_ACTIVE"]) * 1e6
+        kernels.append(ent)
+    out["kernels"] = kernels
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
     print(json.dumps(out, indent=1))
+
+
+def traffic_summary() -> None:
+    """The stored counter figures as a markdown table (one line per kernel and grid)."""
+    with open(TRAFFIC_FILE) as f:
+        tr = json.load(f)
+    print(f"FETCH_SIZE factor {tr['FETCH_SIZE_factor']:.3f}, WRITE_SIZE factor {tr['WRITE_SIZE_factor']:.3f} "
+          f"(the {tr['copy_probe_bytes'] >> 20} MiB copy); sources sha256 {tr['sources_sha256'][:16]}")
+    print()
+    print("| kernel | grid | dispatches | HBM read MB | HBM write MB | MFMA busy | clock GHz |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    for e in sorted(tr["kernels"], key=lambda e: -e.get("hbm_bytes_per_launch", 0)):
+        mb = f"{100 * e['mfma_busy']:.1f}%" if "mfma_busy" in e else "-"
+        ck = f"{e['clock_ghz']:.2f}" if "clock_ghz" in e else "-"
+        print(f"| `{e['kernel']}` | {e['grid']} | {e.get('dispatches', 0)} | {e.get('FETCH_SIZE_bytes', 0) / 1e6:.1f} "
+              f"| {e.get('WRITE_SIZE_bytes', 0) / 1e6:.1f} | {mb} | {ck} |")
 
 
 def visible_pairs(L) -> int:
@@ -502,11 +547,16 @@ def main():
     ap.add_argument("--no-next-rows", action="store_true", help="skip the low-precision / projection lines")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB copy (counter calibration for --write-traffic)")
-    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write profiles/traffic.json from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--write-traffic", nargs="+", metavar="CSV",
+                    help="write profiles/traffic.json from rocprofv3 --pmc runs (FETCH_SIZE csv, WRITE_SIZE "
+                         "csv[, SQ_VALU_MFMA_BUSY_CYCLES + GRBM_GUI_ACTIVE csv]) and exit")
+    ap.add_argument("--traffic-summary", action="store_true", help="print profiles/traffic.json as a table and exit")
     args = ap.parse_args()
     if args.write_traffic:
         write_traffic(*args.write_traffic)
+        return
+    if args.traffic_summary:
+        traffic_summary()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one MI355X; runs on more than one GPU are not supported "
@@ -532,20 +582,34 @@ def main():
         ev_pool.append(e)
         return e
 
+    def scored(L, t, rec, key):
+        """One layer call; with rec, the scoring kernel is bracketed by events (rec[key])."""
+        LY.compress_step(L, t)
+        if rec is not None and L.kind == "csa":
+            a, b = ev(), ev()
+            a.record()
+            LY.score_step(L, t)
+            b.record()
+            rec[key].append((a, b))
+        else:
+            LY.score_step(L, t)
+        LY.topk_step(L, t)
+        LY.attend_step(L, t)
+
     def step(rec=None):
-        for i, (L, t) in enumerate(zip(prefill, tp)):
-            run_phases(L, t, None if rec is None else rec["pre"][i], ev)
+        for L, t in zip(prefill, tp):
+            scored(L, t, rec, "pre_score")
         if rec is not None:
             m = ev()
             m.record()
             rec["mid"].append(m)
-        for i, (L, t) in enumerate(zip(decode, td)):
-            run_phases(L, t, None if rec is None else rec["dec"][i], ev)
+        for L, t in zip(decode, td):
+            scored(L, t, rec, "dec_score")
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    rec = {"pre": [{} for _ in prefill], "dec": [{} for _ in decode], "mid": []}
+    rec = {"pre_score": [], "dec_score": [], "mid": []}
     starts = []
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -570,25 +634,35 @@ def main():
     n_pre = prefill[0].batch * prefill[0].T
     n_dec = decode[0].batch
     value = (n_pre + n_dec) / (ms / 1e3)
+    # phase breakdown from a separate pass (events around every phase add host gaps between the
+    # short decode kernels, so the timed steps above bracket only the scoring kernels)
+    prec = {"pre": [{} for _ in prefill], "dec": [{} for _ in decode]}
+    for _ in range(3):
+        for i, (L, t) in enumerate(zip(prefill, tp)):
+            run_phases(L, t, prec["pre"][i], ev)
+        for i, (L, t) in enumerate(zip(decode, td)):
+            run_phases(L, t, prec["dec"][i], ev)
+    torch.cuda.synchronize()
     phases = {
         "prefill": [dict(layer=f"{L.kind}{i}", **{k: mean_ms(v) for k, v in r.items()})
-                    for i, (L, r) in enumerate(zip(prefill, rec["pre"]))],
-        "decode": [dict(layer=L.kind, **{k: mean_ms(v) for k, v in r.items()}) for L, r in zip(decode, rec["dec"])],
+                    for i, (L, r) in enumerate(zip(prefill, prec["pre"]))],
+        "decode": [dict(layer=L.kind, **{k: mean_ms(v) for k, v in r.items()}) for L, r in zip(decode, prec["dec"])],
+        "note": "separate pass, every phase bracketed by events (the decode figures include launch gaps)",
     }
 
-    score_ms = mean_ms([p for L, r in zip(prefill, rec["pre"]) if L.kind == "csa" for p in r["score"]])
+    score_ms = mean_ms(rec["pre_score"])
     fl = indexer_flops(prefill[0])
     achieved = fl / (score_ms / 1e3) / 1e12
-    tr = load_traffic() or {}
-    traffic = tr.get("indexer_score_mfma_prefill", {}).get("hbm_bytes_per_launch")
+    tr = load_traffic()
+    traffic = traffic_of(tr, "indexer_score_mfma<2, 8>")
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                 "frac": achieved * 1e12 / PEAK_BF16_FLOPS, "traffic": traffic,
                 "kernel": "indexer_score_mfma<2,8> (prefill CSA layers)", "avg_launch_ms": score_ms,
                 "algorithmic_flops_per_launch": fl}
-    dscore_ms = mean_ms(rec["dec"][0]["score"])
+    dscore_ms = mean_ms(rec["dec_score"])
     db = decode_score_bytes(decode[0])
     dach = db / (dscore_ms / 1e3) / 1e9
-    dtraffic = tr.get("indexer_score_mfma_decode", {}).get("hbm_bytes_per_launch")
+    dtraffic = traffic_of(tr, "indexer_score_stream<2, 8>")
     roofline_dec = {"bound": "hbm", "achieved": dach, "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                     "frac": dach * 1e9 / PEAK_HBM_BYTES, "traffic": dtraffic,
                     "kernel": "indexer_score_stream<2,8> (decode CSA layer)", "avg_launch_ms": dscore_ms,
@@ -599,7 +673,7 @@ def main():
                      "algorithmic_bytes": sb,
                      "what": "the whole decode step (window rows, scoring, top-k, CSA and HCA attention)"}
     dattn = {}
-    for L, r in zip(decode, rec["dec"]):
+    for L, r in zip(decode, prec["dec"]):
         e = 2
         keys = min(L.k, L.N) if L.kind == "csa" else min(L.N, (L.pos0 + 1) // L.m)
         by = L.batch * ((keys + L.w) * L.d * e + 2 * L.H * L.d * e + L.H * 4)
