@@ -80,6 +80,25 @@ __device__ __forceinline__ void rope_table(const CompressArgs& a, int gi, int LP
   }
 }
 
+// RoPE at `pos` on the last rope_dims channels of y (a lane group's channel groups), then store.
+template <typename T, int VEC, int CPL>
+__device__ __forceinline__ void finish_rotate_store(const CompressArgs& a, float (&y)[CPL][VEC], int gi, int LPE,
+                                                    const double (&th)[CPL][VEC / 2], int64_t pos, T* op) {
+  const int groups = a.c / VEC;
+  const int rstart = a.c - a.rope_dims;
+#pragma unroll
+  for (int cg = 0; cg < CPL; ++cg) {
+    const int ch0 = (gi + LPE * cg) * VEC;
+    if (gi + LPE * cg >= groups) continue;
+    if (a.rope_dims > 0 && ch0 + VEC > rstart) {
+#pragma unroll
+      for (int p = 0; p < VEC / 2; ++p)
+        if (ch0 + 2 * p >= rstart) rope_apply(th[cg][p], pos, y[cg][2 * p], y[cg][2 * p + 1]);
+    }
+    store_vec<T, VEC>(op + ch0, y[cg]);
+  }
+}
+
 // Entry epilogue for a lane group of LPE lanes holding y[cg][v] = channel (gi + LPE cg) VEC + v:
 // RMSNorm over the c channels, RoPE at `pos` on the last rope_dims channels, store to `op`.
 template <typename T, int VEC, int CPL>
@@ -102,18 +121,7 @@ __device__ __forceinline__ void finish_entry(const CompressArgs& a, float (&y)[C
       for (int v = 0; v < VEC; ++v) y[cg][v] *= inv * (a.norm_w && ch0 < a.c ? a.norm_w[ch0 + v] : 1.f);
     }
   }
-  const int rstart = a.c - a.rope_dims;
-#pragma unroll
-  for (int cg = 0; cg < CPL; ++cg) {
-    const int ch0 = (gi + LPE * cg) * VEC;
-    if (gi + LPE * cg >= groups) continue;
-    if (a.rope_dims > 0 && ch0 + VEC > rstart) {
-#pragma unroll
-      for (int p = 0; p < VEC / 2; ++p)
-        if (ch0 + 2 * p >= rstart) rope_apply(th[cg][p], pos, y[cg][2 * p], y[cg][2 * p + 1]);
-    }
-    store_vec<T, VEC>(op + ch0, y[cg]);
-  }
+  finish_rotate_store<T, VEC, CPL>(a, y, gi, LPE, th, pos, op);
 }
 
 // Rows of entry e of sequence b: CSA [b-half (m rows, when present), a-half (m rows)];
@@ -198,18 +206,128 @@ __global__ __launch_bounds__(256) void compress_rows_kernel(CompressArgs a) {
           for (int v = 0; v < VEC; ++v) y[q][cg][v] = 0.f;
       }
     }
+    // RMSNorm of the EPL rows together: their butterfly reductions are independent, so the
+    // shuffles of different rows overlap instead of running one row after another
+    if (a.apply_norm) {
+      float ss[EPL];
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) {
+        ss[q] = 0.f;
+#pragma unroll
+        for (int cg = 0; cg < CPL; ++cg)
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) ss[q] += y[q][cg][v] * y[q][cg][v];
+      }
+      for (int o = LPE >> 1; o > 0; o >>= 1)
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) ss[q] += __shfl_xor(ss[q], o, 64);
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) {
+        const float inv = rsqrtf(ss[q] / (float)a.c + a.eps);
+#pragma unroll
+        for (int cg = 0; cg < CPL; ++cg) {
+          const int ch0 = (gi + LPE * cg) * VEC;
+#pragma unroll
+          for (int v = 0; v < VEC; ++v) y[q][cg][v] *= inv * (a.norm_w && ch0 < a.c ? a.norm_w[ch0 + v] : 1.f);
+        }
+      }
+    }
 #pragma unroll
     for (int q = 0; q < EPL; ++q) {
       if (t + q >= n_tot) break;
       const int b = (int)((t + q) / a.n_out);
       const int64_t e = (t + q) % a.n_out;
-      finish_entry<T, VEC, CPL>(a, y[q], gi, LPE, th, a.pos0 + e,
-                                (T*)a.out + ((int64_t)b * a.out_ld + e) * a.c);
+      finish_rotate_store<T, VEC, CPL>(a, y[q], gi, LPE, th, a.pos0 + e,
+                                       (T*)a.out + ((int64_t)b * a.out_ld + e) * a.c);
     }
   }
 }
 
-// 2 .. 32 rows per entry: a lane group per entry, online softmax in registers, rows four at a time.
+// 16-byte vector of VEC elements, kept packed until used (4 registers for 8 bf16 or 4 fp32 values).
+template <typename T, int VEC>
+__device__ __forceinline__ u32x4 load16(const T* p) {
+  static_assert(sizeof(T) * VEC == 16, "one 16-byte load per channel group");
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ void unpack16(const u32x4& r, float (&out)[VEC]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(r[i] << 16);
+      out[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(r[i]);
+  }
+}
+
+// 2 .. 8 rows per entry (CSA with m <= 4): a lane group per entry; every row's C, Z and bias vector
+// is loaded (24 loads per lane for 8 rows, packed) before the online softmax runs over them.
+template <typename T, int VEC, int CPL>
+__global__ __launch_bounds__(256) void compress_pool8_kernel(CompressArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int LPE = a.lpe, gi = lane & (LPE - 1), gpw = 64 / LPE;
+  const int groups = a.c / VEC;
+  const int64_t task0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * gpw + lane / LPE;
+  const int64_t ntask = (int64_t)gridDim.x * 4 * gpw;
+  const int64_t n_tot = (int64_t)a.n_out * a.batch;
+  double th[CPL][VEC / 2];
+  rope_table<VEC, CPL>(a, gi, LPE, th);
+  for (int64_t el = task0; el < n_tot; el += ntask) {
+    const int b = (int)(el / a.n_out);
+    const int64_t e = el % a.n_out;
+    int first, nrows;
+    entry_rows(a, e, first, nrows);
+    u32x4 craw[8][CPL], zraw[8][CPL], braw[8][CPL];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int r = first + (i < nrows ? i : nrows - 1);
+      const T *cp, *zp, *bp;
+      entry_row<T>(a, b, e, r, cp, zp, bp);
+#pragma unroll
+      for (int cg = 0; cg < CPL; ++cg) {
+        const int g = gi + LPE * cg < groups ? gi + LPE * cg : groups - 1;
+        craw[i][cg] = load16<T, VEC>(cp + g * VEC);
+        zraw[i][cg] = zp ? load16<T, VEC>(zp + g * VEC) : u32x4{0u, 0u, 0u, 0u};
+        braw[i][cg] = bp ? load16<T, VEC>(bp + g * VEC) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    float mx[CPL][VEC], sm[CPL][VEC], acc[CPL][VEC];
+#pragma unroll
+    for (int cg = 0; cg < CPL; ++cg)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) {
+        mx[cg][v] = -INFINITY;
+        sm[cg][v] = 0.f;
+        acc[cg][v] = 0.f;
+      }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (i >= nrows) break;
+#pragma unroll
+      for (int cg = 0; cg < CPL; ++cg) {
+        float cv[VEC], zv[VEC], bv[VEC];
+        unpack16<T, VEC>(craw[i][cg], cv);
+        unpack16<T, VEC>(zraw[i][cg], zv);
+        unpack16<T, VEC>(braw[i][cg], bv);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) zv[v] += bv[v];
+        softmax_step<VEC>(mx[cg], sm[cg], acc[cg], zv, cv);
+      }
+    }
+    float y[CPL][VEC];
+#pragma unroll
+    for (int cg = 0; cg < CPL; ++cg)
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) y[cg][v] = acc[cg][v] / sm[cg][v];
+    finish_entry<T, VEC, CPL>(a, y, gi, LPE, th, a.pos0 + e * a.m, (T*)a.out + ((int64_t)b * a.out_ld + e) * a.c);
+  }
+}
+
+// 9 .. 32 rows per entry: a lane group per entry, online softmax in registers, rows four at a time.
 template <typename T, int VEC, int CPL>
 __global__ __launch_bounds__(256) void compress_pool_kernel(CompressArgs a) {
   constexpr int RB = 4;
@@ -446,11 +564,13 @@ static void launch_compress_t(CompressArgs& a, int batch, hipStream_t st) {
   // (decode), so that the rows' dependent epilogues run in parallel groups
   const int epl = rows == 1 && n_tot > 4096 ? 4 : 1;
   const int64_t waves = ceil_div(ceil_div(n_tot, epl), gpw);
-  const int64_t wgs = std::min<int64_t>(ceil_div(waves, 4), 2048);
+  const int64_t wgs = std::min<int64_t>(ceil_div(waves, 4), 65535);
   if (rows == 1 && epl == 4)
     hipLaunchKernelGGL((compress_rows_kernel<T, VEC, CPL, 4>), dim3((unsigned)wgs), dim3(256), 0, st, a);
   else if (rows == 1)
     hipLaunchKernelGGL((compress_rows_kernel<T, VEC, CPL, 1>), dim3((unsigned)wgs), dim3(256), 0, st, a);
+  else if (rows <= 8)
+    hipLaunchKernelGGL((compress_pool8_kernel<T, VEC, CPL>), dim3((unsigned)wgs), dim3(256), 0, st, a);
   else
     hipLaunchKernelGGL((compress_pool_kernel<T, VEC, CPL>), dim3((unsigned)wgs), dim3(256), 0, st, a);
 }
