@@ -191,11 +191,16 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
   static_assert(CPR % TPK == 0, "loader mapping");
   constexpr int CPT = CPR / TPK;     // chunks per loader thread per tile
   constexpr int MAXPAIRS = D / 2;
+  // One query per workgroup: its query loads are issued before anything else, so that their
+  // latency overlaps the index and rotary staging and the first key tile. With two queries the
+  // register budget is too tight for that, and they are loaded right before use.
+  constexpr bool QEARLY = QG == 1;
   // double-buffered key tiles as two separately declared arrays: with direct-to-LDS copies
   // the compiler then sees that a copy into one buffer never feeds reads of the other
   __shared__ __attribute__((aligned(16))) uint16_t kt0[32 * ROWE], kt1[32 * ROWE];
   __shared__ __attribute__((aligned(16))) int kvq0[32], kvq1[32];  // logical key -> bit q: valid for query q
   __shared__ float rope_cs[QG][MAXPAIRS][2];
+  __shared__ __attribute__((aligned(16))) float qw_s[D];  // query RMSNorm weights
   __shared__ int idx_s[CSKV_MAX_TOPK];  // CSA: the query's selected entries, staged once
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -226,9 +231,20 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
   const int64_t blk0 = (int64_t)split * bps;
   const int64_t blk1 = blk0 + bps < nblk ? blk0 + bps : nblk;
 
+  // query rows: 16 bytes per lane per k-step, all in flight together
+  const uint16_t* qp = (const uint16_t*)a.q + (((int64_t)b * a.Tq + j) * a.H + (hvalid ? h : 0)) * D;
+  u32x4 qraw[KS];
+  auto load_q = [&]() {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qraw[ks] = *reinterpret_cast<const u32x4*>(qp + ks * 32 + 8 * g);
+  };
+  if constexpr (QEARLY) load_q();
+
   // Stage the selected-entry list in LDS so that row addresses never wait on a global load.
   if (csa)
     for (int i = tid; i < a.k; i += NT) idx_s[i] = idxrow[i];
+  // Query RMSNorm weights (1 when absent), read back as vectors in the query prologue.
+  for (int i = tid; i < D; i += NT) qw_s[i] = a.q_norm_w ? a.q_norm_w[i] : 1.f;
   // Rotary cos/sin of every pair at each query's position, once per workgroup.
   const int npairs = a.rope_dims / 2;
   for (int i = tid; i < QG * npairs; i += NT) {
@@ -238,50 +254,7 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
   }
   __syncthreads();
 
-  // ---- query prologue: RMSNorm, RoPE at t -> bf16 B operands of S^T (lane: head n, dims 32ks+8g..+7)
-  bf16x8 qb[KS];
-  {
-    const uint16_t* qp = (const uint16_t*)a.q + (((int64_t)b * a.Tq + j) * a.H + (hvalid ? h : 0)) * D;
-    float x[KS][8];
-    float ss = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      load_vec<bf16, 8>(reinterpret_cast<const bf16*>(qp + ks * 32 + 8 * g), x[ks]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (!hvalid) x[ks][e] = 0.f;
-        ss += x[ks][e] * x[ks][e];
-      }
-    }
-    ss += __shfl_xor(ss, 16, 64);
-    ss += __shfl_xor(ss, 32, 64);
-    const float inv = a.apply_q_norm ? rsqrtf(ss / (float)D + a.eps) : 1.f;
-    const int rstart = D - a.rope_dims;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[ks][e] *= inv * (a.q_norm_w ? a.q_norm_w[ks * 32 + 8 * g + e] : 1.f);
-      if (a.rope_dims > 0 && ks * 32 + 8 * g + 8 > rstart) {
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int dim = ks * 32 + 8 * g + e;
-          if (dim >= rstart) {
-            const float cs = rope_cs[qi][(dim - rstart) >> 1][0], sn = rope_cs[qi][(dim - rstart) >> 1][1];
-            const float x0 = x[ks][e], x1 = x[ks][e + 1];
-            x[ks][e] = x0 * cs - x1 * sn;
-            x[ks][e + 1] = x0 * sn + x1 * cs;
-          }
-        }
-      }
-      u32x4 pk;
-      pk[0] = pack_bf16x2(x[ks][0], x[ks][1]);
-      pk[1] = pack_bf16x2(x[ks][2], x[ks][3]);
-      pk[2] = pack_bf16x2(x[ks][4], x[ks][5]);
-      pk[3] = pack_bf16x2(x[ks][6], x[ks][7]);
-      qb[ks] = __builtin_bit_cast(bf16x8, pk);
-    }
-  }
-
+  bf16x8 qb[KS];  // query prologue output: bf16 B operands of S^T (lane: head n, dims 32ks+8g..+7)
   float m_ref = -INFINITY, l_run = 0.f;  // per head n, identical in the four lane groups
   f32x4 o[NTILE];                        // O^T tile tt: lane holds dims 16tt+4g+i of head n
 #pragma unroll
@@ -302,13 +275,17 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
     t_q[q] = a.pos0 + (jb + q < a.Tq ? jb + q : jl);
     vis_q[q] = csa ? 0 : visible_n(t_q[q], a.m, a.N);
   }
-  u32x4 pre[CPT];
-  int pre_ok = 0;
-  float pre_sc = 0.f;   // KV8: scale of the entry in flight
-  bool pre8 = false;    // KV8: the entry in flight is an FP8 row (not a window row or padding)
+  // register staging of one key row's share: chunks, validity bits and (KV8) the entry's scale
+  // and whether it is an FP8 row (not a window row or padding)
+  struct Stage {
+    u32x4 v[CPT];
+    int ok;
+    float sc;
+    bool is8;
+  };
   // Loader thread: key u = blk*32 + kr of the key list goes to LDS row kr; its validity
   // bits (bit q: query q of the tile may attend to it) go to the logical slot of row kr.
-  auto gload = [&](int64_t blk) {
+  auto gload = [&](int64_t blk, Stage& st) {
     const int64_t u = blk * 32 + kr;
     const uint16_t* src = nullptr;
     const uint8_t* src8 = nullptr;
@@ -318,7 +295,7 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
       if (s_ >= 0 && s_ < a.N) {
         if constexpr (KV8) {
           src8 = kv8b + s_ * rb8;
-          pre_sc = a.kv_scale[(int64_t)b * a.N + s_];
+          st.sc = a.kv_scale[(int64_t)b * a.N + s_];
         } else {
           src = kvb + s_ * D;
         }
@@ -333,9 +310,9 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int q = 0; q < QG; ++q) ok |= (pos >= t_q[q] - a.w + 1 && pos <= t_q[q]) ? (1 << q) : 0;
     }
-    // pre8 depends on addresses only: selecting on the loaded scale here would wait for that
+    // is8 depends on addresses only: selecting on the loaded scale here would wait for that
     // load before the current tile's compute and expose the full gather latency.
-    pre8 = KV8 && src8 != nullptr;
+    st.is8 = KV8 && src8 != nullptr;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int oc = c0 + TPK * i;  // 16-byte chunk of the bf16 row: dims 8*oc .. +8
@@ -350,25 +327,25 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
       } else if (src) {
         v = *reinterpret_cast<const u32x4*>(src + oc * 8);
       }
-      pre[i] = v;
+      st.v[i] = v;
     }
-    pre_ok = ok;
+    st.ok = ok;
   };
-  auto lstore = [&](uint16_t* ktb, int* kvqb) {
+  auto lstore = [&](uint16_t* ktb, int* kvqb, const Stage& st) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int oc = c0 + TPK * i;
-      u32x4 v = pre[i];
-      if (KV8 && pre8 && oc < nope8) {  // widen 8 codes to bf16 (times the power-of-two scale)
+      u32x4 v = st.v[i];
+      if (KV8 && st.is8 && oc < nope8) {  // widen 8 codes to bf16 (times the power-of-two scale)
         const uint32_t c01 = v.x, c23 = v.y;
-        v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c01, pre_sc, false));
-        v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c01, pre_sc, true));
-        v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c23, pre_sc, false));
-        v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c23, pre_sc, true));
+        v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c01, st.sc, false));
+        v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c01, st.sc, true));
+        v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c23, st.sc, false));
+        v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c23, st.sc, true));
       }
       *reinterpret_cast<u32x4*>(&ktb[kr * ROWE + oc * 8]) = v;
     }
-    if (c0 == 0) kvqb[key_of_row(kr)] = pre_ok;
+    if (c0 == 0) kvqb[key_of_row(kr)] = st.ok;
   };
   // bf16 entries of 512 dims: one key row is one 1 KiB wave copy straight into LDS
   // (global_load_lds_dwordx4, lane l -> bytes 16 l .. 16 l + 15 of the row), so no staging
@@ -480,8 +457,59 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
       o[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), pb, o[tt], 0, 0, 0);
     }
   };
+  // ---- query prologue: RMSNorm, RoPE at t -> qb
+  auto query_prologue = [&]() {
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (!hvalid) qraw[ks] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = __uint_as_float(qraw[ks][e] << 16), x1 = __uint_as_float(qraw[ks][e] & 0xffff0000u);
+        ss += x0 * x0;
+        ss += x1 * x1;
+      }
+    }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float inv = a.apply_q_norm ? rsqrtf(ss / (float)D + a.eps) : 1.f;
+    const int rstart = D - a.rope_dims;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&qw_s[ks * 32 + 8 * g]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&qw_s[ks * 32 + 8 * g + 4]);
+      const float wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[2 * e] = __uint_as_float(qraw[ks][e] << 16) * (inv * wv[2 * e]);
+        x[2 * e + 1] = __uint_as_float(qraw[ks][e] & 0xffff0000u) * (inv * wv[2 * e + 1]);
+      }
+      if (a.rope_dims > 0 && ks * 32 + 8 * g + 8 > rstart) {
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int dim = ks * 32 + 8 * g + e;
+          if (dim >= rstart) {
+            const float cs = rope_cs[qi][(dim - rstart) >> 1][0], sn = rope_cs[qi][(dim - rstart) >> 1][1];
+            const float x0 = x[e], x1 = x[e + 1];
+            x[e] = x0 * cs - x1 * sn;
+            x[e + 1] = x0 * sn + x1 * cs;
+          }
+        }
+      }
+      u32x4 pk;
+      pk[0] = pack_bf16x2(x[0], x[1]);
+      pk[1] = pack_bf16x2(x[2], x[3]);
+      pk[2] = pack_bf16x2(x[4], x[5]);
+      pk[3] = pack_bf16x2(x[6], x[7]);
+      qb[ks] = __builtin_bit_cast(bf16x8, pk);
+    }
+  };
   if constexpr (DMA) {
+    // the first tile's copies are in flight while the queries are prepared
+    if constexpr (!QEARLY) load_q();
     if (blk0 < blk1) dma(blk0, kt0, kvq0);
+    query_prologue();
     wait_barrier();
     // tile pairs: buffer 0 holds the even tiles of the range, buffer 1 the odd ones
     for (int64_t blk = blk0; blk < blk1; blk += 2) {
@@ -495,17 +523,24 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
       }
     }
   } else {
-    // register-staged: the next tile's rows are loaded into registers during this tile
-    if (blk0 < blk1) {
-      gload(blk0);
-      lstore(kt0, kvq0);
+    // register-staged: the next tile's rows are loaded into registers during this tile (the
+    // first one while the queries are prepared)
+    Stage st;
+    if constexpr (QEARLY) {
+      if (blk0 < blk1) gload(blk0, st);
+      query_prologue();
+    } else {
+      load_q();
+      query_prologue();
+      if (blk0 < blk1) gload(blk0, st);
     }
+    if (blk0 < blk1) lstore(kt0, kvq0, st);
     __syncthreads();
     for (int64_t blk = blk0; blk < blk1; ++blk) {
       const bool odd = ((blk - blk0) & 1) != 0;
-      if (blk + 1 < blk1) gload(blk + 1);
+      if (blk + 1 < blk1) gload(blk + 1, st);
       tile(odd ? kt1 : kt0, odd ? kvq1 : kvq0);
-      if (blk + 1 < blk1) lstore(odd ? kt0 : kt1, odd ? kvq0 : kvq1);
+      if (blk + 1 < blk1) lstore(odd ? kt0 : kt1, odd ? kvq0 : kvq1, st);
       __syncthreads();
     }
   }
