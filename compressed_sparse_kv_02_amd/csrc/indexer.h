@@ -29,7 +29,18 @@ struct IdxArgs {
   uint8_t* sel_ws;     // per row: keys [CAP] u32, indices [CAP] i32, part records [MAX_PARTS] int4
   int64_t part_len;    // entries per part
   int kp;              // candidates kept per part
+  // Block maxima: score_key of the largest score of each block of 32 entries of a row (0 when
+  // the block holds no entry of the row), row r of the chunk at bm + (b * bm_rows + r) * bm_ld.
+  // bm_fused: the one-query-per-workgroup scorer writes them as it stores the scores; otherwise
+  // topk_blockmax derives them from the score rows. topk_bm_select reads them.
+  uint32_t* bm;
+  int64_t bm_ld, bm_rows;
+  int bm_fused;
 };
+
+// Rows of up to BM_MAX_BLOCKS blocks of 32 entries can be selected through block maxima.
+constexpr int BM_MAX_BLOCKS = 8192;
+
 
 // ReLU on the bit pattern: for non-NaN x, max(bits(x), 0) as int32 is bits(max(x, 0))
 // (negative floats, -0.0 included, are negative as int32). One VALU op, no NaN canonicalisation.
@@ -53,6 +64,9 @@ IdxPlan plan_indexer(int batch, int64_t Tq, int64_t N, int dtype);
 // Low-precision scoring (dtype CSKV_FP8: E4M3 codes, CSKV_FP4: E2M1 codes) of rows
 // [a.row0, a.row0 + a.nrows) into a.scores (indexer_lowp.hip).
 int launch_scores_lowp(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st);
+
+// Bytes of one row's selection workspace (the several-workgroups-per-row routes).
+int64_t topk_sel_stride();
 
 // Workspace bytes for the several-workgroups-per-row selection of `rows`
 // rows of up to vmax entries; 0 when that route is not taken.

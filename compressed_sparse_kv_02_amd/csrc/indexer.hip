@@ -208,6 +208,17 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
 // dimension is permuted the same way in A and B (lane half h, k-step ks: dims
 // h*8*KS + 8*ks .. +8), so each lane reads one contiguous half row from LDS;
 // every dot product is unchanged.
+// Largest of x over each 32-lane half of the wave, in every lane: quad swaps, the half-row and
+// row mirrors (DPP), then a swap between rows 0-1 and 2-3.
+__device__ __forceinline__ uint32_t max_key32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));  // 7 - lane (8s)
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));  // 15 - lane (16s)
+  const auto sw = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return max(sw[0], sw[1]);
+}
+
 template <int HT, int KS>
 __global__ __launch_bounds__(256) void indexer_score_stream(IdxArgs a) {
   constexpr int DI = 16 * KS;
@@ -296,6 +307,10 @@ __global__ __launch_bounds__(256) void indexer_score_stream(IdxArgs a) {
     part += __shfl_xor(part, 32, 64);
     const int64_t s = key_of(blk);
     if (lane < 32 && s < vj) srow[s] = part;
+    if (a.bm_fused) {  // the block's maximum key, for the selection
+      const uint32_t mk = max_key32(s < vj ? score_key(part) : 0u);
+      if (lane == 0) a.bm[((int64_t)b * a.bm_rows + jr) * a.bm_ld + (s >> 5)] = mk;
+    }
   };
 
 #pragma unroll
@@ -466,20 +481,30 @@ extern "C" int indexer_topk(const void* qI, const float* wI, const void* KI, int
   if (!aligned16(qI, wI, KI, out_idx, workspace)) return CSKV_ERR_MISALIGNED;
   IdxPlan p = plan_indexer(batch, Tq, N, dtype);
   const size_t score_bytes = (size_t)(batch * p.rows_ws * p.ldS * 4);
-  const size_t need_ws = score_bytes + split_ws_bytes((int64_t)batch * p.rows_ws, N, k);
+  const size_t split_bytes = split_ws_bytes((int64_t)batch * p.rows_ws, N, k);
+  const size_t need_ws = score_bytes + split_bytes;
   if (!workspace || ws_bytes < need_ws) return CSKV_ERR_WORKSPACE;
   // the selection area follows the score rows (score_bytes is a multiple of 256: ldS % 64 == 0)
-  uint8_t* sel_ws = need_ws > score_bytes ? (uint8_t*)workspace + score_bytes : nullptr;
-  const size_t sel_bytes = sel_ws ? ws_bytes - score_bytes : 0;
+  uint8_t* sel_ws = split_bytes ? (uint8_t*)workspace + score_bytes : nullptr;
+  const size_t sel_bytes = split_bytes;
 
   hipStream_t hs = (hipStream_t)stream;
   IdxArgs a{};
   a.qI = qI; a.wI = wI; a.KI = KI; a.scores = (float*)workspace; a.out = out_idx;
   a.Tq = Tq; a.N = N; a.pos0 = pos0; a.ldS = p.ldS; a.rows_ws = p.rows_ws;
   a.HI = HI; a.dI = dI; a.m = m; a.k = k;
+  // few long rows scored one query per workgroup (decode): the scorer writes the block maxima
+  // into the rows' selection workspace
+  const bool bm_stream = dtype == CSKV_BF16 && p.qb == 1 && split_bytes && ceil_div(N, (int64_t)32) <= BM_MAX_BLOCKS;
   for (int64_t r0 = 0; r0 < Tq; r0 += p.rows_ws) {
     a.row0 = r0;
     a.nrows = (Tq - r0) < p.rows_ws ? (Tq - r0) : p.rows_ws;
+    if (bm_stream) {
+      a.bm = reinterpret_cast<uint32_t*>(sel_ws);
+      a.bm_ld = topk_sel_stride() / 4;
+      a.bm_rows = a.nrows;
+      a.bm_fused = 1;
+    }
     const int64_t last = pos0 + r0 + a.nrows - 1;
     int64_t vmax = (last + 1) / m;
     if (vmax > N) vmax = N;

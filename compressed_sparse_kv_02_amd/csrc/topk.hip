@@ -450,10 +450,10 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge(IdxArgs a) {
                tau, need, sh);
 }
 
-// Few long rows of at most BM_MAX_BLOCKS blocks of 32 entries (decode at 1M context: 8 rows of
-// 262144): selection through block maxima.
-//  * topk_blockmax (many workgroups): the largest key of every block of 32 entries of the row
-//    (entries past V count as absent) goes to the row's workspace.
+// Rows of at most BM_MAX_BLOCKS blocks of 32 entries: selection through block maxima.
+//  * the largest key of every block of 32 entries of the row (entries past V count as absent):
+//    written by the bf16 one-query-per-workgroup scorer as it stores the scores (indexer_topk
+//    on decode rows), or else by topk_blockmax (many workgroups) from the score rows.
 //  * topk_bm_select (one workgroup per row): tau_b = a lower bound of the k-th largest block
 //    maximum (0 when the row has at most k blocks). Each block maximum is an entry's key, so at
 //    least k entries reach tau_b: the k-th largest key of the row is >= tau_b, and every entry
@@ -462,7 +462,6 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_merge(IdxArgs a) {
 //    top-k among them (radix select + in-order pick) is the row's exact top-k, ties included.
 //    Should they overflow LDS (many equal scores), the row falls back to the exact select over
 //    global memory.
-constexpr int BM_MAX_BLOCKS = 8192;
 constexpr int BM_CAP = 8192;  // gathered candidates held in LDS
 
 __global__ __launch_bounds__(256) void topk_blockmax(IdxArgs a) {
@@ -473,7 +472,7 @@ __global__ __launch_bounds__(256) void topk_blockmax(IdxArgs a) {
   if (V <= a.k) return;
   const int nb = (int)((V + 31) / 32);
   const float* row = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
-  uint32_t* bm = reinterpret_cast<uint32_t*>(a.sel_ws + ((int64_t)b * a.nrows + jr) * TOPK_SEL_STRIDE);
+  uint32_t* bm = a.bm + ((int64_t)b * a.bm_rows + jr) * a.bm_ld;
   // this workgroup: blocks [256 x, 256 x + 256); wave w: 64 of them, 8 per load (8 lanes per block)
   const int blk0 = blockIdx.x * 256 + wave * 64;
   float4 v[8];
@@ -579,13 +578,14 @@ __global__ __launch_bounds__(TOPK_THREADS) void topk_bm_select(IdxArgs a) {
     return;
   }
   const float* row = a.scores + ((int64_t)b * a.rows_ws + jr) * a.ldS;
-  const uint32_t* bm = reinterpret_cast<const uint32_t*>(a.sel_ws + ((int64_t)b * a.nrows + jr) * TOPK_SEL_STRIDE);
+  const uint32_t* bm = a.bm + ((int64_t)b * a.bm_rows + jr) * a.bm_ld;
   const int nb = (int)((V + 31) / 32);
-  // thread t holds block maxima 16 t .. 16 t + 15 (4 vector loads; past nb: absent)
+  // thread t holds block maxima 16 t .. 16 t + 15 (4 vector loads, none past the row's nb
+  // blocks, which bm_ld, a multiple of 4, covers; past nb: absent)
   uint32_t bk[16];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint4 v = *reinterpret_cast<const uint4*>(bm + 16 * tid + 4 * q);
+    const uint4 v = 16 * tid + 4 * q < nb ? *reinterpret_cast<const uint4*>(bm + 16 * tid + 4 * q) : uint4{0u, 0u, 0u, 0u};
     bk[4 * q] = v.x;
     bk[4 * q + 1] = v.y;
     bk[4 * q + 2] = v.z;
@@ -718,6 +718,8 @@ static bool plan_split(int64_t rows, int64_t vmax, int k, SplitPlan& sp) {
   return true;
 }
 
+int64_t topk_sel_stride() { return TOPK_SEL_STRIDE; }
+
 size_t split_ws_bytes(int64_t rows, int64_t vmax, int k) {
   SplitPlan sp;
   return plan_split(rows, vmax, k, sp) ? (size_t)(rows * TOPK_SEL_STRIDE) : 0;
@@ -731,10 +733,17 @@ int launch_select(IdxArgs& a, int batch, void* sel_ws, size_t sel_bytes, hipStre
   if (vmax > a.N) vmax = a.N;
   SplitPlan sp;
   const int64_t rows = (int64_t)batch * a.nrows;
+  if (a.bm_fused) {  // the scorer wrote the block maxima (set only where ws_ok and the rows fit)
+    hipLaunchKernelGGL(topk_bm_select, dim3((unsigned)a.nrows, (unsigned)batch), dim3(TOPK_THREADS), 0, st, a);
+    return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
+  }
   const bool ws_ok = sel_ws && plan_split(rows, vmax, a.k, sp) && sel_bytes >= (size_t)(rows * TOPK_SEL_STRIDE);
   if (ws_ok && ceil_div(vmax, (int64_t)32) <= BM_MAX_BLOCKS) {
     static_assert((int64_t)BM_MAX_BLOCKS * 4 <= TOPK_SEL_STRIDE, "block maxima fit a row's workspace");
     a.sel_ws = (uint8_t*)sel_ws;
+    a.bm = reinterpret_cast<uint32_t*>(sel_ws);
+    a.bm_ld = TOPK_SEL_STRIDE / 4;
+    a.bm_rows = a.nrows;
     hipLaunchKernelGGL(topk_blockmax, dim3((unsigned)ceil_div(ceil_div(vmax, (int64_t)32), (int64_t)256),
                                            (unsigned)a.nrows, (unsigned)batch),
                        dim3(256), 0, st, a);
