@@ -150,8 +150,11 @@ def traffic_summary() -> None:
     print("| kernel | grid | dispatches | HBM read MB | HBM write MB | MFMA busy | clock GHz |")
     print("|---|---:|---:|---:|---:|---:|---:|")
     for e in sorted(tr["kernels"], key=lambda e: -e.get("hbm_bytes_per_launch", 0)):
-        mb = f"{100 * e['mfma_busy']:.1f}%" if "mfma_busy" in e else "-"
-        ck = f"{e['clock_ghz']:.2f}" if "clock_ghz" in e else "-"
+        # GRBM_GUI_ACTIVE also counts the dispatch's set-up and drain: below ~200 us that inflates
+        # the clock and deflates the busy share, so those two are shown for long dispatches only
+        long_run = e.get("duration_us_under_counters", 0) >= 200
+        mb = f"{100 * e['mfma_busy']:.1f}%" if "mfma_busy" in e and (long_run or e["mfma_busy"] == 0) else "-"
+        ck = f"{e['clock_ghz']:.2f}" if "clock_ghz" in e and long_run else "-"
         print(f"| `{e['kernel']}` | {e['grid']} | {e.get('dispatches', 0)} | {e.get('FETCH_SIZE_bytes', 0) / 1e6:.1f} "
               f"| {e.get('WRITE_SIZE_bytes', 0) / 1e6:.1f} | {mb} | {ck} |")
 
