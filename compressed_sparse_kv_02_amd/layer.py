@@ -129,6 +129,12 @@ def make_inputs(L: LayerCall, device="cuda") -> Dict[str, torch.Tensor]:
 
 def compress_step(L: LayerCall, t: Dict[str, torch.Tensor]) -> None:
     """Steps 1-3: append new compressed entries (and indexer keys) and prepare window rows."""
+    entries_step(L, t)
+    window_step(L, t)
+
+
+def entries_step(L: LayerCall, t: Dict[str, torch.Tensor]) -> None:
+    """Steps 1-2: append the entries (and CSA indexer keys) of the blocks the call completes."""
     if L.n_new:
         if L.kind == "csa":
             B.csa_compress(t["kv.Ca"], t["kv.Cb"], t["kv.Za"], t["kv.Zb"], t["kv.B"], L.m, L.pos0,
@@ -140,6 +146,10 @@ def compress_step(L: LayerCall, t: Dict[str, torch.Tensor]) -> None:
         else:
             B.hca_compress(t["kv.C"], t["kv.Z"], t["kv.B"], L.m, L.pos0, apply_norm=True,
                            rope_dims=L.rope_dims, out=t["cache.kv"], out_row0=L.n_cached)
+
+
+def window_step(L: LayerCall, t: Dict[str, torch.Tensor]) -> None:
+    """Step 3: prepare the call's window rows (RMSNorm + RoPE of the raw rows)."""
     B.hca_compress(t["win_raw"], None, None, 1, L.pos0, apply_norm=True, rope_dims=L.rope_dims,
                    out=t["win"], out_row0=L.win_cached)
 
