@@ -352,6 +352,7 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
   // registers. Wave w copies LDS rows w, w + NW, ...; an absent key copies a window row
   // (finite data; its validity bits are 0, so its weight is exactly 0).
   constexpr bool DMA = KVR < 0 && D == 512 && OCC == 2;
+  constexpr bool DMA8 = KV8 && D == 512 && OCC == 2;  // see dma8 below
   auto dma = [&](int64_t blk, uint16_t* ktb, int* kvqb) {
 #pragma unroll
     for (int i = 0; i < 32 / NW; ++i) {
@@ -383,8 +384,92 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
   // every copy of the tile has landed and every wave is done with the other buffer; the
   // explicit full wait is visible to the compiler's wait tracking (one in inline asm is not)
   auto wait_barrier = [&]() {
-    if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (DMA || DMA8) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  // KV8 entries at two workgroups per CU: each stored entry (D - KVR codes, then the KVR RoPE
+  // dims in bf16) is copied straight into LDS at byte D - KVR of its row, which puts the RoPE
+  // dims where the bf16 row has them; the wave that copied a row then widens its codes to bf16
+  // in front of them (expand8). Window rows and absent keys are copied as whole bf16 rows. Lane
+  // l widens the wave's row l / 8 (chunks of 8 codes l % 8, l % 8 + 8, ...) and loads that
+  // row's scale with the copies. A wave's LDS operations run in order, so its reads of the
+  // codes precede its overlapping writes (other lanes' bytes) without a barrier; wave-scope
+  // fences keep the compiler from moving them across each other.
+  constexpr int NCH8 = (D - (KV8 ? KVR : 0)) / 8;  // 8-code chunks per stored entry
+  constexpr int CPT8 = NCH8 >= 8 ? (NCH8 + 7) / 8 : 1;
+  bool exp8 = false;  // DMA8: this thread's expansion row holds codes
+  float sc8 = 0.f;    // DMA8: and its scale
+  auto dma8 = [&](int64_t blk, uint16_t* ktb, int* kvqb) {
+    static_assert(!DMA8 || (32 / NW == 8 && D == 512), "expansion mapping: 8 lanes per row, 8 rows per wave");
+#pragma unroll
+    for (int i = 0; i < 32 / NW; ++i) {
+      const int rr = wave + i * NW;
+      const int L = key_of_row(rr);
+      const int64_t u = blk * 32 + L;
+      const uint16_t* src = (const uint16_t*)a.win + wbase * D;
+      const uint8_t* src8 = nullptr;
+      int ok = 0;
+      if (u < n_comp) {
+        const int64_t s_ = csa ? (int64_t)idx_s[u] : u;
+        if (s_ >= 0 && s_ < a.N) {
+          src8 = kv8b + s_ * rb8;
+#pragma unroll
+          for (int q = 0; q < QG; ++q) ok |= (csa || s_ < vis_q[q]) ? (1 << q) : 0;
+        }
+      } else if (u < n_tot) {
+        const int64_t pos = lo + (u - n_comp);
+        int64_t wr = wr_lo + (u - n_comp);
+        if (wr >= a.W) wr -= a.W;
+        src = (const uint16_t*)a.win + (wbase + wr) * D;
+#pragma unroll
+        for (int q = 0; q < QG; ++q) ok |= (pos >= t_q[q] - a.w + 1 && pos <= t_q[q]) ? (1 << q) : 0;
+      }
+      if (src8) {
+        if (lane * 16 < rb8)
+          __builtin_amdgcn_global_load_lds(
+              (const void*)(src8 + 16 * lane),
+              (__attribute__((address_space(3))) void*)((uint8_t*)&ktb[rr * ROWE] + (D - KVR)), 16, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds((const void*)(src + lane * 8),
+                                         (__attribute__((address_space(3))) void*)(&ktb[rr * ROWE]), 16, 0, 0);
+      }
+      if (lane == 0) kvqb[L] = ok;
+    }
+    {  // the scale of this lane's expansion row
+      const int64_t u = blk * 32 + key_of_row(wave + (lane >> 3) * NW);
+      exp8 = false;
+      if (u < n_comp) {
+        const int64_t s_ = csa ? (int64_t)idx_s[u] : u;
+        if (s_ >= 0 && s_ < a.N) {
+          exp8 = true;
+          sc8 = a.kv_scale[(int64_t)b * a.N + s_];
+        }
+      }
+    }
+  };
+  auto expand8 = [&](uint16_t* ktb) {
+    uint8_t* rowb = (uint8_t*)&ktb[(wave + (lane >> 3) * NW) * ROWE];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    uint2 cd[CPT8];
+#pragma unroll
+    for (int i = 0; i < CPT8; ++i) {
+      const int c = (tid & 7) + 8 * i;
+      cd[i] = (exp8 && c < NCH8) ? *reinterpret_cast<const uint2*>(rowb + (D - KVR) + 8 * c) : uint2{0u, 0u};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int i = 0; i < CPT8; ++i) {
+      const int c = (tid & 7) + 8 * i;
+      if (exp8 && c < NCH8) {
+        u32x4 v;
+        v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)cd[i].x, sc8, false));
+        v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)cd[i].x, sc8, true));
+        v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)cd[i].y, sc8, false));
+        v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)cd[i].y, sc8, true));
+        *reinterpret_cast<u32x4*>(rowb + 16 * c) = v;
+      }
+    }
   };
 
   // one key tile: S^T, online softmax, O^T update, from buffer (ktb, kvqb)
@@ -416,7 +501,7 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
     }
     // sv holds raw dot products; base-2 logits are sv * scale_log2 (> 0, so the maximum commutes)
     float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])), fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    mb = group4_max<OCC == 1 || DMA>(mb) * a.scale_log2;
+    mb = group4_max<OCC == 1 || DMA || DMA8>(mb) * a.scale_log2;
     // lazy reference: move it only when a logit exceeds it by REF_SLACK
     const bool upd = mb > m_ref + REF_SLACK;
     float alpha = 1.f;
@@ -432,7 +517,7 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
       p[i] = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], a.scale_log2, -m_ref));
       ps += p[i];
     }
-    ps = group4_sum<OCC == 1 || DMA>(ps);
+    ps = group4_sum<OCC == 1 || DMA || DMA8>(ps);
     l_run = l_run * alpha + ps;
     if (__ballot(upd) != 0) {
 #pragma unroll
@@ -505,7 +590,36 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
       qb[ks] = __builtin_bit_cast(bf16x8, pk);
     }
   };
-  if constexpr (DMA) {
+  if constexpr (DMA8) {
+    // tile pairs as in the bf16 route below; each wave widens its rows of the next tile once
+    // its own copies have landed, before the barrier that hands the tile over
+    if constexpr (!QEARLY) load_q();
+    if (blk0 < blk1) dma8(blk0, kt0, kvq0);
+    query_prologue();
+    if (blk0 < blk1) {
+      __builtin_amdgcn_s_waitcnt(0);
+      expand8(kt0);
+    }
+    __syncthreads();
+    for (int64_t blk = blk0; blk < blk1; blk += 2) {
+      if (blk + 1 < blk1) dma8(blk + 1, kt1, kvq1);
+      tile(kt0, kvq0);
+      if (blk + 1 < blk1) {
+        __builtin_amdgcn_s_waitcnt(0);
+        expand8(kt1);
+      }
+      __syncthreads();
+      if (blk + 1 < blk1) {
+        if (blk + 2 < blk1) dma8(blk + 2, kt0, kvq0);
+        tile(kt1, kvq1);
+        if (blk + 2 < blk1) {
+          __builtin_amdgcn_s_waitcnt(0);
+          expand8(kt0);
+        }
+        __syncthreads();
+      }
+    }
+  } else if constexpr (DMA) {
     // the first tile's copies are in flight while the queries are prepared
     if constexpr (!QEARLY) load_q();
     if (blk0 < blk1) dma(blk0, kt0, kvq0);
@@ -784,7 +898,7 @@ static void launch_kvr(const AttnArgs& a, dim3 grid, hipStream_t st) {
     // 256-thread workgroups over bf16 entries, not split (CSA prefill with 64 heads, HCA prefill
     // with up to 32 heads and two queries per workgroup): two per CU, so the compiler keeps each
     // lane within 256 registers; built for one per CU they took twice that and ran alone on the CU
-    if constexpr (D == 512 && HW * QG == 4 && KVR < 0) {
+    if constexpr (D == 512 && HW * QG == 4) {
       if (a.n_splits == 1) {
         hipLaunchKernelGGL((attn_mfma<D, HW, QG, KVR, 2>), grid, dim3(HW * QG * 64), 0, st, a);
         return;

@@ -578,6 +578,9 @@ def _kv8_oracle(kv_raw_b, rope):
     ("csa", 2, 50, 64, 0, 4, 24, 16, 16, 64, 16),
     ("hca", 1, 20, 50, 128 * 40, 128, 0, 16, 16, 128, 32),
     ("csa", 1, 17, 40, 4 * 30, 4, 16, 8, 16, 64, 0),
+    ("csa", 1, 9, 500, 4 * 400, 4, 256, 32, 64, 512, 0),
+    ("hca", 1, 12, 100, 128 * 90, 128, 0, 32, 32, 512, 32),
+    ("csa", 2, 5, 300, 4 * 250, 4, 64, 40, 64, 512, 16),
 ])
 def test_attention_kv8_prefill_and_decode(mode, bt, Tq, N, pos0, m, k, w, H, d, rope):
     """Attention over an FP8 + BF16 KV cache equals the oracle's attention over its own
