@@ -660,9 +660,10 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
   }
 
   // ---- epilogue: lane holds O[head n][16tt + 4g + i]
-  if (!hvalid) return;
+  if (!qvalid) return;  // uniform for the wave
   const int64_t row = (int64_t)b * a.Tq + j;
   if (a.n_splits > 1) {
+    if (!hvalid) return;
     float* po = a.part_o + ((row * a.n_splits + split) * a.H + h) * (int64_t)D + 4 * g;
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt) *reinterpret_cast<f32x4*>(po + 16 * tt) = o[tt];
@@ -673,16 +674,15 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
     }
     return;
   }
-  const float z = a.sink ? a.sink[h] * 1.4426950408889634f : -INFINITY;
+  const float z = (a.sink && hvalid) ? a.sink[h] * 1.4426950408889634f : -INFINITY;
   const float M = fmaxf(m_ref, z);
   const float em = m_ref == -INFINITY ? 0.f : exp2f(m_ref - M);
   const float lt = l_run * em + (z == -INFINITY ? 0.f : exp2f(z - M));
   const float fac = lt > 0.f ? em / lt : 0.f;
-  if (a.lse && g == 0) a.lse[row * a.H + h] = (M + log2f(lt)) * 0.6931471805599453f;
+  if (a.lse && g == 0 && hvalid) a.lse[row * a.H + h] = (M + log2f(lt)) * 0.6931471805599453f;
   const int rstart = D - a.rope_dims;
-  uint16_t* op = (uint16_t*)a.out + (row * a.H + h) * (int64_t)D + 4 * g;
-#pragma unroll
-  for (int tt = 0; tt < NTILE; ++tt) {
+  // normalised, de-rotated bf16 values of dims 16tt + 4g .. + 3 of head n
+  auto out4 = [&](int tt) {
     float v[4] = {o[tt][0] * fac, o[tt][1] * fac, o[tt][2] * fac, o[tt][3] * fac};
     const int d0 = 16 * tt + 4 * g;
     if (a.rope_on_output && a.rope_dims > 0 && d0 >= rstart) {
@@ -695,7 +695,30 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
         v[e + 1] = x0 * sn + x1 * cs;
       }
     }
-    store_vec<bf16, 4>(reinterpret_cast<bf16*>(op + 16 * tt), v);
+    return uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  };
+  if constexpr (D == 512 && NW <= 4) {
+    // Through LDS, so that each store instruction writes one whole 1 KiB head row (a lane's
+    // own values cover 32-byte pieces of 16 rows): wave w stages its 16 head rows (padded to
+    // 1040 bytes) in the tile buffers, which every wave has finished with (the loop ended on a
+    // barrier); the regions of different waves are disjoint, so only wave-scope ordering is
+    // needed.
+    static_assert(2 * 16 * (D * 2 + 16) == 2 * 32 * ROWE, "four waves' rows fill the two tile buffers");
+    uint8_t* reg = (uint8_t*)(wave < 2 ? kt0 : kt1) + (wave & 1) * 16 * (D * 2 + 16);
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt) *reinterpret_cast<uint2*>(reg + n * (D * 2 + 16) + 32 * tt + 8 * g) = out4(tt);
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    uint16_t* ob = (uint16_t*)a.out + (row * a.H + hw * 16) * (int64_t)D + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(reg + i * (D * 2 + 16) + 16 * lane);
+      if (hw * 16 + i < a.H) *reinterpret_cast<u32x4*>(ob + (int64_t)i * D) = v;
+    }
+  } else {
+    if (!hvalid) return;
+    uint16_t* op = (uint16_t*)a.out + (row * a.H + h) * (int64_t)D + 4 * g;
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt) *reinterpret_cast<uint2*>(op + 16 * tt) = out4(tt);
   }
 }
 
