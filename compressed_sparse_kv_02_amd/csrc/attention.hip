@@ -663,11 +663,30 @@ __global__ __launch_bounds__(HW * QG * 64, OCC) void attn_mfma(AttnArgs a) {
   if (!qvalid) return;  // uniform for the wave
   const int64_t row = (int64_t)b * a.Tq + j;
   if (a.n_splits > 1) {
-    if (!hvalid) return;
-    float* po = a.part_o + ((row * a.n_splits + split) * a.H + h) * (int64_t)D + 4 * g;
+    if constexpr (D == 512 && NW <= 4) {
+      // fp32 partials through LDS as whole rows too, in two halves of 256 dims (1 KiB each)
+      uint8_t* reg = (uint8_t*)(wave < 2 ? kt0 : kt1) + (wave & 1) * 16 * (D * 2 + 16);
+      float* pw = a.part_o + ((row * a.n_splits + split) * a.H + hw * 16) * (int64_t)D + 4 * lane;
 #pragma unroll
-    for (int tt = 0; tt < NTILE; ++tt) *reinterpret_cast<f32x4*>(po + 16 * tt) = o[tt];
-    if (g == 0) {
+      for (int half = 0; half < 2; ++half) {
+        if (half) __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");  // the first half's reads precede
+#pragma unroll
+        for (int tt = 0; tt < NTILE / 2; ++tt)
+          *reinterpret_cast<f32x4*>(reg + n * (D * 2 + 16) + 64 * tt + 16 * g) = o[half * (NTILE / 2) + tt];
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(reg + i * (D * 2 + 16) + 16 * lane);
+          if (hw * 16 + i < a.H) *reinterpret_cast<f32x4*>(pw + (int64_t)i * D + half * (D / 2)) = v;
+        }
+      }
+    } else {
+      if (!hvalid) return;
+      float* po = a.part_o + ((row * a.n_splits + split) * a.H + h) * (int64_t)D + 4 * g;
+#pragma unroll
+      for (int tt = 0; tt < NTILE; ++tt) *reinterpret_cast<f32x4*>(po + 16 * tt) = o[tt];
+    }
+    if (g == 0 && hvalid) {
       float* pm = a.part_ml + ((row * a.n_splits + split) * a.H + h) * 2;
       pm[0] = m_ref;
       pm[1] = l_run;
