@@ -489,6 +489,8 @@ def _random_idx(bt, Tq, pos0, m, N, k, seed):
     ("bf16", "csa", 2, 9, 400, 4 * 390, 4, 64, 128, 64, 512, 64, False, True),
     ("bf16", "csa", 1, 20, 200, 4 * 150, 4, 16, 8, 64, 512, 64, True, True),   # one key tile (16 + 8 keys)
     ("bf16", "csa", 2, 10, 300, 4 * 290, 4, 64, 16, 64, 512, 64, False, True),  # three key tiles (64 + 16 keys)
+    ("bf16", "hca", 2, 33, 150, 128 * 120, 128, 0, 64, 32, 512, 64, True, True),  # odd Tq: a half-empty 2-query block
+    ("bf16", "csa", 1, 12, 300, 4 * 250, 4, 128, 32, 40, 512, 64, True, True),  # 40 heads: a partly empty head group
 ])
 def test_attention_prefill(dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink):
     say("attention", dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink)
