@@ -41,8 +41,8 @@ _SIGS = {
     "hca_compress": (_I, [_P, _P, _P, _I, _L, _I, _I, _L, _I, _P, _F, _I, _F, _P, _L, _I, _P]),
     "cskv_indexer_workspace_size": (_Z, [_I, _L, _L, _I, _I, _I]),
     "indexer_topk": (_I, [_P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _I, _P, _P, _Z, _I, _P]),
-    "indexer_scores": (_I, [_P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _P, _L, _I, _P]),
-    "topk_select": (_I, [_P, _L, _I, _L, _L, _L, _I, _I, _P, _P, _Z, _P]),
+    "indexer_scores": (_I, [_P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _P, _L, _P, _L, _I, _P]),
+    "topk_select": (_I, [_P, _L, _P, _L, _I, _L, _L, _L, _I, _I, _P, _P, _Z, _P]),
     "cskv_topk_workspace_size": (_Z, [_I, _L, _L, _I]),
     "cskv_quantize_fp8": (_I, [_P, _L, _I, _I, _P, _P, _P]),
     "indexer_scores_fp8": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _P, _L, _P]),
@@ -216,16 +216,36 @@ def score_ld(N: int) -> int:
     return max(64, (N + 63) // 64 * 64)
 
 
-def indexer_scores(qI, wI, KI, pos0: int, m: int, scores=None) -> torch.Tensor:
-    """Lightning-indexer scores [batch, Tq, ld] fp32 (valid for s < V_t)."""
+def block_max_ld(N: int) -> int:
+    """Row stride used for block-maximum matrices: ceil(N / 32) rounded up to 4 blocks."""
+    return max(4, ((N + 31) // 32 + 3) // 4 * 4)
+
+
+def _check_bm(name: str, bm: torch.Tensor, batch: int, Tq: int, N: int) -> None:
+    _need(bm.dtype == torch.int32 and bm.dim() == 3 and tuple(bm.shape[:2]) == (batch, Tq)
+          and bm.shape[2] >= (N + 31) // 32 and bm.is_contiguous(),
+          f"{name}: block_max must be contiguous int32 [{batch}, {Tq}, >= {(N + 31) // 32}], got "
+          f"{bm.dtype} {tuple(bm.shape)}")
+
+
+def indexer_scores(qI, wI, KI, pos0: int, m: int, scores=None, block_max=None) -> torch.Tensor:
+    """Lightning-indexer scores [batch, Tq, ld] fp32 (valid for s < V_t).
+
+    `block_max` (optional, int32 [batch, Tq, >= ceil(N/32)] holding uint32 bit patterns) also
+    receives each 32-entry block's largest order key, for topk_select.
+    """
     batch, Tq, HI, dI = qI.shape
     N = KI.shape[1]
     if scores is None:
         scores = torch.empty(batch, Tq, score_ld(N), dtype=torch.float32, device=qI.device)
     _check_scores("indexer_scores", scores, batch, Tq, N)
+    bm, bm_ld = None, 0
+    if block_max is not None:
+        _check_bm("indexer_scores", block_max, batch, Tq, N)
+        bm, bm_ld = _ptr(block_max), block_max.shape[-1]
     _check("indexer_scores", lib().indexer_scores(
-        _ptr(qI), _ptr(wI), _ptr(KI), batch, Tq, N, HI, dI, pos0, m, _ptr(scores), scores.shape[-1],
-        _dtype(qI), _stream(qI)))
+        _ptr(qI), _ptr(wI), _ptr(KI), batch, Tq, N, HI, dI, pos0, m, _ptr(scores), scores.shape[-1], bm,
+        bm_ld, _dtype(qI), _stream(qI)))
     return scores
 
 
@@ -233,11 +253,13 @@ def topk_workspace_bytes(batch: int, Tq: int, N: int, k: int) -> int:
     return int(lib().cskv_topk_workspace_size(batch, Tq, N, k))
 
 
-def topk_select(scores, N: int, pos0: int, m: int, k: int, out=None, workspace=None) -> torch.Tensor:
+def topk_select(scores, N: int, pos0: int, m: int, k: int, out=None, workspace=None, block_max=None) -> torch.Tensor:
     """Top-k selection from a score matrix written by indexer_scores.
 
     `workspace` (optional, cskv_topk_workspace_size bytes) lets few long rows be
-    selected with several workgroups per row; the result is the same without it.
+    selected with several workgroups per row; `block_max` (optional) are the
+    block maxima indexer_scores wrote beside these scores. The result is the
+    same with or without either.
     """
     batch, Tq, ld = scores.shape
     if out is None:
@@ -245,8 +267,12 @@ def topk_select(scores, N: int, pos0: int, m: int, k: int, out=None, workspace=N
     _check_scores("topk_select", scores, batch, Tq, N)
     _check_idx("topk_select", out, batch, Tq, k)
     ws, nbytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
-    _check("topk_select", lib().topk_select(_ptr(scores), ld, batch, Tq, N, pos0, m, k, _ptr(out), ws, nbytes,
-                                            _stream(scores)))
+    bm, bm_ld = None, 0
+    if block_max is not None:
+        _check_bm("topk_select", block_max, batch, Tq, N)
+        bm, bm_ld = _ptr(block_max), block_max.shape[-1]
+    _check("topk_select", lib().topk_select(_ptr(scores), ld, bm, bm_ld, batch, Tq, N, pos0, m, k, _ptr(out), ws,
+                                            nbytes, _stream(scores)))
     return out
 
 

@@ -41,6 +41,13 @@ struct IdxArgs {
 // Rows of up to BM_MAX_BLOCKS blocks of 32 entries can be selected through block maxima.
 constexpr int BM_MAX_BLOCKS = 8192;
 
+// Rows whose visible entries run from vmin to vmax (the first and last row of a launch) take the
+// block-maxima route: every row has at least 2k blocks, so the k-th largest block maximum leaves a
+// few k candidates rather than the whole row, and at most BM_MAX_BLOCKS.
+inline bool bm_route(int64_t vmin, int64_t vmax, int k) {
+  return ceil_div(vmin, (int64_t)32) >= 2 * (int64_t)k && ceil_div(vmax, (int64_t)32) <= BM_MAX_BLOCKS;
+}
+
 
 // ReLU on the bit pattern: for non-NaN x, max(bits(x), 0) as int32 is bits(max(x, 0))
 // (negative floats, -0.0 included, are negative as int32). One VALU op, no NaN canonicalisation.

@@ -27,9 +27,12 @@ namespace cskv {
 
 // Prefill rows: 8 queries per workgroup, one per wave, sharing 256-key LDS tiles.
 // Each 32-key sub-block runs in two phases of KS/2 k-steps. A phase issues the
-// LDS reads of the next phase's B operands, then its own MFMAs, interleaved with
-// half of the previous sub-block's ReLU / weighted head-sum; scheduling barriers
-// keep the reads one phase (KS/2 x HT MFMAs) ahead of their use.
+// MFMAs of its first k-step, then the LDS reads of the next phase's B operands,
+// then its remaining MFMAs, interleaved with half of the previous sub-block's
+// ReLU / weighted head-sum; scheduling barriers keep the reads about one phase
+// ahead of their use. The compiler waits for every LDS read in flight before a
+// phase's first MFMA, so issuing the next reads after that point leaves it
+// waiting only for reads made a phase earlier (1% faster than reads first).
 template <int HT, int KS>
 __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
   constexpr int QB = 8;                // queries per workgroup (one per wave)
@@ -117,9 +120,9 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
 #pragma unroll
     for (int i = 0; i < KH; ++i) dst[i] = *reinterpret_cast<const bf16x8*>(kp + bofs[h * KH + i]);
   };
-  auto mmaH = [&](const bf16x8 (&bv)[KH], int h, f32x16 (&acc)[HT]) {
+  auto mmaH = [&](const bf16x8 (&bv)[KH], int h, f32x16 (&acc)[HT], int i0, int i1) {
 #pragma unroll
-    for (int i = 0; i < KH; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int ks = h * KH + i;
 #pragma unroll
       for (int ht = 0; ht < HT; ++ht)
@@ -166,17 +169,21 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
       // the previous sub-block (of this tile, or the last of the previous tile) is epilogued here
       const bool prev = sb > 0 || it > 0;
       const int sp = t0 + sb * 32 - 32;
-      // phase 0
+      // phase 0: its first k-step, then the reads of phase 1's operands, then the rest
+      mmaH(b0, 0, acc[sb & 1], 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
       rdB(kp + sb * 32 * DI, 1, b1);
       __builtin_amdgcn_sched_barrier(0);
-      mmaH(b0, 0, acc[sb & 1]);
+      mmaH(b0, 0, acc[sb & 1], 1, KH);
       float part = 0.f;
       if (prev) part = epiH(acc[(sb + 1) & 1], 0, 0.f);
       __builtin_amdgcn_sched_barrier(0);
       // phase 1
+      mmaH(b1, 1, acc[sb & 1], 0, 1);
+      __builtin_amdgcn_sched_barrier(0);
       if (sb + 1 < SUB) rdB(kp + (sb + 1) * 32 * DI, 0, b0);
       __builtin_amdgcn_sched_barrier(0);
-      mmaH(b1, 1, acc[sb & 1]);
+      mmaH(b1, 1, acc[sb & 1], 1, KH);
       if (prev) finish(epiH(acc[(sb + 1) & 1], 1, part), sp);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -493,21 +500,22 @@ extern "C" int indexer_topk(const void* qI, const float* wI, const void* KI, int
   a.qI = qI; a.wI = wI; a.KI = KI; a.scores = (float*)workspace; a.out = out_idx;
   a.Tq = Tq; a.N = N; a.pos0 = pos0; a.ldS = p.ldS; a.rows_ws = p.rows_ws;
   a.HI = HI; a.dI = dI; a.m = m; a.k = k;
-  // few long rows scored one query per workgroup (decode): the scorer writes the block maxima
-  // into the rows' selection workspace
-  const bool bm_stream = dtype == CSKV_BF16 && p.qb == 1 && split_bytes && ceil_div(N, (int64_t)32) <= BM_MAX_BLOCKS;
   for (int64_t r0 = 0; r0 < Tq; r0 += p.rows_ws) {
     a.row0 = r0;
     a.nrows = (Tq - r0) < p.rows_ws ? (Tq - r0) : p.rows_ws;
-    if (bm_stream) {
-      a.bm = reinterpret_cast<uint32_t*>(sel_ws);
-      a.bm_ld = topk_sel_stride() / 4;
-      a.bm_rows = a.nrows;
-      a.bm_fused = 1;
-    }
     const int64_t last = pos0 + r0 + a.nrows - 1;
     int64_t vmax = (last + 1) / m;
     if (vmax > N) vmax = N;
+    int64_t vmin = (pos0 + r0 + 1) / m;
+    if (vmin > N) vmin = N;
+    // few long rows scored one query per workgroup (decode): the scorer writes the block maxima
+    // into the rows' selection workspace
+    a.bm_fused = dtype == CSKV_BF16 && p.qb == 1 && split_bytes && bm_route(vmin, vmax, k);
+    if (a.bm_fused) {
+      a.bm = reinterpret_cast<uint32_t*>(sel_ws);
+      a.bm_ld = topk_sel_stride() / 4;
+      a.bm_rows = a.nrows;
+    }
     if (vmax > k) {  // rows with V_t <= k need no scores
       st = launch_scores(a, batch, (int)p.qb, dtype, hs);
       if (st) return st;
@@ -520,17 +528,25 @@ extern "C" int indexer_topk(const void* qI, const float* wI, const void* KI, int
 
 extern "C" int indexer_scores(const void* qI, const float* wI, const void* KI, int batch, int64_t Tq,
                               int64_t N, int HI, int dI, int64_t pos0, int m, float* scores,
-                              int64_t ld, int dtype, void* stream) {
+                              int64_t ld, uint32_t* block_max, int64_t bm_ld, int dtype, void* stream) {
   int st = check_indexer_shape(batch, Tq, N, HI, dI, pos0, m, dtype);
   if (st) return st;
   if (ld < N || ld % 4 != 0) return CSKV_ERR_BAD_SHAPE;
+  if (block_max && dtype != CSKV_BF16) return CSKV_ERR_UNSUPPORTED;
+  if (block_max && (bm_ld < ceil_div(N, (int64_t)32) || bm_ld % 4 != 0)) return CSKV_ERR_BAD_SHAPE;
   if (batch == 0 || Tq == 0) return CSKV_OK;
   if (!qI || !wI || !scores || (N > 0 && !KI)) return CSKV_ERR_INVALID_ARG;
-  if (!aligned16(qI, wI, KI, scores)) return CSKV_ERR_MISALIGNED;
+  if (!aligned16(qI, wI, KI, scores, block_max)) return CSKV_ERR_MISALIGNED;
   IdxArgs a{};
   a.qI = qI; a.wI = wI; a.KI = KI; a.scores = scores;
   a.Tq = Tq; a.N = N; a.pos0 = pos0; a.ldS = ld; a.rows_ws = Tq; a.row0 = 0; a.nrows = Tq;
   a.HI = HI; a.dI = dI; a.m = m;
   const int qb = (dtype == CSKV_BF16 && Tq >= 64) ? 8 : 1;
+  if (block_max && qb == 1) {  // the one-query-per-workgroup scorer writes the block maxima
+    a.bm = block_max;
+    a.bm_ld = bm_ld;
+    a.bm_rows = Tq;
+    a.bm_fused = 1;
+  }
   return launch_scores(a, batch, qb, dtype, (hipStream_t)stream);
 }

@@ -733,12 +733,14 @@ int launch_select(IdxArgs& a, int batch, void* sel_ws, size_t sel_bytes, hipStre
   if (vmax > a.N) vmax = a.N;
   SplitPlan sp;
   const int64_t rows = (int64_t)batch * a.nrows;
-  if (a.bm_fused) {  // the scorer wrote the block maxima (set only where ws_ok and the rows fit)
+  int64_t vmin = (a.pos0 + a.row0 + 1) / a.m;
+  if (vmin > a.N) vmin = a.N;
+  if (a.bm_fused) {  // the scorer wrote the block maxima (set only where bm_route holds)
     hipLaunchKernelGGL(topk_bm_select, dim3((unsigned)a.nrows, (unsigned)batch), dim3(TOPK_THREADS), 0, st, a);
     return hipGetLastError() == hipSuccess ? CSKV_OK : CSKV_ERR_HIP;
   }
   const bool ws_ok = sel_ws && plan_split(rows, vmax, a.k, sp) && sel_bytes >= (size_t)(rows * TOPK_SEL_STRIDE);
-  if (ws_ok && ceil_div(vmax, (int64_t)32) <= BM_MAX_BLOCKS) {
+  if (ws_ok && bm_route(vmin, vmax, a.k)) {
     static_assert((int64_t)BM_MAX_BLOCKS * 4 <= TOPK_SEL_STRIDE, "block maxima fit a row's workspace");
     a.sel_ws = (uint8_t*)sel_ws;
     a.bm = reinterpret_cast<uint32_t*>(sel_ws);
@@ -770,19 +772,29 @@ extern "C" size_t cskv_topk_workspace_size(int batch, int64_t Tq, int64_t N, int
   return split_ws_bytes((int64_t)batch * Tq, N, k);
 }
 
-extern "C" int topk_select(const float* scores, int64_t ld, int batch, int64_t Tq, int64_t N,
-                           int64_t pos0, int m, int k, int32_t* out_idx, void* workspace, size_t ws_bytes,
-                           void* stream) {
+extern "C" int topk_select(const float* scores, int64_t ld, const uint32_t* block_max, int64_t bm_ld, int batch,
+                           int64_t Tq, int64_t N, int64_t pos0, int m, int k, int32_t* out_idx, void* workspace,
+                           size_t ws_bytes, void* stream) {
   if (batch < 0 || Tq < 0 || N < 0 || pos0 < 0 || m < 1 || ld < N) return CSKV_ERR_BAD_SHAPE;
   if (ld % 4 != 0) return CSKV_ERR_BAD_SHAPE;
+  if (block_max && (bm_ld < ceil_div(N, (int64_t)32) || bm_ld % 4 != 0)) return CSKV_ERR_BAD_SHAPE;
   if (k < 1) return CSKV_ERR_BAD_SHAPE;
   if (k > CSKV_MAX_TOPK) return CSKV_ERR_UNSUPPORTED;
   if (batch == 0 || Tq == 0) return CSKV_OK;
   if (!out_idx || (N > 0 && !scores)) return CSKV_ERR_INVALID_ARG;
-  if (!aligned16(scores, out_idx, workspace)) return CSKV_ERR_MISALIGNED;
+  if (!aligned16(scores, out_idx, workspace, block_max)) return CSKV_ERR_MISALIGNED;
   IdxArgs a{};
   a.scores = (float*)scores; a.out = out_idx;
   a.Tq = Tq; a.N = N; a.pos0 = pos0; a.ldS = ld; a.rows_ws = Tq; a.row0 = 0; a.nrows = Tq;
   a.m = m; a.k = k;
+  int64_t vmin = (pos0 + 1) / m, vmax = (pos0 + Tq) / m;
+  if (vmin > N) vmin = N;
+  if (vmax > N) vmax = N;
+  if (block_max && Tq < 64 && bm_route(vmin, vmax, k)) {  // block maxima written by indexer_scores
+    a.bm = const_cast<uint32_t*>(block_max);
+    a.bm_ld = bm_ld;
+    a.bm_rows = Tq;
+    a.bm_fused = 1;
+  }
   return launch_select(a, batch, workspace, workspace ? ws_bytes : 0, (hipStream_t)stream);
 }

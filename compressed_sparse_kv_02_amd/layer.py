@@ -13,7 +13,8 @@ CSA layer, in order:
   2. csa_compress  indexer-key streams -> new indexer keys, appended;
   3. hca_compress  (m' = 1) raw rows of the new tokens -> window rows;
   4. indexer_scores + topk_select (the two halves of indexer_topk, kept
-                   apart so the scoring kernel can be timed on its own);
+                   apart so the scoring kernel can be timed on its own; the
+                   scorer's block maxima let long rows skip a score pass);
   5. compressed_attn_prefill / _decode (CSA mode).
 HCA layer: hca_compress (m') -> append, window rows, attention (HCA mode).
 
@@ -116,6 +117,8 @@ def make_inputs(L: LayerCall, device="cuda") -> Dict[str, torch.Tensor]:
         t["wI"] = uniform_device(L.seed, f"{L.name}.wI", (Bt, T, L.HI), device)
         t["idx"] = torch.empty(Bt, T, L.k, dtype=torch.int32, device=device)
         t["ws.scores"] = torch.empty(Bt, T, B.score_ld(L.N), dtype=torch.float32, device=device)
+        if L.dtype == "bf16":  # block maxima beside the scores, for the selection of long rows
+            t["ws.bm"] = torch.empty(Bt, T, B.block_max_ld(L.N), dtype=torch.int32, device=device)
         nsel = B.topk_workspace_bytes(Bt, T, L.N, L.k)
         if nsel:
             t["ws.topk"] = torch.empty(nsel, dtype=torch.uint8, device=device)
@@ -157,13 +160,15 @@ def window_step(L: LayerCall, t: Dict[str, torch.Tensor]) -> None:
 def score_step(L: LayerCall, t: Dict[str, torch.Tensor]) -> None:
     """Step 4a (CSA only): lightning-indexer scores of every query over the whole cache."""
     if L.kind == "csa":
-        B.indexer_scores(t["qI"], t["wI"], t["cache.ik"], L.pos0, L.m, scores=t["ws.scores"])
+        B.indexer_scores(t["qI"], t["wI"], t["cache.ik"], L.pos0, L.m, scores=t["ws.scores"],
+                         block_max=t.get("ws.bm"))
 
 
 def topk_step(L: LayerCall, t: Dict[str, torch.Tensor]) -> None:
     """Step 4b (CSA only): per-query top-k of the scores (indexer_topk's second half)."""
     if L.kind == "csa":
-        B.topk_select(t["ws.scores"], L.N, L.pos0, L.m, L.k, out=t["idx"], workspace=t.get("ws.topk"))
+        B.topk_select(t["ws.scores"], L.N, L.pos0, L.m, L.k, out=t["idx"], workspace=t.get("ws.topk"),
+                      block_max=t.get("ws.bm"))
 
 
 def select_step(L: LayerCall, t: Dict[str, torch.Tensor]) -> None:
@@ -239,6 +244,8 @@ class DecodeStream:
         if L.kind == "csa":
             self.idx = torch.empty(Bt, 1, L.k, dtype=torch.int32, device=device)
             self.scores = torch.empty(Bt, 1, B.score_ld(capacity), dtype=torch.float32, device=device)
+            self.bm = (torch.empty(Bt, 1, B.block_max_ld(capacity), dtype=torch.int32, device=device)
+                       if L.dtype == "bf16" else None)
             nsel = B.topk_workspace_bytes(Bt, 1, capacity, L.k)
             self.ws_topk = torch.empty(nsel, dtype=torch.uint8, device=device) if nsel else None
         self.n_entries = 0
@@ -279,8 +286,9 @@ class DecodeStream:
         mode = B.CSA if L.kind == "csa" else B.HCA
         idx = None
         if L.kind == "csa":
-            B.indexer_scores(qI, wI, self.cache["ik"], t, L.m, scores=self.scores)
-            B.topk_select(self.scores, self.capacity, t, L.m, L.k, out=self.idx, workspace=self.ws_topk)
+            B.indexer_scores(qI, wI, self.cache["ik"], t, L.m, scores=self.scores, block_max=self.bm)
+            B.topk_select(self.scores, self.capacity, t, L.m, L.k, out=self.idx, workspace=self.ws_topk,
+                          block_max=self.bm)
             idx = self.idx
         return B.compressed_attn_decode(mode, q, self.cache["kv"], idx, self.win, 0, sink, t, L.m, L.w, k=L.k,
                                         apply_q_norm=True, rope_dims=L.rope_dims, rope_on_output=True,

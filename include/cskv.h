@@ -166,12 +166,34 @@ int indexer_topk(const void* qI, const float* wI, const void* KI, int batch, int
  * does (k largest of the first V_t scores, smaller index first among equal
  * scores, ascending, -1 padded). Its workspace is optional (see
  * cskv_topk_workspace_size); ld % 4 == 0 and 16-byte aligned rows.
+ *
+ * Block maxima (optional; NULL = none), for decode-shaped calls. With
+ * block_max != NULL (dtype CSKV_BF16 only, else CSKV_ERR_UNSUPPORTED) and
+ * Tq < 64, indexer_scores also writes, for every 32-entry block
+ * i < ceil(V_t / 32) of query j,
+ *   block_max[(b*Tq + j)*bm_ld + i] = max over s in [32 i, min(32 i + 32, V_t))
+ *                                     of key(scores[(b*Tq + j)*ld + s])
+ * where key(x) is the fp32 bit pattern of x with the sign bit set when x is
+ * non-negative and every bit flipped when it is negative (larger x, larger
+ * key; key > 0 for every score). Later blocks, and the whole of block_max
+ * when Tq >= 64, are left untouched (the many-query scorer is bound by the
+ * matrix cores, and the maxima would cost it more than they save).
+ *   block_max : [batch, Tq, bm_ld] uint32, bm_ld >= ceil(N / 32), bm_ld % 4 == 0,
+ *               16-byte aligned (else CSKV_ERR_BAD_SHAPE / CSKV_ERR_MISALIGNED)
+ * topk_select given the block maxima that indexer_scores wrote with the same
+ * batch, Tq, N, pos0 and m reads only the blocks of largest maxima of long
+ * rows, without a pass over the whole score rows: it does so when Tq < 64 and
+ * every row of the call has at least 2k blocks and at most 8192 (k = 1024:
+ * 65536 <= V_t <= 262144), and ignores them otherwise. The result is the same
+ * either way; maxima that do not match the scores give an unspecified
+ * selection (within the row's first V_t entries).
  */
 int indexer_scores(const void* qI, const float* wI, const void* KI, int batch, int64_t Tq, int64_t N,
-                   int HI, int dI, int64_t pos0, int m, float* scores, int64_t ld, int dtype,
-                   void* stream);
-int topk_select(const float* scores, int64_t ld, int batch, int64_t Tq, int64_t N, int64_t pos0, int m,
-                int k, int32_t* out_idx, void* workspace, size_t ws_bytes, void* stream);
+                   int HI, int dI, int64_t pos0, int m, float* scores, int64_t ld, uint32_t* block_max,
+                   int64_t bm_ld, int dtype, void* stream);
+int topk_select(const float* scores, int64_t ld, const uint32_t* block_max, int64_t bm_ld, int batch,
+                int64_t Tq, int64_t N, int64_t pos0, int m, int k, int32_t* out_idx, void* workspace,
+                size_t ws_bytes, void* stream);
 
 /*
  * cskv_topk_workspace_size -- device bytes topk_select may use to select few

@@ -120,9 +120,31 @@ def test_indexer_topk_validation(L):
     assert need >= 64 * 1000 * 4
 
 
+def test_indexer_scores_validation(L):
+    f = L.indexer_scores
+    base = dict(qI=P, wI=P, KI=P, batch=1, Tq=64, N=1000, HI=64, dI=128, pos0=0, m=4, scores=P, ld=1024,
+                bm=None, bm_ld=0, dt=0, st=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*a.values())
+    assert call(ld=999) == SHAPE       # ld < N
+    assert call(ld=1026) == SHAPE      # ld % 4 != 0
+    assert call(scores=None) == INVALID
+    assert call(scores=P + 4) == MISALIGNED
+    # block maxima: one per 32 entries (ceil(1000 / 32) = 32), bf16 scorers only
+    assert call(bm=P, bm_ld=32, dt=1) == UNSUPPORTED
+    assert call(bm=P, bm_ld=28) == SHAPE
+    assert call(bm=P, bm_ld=34) == SHAPE
+    assert call(bm=P + 8, bm_ld=32) == MISALIGNED
+    assert call(bm=P, bm_ld=32, Tq=0) == OK
+    assert call(Tq=0) == OK
+
+
 def test_topk_select_validation(L):
     f = L.topk_select
-    base = dict(scores=P, ld=1024, batch=1, Tq=4, N=1000, pos0=0, m=4, k=64, out=P, ws=None, wsb=0, st=None)
+    base = dict(scores=P, ld=1024, bm=None, bm_ld=0, batch=1, Tq=4, N=1000, pos0=0, m=4, k=64, out=P, ws=None,
+                wsb=0, st=None)
 
     def call(**kw):
         a = dict(base, **kw)
@@ -134,6 +156,9 @@ def test_topk_select_validation(L):
     assert call(out=None) == INVALID
     assert call(out=P + 8) == MISALIGNED
     assert call(ws=P + 8, wsb=1 << 20) == MISALIGNED
+    assert call(bm=P, bm_ld=28) == SHAPE     # fewer than ceil(N / 32) blocks per row
+    assert call(bm=P, bm_ld=33) == SHAPE     # bm_ld % 4 != 0
+    assert call(bm=P + 4, bm_ld=32) == MISALIGNED
     assert call(Tq=0) == OK
     # the two-kernel route is offered to few rows of at least 4 x 8192 entries only
     assert L.cskv_topk_workspace_size(8, 1, 262144, 1024) > 0

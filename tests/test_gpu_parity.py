@@ -148,6 +148,64 @@ def test_indexer_decode_1m_full():
         check_topk_row(idx[b, 0], I, 262144, 1024, what=f"b{b}")
 
 
+def block_max_of(sc, pos0, m, N):
+    """[batch, Tq, ceil(N/32)] int64: each 32-entry block's largest order key among the first V_t
+    scores of a row (key: the fp32 bits with the sign bit set for non-negative scores, all bits
+    flipped for negative ones; 0 where the block holds no visible entry)."""
+    bt, Tq, _ = sc.shape
+    nb = (N + 31) // 32
+    u = sc[..., :N].contiguous().view(torch.int32).to(torch.int64) & 0xFFFFFFFF
+    key = torch.where(u >= 0x80000000, u ^ 0xFFFFFFFF, u | 0x80000000)
+    V = torch.tensor([O.visible(pos0 + r, m, N) for r in range(Tq)], device=sc.device)
+    s = torch.arange(N, device=sc.device)
+    key = torch.where(s[None, None, :] < V[None, :, None], key, torch.zeros_like(key))
+    return torch.nn.functional.pad(key, (0, nb * 32 - N)).view(bt, Tq, nb, 32).amax(-1)
+
+
+def _as_block_max(key, N):
+    """int64 keys -> the int32 bit patterns of a [batch, Tq, block_max_ld(N)] block-maximum matrix."""
+    bm = torch.zeros(*key.shape[:2], B.block_max_ld(N), dtype=torch.int32, device=key.device)
+    bm[..., :key.shape[-1]] = torch.where(key >= 2 ** 31, key - 2 ** 32, key).to(torch.int32)
+    return bm
+
+
+@pytest.mark.parametrize("bt,Tq,N,HI,dI,pos0,k", [
+    (3, 1, 90000, 64, 128, 4 * 90000, 1024),          # decode rows of 2813 blocks
+    (2, 5, 262144, 64, 128, 4 * 262144 - 5, 1024),    # 8192 blocks (the most)
+    (1, 63, 5000, 20, 64, 4 * 5000 - 70, 64),         # the most queries written, 20 heads, 157 blocks
+    (2, 3, 40000, 64, 128, 4 * 40000, 1024),          # 1250 blocks, fewer than 2k: maxima unused
+    (2, 100, 70000, 64, 128, 4 * 70000 - 120, 1024),  # 100 queries: maxima left untouched, unused
+])
+def test_indexer_block_max(bt, Tq, N, HI, dI, pos0, k):
+    """indexer_scores' block maxima (calls of fewer than 64 queries) equal the definition over the
+    scores it wrote; the selection given them equals the selection without them, indexer_topk's,
+    and (sampled rows) the oracle's."""
+    say("indexer block maxima", bt, Tq, N, HI, dI, pos0, k)
+    qI = gen(29, "bm.q", (bt, Tq, HI, dI))
+    KI = gen(29, "bm.k", (bt, N, dI))
+    wI = uniform_device(29, "bm.w", (bt, Tq, HI), DEV)
+    bm = torch.full((bt, Tq, B.block_max_ld(N)), -1, dtype=torch.int32, device=DEV)
+    sc = B.indexer_scores(qI, wI, KI, pos0, 4, block_max=bm)
+    a = B.topk_select(sc, N, pos0, 4, k, block_max=bm)
+    b = B.topk_select(sc, N, pos0, 4, k)
+    c = B.indexer_topk(qI, wI, KI, pos0, 4, k)
+    torch.cuda.synchronize()
+    if Tq < 64:
+        key = block_max_of(sc, pos0, 4, N).cpu()
+        got = bm.cpu().to(torch.int64) & 0xFFFFFFFF
+        for r in range(Tq):
+            nb = (O.visible(pos0 + r, 4, N) + 31) // 32
+            assert torch.equal(got[:, r, :nb], key[:, r, :nb]), r
+    else:
+        assert bool((bm == -1).all())
+    assert torch.equal(a, b)
+    assert torch.equal(a, c)
+    a = a.cpu().numpy()
+    for bb, r in {(0, 0), (bt - 1, Tq - 1)}:
+        I = O.indexer_scores(np64(qI[bb, r:r + 1]), np64(wI[bb, r:r + 1]), np64(KI[bb]), pos0 + r, 4)[0]
+        check_topk_row(a[bb, r], I, O.visible(pos0 + r, 4, N), k, what=f"b{bb} r{r}")
+
+
 @pytest.mark.parametrize("kind,bt,Tq,N,k", [
     ("normal", 2, 3, 200000, 1024),
     ("normal", 1, 2, 262144, 2048),   # max k: 32 parts x 256 candidates
@@ -156,13 +214,14 @@ def test_indexer_decode_1m_full():
     ("ties", 2, 2, 65536, 2048),      # 16 distinct values: ties across parts
     ("equal", 1, 1, 40000, 100),      # one value: the first k indices
     ("normal", 8, 1, 262144, 1024),   # the decode shape: block maxima, 8192 blocks per row
-    ("normal", 1, 2, 40000, 1024),    # 1250 blocks: the candidate blocks are most of the row
+    ("normal", 1, 2, 40000, 1024),    # 1250 blocks, fewer than 2k: parts + merge
     ("normal", 1, 2, 300000, 1024),   # more than 8192 blocks: parts + merge
+    ("ties", 1, 2, 262144, 1024),     # block maxima route, candidates overflow LDS: exact fallback
 ])
 def test_topk_split_route(kind, bt, Tq, N, k):
-    """Few long rows go through a several-workgroups-per-row route (block maxima up to 8192 blocks of
-    32 entries, parts + merge beyond); it must equal the one-workgroup-per-row route and the oracle's
-    top-k exactly (same fp32 scores on both sides)."""
+    """Few long rows go through a several-workgroups-per-row route (block maxima from 2k up to 8192
+    blocks of 32 entries, parts + merge otherwise); it must equal the one-workgroup-per-row route, the
+    selection given block maxima, and the oracle's top-k exactly (same fp32 scores on every side)."""
     say("topk split route", kind, bt, Tq, N, k)
     ld = B.score_ld(N)
     if kind == "normal":
@@ -179,8 +238,10 @@ def test_topk_split_route(kind, bt, Tq, N, k):
     ws = torch.empty(B.topk_workspace_bytes(bt, Tq, N, k), dtype=torch.uint8, device=DEV)
     a = B.topk_select(sc, N, pos0, 4, k, workspace=ws)
     b = B.topk_select(sc, N, pos0, 4, k)
+    c = B.topk_select(sc, N, pos0, 4, k, block_max=_as_block_max(block_max_of(sc, pos0, 4, N), N))
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+    assert torch.equal(a, c)
     a, scn = a.cpu().numpy(), sc.cpu().numpy().astype(np.float64)
     for bb in range(bt):
         for r in range(Tq):
