@@ -136,6 +136,30 @@ def test_hca_uniform_is_block_mean():
     assert np.allclose(out, X.reshape(2, 128, 4).mean(axis=1), atol=1e-13)
 
 
+def test_hca_positional_bias_enters_the_softmax():
+    # The bias B[p] is added to the logit of row p of every block ("Paper Breakdown:
+    # DeepSeek-V4", §2.3.2: softmax of Z + B over the block's m' rows).
+    m, c = 4, 3
+    X = rng.normal(size=(2 * m, c))
+    # Z = -B cancels the bias: uniform weights, the block mean.
+    Bv = rng.normal(size=(m, c)) * 3
+    out = O.hca_compress(X, -np.tile(Bv, (2, 1)), Bv, m=m)
+    assert np.allclose(out, X.reshape(2, m, c).mean(axis=1), atol=1e-13)
+    # Z = 0 with one large bias per channel selects that row of each block, per channel.
+    rows = np.array([0, 3, 1])
+    Bh = np.zeros((m, c))
+    Bh[rows, np.arange(c)] = 1e4
+    out = O.hca_compress(X, None, Bh, m=m)
+    expect = np.stack([X[i * m + rows, np.arange(c)] for i in range(2)])
+    assert np.allclose(out, expect, atol=1e-12)
+    # A bias of log(3) on row 1 only: weights 1:3:1:1 in every block.
+    B3 = np.zeros((m, c))
+    B3[1] = math.log(3.0)
+    out = O.hca_compress(X, None, B3, m=m)
+    w = np.array([1.0, 3.0, 1.0, 1.0]) / 6.0
+    assert np.allclose(out, np.einsum("p,ipc->ic", w, X.reshape(2, m, c)), atol=1e-13)
+
+
 # ---------------------------------------------------------- RMSNorm and RoPE
 
 def test_rmsnorm_closed_form_and_unit_rms():
