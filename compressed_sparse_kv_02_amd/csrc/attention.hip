@@ -1125,11 +1125,10 @@ extern "C" int compressed_attn_prefill_kv8(int mode, const void* q, const uint8_
                            rope_on_output, out, lse, CSKV_BF16, stream);
 }
 
-// Splits per query: about one workgroup per compute unit (256) over the whole call, at
-// least 4 key tiles each. Every split costs a query prologue and an fp32 partial of
-// H x d written and merged, so more splits than CUs only add traffic.
-// Automatic split count: about one workgroup per CU over the call (256 / queries), at least 4 key
-// tiles per split, at most 256. Without the key count this is bounded by the first term alone.
+// Automatic split count: about one workgroup per CU over the call (256 / queries), at least 2 key
+// tiles per split, at most 256. Every split costs a query prologue and an fp32 partial of H x d
+// written and merged, so more splits than CUs only add traffic. Without the key count this is
+// bounded by the first term alone.
 static int64_t auto_splits_bound(int batch, int64_t Tq) {
   int64_t s = (256 + batch * Tq - 1) / (batch * Tq);
   return s > 256 ? 256 : (s < 1 ? 1 : s);
@@ -1139,7 +1138,7 @@ static int decode_splits(int batch, int64_t Tq, int64_t max_k, int n_splits) {
   if (n_splits > 0) return n_splits;
   const int64_t nblk = (max_k + 31) / 32;
   int64_t s = auto_splits_bound(batch, Tq);
-  const int64_t cap = (nblk + 3) / 4;
+  const int64_t cap = (nblk + 1) / 2;
   if (s > cap) s = cap;
   if (s < 1) s = 1;
   return (int)s;

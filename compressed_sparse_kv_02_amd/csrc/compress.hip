@@ -415,9 +415,12 @@ __global__ __launch_bounds__(NW * 64) void compress_block_kernel(CompressArgs a)
       sm[cg][v] = 0.f;
       acc[cg][v] = 0.f;
     }
-  constexpr int RB = 4;
+  // RB rows per wave per round, every load of the round issued before the first softmax step
+  // (raw 16-byte pieces, widened at use): a 128-row entry at 8 waves is one round trip
+  static_assert(VEC * sizeof(T) == 16, "16-byte pieces");
+  constexpr int RB = (NW >= 16 ? 8 : 16) / CPL;  // 48 or 24 loads per lane in flight
   for (int r0 = wave; r0 < nrows; r0 += NW * RB) {
-    float cv[RB][CPL][VEC], zv[RB][CPL][VEC];
+    uint4 craw[RB][CPL], zraw[RB][CPL], braw[RB][CPL];
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int rr = r0 + i * NW;
@@ -427,26 +430,24 @@ __global__ __launch_bounds__(NW * 64) void compress_block_kernel(CompressArgs a)
 #pragma unroll
       for (int cg = 0; cg < CPL; ++cg) {
         const int g = lane + 64 * cg < groups ? lane + 64 * cg : groups - 1;
-        load_vec<T, VEC>(cp + g * VEC, cv[i][cg]);
-        if (zp) {
-          load_vec<T, VEC>(zp + g * VEC, zv[i][cg]);
-        } else {
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) zv[i][cg][v] = 0.f;
-        }
-        if (bp) {
-          float bv[VEC];
-          load_vec<T, VEC>(bp + g * VEC, bv);
-#pragma unroll
-          for (int v = 0; v < VEC; ++v) zv[i][cg][v] += bv[v];
-        }
+        craw[i][cg] = *reinterpret_cast<const uint4*>(cp + g * VEC);
+        zraw[i][cg] = zp ? *reinterpret_cast<const uint4*>(zp + g * VEC) : uint4{0u, 0u, 0u, 0u};
+        braw[i][cg] = bp ? *reinterpret_cast<const uint4*>(bp + g * VEC) : uint4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       if (r0 + i * NW >= nrows) break;
 #pragma unroll
-      for (int cg = 0; cg < CPL; ++cg) softmax_step<VEC>(mx[cg], sm[cg], acc[cg], zv[i][cg], cv[i][cg]);
+      for (int cg = 0; cg < CPL; ++cg) {
+        float cv[VEC], zv[VEC], bv[VEC];
+        unpack16<T, VEC>(craw[i][cg], cv);
+        unpack16<T, VEC>(zraw[i][cg], zv);
+        unpack16<T, VEC>(braw[i][cg], bv);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) zv[v] += bv[v];  // an absent Z or B reads as +0
+        softmax_step<VEC>(mx[cg], sm[cg], acc[cg], zv, cv);
+      }
     }
   }
 #pragma unroll

@@ -49,6 +49,22 @@ struct Elem<bf16> {
   static __device__ __forceinline__ void store(bf16* p, int64_t i, float x) { p[i].v = f2bf(x); }
 };
 
+// The VEC elements of one 16-byte piece (8 bf16 or 4 fp32 values) as fp32.
+template <typename T, int VEC>
+__device__ __forceinline__ void unpack16(const uint4 r, float* out) {
+  static_assert(VEC * sizeof(T) == 16, "16-byte piece");
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (sizeof(T) == 2) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    } else {
+      out[i] = __uint_as_float(w[i]);
+    }
+  }
+}
+
 // Load VEC consecutive elements (VEC * sizeof(T) bytes, aligned) as fp32.
 template <typename T, int VEC>
 __device__ __forceinline__ void load_vec(const T* p, float* out) {

@@ -378,7 +378,7 @@ int compressed_attn_prefill(int mode, const void* q, const void* kv, const int32
  * kernel combines the splits in a fixed order. Arguments as in
  * compressed_attn_prefill, plus:
  *   n_splits  : 0 = choose from the shape (S = min(ceil(256 / (batch * Tq)),
- *               ceil(key tiles / 4), 256), a key tile being 32 keys); else
+ *               ceil(key tiles / 2), 256), a key tile being 32 keys); else
  *               1 .. 256 splits per query
  *   workspace : cskv_decode_workspace_size(...) bytes of device memory: the
  *               fp32 partials, batch * Tq * S * H * (d + 2) * 4 bytes when
