@@ -159,6 +159,62 @@ def traffic_summary() -> None:
               f"| {e.get('WRITE_SIZE_bytes', 0) / 1e6:.1f} | {mb} | {ck} |")
 
 
+# what each (kernel, grid) of the profiled bench run is, for the kernel-time table
+KERNEL_ROLES = {
+    ("indexer_score_mfma<2, 8>", 524288): "chunk CSA scoring (2 x 4096 queries, 131072 keys)",
+    ("attn_mfma<512, 4, 2, -1, 1>", 2097152): "chunk HCA attention (8192 queries, 64 heads)",
+    ("attn_mfma<512, 4, 1, -1, 2>", 16777216): "64K CSA attention",
+    ("attn_mfma<512, 4, 1, -1, 2>", 2097152): "chunk CSA attention (8192 queries, 64 heads)",
+    ("indexer_score_mfma<2, 8>", 4194304): "64K CSA scoring",
+    ("topk_select", 4194304): "chunk CSA top-k (8192 rows)",
+    ("topk_select", 33554432): "64K CSA top-k (65536 rows)",
+    ("attn_mfma<512, 2, 2, -1, 2>", 2097152): "16K HCA attention (32 heads)",
+    ("indexer_score_stream<2, 8>", 262144): "decode CSA scoring (8 x 262144 keys)",
+    ("compress_block_kernel<bf16, 8, 1, 8>", 32768): "chunk HCA compression (2 x 32 entries of 128 rows)",
+    ("compress_rows_kernel<bf16, 8, 1, 4>", 131072): "chunk window rows (2 x 4096)",
+    ("compress_pool8_kernel<bf16, 8, 1>", 1048576): "64K CSA KV compression (16384 entries)",
+    ("attn_mfma<512, 4, 1, -1, 1>", 65536): "decode HCA attention (32 splits)",
+    ("compress_pool8_kernel<bf16, 8, 1>", 131072): "chunk CSA KV compression (2 x 1024 entries)",
+    ("compress_rows_kernel<bf16, 8, 1, 4>", 1048576): "64K CSA window rows",
+    ("topk_bm_select", 4096): "decode top-k: select",
+    ("attn_mfma<512, 4, 1, -1, 1>", 36864): "decode CSA attention (18 splits)",
+    ("compress_block_kernel<bf16, 8, 1, 8>", 65536): "16K HCA compression (128 entries)",
+    ("compress_rows_kernel<bf16, 8, 1, 1>", 512): "decode window rows (8)",
+    ("attn_merge<bf16>", 131072): "decode split merge",
+    ("compress_pool8_kernel<bf16, 8, 1>", 32768): "chunk CSA indexer-key compression",
+    ("compress_pool8_kernel<bf16, 8, 1>", 262144): "64K CSA indexer-key compression",
+    ("compress_rows_kernel<bf16, 8, 1, 4>", 262144): "16K HCA window rows",
+}
+
+
+def kernel_table(trace_csv: str) -> None:
+    """Per-dispatch kernel times of a rocprofv3 --kernel-trace csv as a markdown table, one line per
+    library kernel and launch grid (work-items); other kernels (torch's input synthesis) are left out."""
+    import collections
+    import csv
+    import re
+
+    def short(name):
+        name = re.sub(r"^void ", "", name).replace("cskv::", "")
+        return re.sub(r"\(.*\)$", "", name).strip()
+
+    times = collections.defaultdict(list)
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            n = short(r["Kernel_Name"])
+            if not n.startswith(("indexer_", "attn_", "topk_", "compress_", "quantize_", "gemm_")):
+                continue
+            g = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) if "Grid_Size_X" in r \
+                else int(r["Grid_Size"])
+            times[(n, g)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    total = sum(sum(v) for v in times.values())
+    print("| kernel | grid (work-items) | what | dispatches | avg (us) | min (us) | max (us) | % of our kernels' time |")
+    print("|---|---:|---|---:|---:|---:|---:|---:|")
+    for (n, g), v in sorted(times.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{n}` | {g} | {KERNEL_ROLES.get((n, g), '-')} | {len(v)} | {sum(v) / len(v):.1f} | {min(v):.1f} "
+              f"| {max(v):.1f} | {100 * sum(v) / total:.2f} |")
+
+
 def visible_pairs(L) -> int:
     """Sum over the call's queries of the visible compressed entries (indexer (t, s) pairs)."""
     tot = 0
@@ -554,7 +610,12 @@ def main():
                     help="write profiles/traffic.json from rocprofv3 --pmc runs (FETCH_SIZE csv, WRITE_SIZE "
                          "csv[, SQ_VALU_MFMA_BUSY_CYCLES + GRBM_GUI_ACTIVE csv]) and exit")
     ap.add_argument("--traffic-summary", action="store_true", help="print profiles/traffic.json as a table and exit")
+    ap.add_argument("--kernel-table", metavar="CSV",
+                    help="print the kernel times of a rocprofv3 --kernel-trace csv as a table and exit")
     args = ap.parse_args()
+    if args.kernel_table:
+        kernel_table(args.kernel_table)
+        return
     if args.write_traffic:
         write_traffic(*args.write_traffic)
         return
