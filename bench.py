@@ -523,8 +523,12 @@ def kv_fp8_attention_rows(prefill, tp, decode, td, reps: int = 3):
             call = lambda kv, s_: B.compressed_attn_decode(mode, t["q"], kv, idx, t["win"], L.win_pos0, t["sink"],
                                                            L.pos0, L.m, L.w, kv_scale=s_, **kw)
         else:
+            # HCA: the entries are widened once per call into a workspace allocated here, outside the timing
+            nws = int(B.lib().cskv_prefill_kv8_workspace_size(mode, L.batch, L.N, L.d))
+            ws8 = torch.empty(nws, dtype=torch.uint8, device=t["q"].device) if nws else None
             call = lambda kv, s_: B.compressed_attn_prefill(mode, t["q"], kv, idx, t["win"], L.win_pos0, t["sink"],
-                                                            L.pos0, L.m, L.w, kv_scale=s_, **kw)
+                                                            L.pos0, L.m, L.w, kv_scale=s_,
+                                                            **(dict(kw, workspace=ws8) if s_ is not None else kw))
         ms16 = timed(lambda: call(t["cache.kv"], None))
         ms8 = timed(lambda: call(rows, sc))
         res[tag] = {"bf16_cache_ms": ms16, "fp8_cache_ms": ms8,

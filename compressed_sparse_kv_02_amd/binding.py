@@ -25,7 +25,8 @@ EXPORTS = ("cskv_version", "cskv_status_string", "csa_compress", "hca_compress",
            "cskv_quantize_fp4", "indexer_scores_fp4", "indexer_topk_fp4",
            "cskv_quantize_mxfp4", "indexer_scores_mxfp4", "indexer_topk_mxfp4",
            "cskv_quantize_mxfp8", "indexer_scores_mxfp8", "indexer_topk_mxfp8",
-           "cskv_quantize_kv_fp8", "compressed_attn_prefill_kv8", "compressed_attn_decode_kv8",
+           "cskv_quantize_kv_fp8", "compressed_attn_prefill_kv8", "cskv_prefill_kv8_workspace_size",
+           "compressed_attn_decode_kv8",
            "compressed_attn_prefill",
            "cskv_decode_workspace_size", "compressed_attn_decode", "compressed_attn_decode_noalloc",
            "cskv_lowrank_proj", "cskv_grouped_out_proj")
@@ -58,7 +59,8 @@ _SIGS = {
     "indexer_topk_mxfp8": (_I, [_P, _P, _P, _P, _P, _I, _L, _L, _I, _I, _L, _I, _I, _P, _P, _Z, _P]),
     "cskv_quantize_kv_fp8": (_I, [_P, _I, _L, _I, _I, _I, _P, _P, _L, _P]),
     "compressed_attn_prefill_kv8": (_I, [_I, _P, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
-                                         _I, _P, _F, _I, _F, _F, _I, _P, _P, _P]),
+                                         _I, _P, _F, _I, _F, _F, _I, _P, _Z, _P, _P, _P]),
+    "cskv_prefill_kv8_workspace_size": (_Z, [_I, _I, _L, _I]),
     "compressed_attn_decode_kv8": (_I, [_I, _P, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
                                         _I, _P, _F, _I, _F, _F, _I, _I, _P, _Z, _P, _P, _P]),
     "compressed_attn_prefill": (_I, [_I, _P, _P, _P, _P, _L, _L, _P, _I, _L, _L, _L, _I, _I, _I, _I, _I,
@@ -433,17 +435,24 @@ def compressed_attn_prefill(mode: int, q, kv, idx, win, win_pos0: int, sink, pos
                             w: int, k: int = 0, apply_q_norm: bool = True, q_norm_w=None,
                             eps: float = 1e-6, rope_dims: int = 0, rope_base: float = 10000.0,
                             scale: float = 0.0, rope_on_output: bool = True, out=None, lse=None,
-                            return_lse: bool = False, kv_scale=None):
+                            return_lse: bool = False, kv_scale=None, workspace=None):
     """CSA / HCA attention for a chunk of queries: out [batch, Tq, H, d] (and lse [batch, Tq, H]).
 
     With kv_scale, kv is an FP8 KV cache written by quantize_kv_fp8 ([batch, N, row bytes] uint8).
+    HCA over such a cache widens the entries once into `workspace` (allocated here when None;
+    an empty tensor selects the route that widens each gathered tile instead).
     """
     args, out, lse = _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_norm,
                                   q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output, out, lse,
                                   return_lse)
     if kv_scale is not None:  # FP8 KV storage: kv holds the stored entries (uint8 rows)
+        batch, N = kv.shape[0], kv.shape[1]
+        need = int(lib().cskv_prefill_kv8_workspace_size(mode, batch, N, q.shape[-1]))
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+        ws, ws_bytes = (None, 0) if workspace is None or workspace.numel() == 0 else (workspace, workspace.numel())
         _check("compressed_attn_prefill_kv8", lib().compressed_attn_prefill_kv8(
-            *args[:3], _ptr(kv_scale), *args[3:], _ptr(out), _ptr(lse), _stream(q)))
+            *args[:3], _ptr(kv_scale), *args[3:], _ptr(ws), ws_bytes, _ptr(out), _ptr(lse), _stream(q)))
     else:
         _check("compressed_attn_prefill", lib().compressed_attn_prefill(
             *args, _ptr(out), _ptr(lse), _dtype(q), _stream(q)))

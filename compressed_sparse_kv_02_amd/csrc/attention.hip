@@ -1113,13 +1113,64 @@ extern "C" int compressed_attn_prefill(int mode, const void* q, const void* kv, 
                            dtype, stream);
 }
 
+// FP8 + BF16 stored entries -> bf16 rows: each 8-code chunk widened exactly (E4M3 times the entry's
+// power-of-two scale, the same conversion the attention loader applies), the RoPE dims copied. One
+// wave per entry, 16-byte pieces.
+__global__ __launch_bounds__(256) void dequant_kv8_kernel(const uint8_t* kv, const float* kv_scale, int64_t rows,
+                                                          int d, int rope, uint16_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int nope = d - rope;
+  const uint8_t* src = kv + r * (int64_t)(nope + 2 * rope);
+  uint16_t* dst = out + r * (int64_t)d;
+  const float sc = kv_scale[r];
+  const int nch8 = nope / 8, nch = nch8 + rope / 8;
+  for (int c = lane; c < nch; c += 64) {
+    u32x4 v;
+    if (c < nch8) {
+      const uint2 cc = *reinterpret_cast<const uint2*>(src + 8 * c);
+      v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)cc.x, sc, false));
+      v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)cc.x, sc, true));
+      v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)cc.y, sc, false));
+      v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)cc.y, sc, true));
+    } else {
+      v = *reinterpret_cast<const u32x4*>(src + nope + 16 * (c - nch8));
+    }
+    *reinterpret_cast<u32x4*>(dst + 8 * c) = v;
+  }
+}
+
+// HCA prefill over an FP8 cache: every query of the call reads every visible entry, so the
+// entries are widened once into the workspace and the bf16 kernels run on them.
+extern "C" size_t cskv_prefill_kv8_workspace_size(int mode, int batch, int64_t N, int d) {
+  if (mode != CSKV_MODE_HCA || batch <= 0 || N <= 0 || d <= 0) return 0;
+  return (size_t)batch * (size_t)N * (size_t)d * 2;
+}
+
 extern "C" int compressed_attn_prefill_kv8(int mode, const void* q, const uint8_t* kv, const float* kv_scale,
                                            const int32_t* idx, const void* win, int64_t win_pos0, int64_t W,
                                            const float* sink, int batch, int64_t Tq, int64_t N, int64_t pos0,
                                            int m, int k, int w, int H, int d, int apply_q_norm,
                                            const float* q_norm_w, float eps, int rope_dims, float rope_base,
-                                           float scale, int rope_on_output, void* out, float* lse, void* stream) {
+                                           float scale, int rope_on_output, void* workspace, size_t ws_bytes,
+                                           void* out, float* lse, void* stream) {
   if (N > 0 && !kv_scale) return CSKV_ERR_INVALID_ARG;
+  if (mode == CSKV_MODE_HCA && workspace && N > 0 && batch > 0 && Tq > 0) {
+    int st = validate_attn(mode, q, kv, idx, win, win_pos0, W, sink, batch, Tq, N, pos0, m, k, w, H, d,
+                           apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale, out, lse, CSKV_BF16);
+    if (!st) st = validate_kv8(kv_scale, N, d, rope_dims, CSKV_BF16);
+    if (st) return st;
+    if (!aligned16(workspace)) return CSKV_ERR_MISALIGNED;
+    if (ws_bytes < cskv_prefill_kv8_workspace_size(mode, batch, N, d)) return CSKV_ERR_WORKSPACE;
+    const int64_t rows = (int64_t)batch * N;
+    hipLaunchKernelGGL(dequant_kv8_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, (hipStream_t)stream,
+                       kv, kv_scale, rows, d, rope_dims, (uint16_t*)workspace);
+    if (hipGetLastError() != hipSuccess) return CSKV_ERR_HIP;
+    return attn_prefill_impl(mode, q, workspace, nullptr, idx, win, win_pos0, W, sink, batch, Tq, N, pos0, m, k,
+                             w, H, d, apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output,
+                             out, lse, CSKV_BF16, stream);
+  }
   return attn_prefill_impl(mode, q, kv, N > 0 ? kv_scale : nullptr, idx, win, win_pos0, W, sink, batch, Tq, N,
                            pos0, m, k, w, H, d, apply_q_norm, q_norm_w, eps, rope_dims, rope_base, scale,
                            rope_on_output, out, lse, CSKV_BF16, stream);

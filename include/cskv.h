@@ -440,6 +440,15 @@ int compressed_attn_decode_noalloc(int mode, const void* q, const void* kv, cons
  *   [batch, N]; q, win and out are bf16. The loader widens each entry to
  *   bf16 exactly (E4M3 times a power of two is a bf16 value), so the result
  *   is the bf16 attention over the dequantised entries.
+ *   compressed_attn_prefill_kv8 takes an optional workspace: for HCA (every
+ *   query reads every visible entry) with workspace != NULL, the entries are
+ *   widened once into it (bf16 [batch, N, d], 16-byte aligned,
+ *   cskv_prefill_kv8_workspace_size bytes, else CSKV_ERR_WORKSPACE) and the
+ *   bf16 kernels run on them; the result is bit-identical to the route
+ *   without a workspace, which widens each gathered tile in LDS. CSA ignores
+ *   the workspace (NULL allowed).
+ * cskv_prefill_kv8_workspace_size -- batch * N * d * 2 for HCA, 0 for CSA or
+ *   arguments the call would reject.
  */
 int cskv_quantize_kv_fp8(const void* x, int batch, int64_t n, int d, int rope_dims, int dtype, uint8_t* out,
                          float* scales, int64_t out_ld, void* stream);
@@ -448,7 +457,8 @@ int compressed_attn_prefill_kv8(int mode, const void* q, const uint8_t* kv, cons
                                 const float* sink, int batch, int64_t Tq, int64_t N, int64_t pos0, int m,
                                 int k, int w, int H, int d, int apply_q_norm, const float* q_norm_w,
                                 float eps, int rope_dims, float rope_base, float scale, int rope_on_output,
-                                void* out, float* lse, void* stream);
+                                void* workspace, size_t ws_bytes, void* out, float* lse, void* stream);
+size_t cskv_prefill_kv8_workspace_size(int mode, int batch, int64_t N, int d);
 int compressed_attn_decode_kv8(int mode, const void* q, const uint8_t* kv, const float* kv_scale,
                                const int32_t* idx, const void* win, int64_t win_pos0, int64_t W,
                                const float* sink, int batch, int64_t Tq, int64_t N, int64_t pos0, int m,

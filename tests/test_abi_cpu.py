@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 30, names
+    assert len(names) == 31, names
     for n in names:
         assert hasattr(L, n), n
     from compressed_sparse_kv_02_amd import binding
@@ -247,7 +247,7 @@ def test_kv8_validation(L):
     f = L.compressed_attn_prefill_kv8
     base = dict(mode=0, q=P, kv=P, ks=P, idx=P, win=P, wp0=0, W=64, sink=None, batch=1, Tq=64, N=16,
                 pos0=0, m=4, k=16, w=16, H=64, d=512, qn=1, qnw=None, eps=1e-6, rd=64, rb=1e4,
-                scale=0.0, roo=1, out=P, lse=None, st=None)
+                scale=0.0, roo=1, ws=None, wsb=0, out=P, lse=None, st=None)
 
     def call(**kw):
         a = dict(base, **kw)
@@ -257,6 +257,14 @@ def test_kv8_validation(L):
     assert call(rd=48) == UNSUPPORTED
     assert call(ks=P + 4) == MISALIGNED
     assert call(Tq=0) == OK
+    # HCA with a workspace: the entries are widened into it first, so it is checked before any launch
+    sz = L.cskv_prefill_kv8_workspace_size
+    assert sz(1, 2, 16, 512) == 2 * 16 * 512 * 2 and sz(0, 2, 16, 512) == 0 and sz(1, 0, 16, 512) == 0
+    need = sz(1, 1, 16, 512)
+    assert call(mode=1, ws=P, wsb=need - 1) == WS
+    assert call(mode=1, ws=P + 8, wsb=need) == MISALIGNED
+    assert call(mode=1, ws=P, wsb=need, rd=48) == UNSUPPORTED
+    assert call(mode=0, ws=P, wsb=0, Tq=0) == OK  # CSA ignores the workspace
 
 
 def test_attention_validation(L):

@@ -59,7 +59,8 @@ def test_csa_compress(dtype, c, m, T, pos0, norm, rope):
 @pytest.mark.parametrize("c,m,T,pos0,withZ,norm,rope", [
     (512, 128, 300, 0, True, True, 64), (512, 128, 1024, 128 * 7, True, True, 64), (64, 16, 50, 0, False, True, 16),
     (512, 1, 37, 1000, False, True, 64), (128, 1, 5, 0, True, False, 0), (512, 4096, 4096, 0, True, True, 64),
-    (1024, 1, 9, 3, False, True, 10), (1024, 64, 200, 128, True, True, 64), (40, 8, 100, 16, True, True, 2)])
+    (1024, 1, 9, 3, False, True, 10), (1024, 64, 200, 128, True, True, 64), (40, 8, 100, 16, True, True, 2),
+    (512, 128, 260, 256, False, True, 64), (256, 48, 100, 0, False, False, 0)])
 def test_hca_compress(dtype, c, m, T, pos0, withZ, norm, rope):
     say("hca_compress", dtype, c, m, T, pos0, withZ, norm, rope)
     bt = 2
@@ -657,7 +658,19 @@ def test_attention_kv8_prefill_and_decode(mode, bt, Tq, N, pos0, m, k, w, H, d, 
     idx = torch.from_numpy(_random_idx(bt, Tq, pos0, m, N, k, 4)).to(DEV) if mode == "csa" else None
     md = B.CSA if mode == "csa" else B.HCA
     rows, sc = B.quantize_kv_fp8(kv, rope)
-    o = B.compressed_attn_prefill(md, q, rows, idx, win, wp0, sk, pos0, m, w, k=k, rope_dims=rope, kv_scale=sc)
+    ws = None
+    if mode == "hca":  # entries widened once into a workspace; the tile route must agree bit for bit
+        ws = torch.empty(B.lib().cskv_prefill_kv8_workspace_size(md, bt, N, d), dtype=torch.uint8, device=DEV)
+        ot = B.compressed_attn_prefill(md, q, rows, idx, win, wp0, sk, pos0, m, w, k=k, rope_dims=rope,
+                                       kv_scale=sc, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    o = B.compressed_attn_prefill(md, q, rows, idx, win, wp0, sk, pos0, m, w, k=k, rope_dims=rope, kv_scale=sc,
+                                  workspace=ws)
+    if ws is not None:
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ot.view(torch.int16)), "workspace and tile routes differ"
+        wide = ws.view(torch.bfloat16).view(bt, N, d)
+        for b in range(bt):  # the widened entries are the exact dequantisation
+            assert np.array_equal(np64(wide[b]), _kv8_oracle(kv[b], rope))
     last = Tq - 1
     od = B.compressed_attn_decode(md, q[:, last:].contiguous(), rows, idx[:, last:].contiguous() if idx is not None
                                   else None, win, wp0, sk, pos0 + last, m, w, k=k, rope_dims=rope, kv_scale=sc)
