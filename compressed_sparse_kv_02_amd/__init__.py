@@ -29,6 +29,7 @@ from .binding import (  # noqa: F401
     quantize_kv_fp8,
     compressed_attn_prefill,
     compressed_attn_decode,
+    compressed_attn_decode_noalloc,
     lowrank_proj,
     grouped_out_proj,
 )

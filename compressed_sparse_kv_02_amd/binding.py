@@ -408,10 +408,24 @@ def quantize_kv_fp8(x, rope_dims: int, out=None, scales=None, out_row0: int = 0)
 
 
 def _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_norm, q_norm_w, eps,
-                 rope_dims, rope_base, scale, rope_on_output, out, lse, return_lse):
+                 rope_dims, rope_base, scale, rope_on_output, out, lse, return_lse, kv_scale=None):
     batch, Tq, H, d = q.shape
     N = kv.shape[1]
     W = win.shape[1]
+    # the entries' row width and the per-entry scales bound every gathered row
+    if kv_scale is None:
+        _need(kv.dim() == 3 and kv.shape[2] == d and kv.dtype == q.dtype,
+              f"attention: kv must be {q.dtype} [batch, N, {d}]")
+    else:
+        rb = kv_fp8_row_bytes(d, rope_dims)
+        _need(kv.dim() == 3 and kv.shape[2] == rb and kv.dtype == torch.uint8,
+              f"attention (FP8 cache): kv must be uint8 [batch, N, {rb}]")
+        _need(kv_scale.dtype == torch.float32 and tuple(kv_scale.shape) == (batch, N),
+              f"attention (FP8 cache): kv_scale must be fp32 [{batch}, {N}]")
+    _need(sink is None or (sink.dtype == torch.float32 and sink.numel() == H), f"attention: sink must be fp32 [{H}]")
+    _need(q_norm_w is None or (q_norm_w.dtype == torch.float32 and q_norm_w.numel() == d),
+          f"attention: q_norm_w must be fp32 [{d}]")
+    _need(win.dtype == q.dtype, "attention: win must have q's dtype")
     if out is None:
         out = torch.empty_like(q)
     if lse is None and return_lse:
@@ -444,7 +458,7 @@ def compressed_attn_prefill(mode: int, q, kv, idx, win, win_pos0: int, sink, pos
     """
     args, out, lse = _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_norm,
                                   q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output, out, lse,
-                                  return_lse)
+                                  return_lse, kv_scale)
     if kv_scale is not None:  # FP8 KV storage: kv holds the stored entries (uint8 rows)
         batch, N = kv.shape[0], kv.shape[1]
         need = int(lib().cskv_prefill_kv8_workspace_size(mode, batch, N, q.shape[-1]))
@@ -471,7 +485,7 @@ def compressed_attn_decode(mode: int, q, kv, idx, win, win_pos0: int, sink, pos0
     """Split-K attention of a few new tokens against a long cache (same result as prefill)."""
     args, out, lse = _attn_common(mode, q, kv, idx, win, win_pos0, sink, pos0, m, k, w, apply_q_norm,
                                   q_norm_w, eps, rope_dims, rope_base, scale, rope_on_output, out, lse,
-                                  return_lse)
+                                  return_lse, kv_scale)
     batch, Tq, H, d = q.shape
     need = decode_workspace_bytes(batch, Tq, H, d, n_splits)
     if workspace is None or workspace.numel() < need:
