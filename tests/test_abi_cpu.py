@@ -355,6 +355,34 @@ def test_binding_rejects_appends_past_the_cache():
         binding.csa_compress(x, x, x, x, B, 4, out=cache, out_row0=6)
 
 
+def test_binding_rejects_mismatched_attention_buffers():
+    # entry rows, FP8 scales, sinks and norm weights bound what the kernels read: checked first
+    import torch
+    from compressed_sparse_kv_02_amd import binding
+    bt, Tq, H, d, N = 2, 4, 8, 64, 12
+    q = torch.zeros(bt, Tq, H, d)
+    win = torch.zeros(bt, 16, d)
+    kv = torch.zeros(bt, N, d)
+    call = lambda **kw: binding.compressed_attn_prefill(binding.HCA, q, kw.pop("kv", kv), None, win, 0,
+                                                        kw.pop("sink", None), 0, 4, 16, **kw)
+    with pytest.raises(binding.CskvError, match="kv must be"):
+        call(kv=torch.zeros(bt, N, d + 8))
+    with pytest.raises(binding.CskvError, match="kv must be"):
+        call(kv=torch.zeros(bt, N, d, dtype=torch.bfloat16))
+    with pytest.raises(binding.CskvError, match="sink"):
+        call(sink=torch.zeros(H + 1))
+    with pytest.raises(binding.CskvError, match="q_norm_w"):
+        call(q_norm_w=torch.zeros(d - 1))
+    rb = binding.kv_fp8_row_bytes(d, 16)
+    kv8 = torch.zeros(bt, N, rb, dtype=torch.uint8)
+    with pytest.raises(binding.CskvError, match="kv must be uint8"):
+        call(kv=torch.zeros(bt, N, rb + 16, dtype=torch.uint8), kv_scale=torch.zeros(bt, N), rope_dims=16)
+    with pytest.raises(binding.CskvError, match="kv_scale"):
+        call(kv=kv8, kv_scale=torch.zeros(bt, N - 1), rope_dims=16)
+    with pytest.raises(binding.CskvError, match="not on the GPU"):  # consistent buffers reach the device check
+        call()
+
+
 def test_decode_workspace_size_follows_the_split_policy(L):
     f = L.cskv_decode_workspace_size
     per = lambda b, tq, s, H=64, d=512: b * tq * s * H * (d + 2) * 4
