@@ -490,6 +490,57 @@ def lowp_indexer_rows(prefill, tp, decode, td, reps: int = 3):
     return out
 
 
+def decode_step_lowp_rows(decode, td, bf16_ms: float, steps: int = 20):
+    """The whole decode step with the CSA layer's indexer on MX-FP4 or MX-FP8 keys (the pages' V4
+    and V3.2 indexer precisions): the key cache is stored quantised (quantised once, outside the
+    timing, as a cache written in that format would be), and each step quantises its queries, then
+    scores and selects with indexer_topk_mx*; everything else is the bf16 step's. Timed with
+    events around `steps` whole steps."""
+    import torch
+    from compressed_sparse_kv_02_amd import binding as B
+    from compressed_sparse_kv_02_amd import layer as LY
+
+    out = {}
+    Lc, tc = decode[0], td[0]
+    for fmt, quant, topk, bits in (("mxfp4", B.quantize_mxfp4, B.indexer_topk_mxfp4, 4),
+                                   ("mxfp8", B.quantize_mxfp8, B.indexer_topk_mxfp8, 8)):
+        kc, ks = quant(tc["cache.ik"])
+        ws = torch.empty(max(16, B.indexer_workspace_bytes(Lc.batch, Lc.T, Lc.N, Lc.HI, Lc.k,
+                                                             B.MXFP4 if bits == 4 else B.MXFP8)),
+                         dtype=torch.uint8, device=tc["q"].device)
+
+        def step():
+            LY.compress_step(Lc, tc)
+            qc, qs = quant(tc["qI"])
+            topk(qc, qs, tc["wI"], kc, ks, Lc.pos0, Lc.m, Lc.k, out=tc["idx"], workspace=ws)
+            LY.attend_step(Lc, tc)
+            for L, t in zip(decode[1:], td[1:]):
+                LY.run_layer(L, t)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / steps
+        # the bf16 step's bytes with the indexer keys and queries at the format's size (codes plus
+        # one E8M0 scale byte per 32 values)
+        per = lambda n: n * bits // 8 + n // 32
+        by = decode_step_bytes(decode) - Lc.batch * (Lc.N + Lc.HI) * Lc.dI * 2 + \
+            Lc.batch * (Lc.N + Lc.HI) * per(Lc.dI)
+        out[f"decode_step_{fmt}_indexer"] = {
+            "ms": ms, "query_tokens_per_s": Lc.batch / (ms / 1e3), "algorithmic_bytes": by,
+            "achieved_GBps": by / (ms / 1e3) / 1e9, "frac_hbm": by / (ms / 1e3) / PEAK_HBM_BYTES,
+            "bf16_step_ms": bf16_ms}
+        del kc, ks, ws
+    LY.select_step(Lc, tc)  # leave the bf16 selection in place
+    return out
+
+
 def kv_fp8_attention_rows(prefill, tp, decode, td, reps: int = 3):
     """Attention over FP8 + BF16 stored entries beside the bf16 cache, same inputs.
 
@@ -772,7 +823,8 @@ def main():
         out["configs"] = prefill_config_rows()
     if not args.no_next_rows:
         out["next_rows"] = dict(lowp_indexer_rows(prefill, tp, decode, td), projections=projection_rows(prefill),
-                                kv_fp8_attention=kv_fp8_attention_rows(prefill, tp, decode, td))
+                                kv_fp8_attention=kv_fp8_attention_rows(prefill, tp, decode, td),
+                                **decode_step_lowp_rows(decode, td, dec_ms))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(prefill, decode, tp, td, args.cpu_budget)
     print(json.dumps(out), flush=True)
