@@ -40,3 +40,23 @@ def test_decode_step_and_attention_counts():
     assert bench.attn_pairs(L) == 3 * (2 + 2) and bench.attn_flops(L) == 4 * 2 * 64 * 12
     Lc = LY.LayerCall("csa", 1, 3, 8, 2, d=64, H=2, m=4, w=2, k=1)
     assert bench.attn_pairs(Lc) == 3 * (1 + 2)
+
+
+def test_kernel_table_from_a_trace(tmp_path):
+    # one line per library kernel and launch grid, torch's own kernels left out, times in us
+    p = tmp_path / "run_kernel_trace.csv"
+    rows = [("void cskv::attn_mfma<512, 4, 1, -1, 1>(cskv::AttnArgs)", 256, 144, 1, 1000, 25000),
+            ("void cskv::attn_mfma<512, 4, 1, -1, 1>(cskv::AttnArgs)", 256, 144, 1, 30000, 53000),
+            ("void cskv::attn_merge<cskv::bf16>(cskv::AttnArgs)", 256, 512, 1, 60000, 68000),
+            ("void at::native::vectorized_elementwise_kernel<4>(int)", 128, 4, 1, 0, 900)]
+    with open(p, "w") as f:
+        f.write("Kernel_Name,Grid_Size_X,Grid_Size_Y,Grid_Size_Z,Start_Timestamp,End_Timestamp\n")
+        for n, x, y, z, a, b in rows:
+            f.write(f'"{n}",{x},{y},{z},{a},{b}\n')
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--kernel-table", str(p)],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("| `")]
+    assert len(lines) == 2
+    assert lines[0].startswith("| `attn_mfma<512, 4, 1, -1, 1>` | 36864 | decode CSA attention (18 splits) | 2 | 23.5 | 23.0 | 24.0 |")
+    assert lines[1].startswith("| `attn_merge<bf16>` | 131072 | decode split merge | 1 | 8.0 |")
