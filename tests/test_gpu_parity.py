@@ -553,6 +553,10 @@ def _random_idx(bt, Tq, pos0, m, N, k, seed):
     ("bf16", "csa", 2, 10, 300, 4 * 290, 4, 64, 16, 64, 512, 64, False, True),  # three key tiles (64 + 16 keys)
     ("bf16", "hca", 2, 33, 150, 128 * 120, 128, 0, 64, 32, 512, 64, True, True),  # odd Tq: a half-empty 2-query block
     ("bf16", "csa", 1, 12, 300, 4 * 250, 4, 128, 32, 40, 512, 64, True, True),  # 40 heads: a partly empty head group
+    # HCA with 49-64 heads of 512 dims: window-only rows from position 0, a partly empty head group without
+    # sinks, and a two-tile key list with RoPE on 16 dims and no output de-rotation
+    ("bf16", "hca", 1, 70, 5, 0, 128, 0, 16, 56, 512, 64, True, True),
+    ("bf16", "hca", 2, 20, 40, 128 * 30, 128, 0, 24, 50, 512, 16, False, False),
 ])
 def test_attention_prefill(dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink):
     say("attention", dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink)
