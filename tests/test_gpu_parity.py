@@ -557,6 +557,9 @@ def _random_idx(bt, Tq, pos0, m, N, k, seed):
     # sinks, and a two-tile key list with RoPE on 16 dims and no output de-rotation
     ("bf16", "hca", 1, 70, 5, 0, 128, 0, 16, 56, 512, 64, True, True),
     ("bf16", "hca", 2, 20, 40, 128 * 30, 128, 0, 24, 50, 512, 16, False, False),
+    # 32 heads: four queries per workgroup, the last block with 2 of 4 queries
+    ("bf16", "hca", 1, 6, 80, 128 * 60, 128, 0, 128, 32, 512, 64, True, True),
+    ("bf16", "hca", 2, 13, 50, 128 * 20, 128, 0, 32, 24, 512, 32, True, False),
 ])
 def test_attention_prefill(dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink):
     say("attention", dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink)
