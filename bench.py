@@ -168,7 +168,7 @@ KERNEL_ROLES = {
     ("indexer_score_mfma<2, 8>", 4194304): "64K CSA scoring",
     ("topk_select", 4194304): "chunk CSA top-k (8192 rows)",
     ("topk_select", 33554432): "64K CSA top-k (65536 rows)",
-    ("attn_mfma<512, 2, 4, -1, 1>", 1048576): "16K HCA attention (32 heads, 4 queries per workgroup)",
+    ("attn_mfma<512, 2, 4, -1, 1>", 2097152): "16K HCA attention (32 heads, 4 queries per workgroup)",
     ("indexer_score_stream<2, 8>", 262144): "decode CSA scoring (8 x 262144 keys)",
     ("compress_block_kernel<bf16, 8, 1, 8>", 32768): "chunk HCA compression (2 x 32 entries of 128 rows)",
     ("compress_rows_kernel<bf16, 8, 1, 4>", 131072): "chunk window rows (2 x 4096)",
