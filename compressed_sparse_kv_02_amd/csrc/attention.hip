@@ -938,9 +938,10 @@ __global__ __launch_bounds__(256) void attn_f32(AttnArgs a) {
 template <int D, int HW, int QG, int KVR>
 static void launch_kvr(const AttnArgs& a, dim3 grid, hipStream_t st) {
   if constexpr (KVR <= D) {
-    // 256-thread workgroups over bf16 entries, not split (CSA prefill with 64 heads, HCA prefill
-    // with up to 32 heads and two queries per workgroup): two per CU, so the compiler keeps each
-    // lane within 256 registers; built for one per CU they took twice that and ran alone on the CU
+    // 256-thread workgroups over bf16 entries, not split (CSA prefill with 49-64 heads; HCA
+    // prefill with 17-32 heads and two queries per workgroup, taken for calls of 2-3 queries):
+    // two per CU, so the compiler keeps each lane within 256 registers; built for one per CU they
+    // took twice that and ran alone on the CU
     if constexpr (D == 512 && HW * QG == 4) {
       if (a.n_splits == 1) {
         hipLaunchKernelGGL((attn_mfma<D, HW, QG, KVR, 2>), grid, dim3(HW * QG * 64), 0, st, a);
