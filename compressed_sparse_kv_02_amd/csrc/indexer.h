@@ -53,6 +53,18 @@ inline bool bm_route(int64_t vmin, int64_t vmax, int k) {
 // (negative floats, -0.0 included, are negative as int32). One VALU op, no NaN canonicalisation.
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// Largest of x over each 32-lane half of the wave, in every lane: quad swaps, the half-row and
+// row mirrors (DPP), then a swap between rows 0-1 and 2-3.
+__device__ __forceinline__ uint32_t max_key32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));  // 7 - lane (8s)
+  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));  // 15 - lane (16s)
+  const auto sw = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return max(sw[0], sw[1]);
+}
+
+
 // Scores of rows [a.row0, a.row0 + a.nrows) into a.scores; bf16 takes qb
 // queries per workgroup (8 for prefill, 1 for decode).
 int launch_scores(IdxArgs& a, int batch, int qb, int dtype, hipStream_t st);

@@ -215,17 +215,6 @@ __global__ __launch_bounds__(512) void indexer_score_mfma(IdxArgs a) {
 // dimension is permuted the same way in A and B (lane half h, k-step ks: dims
 // h*8*KS + 8*ks .. +8), so each lane reads one contiguous half row from LDS;
 // every dot product is unchanged.
-// Largest of x over each 32-lane half of the wave, in every lane: quad swaps, the half-row and
-// row mirrors (DPP), then a swap between rows 0-1 and 2-3.
-__device__ __forceinline__ uint32_t max_key32(uint32_t x) {
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false));   // lane ^ 1
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false));   // lane ^ 2
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false));  // 7 - lane (8s)
-  x = max(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x140, 0xF, 0xF, false));  // 15 - lane (16s)
-  const auto sw = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  return max(sw[0], sw[1]);
-}
-
 template <int HT, int KS>
 __global__ __launch_bounds__(256) void indexer_score_stream(IdxArgs a) {
   constexpr int DI = 16 * KS;

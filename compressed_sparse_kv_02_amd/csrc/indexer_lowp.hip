@@ -514,7 +514,12 @@ __global__ __launch_bounds__(256) void indexer_score_lowp_stream(IdxArgs a) {
       for (int i = 0; i < 16; ++i) part = __builtin_fmaf(relu_bits(acc[ht][i]), wv[ht][i], part);
     part += __shfl_xor(part, 32, 64);
     const int64_t s = key_of(blk);
-    if (lane < 32 && s < vj) srow[s] = MX ? part : part * sc;
+    const float sval = MX ? part : part * sc;
+    if (lane < 32 && s < vj) srow[s] = sval;
+    if (a.bm_fused) {  // the block's maximum key, for the selection (as the bf16 decode scorer)
+      const uint32_t mk = max_key32(s < vj ? score_key(sval) : 0u);
+      if (lane == 0) a.bm[((int64_t)b * a.bm_rows + jr) * a.bm_ld + (s >> 5)] = mk;
+    }
   };
 
 #pragma unroll
@@ -710,6 +715,16 @@ static int topk_lowp(int dtype, const uint8_t* qI, const float* q_scale, const f
     const int64_t last = pos0 + r0 + a.nrows - 1;
     int64_t vmax = (last + 1) / m;
     if (vmax > N) vmax = N;
+    int64_t vmin = (pos0 + r0 + 1) / m;
+    if (vmin > N) vmin = N;
+    // few long rows scored one query per workgroup (decode): the scorer writes the block maxima
+    // into the rows' selection workspace, and the selection reads them
+    a.bm_fused = p.qb == 1 && sel_ws && bm_route(vmin, vmax, k);
+    if (a.bm_fused) {
+      a.bm = reinterpret_cast<uint32_t*>(sel_ws);
+      a.bm_ld = topk_sel_stride() / 4;
+      a.bm_rows = a.nrows;
+    }
     if (vmax > k) {  // rows with V_t <= k need no scores
       st = launch_scores_lowp(a, batch, (int)p.qb, dtype, hs);
       if (st) return st;
