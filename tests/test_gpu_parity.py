@@ -560,6 +560,7 @@ def _random_idx(bt, Tq, pos0, m, N, k, seed):
     # 32 heads: four queries per workgroup, the last block with 2 of 4 queries
     ("bf16", "hca", 1, 6, 80, 128 * 60, 128, 0, 128, 32, 512, 64, True, True),
     ("bf16", "hca", 2, 13, 50, 128 * 20, 128, 0, 32, 24, 512, 32, True, False),
+    ("bf16", "hca", 2, 3, 70, 128 * 60, 128, 0, 128, 32, 512, 64, True, True),  # 3 queries: two per workgroup
 ])
 def test_attention_prefill(dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink):
     say("attention", dtype, mode, bt, Tq, N, pos0, m, k, w, H, d, rope, roo, sink)
